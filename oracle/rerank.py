@@ -1,0 +1,42 @@
+"""The whole reranking path for one draft block, step by step.
+
+LiLiCorr paper, Section 3.5: one network pass produces every in and out
+vector, the pair scores are batched products, and a greedy walk commits the
+block left to right. Blocks are independent.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .topk_lse import topk_lse
+from .encoder import encode_block
+from .scores import pair_scores
+from .walk import greedy_walk, WalkResult
+from .weights import OracleWeights
+
+
+@dataclass
+class BlockResult:
+    idx: np.ndarray        # int64 [B, K]
+    logp: np.ndarray       # float32 [B, K]
+    lse: np.ndarray        # float64 [B]
+    outv: np.ndarray       # float64 [B, K, d_e] (bf16 values)
+    inv: np.ndarray        # float64 [B, K, d_e]
+    cos: np.ndarray        # float32 [B-1, K, K]
+    walk: WalkResult
+
+    @property
+    def tokens(self) -> np.ndarray:
+        return self.walk.tokens
+
+
+def rerank_block(logits_block: np.ndarray, K: int, w: OracleWeights, alpha: float = 1.0,
+                 use_logp: bool = True, trace: dict | None = None) -> BlockResult:
+    """logits_block: [B, V] float32 values or uint16 bfloat16 bit patterns."""
+    idx, logp, lse = topk_lse(logits_block, K)
+    outv, inv = encode_block(idx, logp, w, trace)
+    cos = pair_scores(outv, inv)
+    walk = greedy_walk(idx, logp, cos, alpha, use_logp)
+    return BlockResult(idx, logp, lse, outv, inv, cos, walk)

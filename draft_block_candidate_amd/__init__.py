@@ -1,0 +1,329 @@
+"""Python binding of liblilicorr.so, the gfx950 LiLiCorr reranking library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch provides device memory and the current stream. The entry
+points and their contracts are those of include/lilicorr.h. Importing this
+module does not need a GPU; calling a compute entry point without the built
+library raises ``LilicorrUnavailable``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblilicorr.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EWEIGHTS, EHIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+EPI_F32, EPI_BF16, EPI_SILU_BF16, EPI_RESID_F32 = 0, 1, 2, 3
+ABI_VERSION = 1
+MAX_SLOTS, MAX_TOPK, MAX_LATTICE = 64, 64, 512
+
+
+class LilicorrUnavailable(RuntimeError):
+    pass
+
+
+class LilicorrError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("heads", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("d_e", ctypes.c_int32), ("layers", ctypes.c_int32)]
+
+
+class WeightsDesc(ctypes.Structure):
+    _fields_ = [("dims", Dims), ("vocab", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("dev", ctypes.c_void_p), ("bytes", ctypes.c_size_t)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("num_blocks", ctypes.c_int32),
+                ("logits_dtype", ctypes.c_int32), ("alpha", ctypes.c_float),
+                ("use_logp", ctypes.c_int32), ("weights", ctypes.POINTER(WeightsDesc)),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stream", ctypes.c_void_p),
+                ("dbg_topk_idx", ctypes.c_void_p), ("dbg_topk_logp", ctypes.c_void_p),
+                ("dbg_lse", ctypes.c_void_p), ("dbg_outv", ctypes.c_void_p),
+                ("dbg_inv", ctypes.c_void_p), ("dbg_cos", ctypes.c_void_p),
+                ("dbg_score", ctypes.c_void_p), ("dbg_gap", ctypes.c_void_p)]
+
+
+_c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_SIGNATURES = {
+    "lilicorr_rerank": (_c_int, [_vp, _c_int, _c_int, _c_int, ctypes.POINTER(Params), _vp]),
+    "lilicorr_validate": (_c_int, [_vp, _c_int, _c_int, _c_int, ctypes.POINTER(Params), _vp]),
+    "lilicorr_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Dims)]),
+    "lilicorr_weights_bytes": (_c_size, [ctypes.POINTER(Dims), _c_int]),
+    "lilicorr_weights_init": (_c_int, [ctypes.POINTER(WeightsDesc), _vp]),
+    "lilicorr_weights_tensor": (_c_int, [ctypes.POINTER(Dims), _c_int, _c_int, ctypes.POINTER(_c_size),
+                                         ctypes.POINTER(_c_size), ctypes.POINTER(_c_int)]),
+    "lilicorr_strerror": (ctypes.c_char_p, [_c_int]),
+    "lilicorr_topk_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "lilicorr_topk_lse": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp, _vp, _vp]),
+    "lilicorr_pair_scores": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "lilicorr_greedy_walk": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _f, _c_int, _vp, _vp, _vp, _vp]),
+    "lilicorr_linear": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp]),
+    "lilicorr_rmsnorm": (_c_int, [_vp, _c_int, _c_int, _vp, _f, _vp, _vp]),
+    "lilicorr_lattice_attention": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load liblilicorr.so (built in-tree by draft_block_candidate_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LilicorrUnavailable(
+                f"{LIB_PATH} is missing: build it with `python -m draft_block_candidate_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().lilicorr_strerror(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != OK:
+        raise LilicorrError(code, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require_cuda(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass(frozen=True)
+class EncoderDims:
+    hidden: int
+    heads: int
+    ffn: int
+    d_e: int
+    layers: int = 2
+
+    def c(self) -> Dims:
+        return Dims(self.hidden, self.heads, self.ffn, self.d_e, self.layers)
+
+
+def weights_bytes(dims: EncoderDims, vocab: int) -> int:
+    d = dims.c()
+    return int(lib().lilicorr_weights_bytes(ctypes.byref(d), vocab))
+
+
+def workspace_bytes(N: int, B: int, V: int, K: int, dims: EncoderDims) -> int:
+    d = dims.c()
+    return int(lib().lilicorr_workspace_bytes(N, B, V, K, ctypes.byref(d)))
+
+
+def weights_tensor_info(dims: EncoderDims, vocab: int, tensor_id: int):
+    d = dims.c()
+    off, n, dt = _c_size(), _c_size(), _c_int()
+    _check(lib().lilicorr_weights_tensor(ctypes.byref(d), vocab, tensor_id, ctypes.byref(off),
+                                         ctypes.byref(n), ctypes.byref(dt)), "weights_tensor")
+    return int(off.value), int(n.value), int(dt.value)
+
+
+class Weights:
+    """Device blob of synthetic encoder weights, filled by lilicorr_weights_init."""
+
+    def __init__(self, dims: EncoderDims, vocab: int, seed: int = 42, device="cuda"):
+        torch = _torch()
+        self.dims, self.vocab, self.seed = dims, vocab, seed
+        nbytes = weights_bytes(dims, vocab)
+        if nbytes == 0:
+            raise LilicorrError(EUNSUPPORTED, "weights_bytes")
+        self.blob = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.desc = WeightsDesc(dims.c(), vocab, seed, ctypes.c_void_p(self.blob.data_ptr()), nbytes)
+        _check(lib().lilicorr_weights_init(ctypes.byref(self.desc), _stream()), "weights_init")
+
+    def tensor(self, tensor_id: int):
+        """View of one stored tensor (bf16 as torch.bfloat16, else float32), flat."""
+        torch = _torch()
+        off, n, dt = weights_tensor_info(self.dims, self.vocab, tensor_id)
+        size = 2 if dt == BF16 else 4
+        raw = self.blob[off:off + n * size]
+        return raw.view(torch.bfloat16) if dt == BF16 else raw.view(torch.float32)
+
+
+def _logits_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError("logits must be bfloat16 or float32")
+
+
+class Workspace:
+    """Reusable device scratch for rerank calls of one shape."""
+
+    def __init__(self, N, B, V, K, dims: EncoderDims, device="cuda"):
+        torch = _torch()
+        self.nbytes = workspace_bytes(N, B, V, K, dims)
+        if self.nbytes == 0:
+            raise LilicorrError(EINVAL, "workspace_bytes")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+
+def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1.0, use_logp=True,
+                stream=None, dbg=None) -> Params:
+    p = Params()
+    p.abi_version = ABI_VERSION
+    p.num_blocks = N
+    p.logits_dtype = logits_dtype
+    p.alpha = alpha
+    p.use_logp = 1 if use_logp else 0
+    p.weights = ctypes.pointer(weights.desc)
+    p.workspace = ctypes.c_void_p(workspace.buf.data_ptr())
+    p.workspace_bytes = workspace.nbytes
+    p.stream = stream if stream is not None else _stream()
+    for k, v in (dbg or {}).items():
+        setattr(p, "dbg_" + k, ctypes.c_void_p(v.data_ptr()))
+    return p
+
+
+def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool = True,
+           workspace: Workspace | None = None, debug: bool = False, out=None):
+    """Rerank [N, B, V] device logits; returns int32 tokens [N, B] (and debug tensors)."""
+    torch = _torch()
+    _require_cuda(logits, "logits")
+    N, B, V = logits.shape
+    dev = logits.device
+    if workspace is None:
+        workspace = Workspace(N, B, V, K, weights.dims, device=dev)
+    if out is None:
+        out = torch.empty((N, B), dtype=torch.int32, device=dev)
+    dbg = None
+    if debug:
+        de = weights.dims.d_e
+        dbg = {
+            "topk_idx": torch.empty((N, B, K), dtype=torch.int32, device=dev),
+            "topk_logp": torch.empty((N, B, K), dtype=torch.float32, device=dev),
+            "lse": torch.empty((N, B), dtype=torch.float32, device=dev),
+            "outv": torch.empty((N, B, K, de), dtype=torch.bfloat16, device=dev),
+            "inv": torch.empty((N, B, K, de), dtype=torch.bfloat16, device=dev),
+            "cos": torch.empty((N, max(B - 1, 1), K, K), dtype=torch.float32, device=dev),
+            "score": torch.empty((N, B), dtype=torch.float32, device=dev),
+            "gap": torch.empty((N, B), dtype=torch.float32, device=dev),
+        }
+    p = make_params(N, _logits_dtype(logits), weights, workspace, alpha, use_logp, dbg=dbg)
+    _check(lib().lilicorr_rerank(_ptr(logits), B, V, K, ctypes.byref(p), _ptr(out)), "rerank")
+    return (out, dbg) if debug else out
+
+
+def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
+             weights_desc: WeightsDesc | None, workspace_ptr: int, workspace_nbytes: int,
+             out_ptr: int, abi_version: int = ABI_VERSION, use_logp: int = 1) -> int:
+    """Host-only argument check of rerank (no GPU needed); returns the status code."""
+    p = Params()
+    p.abi_version = abi_version
+    p.num_blocks = N
+    p.logits_dtype = logits_dtype
+    p.alpha = 1.0
+    p.use_logp = use_logp
+    p.weights = ctypes.pointer(weights_desc) if weights_desc is not None else None
+    p.workspace = ctypes.c_void_p(workspace_ptr)
+    p.workspace_bytes = workspace_nbytes
+    return int(lib().lilicorr_validate(ctypes.c_void_p(logits_ptr), B, V, K, ctypes.byref(p),
+                                       ctypes.c_void_p(out_ptr)))
+
+
+def topk_lse(logits2d, K: int):
+    """Fused log-partition + exact top-K of [rows, V] device logits."""
+    torch = _torch()
+    _require_cuda(logits2d, "logits")
+    rows, V = logits2d.shape
+    nbytes = int(lib().lilicorr_topk_workspace_bytes(rows, V, K))
+    if nbytes == 0:
+        raise LilicorrError(EINVAL, "topk_workspace_bytes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=logits2d.device)
+    idx = torch.empty((rows, K), dtype=torch.int32, device=logits2d.device)
+    logp = torch.empty((rows, K), dtype=torch.float32, device=logits2d.device)
+    lse = torch.empty((rows,), dtype=torch.float32, device=logits2d.device)
+    _check(lib().lilicorr_topk_lse(_ptr(logits2d), rows, V, K, _logits_dtype(logits2d), _ptr(ws), nbytes,
+                                   _ptr(idx), _ptr(logp), _ptr(lse), _stream()), "topk_lse")
+    return idx, logp, lse
+
+
+def pair_scores(outv, inv):
+    """outv, inv: [N, B, K, d_e] bf16 device tensors -> cos [N, B-1, K, K] float32."""
+    torch = _torch()
+    _require_cuda(outv, "outv")
+    _require_cuda(inv, "inv")
+    N, B, K, de = outv.shape
+    cos = torch.empty((N, B - 1, K, K), dtype=torch.float32, device=outv.device)
+    _check(lib().lilicorr_pair_scores(_ptr(outv), _ptr(inv), N, B, K, de, _ptr(cos), _stream()),
+           "pair_scores")
+    return cos
+
+
+def greedy_walk(topk_idx, topk_logp, cos, alpha: float = 1.0, use_logp: bool = True):
+    """Greedy commit; returns (tokens int32 [N,B], score, gap float32 [N,B])."""
+    torch = _torch()
+    N, B, K = topk_idx.shape
+    dev = topk_idx.device
+    out = torch.empty((N, B), dtype=torch.int32, device=dev)
+    score = torch.empty((N, B), dtype=torch.float32, device=dev)
+    gap = torch.empty((N, B), dtype=torch.float32, device=dev)
+    _check(lib().lilicorr_greedy_walk(_ptr(topk_idx), _ptr(topk_logp), _ptr(cos), N, B, K, alpha,
+                                      1 if use_logp else 0, _ptr(out), _ptr(score), _ptr(gap), _stream()),
+           "greedy_walk")
+    return out, score, gap
+
+
+def linear(A, W, bias=None, epilogue: int = EPI_F32, resid=None):
+    """Y = A W^T + bias on MFMA with the given epilogue; A [M, Kd], W [N, Kd] bf16."""
+    torch = _torch()
+    M, Kd = A.shape
+    N = W.shape[0]
+    if epilogue in (EPI_F32, EPI_RESID_F32):
+        out = resid if (epilogue == EPI_RESID_F32 and resid is not None) else torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _check(lib().lilicorr_linear(_ptr(A), M, Kd, _ptr(W), N, _ptr(bias), epilogue, _ptr(resid), _ptr(out),
+                                 _stream()), "linear")
+    return out
+
+
+def rmsnorm(x, gamma, eps: float = 1e-6):
+    torch = _torch()
+    M, H = x.shape
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _check(lib().lilicorr_rmsnorm(_ptr(x), M, H, _ptr(gamma), eps, _ptr(out), _stream()), "rmsnorm")
+    return out
+
+
+def lattice_attention(qkv, N: int, B: int, K: int, hidden: int, heads: int, dist, same):
+    torch = _torch()
+    out = torch.empty((N * B * K, hidden), dtype=torch.bfloat16, device=qkv.device)
+    _check(lib().lilicorr_lattice_attention(_ptr(qkv), N, B, K, hidden, heads, _ptr(dist), _ptr(same),
+                                            _ptr(out), _stream()), "lattice_attention")
+    return out

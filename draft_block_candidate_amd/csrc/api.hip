@@ -1,0 +1,291 @@
+// C ABI of the library: argument checks, workspace carve-up and the launch
+// sequence of the reranking path. See include/lilicorr.h for the contract.
+#include <atomic>
+#include <cstring>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "layout.hpp"
+#include "lilicorr.h"
+
+using namespace ll;
+
+namespace {
+
+constexpr float kRmsEps = 1e-6f;
+
+bool dims_supported(const lilicorr_dims* d) {
+  if (!d) return false;
+  if (d->layers != 2) return false;
+  if (d->hidden < 64 || d->hidden > 4096 || d->hidden % 64) return false;
+  if (d->heads < 1 || d->hidden % d->heads) return false;
+  const int dh = d->hidden / d->heads;
+  if (dh != 32 && dh != 64 && dh != 128) return false;
+  if (d->ffn < 64 || d->ffn > 16384 || d->ffn % 64) return false;
+  if (d->d_e < 32 || d->d_e > 512 || d->d_e % 32) return false;
+  return true;
+}
+
+bool sizes_ok(int N, int B, int V, int K) {
+  if (N < 1 || B < 1 || B > LILICORR_MAX_SLOTS || K < 1 || K > LILICORR_MAX_TOPK) return false;
+  if (V < K) return false;
+  if (B * K > LILICORR_MAX_LATTICE) return false;
+  // row-local indices and per-launch grid sizes stay within 32 bits
+  if ((int64_t)N * B * K > (int64_t)1 << 30) return false;
+  return true;
+}
+
+// gfx950 check, once per device (the code objects are built for gfx950 only).
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LILICORR_EHIP;
+  if (dev < 0 || dev >= 64) return LILICORR_EUNSUPPORTED;
+  int st = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LILICORR_EHIP;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? LILICORR_OK : LILICORR_EUNSUPPORTED;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LILICORR_OK : LILICORR_EHIP; }
+
+#define LL_TRY(expr)                                \
+  do {                                              \
+    hipError_t _e = (expr);                         \
+    if (_e != hipSuccess) return LILICORR_EHIP;     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* lilicorr_strerror(int code) {
+  switch (code) {
+    case LILICORR_OK: return "ok";
+    case LILICORR_EINVAL: return "invalid argument";
+    case LILICORR_EUNSUPPORTED: return "unsupported dtype, geometry or device (gfx950 only)";
+    case LILICORR_EWORKSPACE: return "workspace missing or too small";
+    case LILICORR_EWEIGHTS: return "weights do not match the requested dims/vocabulary";
+    case LILICORR_EHIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t lilicorr_weights_bytes(const lilicorr_dims* dims, int V) {
+  if (!dims_supported(dims) || V < 1) return 0;
+  return weights_total_bytes(*dims, V);
+}
+
+int lilicorr_weights_tensor(const lilicorr_dims* dims, int V, int id, size_t* offset_bytes,
+                            size_t* numel, int* dtype) {
+  if (!dims_supported(dims) || V < 1) return LILICORR_EINVAL;
+  auto specs = weight_specs(*dims, V);
+  const TensorSpec* s = find_spec(specs, id);
+  if (!s) return LILICORR_EINVAL;
+  if (offset_bytes) *offset_bytes = s->offset;
+  if (numel) *numel = s->numel();
+  if (dtype) *dtype = s->kind == WK_BF16 ? LILICORR_BF16 : LILICORR_F32;
+  return LILICORR_OK;
+}
+
+size_t lilicorr_workspace_bytes(int N, int B, int V, int K, const lilicorr_dims* dims) {
+  if (!sizes_ok(N, B, V, K) || !dims_supported(dims)) return 0;
+  return rerank_ws_layout(N, B, V, K, *dims).total;
+}
+
+size_t lilicorr_topk_workspace_bytes(int rows, int V, int K) {
+  if (rows < 1 || K < 1 || K > LILICORR_MAX_TOPK || V < K) return 0;
+  return topk_ws_layout(rows, V, K).total;
+}
+
+int lilicorr_weights_init(lilicorr_weights* w, void* stream) {
+  if (!w) return LILICORR_EINVAL;
+  if (w->vocab < 1) return LILICORR_EINVAL;
+  if (!dims_supported(&w->dims)) return LILICORR_EUNSUPPORTED;
+  if (!w->dev || ((uintptr_t)w->dev & 255)) return LILICORR_EINVAL;
+  if (w->bytes < weights_total_bytes(w->dims, w->vocab)) return LILICORR_EWEIGHTS;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  auto specs = weight_specs(w->dims, w->vocab);
+  for (const auto& s : specs) {
+    // splitmix64 of seed ^ (t << 40): the per-tensor key (host side)
+    uint64_t z = (w->seed ^ ((uint64_t)s.id << 40)) + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    const uint64_t key = z ^ (z >> 31);
+    LL_TRY(launch_weights_init((char*)w->dev + s.offset, s.numel(), key, s.kind, s.scale,
+                               (hipStream_t)stream));
+  }
+  return LILICORR_OK;
+}
+
+int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_params* p,
+                      const int32_t* out_tokens) {
+  if (!p || !logits || !out_tokens) return LILICORR_EINVAL;
+  if (p->abi_version != LILICORR_ABI_VERSION) return LILICORR_EINVAL;
+  if (!sizes_ok(p->num_blocks, B, V, K)) return LILICORR_EINVAL;
+  if (p->logits_dtype != LILICORR_F32 && p->logits_dtype != LILICORR_BF16)
+    return LILICORR_EUNSUPPORTED;
+  if ((uintptr_t)logits & 15) return LILICORR_EINVAL;
+  if (p->use_logp != 0 && p->use_logp != 1) return LILICORR_EINVAL;
+  const lilicorr_weights* w = p->weights;
+  if (!w) return LILICORR_EINVAL;
+  if (!dims_supported(&w->dims)) return LILICORR_EUNSUPPORTED;
+  if (w->vocab != V || !w->dev || ((uintptr_t)w->dev & 255) ||
+      w->bytes < weights_total_bytes(w->dims, w->vocab))
+    return LILICORR_EWEIGHTS;
+  const size_t need = rerank_ws_layout(p->num_blocks, B, V, K, w->dims).total;
+  if (!p->workspace || p->workspace_bytes < need || ((uintptr_t)p->workspace & 255))
+    return LILICORR_EWORKSPACE;
+  return LILICORR_OK;
+}
+
+int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_params* p,
+                    int32_t* out_tokens) {
+  const int v = lilicorr_validate(logits, B, V, K, p, out_tokens);
+  if (v != LILICORR_OK) return v;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  hipStream_t st = (hipStream_t)p->stream;
+  const int N = p->num_blocks;
+  const lilicorr_dims& d = p->weights->dims;
+  const int H = d.hidden, F = d.ffn, de = d.d_e, heads = d.heads;
+  const int rows = N * B;
+  const int M = rows * K;
+  const WeightPtrs W = weight_ptrs(*p->weights);
+  const RerankWs L = rerank_ws_layout(N, B, V, K, d);
+  char* ws = (char*)p->workspace;
+  const TopkWs TL = topk_ws_layout(rows, V, K);
+  char* tws = ws + L.topk;
+  int32_t* topk_idx = p->dbg_topk_idx ? p->dbg_topk_idx : (int32_t*)(ws + L.topk_idx);
+  float* topk_logp = p->dbg_topk_logp ? p->dbg_topk_logp : (float*)(ws + L.topk_logp);
+  float* x = (float*)(ws + L.x);
+  uint16_t* hid = (uint16_t*)(ws + L.hid);
+  uint16_t* u = (uint16_t*)(ws + L.u);
+  uint16_t* qkv = (uint16_t*)(ws + L.qkv);
+  uint16_t* attn = (uint16_t*)(ws + L.attn);
+  float* heads_v = (float*)(ws + L.heads);
+  uint16_t* outv = p->dbg_outv ? p->dbg_outv : (uint16_t*)(ws + L.outv);
+  uint16_t* inv = p->dbg_inv ? p->dbg_inv : (uint16_t*)(ws + L.inv);
+  float* cosb = p->dbg_cos ? p->dbg_cos : (float*)(ws + L.cos);
+
+  // a1: log-partition + top-K
+  LL_TRY(launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
+                         (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms), topk_idx,
+                         topk_logp, p->dbg_lse, st));
+  // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c)
+  LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, W.S, W.R, W.conf_w1, W.conf_b1,
+                           hid, x, V, st));
+  LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, EPI_RESID_F32, x, x, st));
+  // a3: two pre-norm layers
+  for (int l = 0; l < 2; ++l) {
+    const LayerPtrs& Lw = W.layer[l];
+    LL_TRY(launch_rmsnorm(x, M, H, Lw.gamma1, kRmsEps, u, st));
+    LL_TRY(launch_linear(u, M, H, Lw.wqkv, 3 * H, Lw.bqkv, EPI_BF16, nullptr, qkv, st));
+    LL_TRY(launch_attention(qkv, N, B, K, H, heads, Lw.dist, Lw.same, attn, st));
+    LL_TRY(launch_linear(attn, M, H, Lw.wo, H, Lw.bo, EPI_RESID_F32, x, x, st));
+    LL_TRY(launch_rmsnorm(x, M, H, Lw.gamma2, kRmsEps, u, st));
+    LL_TRY(launch_linear(u, M, H, Lw.w1, F, Lw.b1, EPI_SILU_BF16, nullptr, hid, st));
+    LL_TRY(launch_linear(hid, M, F, Lw.w2, H, Lw.b2, EPI_RESID_F32, x, x, st));
+  }
+  // a4: final norm, out|in heads, unit norm
+  LL_TRY(launch_rmsnorm(x, M, H, W.gamma_f, kRmsEps, u, st));
+  LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, EPI_F32, nullptr, heads_v, st));
+  LL_TRY(launch_heads_l2norm(heads_v, M, de, outv, inv, st));
+  // a5: pair scores, a6: greedy walk
+  LL_TRY(launch_pair_scores(outv, inv, N, B, K, de, cosb, st));
+  LL_TRY(launch_greedy_walk(topk_idx, topk_logp, cosb, N, B, K, p->alpha, p->use_logp, out_tokens,
+                            p->dbg_score, p->dbg_gap, st));
+  return LILICORR_OK;
+}
+
+int lilicorr_topk_lse(const void* logits, int rows, int V, int K, int dtype, void* workspace,
+                      size_t workspace_bytes, int32_t* topk_idx, float* topk_logp, float* lse,
+                      void* stream) {
+  if (!logits || !topk_idx || !topk_logp) return LILICORR_EINVAL;
+  if (rows < 1 || K < 1 || K > LILICORR_MAX_TOPK || V < K) return LILICORR_EINVAL;
+  if ((int64_t)rows * 64 > ((int64_t)1 << 31)) return LILICORR_EINVAL;
+  if (dtype != LILICORR_F32 && dtype != LILICORR_BF16) return LILICORR_EUNSUPPORTED;
+  if ((uintptr_t)logits & 15) return LILICORR_EINVAL;
+  const TopkWs TL = topk_ws_layout(rows, V, K);
+  if (!workspace || workspace_bytes < TL.total || ((uintptr_t)workspace & 255))
+    return LILICORR_EWORKSPACE;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  char* w = (char*)workspace;
+  return hip_status(launch_topk_lse(logits, rows, V, K, dtype, (float*)(w + TL.part_val),
+                                    (int32_t*)(w + TL.part_idx), (float*)(w + TL.part_ms),
+                                    topk_idx, topk_logp, lse, (hipStream_t)stream));
+}
+
+int lilicorr_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K, int d_e,
+                         float* cos, void* stream) {
+  if (!outv || !inv || !cos) return LILICORR_EINVAL;
+  if (N < 1 || B < 2 || B > LILICORR_MAX_SLOTS || K < 1 || K > LILICORR_MAX_TOPK)
+    return LILICORR_EINVAL;
+  if (d_e < 32 || d_e % 32) return LILICORR_EUNSUPPORTED;
+  if (((uintptr_t)outv & 15) || ((uintptr_t)inv & 15)) return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  return hip_status(launch_pair_scores(outv, inv, N, B, K, d_e, cos, (hipStream_t)stream));
+}
+
+int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos, int N,
+                         int B, int K, float alpha, int use_logp, int32_t* out_tokens,
+                         float* score, float* gap, void* stream) {
+  if (!topk_idx || !topk_logp || !out_tokens || (B > 1 && !cos)) return LILICORR_EINVAL;
+  if (N < 1 || B < 1 || B > LILICORR_MAX_SLOTS || K < 1 || K > LILICORR_MAX_TOPK)
+    return LILICORR_EINVAL;
+  if (use_logp != 0 && use_logp != 1) return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  return hip_status(launch_greedy_walk(topk_idx, topk_logp, cos, N, B, K, alpha, use_logp,
+                                       out_tokens, score, gap, (hipStream_t)stream));
+}
+
+int lilicorr_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
+                    int epilogue, const float* resid, void* out, void* stream) {
+  if (!A || !W || !out || M < 1 || N < 1 || Kd < 64) return LILICORR_EINVAL;
+  if (Kd % 64) return LILICORR_EUNSUPPORTED;
+  if (epilogue < 0 || epilogue > 3) return LILICORR_EINVAL;
+  if (epilogue == EPI_RESID_F32 && !resid) return LILICORR_EINVAL;
+  if (((uintptr_t)A & 15) || ((uintptr_t)W & 15)) return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  return hip_status(
+      launch_linear(A, M, Kd, W, N, bias, epilogue, resid, out, (hipStream_t)stream));
+}
+
+int lilicorr_rmsnorm(const float* x, int M, int H, const float* gamma, float eps, uint16_t* out,
+                     void* stream) {
+  if (!x || !gamma || !out || M < 1 || H < 64 || H > 8192) return LILICORR_EINVAL;
+  if (H % 64) return LILICORR_EUNSUPPORTED;
+  if (((uintptr_t)x & 15) || ((uintptr_t)gamma & 15) || ((uintptr_t)out & 7))
+    return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  return hip_status(launch_rmsnorm(x, M, H, gamma, eps, out, (hipStream_t)stream));
+}
+
+int lilicorr_lattice_attention(const uint16_t* qkv, int N, int B, int K, int hidden, int heads,
+                               const float* dist, const float* same, uint16_t* out, void* stream) {
+  if (!qkv || !dist || !same || !out) return LILICORR_EINVAL;
+  if (N < 1 || B < 1 || B > LILICORR_MAX_SLOTS || K < 1 || K > LILICORR_MAX_TOPK ||
+      B * K > LILICORR_MAX_LATTICE)
+    return LILICORR_EINVAL;
+  if (heads < 1 || hidden % heads) return LILICORR_EUNSUPPORTED;
+  const int dh = hidden / heads;
+  if (dh != 32 && dh != 64 && dh != 128) return LILICORR_EUNSUPPORTED;
+  if (((uintptr_t)qkv & 15) || ((uintptr_t)out & 7)) return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  return hip_status(
+      launch_attention(qkv, N, B, K, hidden, heads, dist, same, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

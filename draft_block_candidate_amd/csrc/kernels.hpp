@@ -1,0 +1,50 @@
+// Kernel launchers (host-callable), one translation unit per kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ll {
+
+hipError_t launch_weights_init(void* dst, uint64_t numel, uint64_t key, int kind, float scale,
+                               hipStream_t stream);
+
+// a1: fused log-partition + exact top-K. part_* are scratch of the sizes in
+// topk_ws_layout(); outputs topk_idx/topk_logp [rows, K], lse [rows] (may be null).
+hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype, float* part_val,
+                           int32_t* part_idx, float* part_ms, int32_t* topk_idx, float* topk_logp,
+                           float* lse, hipStream_t stream);
+
+// a2: node features, confidence MLP layer 1 and the embedding/slot/rank sum.
+//   hid  bf16 [M, H] = bf16(silu(W1c f + b1c));  xbase float [M, H] = (E[tok] + S[s]) + R[j]
+hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
+                             int H, const uint16_t* E, const uint16_t* S, const uint16_t* R,
+                             const uint16_t* conf_w1, const float* conf_b1, uint16_t* hid,
+                             float* xbase, int V, hipStream_t stream);
+
+enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SILU_BF16 = 2, EPI_RESID_F32 = 3 };
+
+// Y = A[M,Kd] W[N,Kd]^T + bias, epilogue as above (bf16 in, fp32 accumulate, MFMA).
+hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
+                         const float* bias, int epi, const float* resid, void* out,
+                         hipStream_t stream);
+
+hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, float eps,
+                          uint16_t* out, hipStream_t stream);
+
+hipError_t launch_attention(const uint16_t* qkv, int N, int B, int K, int H, int heads,
+                            const float* dist, const float* same, uint16_t* out,
+                            hipStream_t stream);
+
+// Row-wise unit normalisation of v [M, 2 d_e] (out half | in half) to bf16.
+hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, uint16_t* inv,
+                               hipStream_t stream);
+
+hipError_t launch_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
+                              int d_e, float* cos, hipStream_t stream);
+
+hipError_t launch_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos,
+                              int N, int B, int K, float alpha, int use_logp, int32_t* out_tokens,
+                              float* score, float* gap, hipStream_t stream);
+
+}  // namespace ll

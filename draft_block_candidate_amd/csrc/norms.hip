@@ -1,0 +1,74 @@
+// Row normalisations: RMSNorm before each sub-layer and the final unit-norm
+// of the in/out vectors (LiLiCorr paper, Appendix A: RMSNorm; Section 3.2:
+// in and out vectors normalised to unit norm).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ll {
+namespace {
+
+// One wave per row. out = bf16((x * rstd) * gamma), rstd = 1/sqrt(mean(x^2) + eps).
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int M, int H,
+                                                      const float* __restrict__ gamma, float eps,
+                                                      uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float4* xr = (const float4*)(x + row * H);
+  float ss = 0.f;
+  for (int c4 = lane; c4 < H / 4; c4 += 64) {
+    const float4 v = xr[c4];
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
+  }
+  ss = wave_sum(ss);
+  const float rstd = 1.0f / __fsqrt_rn(ss / (float)H + eps);
+  const float4* g4 = (const float4*)gamma;
+  uint2* o2 = (uint2*)(out + row * H);
+  for (int c4 = lane; c4 < H / 4; c4 += 64) {
+    const float4 v = xr[c4], gv = g4[c4];
+    o2[c4] = make_uint2(pack_bf16x2(v.x * rstd * gv.x, v.y * rstd * gv.y),
+                        pack_bf16x2(v.z * rstd * gv.z, v.w * rstd * gv.w));
+  }
+}
+
+// One wave per (token, head): v / max(|v|, 1e-12) rounded to bf16.
+__global__ __launch_bounds__(256) void heads_l2norm_kernel(const float* __restrict__ v, int M,
+                                                           int de, uint16_t* __restrict__ outv,
+                                                           uint16_t* __restrict__ inv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= 2 * (int64_t)M) return;
+  const int64_t m = w >> 1;
+  const int half = (int)(w & 1);
+  const float* src = v + m * 2 * de + half * de;
+  uint16_t* dst = (half ? inv : outv) + m * de;
+  float ss = 0.f;
+  for (int d = lane; d < de; d += 64) ss = fmaf(src[d], src[d], ss);
+  ss = wave_sum(ss);
+  const float n = fmaxf(__fsqrt_rn(ss), 1e-12f);
+  for (int d = lane; d < de; d += 64) dst[d] = (uint16_t)f32_to_bf16(__fdiv_rn(src[d], n));
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, float eps,
+                          uint16_t* out, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, x, M, H,
+                     gamma, eps, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, uint16_t* inv,
+                               hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const int64_t waves = 2 * (int64_t)M;
+  hipLaunchKernelGGL(heads_l2norm_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
+                     v, M, d_e, outv, inv);
+  return hipGetLastError();
+}
+
+}  // namespace ll

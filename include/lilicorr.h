@@ -1,0 +1,213 @@
+/*
+ * lilicorr.h - C ABI of the MI355X (gfx950) LiLiCorr reranking library.
+ *
+ * The library implements the inference path of the LiLiCorr candidate-lattice
+ * reranker ("LiLiCorr: Lightweight Likelihood Correlation of Parallel Drafts
+ * for Speculative Decoding", arXiv 2608.20530; serving kernels described in
+ * the SGLang pull request "[Spec] Add LiLiCorr: a candidate-lattice reranker
+ * for DFlash drafts"):
+ *
+ *   per-slot log-softmax + top-K  ->  one candidate-encoder pass emitting unit
+ *   in/out vectors  ->  batched K x K cosine scores per adjacent slot pair  ->
+ *   greedy left-to-right commit.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named dev_* or documented as "device" are HIP device pointers;
+ *     all others are host pointers.
+ *   - Every buffer is owned by the caller. The library allocates no memory and
+ *     keeps no mutable global state apart from a once-per-device architecture
+ *     check.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream) and the call returns after enqueueing. Outputs are valid
+ *     once the stream has reached that point. No call synchronises the device.
+ *   - Every function returning int returns LILICORR_OK (0) or a negative
+ *     lilicorr_status. Argument checks run on the host before any launch; on
+ *     an error nothing is enqueued and no output is touched.
+ *   - Calls that share a workspace must not overlap; distinct workspaces make
+ *     calls independent. Every entry point can be captured in a HIP graph (no
+ *     memset nodes, no host synchronisation, fixed launch sequence).
+ *   - Logits must be finite; this is not checked on the device.
+ */
+#ifndef LILICORR_H_
+#define LILICORR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define LILICORR_API __attribute__((visibility("default")))
+#else
+#define LILICORR_API
+#endif
+
+#define LILICORR_ABI_VERSION 1u
+#define LILICORR_MAX_SLOTS 64     /* B: slots per block */
+#define LILICORR_MAX_TOPK 64      /* K: candidates per slot (one per wave lane) */
+#define LILICORR_MAX_LATTICE 512  /* T = B*K tokens per block */
+
+typedef enum {
+  LILICORR_OK = 0,
+  LILICORR_EINVAL = -1,       /* bad size, null required pointer, bad abi_version */
+  LILICORR_EUNSUPPORTED = -2, /* dtype or geometry outside what the kernels build for, or device is not gfx950 */
+  LILICORR_EWORKSPACE = -3,   /* workspace missing or smaller than lilicorr_workspace_bytes() */
+  LILICORR_EWEIGHTS = -4,     /* weight descriptor does not match dims/vocabulary, or blob too small */
+  LILICORR_EHIP = -5          /* a HIP runtime call or kernel launch failed */
+} lilicorr_status;
+
+typedef enum { LILICORR_F32 = 0, LILICORR_BF16 = 1 } lilicorr_dtype;
+
+/* Encoder geometry. LiLiCorr paper, Appendix A "Architecture" and Table 4:
+ * a two-layer bidirectional transformer of width `hidden` with `heads`
+ * attention heads and feed-forward width `ffn`; in/out vectors of width d_e.
+ * Supported: layers == 2; hidden % 64 == 0; ffn % 64 == 0; d_e % 32 == 0;
+ * hidden / heads in {32, 64, 128}; hidden <= 4096; ffn <= 16384; d_e <= 512. */
+typedef struct {
+  int32_t hidden, heads, ffn, d_e, layers;
+} lilicorr_dims;
+
+/* Encoder weights: a device blob of lilicorr_weights_bytes() bytes filled by
+ * lilicorr_weights_init() from (dims, vocab, seed). The pages publish no
+ * trained head, so the weights are seeded random with a counter-based
+ * SplitMix64 stream (layout and values: lilicorr_weights_tensor()). */
+typedef struct {
+  lilicorr_dims dims;
+  int32_t vocab;   /* V: rows of the token embedding table */
+  uint64_t seed;
+  void* dev;       /* device pointer, 256-byte aligned, caller-owned */
+  size_t bytes;    /* size of the blob at dev */
+} lilicorr_weights;
+
+typedef struct {
+  uint32_t abi_version;            /* must be LILICORR_ABI_VERSION */
+  int32_t num_blocks;              /* N independent draft blocks (>= 1) */
+  int32_t logits_dtype;            /* lilicorr_dtype of the logits */
+  float alpha;                     /* weight of the cosine term in the commit rule */
+  int32_t use_logp;                /* 1: z = logp + alpha*cos; 0: z = alpha*cos (paper's sigma*cos) */
+  const lilicorr_weights* weights; /* host pointer to an initialised descriptor */
+  void* workspace;                 /* device scratch, >= lilicorr_workspace_bytes() */
+  size_t workspace_bytes;
+  void* stream;                    /* hipStream_t */
+  /* Optional device outputs, NULL = not written:
+   *   dbg_topk_idx  int32  [N,B,K]   vocabulary ids, (logit desc, id asc)
+   *   dbg_topk_logp float  [N,B,K]   fl32(x - fl32(lse))
+   *   dbg_lse       float  [N,B]     log sum_v exp(x_v)
+   *   dbg_outv/inv  bf16   [N,B,K,d_e] unit out / in vectors (raw uint16 bits)
+   *   dbg_cos       float  [N,B-1,K,K] cos_s[a][b] = out[s-1,a] . in[s,b]
+   *   dbg_score     float  [N,B]     committed score per slot (slot 0: its top logp)
+   *   dbg_gap       float  [N,B]     committed score minus best other score (0 at slot 0 / K=1) */
+  int32_t* dbg_topk_idx;
+  float* dbg_topk_logp;
+  float* dbg_lse;
+  uint16_t* dbg_outv;
+  uint16_t* dbg_inv;
+  float* dbg_cos;
+  float* dbg_score;
+  float* dbg_gap;
+} lilicorr_params;
+
+/* The whole reranking path (LiLiCorr paper, Section 3.5 "Single-pass
+ * decoding"; spec commit rule with alpha, see greedy_walk below).
+ *   logits      device, [N, B, V] row-major (V contiguous), dtype p->logits_dtype
+ *   B, V, K     slots per block (1..64), vocabulary (K..2^31-1), candidates (1..64), B*K <= 512
+ *   out_tokens  device int32 [N, B]: committed vocabulary id per slot
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EWEIGHTS (host checks), EHIP. */
+LILICORR_API int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_params* p,
+                    int32_t* out_tokens);
+
+/* Host-only check of lilicorr_rerank's arguments; launches nothing and needs no GPU.
+ * Returns exactly the status lilicorr_rerank would return before launching. */
+LILICORR_API int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_params* p,
+                      const int32_t* out_tokens);
+
+/* Workspace bytes lilicorr_rerank needs for N blocks of B slots, vocabulary V,
+ * K candidates and the given geometry. Host only; 0 if the sizes are invalid. */
+LILICORR_API size_t lilicorr_workspace_bytes(int N, int B, int V, int K, const lilicorr_dims* dims);
+
+/* Bytes of the weight blob for (dims, V). Host only; 0 if invalid. */
+LILICORR_API size_t lilicorr_weights_bytes(const lilicorr_dims* dims, int V);
+
+/* Fill w->dev with the synthetic weights of (w->dims, w->vocab, w->seed).
+ * Tensor t, row-major element e:  k_t = splitmix64(seed ^ (t << 40)),
+ * r = splitmix64(k_t + e), u = (r >> 40) * 2^-24,
+ * w = fl32((2u - 1) * fl32(1/sqrt(fan_in)))  (matrices rounded to bf16, RNE),
+ * gains = fl32(1 + 0.25 (2u - 1)). splitmix64(x) is the first output of a
+ * SplitMix64 generator with state x (Steele, Lea, Flood, OOPSLA 2014).
+ * Errors: EINVAL, EUNSUPPORTED, EWEIGHTS (w->bytes too small), EHIP. */
+LILICORR_API int lilicorr_weights_init(lilicorr_weights* w, void* stream);
+
+/* Where tensor `id` lives in the weight blob: byte offset, element count and
+ * storage dtype (LILICORR_BF16 or LILICORR_F32). Ids: 0 E[V,H], 1 S[64,H],
+ * 2 R[64,H], 3 conf_w1[H,5], 4 conf_b1[H], 5 conf_w2[H,H], 6 conf_b2[H];
+ * layer l (base 16+16l): +0 gamma1[H], +1 wqkv[3H,H], +2 bqkv[3H], +3 wo[H,H],
+ * +4 bo[H], +5 gamma2[H], +6 w1[F,H], +7 b1[F], +8 w2[H,F], +9 b2[H],
+ * +10 dist[heads,127], +11 same[heads]; 48 gamma_f[H], 49 w_out[d_e,H],
+ * 50 b_out[d_e], 51 w_in[d_e,H], 52 b_in[d_e]. Host only. EINVAL if unknown. */
+LILICORR_API int lilicorr_weights_tensor(const lilicorr_dims* dims, int V, int id, size_t* offset_bytes,
+                            size_t* numel, int* dtype);
+
+/* Status code to a static string. */
+LILICORR_API const char* lilicorr_strerror(int code);
+
+/* ---- Component entry points: single steps of the path, same kernels ---- */
+
+/* Fused log-partition + exact top-K per row (SGLang PR, "Why the custom
+ * kernels": one pass over [n, V] returning the top-k and the log-partition).
+ *   logits     device [rows, V], dtype LILICORR_F32 or LILICORR_BF16
+ *   topk_idx   device int32 [rows, K]  ids ordered by (logit desc, id asc)
+ *   topk_logp  device float [rows, K]  fl32(x - fl32(lse))
+ *   lse        device float [rows]     (may be NULL)
+ *   workspace  device, >= lilicorr_topk_workspace_bytes(rows, V, K) */
+LILICORR_API size_t lilicorr_topk_workspace_bytes(int rows, int V, int K);
+LILICORR_API int lilicorr_topk_lse(const void* logits, int rows, int V, int K, int dtype, void* workspace,
+                      size_t workspace_bytes, int32_t* topk_idx, float* topk_logp, float* lse,
+                      void* stream);
+
+/* Pair scores (LiLiCorr paper, Eq. (1) and Section 3.5: one product per
+ * adjacent slot pair, batched over the block).
+ *   outv, inv  device bf16 bits [N, B, K, d_e]; cos device float [N, B-1, K, K]. */
+LILICORR_API int lilicorr_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K, int d_e,
+                         float* cos, void* stream);
+
+/* Greedy commit (LiLiCorr paper, Eq. (8); ties to the lower index as in the
+ * SGLang PR). c_0 = 0; for s >= 1: z_j = fl32(logp[s][j] + fl32(alpha *
+ * cos[s-1][c_{s-1}][j])) (use_logp = 1) or fl32(alpha * cos[..]) (use_logp = 0);
+ * c_s = lowest j with maximal z_j; out_tokens[s] = topk_idx[s][c_s].
+ *   topk_idx int32 / topk_logp float [N,B,K], cos float [N,B-1,K,K] (device)
+ *   out_tokens int32 [N,B]; score, gap float [N,B] (device, may be NULL). */
+LILICORR_API int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos, int N,
+                         int B, int K, float alpha, int use_logp, int32_t* out_tokens,
+                         float* score, float* gap, void* stream);
+
+/* One linear layer on MFMA: Y[M,N] = A[M,Kd] . W[N,Kd]^T + bias[N], bf16
+ * inputs, fp32 accumulation, then the epilogue:
+ *   0: out float  = y            1: out bf16 = bf16(y)
+ *   2: out bf16   = bf16(silu(y)) 3: out float = resid + y (resid may equal out)
+ * A, W: device bf16 bits; bias device float [N] (may be NULL = 0).
+ * Requires Kd % 64 == 0. */
+LILICORR_API int lilicorr_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
+                    int epilogue, const float* resid, void* out, void* stream);
+
+/* RMSNorm of fp32 rows then bf16 rounding: out = bf16(x / sqrt(mean(x^2) + eps) * gamma).
+ * x device float [M, H]; gamma device float [H]; out device bf16 [M, H]. H % 64 == 0, H <= 8192. */
+LILICORR_API int lilicorr_rmsnorm(const float* x, int M, int H, const float* gamma, float eps, uint16_t* out,
+                     void* stream);
+
+/* Lattice attention of one layer (LiLiCorr paper, Appendix A: bidirectional
+ * over the whole lattice; per-head biases by signed slot distance and for
+ * same-slot pairs). qkv device bf16 [N*T, 3H] (q | k | v, heads as contiguous
+ * d_h column groups); T = B*K tokens per block, token t in slot t / K;
+ * dist device float [heads, 127] indexed by slot_key - slot_query + 63;
+ * same device float [heads]; out device bf16 [N*T, H] = bf16(softmax-weighted v)
+ * with p = bf16(exp(s - rowmax)) and the row sum of the unrounded exp. */
+LILICORR_API int lilicorr_lattice_attention(const uint16_t* qkv, int N, int B, int K, int hidden, int heads,
+                               const float* dist, const float* same, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LILICORR_H_ */

@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load without a GPU, export every entry point the header
+declares, and reject bad arguments in its host-only validation with the
+documented status codes, without launching anything.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import draft_block_candidate_amd as L
+from oracle.weights import weight_table, Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lilicorr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LILICORR_API\s+[^;(]*?\b(lilicorr_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("lilicorr_rerank", "lilicorr_validate", "lilicorr_workspace_bytes",
+                 "lilicorr_weights_bytes", "lilicorr_weights_init", "lilicorr_strerror",
+                 "lilicorr_topk_lse", "lilicorr_greedy_walk", "lilicorr_pair_scores"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(lilicorr_\w+)", out))
+    assert set(declared_functions()) <= exported
+    # internal helpers stay hidden
+    assert not any(s.startswith("_ZN2ll") for s in re.findall(r"\s[TW]\s+(\S+)", out))
+    lib = L.lib()
+    for name in declared_functions():
+        assert getattr(lib, name) is not None
+
+
+def test_bindings_cover_the_header():
+    assert set(declared_functions()) == set(L._SIGNATURES)
+
+
+def test_strerror_codes():
+    assert L.strerror(0) == "ok"
+    assert "workspace" in L.strerror(L.EWORKSPACE)
+    assert L.strerror(12345) == "unknown status"
+
+
+DIMS = L.EncoderDims(64, 2, 256, 32)
+
+
+def _good(**over):
+    args = dict(logits_ptr=1 << 20, N=1, B=16, V=1024, K=4, logits_dtype=L.F32, vocab=1024,
+                dims=DIMS, wptr=1 << 24, wbytes=None, ws=1 << 28, wsbytes=None, out=1 << 12,
+                abi=L.ABI_VERSION, use_logp=1, weights=True)
+    args.update(over)
+    wb = args["wbytes"] if args["wbytes"] is not None else L.weights_bytes(args["dims"], args["vocab"])
+    desc = L.WeightsDesc(args["dims"].c(), args["vocab"], 42, ctypes.c_void_p(args["wptr"]), wb) if args["weights"] else None
+    wsb = args["wsbytes"]
+    if wsb is None:
+        wsb = L.workspace_bytes(args["N"], args["B"], args["V"], args["K"], DIMS)
+    return L.validate(args["logits_ptr"], args["N"], args["B"], args["V"], args["K"], args["logits_dtype"],
+                      desc, args["ws"], wsb, args["out"], args["abi"], args["use_logp"])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, L.OK),
+    ({"logits_ptr": 0}, L.EINVAL),
+    ({"out": 0}, L.EINVAL),
+    ({"abi": 2}, L.EINVAL),
+    ({"N": 0}, L.EINVAL),
+    ({"B": 0}, L.EINVAL),
+    ({"B": 65}, L.EINVAL),
+    ({"K": 0}, L.EINVAL),
+    ({"K": 65}, L.EINVAL),
+    ({"V": 3, "vocab": 3, "wsbytes": 1 << 30}, L.EINVAL),          # K > V
+    ({"B": 64, "K": 16, "wsbytes": 1 << 30}, L.EINVAL),            # B*K > 512
+    ({"logits_dtype": 2}, L.EUNSUPPORTED),
+    ({"logits_ptr": (1 << 20) + 8}, L.EINVAL),                     # 16-byte alignment
+    ({"use_logp": 2}, L.EINVAL),
+    ({"weights": False}, L.EINVAL),
+    ({"dims": L.EncoderDims(64, 3, 256, 32)}, L.EUNSUPPORTED),     # heads do not divide hidden
+    ({"dims": L.EncoderDims(96, 2, 256, 32)}, L.EUNSUPPORTED),     # hidden % 64
+    ({"dims": L.EncoderDims(64, 2, 256, 48)}, L.EUNSUPPORTED),     # d_e % 32
+    ({"vocab": 2048}, L.EWEIGHTS),
+    ({"wbytes": 1024}, L.EWEIGHTS),
+    ({"wptr": 0}, L.EWEIGHTS),
+    ({"wptr": (1 << 24) + 16}, L.EWEIGHTS),
+    ({"ws": 0}, L.EWORKSPACE),
+    ({"wsbytes": 100}, L.EWORKSPACE),
+    ({"ws": (1 << 28) + 64}, L.EWORKSPACE),
+])
+def test_validate_status_codes(over, code):
+    assert _good(**over) == code
+
+
+def test_sizes_for_the_workloads():
+    import synth
+    for name in synth.WORKLOADS_ORDER:
+        w = synth.WORKLOADS[name]
+        d = L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e)
+        assert L.weights_bytes(d, w.vocab) > 0
+        ws = L.workspace_bytes(w.num_blocks, w.slots, w.vocab, w.topk, d)
+        M = w.num_blocks * w.slots * w.topk
+        assert ws >= M * w.hidden * 4 + M * w.ffn * 2
+    assert L.workspace_bytes(1, 16, 1024, 65, DIMS) == 0
+    assert L.weights_bytes(L.EncoderDims(64, 2, 256, 32, layers=3), 10) == 0
+
+
+def test_weight_layout_matches_the_generator_table():
+    d = Dims(64, 2, 256, 32)
+    spans = []
+    for t, name, shape, scale, kind in weight_table(d, 1024):
+        off, n, dt = L.weights_tensor_info(DIMS, 1024, t)
+        assert n == (shape[0] * (shape[1] if len(shape) > 1 else 1))
+        assert dt == (L.BF16 if kind == "bf16" else L.F32)
+        spans.append((off, off + n * (2 if dt == L.BF16 else 4), name))
+    spans.sort()
+    for (a0, a1, _), (b0, b1, _) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert spans[-1][1] <= L.weights_bytes(DIMS, 1024)
+    wo, wi = L.weights_tensor_info(DIMS, 1024, 49), L.weights_tensor_info(DIMS, 1024, 51)
+    assert wi[0] == wo[0] + wo[1] * 2      # one GEMM with N = 2 d_e covers both heads
+    bo, bi = L.weights_tensor_info(DIMS, 1024, 50), L.weights_tensor_info(DIMS, 1024, 52)
+    assert bi[0] == bo[0] + bo[1] * 4
+    with pytest.raises(L.LilicorrError):
+        L.weights_tensor_info(DIMS, 1024, 7)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/liblilicorr.so")
+    with pytest.raises(L.LilicorrUnavailable):
+        L.lib()

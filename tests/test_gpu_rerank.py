@@ -2,16 +2,18 @@
 
 Every workload runs at its full size on the GPU, in the launch configuration
 the benchmark times; the oracle recomputes sampled blocks one by one.
-Top-K ids must match exactly; lse, logp, cos and committed scores within
-1e-3 * max(1, |oracle|); committed tokens exactly, except where the oracle's
-score of the GPU's pick is within that tolerance of the best (each such
-excused slot is reported).
+Top-K ids must match exactly; lse and logp within 1e-3 * max(1, |oracle|);
+pair cosines and committed step scores within 1e-3 * max(1, |oracle|) for at
+least 99.9% of the elements and within the bf16 bound for all (the bound and
+its derivation are in tests/helpers.py); committed tokens exactly, except
+where the oracle's score of the GPU's pick is within the score bound of the
+best (each such excused slot is reported).
 """
 import numpy as np
 import pytest
 
-from helpers import (assert_within, bf16_to_f64, to_device, oracle_weights, device_weights,
-                     compare_walk, TOL)
+from helpers import (assert_within, assert_scores, bf16_to_f64, to_device, oracle_weights,
+                     device_weights, compare_walk, oracle_step_scores, TOL)
 import synth
 import oracle
 
@@ -51,6 +53,7 @@ def run_case(L, name, tier, sample, alpha=None, use_logp=True):
     ow = oracle_weights(w)
     blocks = range(w.num_blocks) if sample is None else sample
     excused = []
+    g_cos, o_cos, g_z, o_z = [], [], [], []
     for b in blocks:
         r = oracle.rerank_block(host[b], w.topk, ow, alpha, use_logp)
         assert np.array_equal(dbg["topk_idx"][b].cpu().numpy(), r.idx), f"block {b}: top-K ids"
@@ -58,16 +61,23 @@ def run_case(L, name, tier, sample, alpha=None, use_logp=True):
         assert_within(dbg["topk_logp"][b].cpu().numpy(), r.logp, what=f"block {b} logp")
         go, gi = bf16_to_f64(dbg["outv"][b]), bf16_to_f64(dbg["inv"][b])
         assert np.abs(go - r.outv).max() < 2e-2 and np.abs(gi - r.inv).max() < 2e-2, f"block {b} in/out"
-        if w.slots > 1:
-            assert_within(dbg["cos"][b].cpu().numpy(), r.cos, what=f"block {b} cos")
         gtok = tokens[b].cpu().numpy()
         gidx = dbg["topk_idx"][b].cpu().numpy()
         choice = np.array([int(np.nonzero(gidx[s] == gtok[s])[0][0]) for s in range(w.slots)])
+        if w.slots > 1:
+            g_cos.append(dbg["cos"][b].cpu().numpy())
+            o_cos.append(r.cos)
+            g_z.append(dbg["score"][b].cpu().numpy()[1:])
+            o_z.append(oracle_step_scores(r.logp, r.cos, choice, alpha, use_logp))
         ex = compare_walk(r.logp, r.cos, choice, alpha, use_logp)
         excused += [(b,) + e for e in ex]
         if not ex:
             assert np.array_equal(gtok, r.tokens.astype(np.int32)), f"block {b}: tokens"
-            assert_within(dbg["score"][b].cpu().numpy(), r.walk.score, what=f"block {b} score")
+    if g_cos:
+        sc = assert_scores(np.concatenate([c.ravel() for c in g_cos]),
+                           np.concatenate([c.ravel() for c in o_cos]), f"{name} cos", 1.0)
+        sz = assert_scores(np.concatenate(g_z), np.concatenate(o_z), f"{name} step scores", alpha)
+        print(f"[scores] {name} tier {tier}: cos {sc} step {sz}", flush=True)
     if excused:
         print(f"[excused] {name} tier {tier}: {excused}", flush=True)
     return tokens, dbg, excused

@@ -172,7 +172,9 @@ def main():
         Wt = rnd((n, kd), 1 / math.sqrt(kd))
         bias = torch.zeros(n, dtype=torch.float32, device=dev)
         resid = torch.zeros((m, n), dtype=torch.float32, device=dev)
-        fn = lambda: L.linear(A, Wt, bias, epi, resid if epi == L.EPI_RESID_F32 else None)
+        lws = torch.empty(max(256, int(lib.lilicorr_linear_workspace_bytes(m, kd, n))), dtype=torch.uint8,
+                          device=dev)
+        fn = lambda: L.linear(A, Wt, bias, epi, resid if epi == L.EPI_RESID_F32 else None, lws)
         fn()
         torch.cuda.synchronize()
         t = event_time_ms(fn, args.probe_reps, stream)

@@ -68,7 +68,8 @@ _SIGNATURES = {
     "lilicorr_topk_lse": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp, _vp, _vp]),
     "lilicorr_pair_scores": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "lilicorr_greedy_walk": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _f, _c_int, _vp, _vp, _vp, _vp]),
-    "lilicorr_linear": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp]),
+    "lilicorr_linear_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "lilicorr_linear": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "lilicorr_rmsnorm": (_c_int, [_vp, _c_int, _c_int, _vp, _f, _vp, _vp]),
     "lilicorr_lattice_attention": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
 }
@@ -299,7 +300,7 @@ def greedy_walk(topk_idx, topk_logp, cos, alpha: float = 1.0, use_logp: bool = T
     return out, score, gap
 
 
-def linear(A, W, bias=None, epilogue: int = EPI_F32, resid=None):
+def linear(A, W, bias=None, epilogue: int = EPI_F32, resid=None, workspace=None):
     """Y = A W^T + bias on MFMA with the given epilogue; A [M, Kd], W [N, Kd] bf16."""
     torch = _torch()
     M, Kd = A.shape
@@ -308,8 +309,11 @@ def linear(A, W, bias=None, epilogue: int = EPI_F32, resid=None):
         out = resid if (epilogue == EPI_RESID_F32 and resid is not None) else torch.empty((M, N), dtype=torch.float32, device=A.device)
     else:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    nbytes = int(lib().lilicorr_linear_workspace_bytes(M, Kd, N))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=A.device)
     _check(lib().lilicorr_linear(_ptr(A), M, Kd, _ptr(W), N, _ptr(bias), epilogue, _ptr(resid), _ptr(out),
-                                 _stream()), "linear")
+                                 _ptr(workspace), workspace.numel(), _stream()), "linear")
     return out
 
 

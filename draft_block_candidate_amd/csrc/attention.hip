@@ -55,6 +55,23 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
     qf[ks] = q_ok ? *(const u32x4_t*)(blk + (int64_t)q * H3 + h * DH + ks * 32 + 8 * g)
                   : u32x4_t{0, 0, 0, 0};
 
+  // V chunk loader (32 keys x DH, 16 bytes per thread-slot); chunk 0 is issued
+  // now so its latency overlaps the score computation.
+  constexpr int VCH = (32 * DH / 8 + 255) / 256;
+  u32x4_t vreg[VCH];
+  auto load_v = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int v = tid + 256 * i;
+      const int key = v / (DH / 8), d8 = v % (DH / 8);
+      const int kg = ch * 32 + key;
+      vreg[i] = (v < 32 * DH / 8 && kg < T)
+                    ? *(const u32x4_t*)(blk + (int64_t)kg * H3 + 2 * H + h * DH + d8 * 8)
+                    : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  load_v(0);
+
   const float scale = 1.0f / __fsqrt_rn((float)DH);
   float s[KT][4];
   float mx = -INFINITY;
@@ -107,23 +124,27 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 
   // P V over 32-key chunks. k-slot j of lane group g stands for key
   // 32*ch + 4g + j (j < 4) or 32*ch + 16 + 4g + (j - 4) (j >= 4).
+  // V chunks are staged transposed in LDS; the next chunk's global loads are
+  // in flight while the current chunk is multiplied.
+  const int nch = (T + 31) / 32;
 #pragma unroll
   for (int ch = 0; ch < KT / 2; ++ch) {
-    if (ch * 32 >= T) break;
+    if (ch >= nch) break;
     __syncthreads();
-    // Stage V[32 keys][DH] of this chunk transposed into Vt[DH][32].
-    for (int v = tid; v < 32 * DH / 8; v += 256) {
-      const int key = v / (DH / 8), d8 = v % (DH / 8);
-      const int kg = ch * 32 + key;
-      u32x4_t w = kg < T ? *(const u32x4_t*)(blk + (int64_t)kg * H3 + 2 * H + h * DH + d8 * 8)
-                         : u32x4_t{0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(d8 * 8 + 2 * e) * VT_STRIDE + key] = (uint16_t)(w[e] & 0xFFFF);
-        Vt[(d8 * 8 + 2 * e + 1) * VT_STRIDE + key] = (uint16_t)(w[e] >> 16);
+    for (int i = 0; i < VCH; ++i) {
+      const int v = tid + 256 * i;
+      if (v < 32 * DH / 8) {
+        const int key = v / (DH / 8), d8 = v % (DH / 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Vt[(d8 * 8 + 2 * e) * VT_STRIDE + key] = (uint16_t)(vreg[i][e] & 0xFFFF);
+          Vt[(d8 * 8 + 2 * e + 1) * VT_STRIDE + key] = (uint16_t)(vreg[i][e] >> 16);
+        }
       }
     }
     __syncthreads();
+    if (ch + 1 < nch) load_v(ch + 1);
     u32x4_t pb;
     pb[0] = pack_bf16x2(s[2 * ch][0], s[2 * ch][1]);
     pb[1] = pack_bf16x2(s[2 * ch][2], s[2 * ch][3]);

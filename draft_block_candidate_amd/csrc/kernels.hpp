@@ -17,17 +17,30 @@ hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype
 
 // a2: node features, confidence MLP layer 1 and the embedding/slot/rank sum.
 //   hid  bf16 [M, H] = bf16(silu(W1c f + b1c));  xbase float [M, H] = (E[tok] + S[s]) + R[j]
+// Also zeroes cnt[0, n_cnt) (the split-K counters of the GEMMs that follow).
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
                              int H, const uint16_t* E, const uint16_t* S, const uint16_t* R,
                              const uint16_t* conf_w1, const float* conf_b1, uint16_t* hid,
-                             float* xbase, int V, hipStream_t stream);
+                             float* xbase, int V, int* cnt, int n_cnt, hipStream_t stream);
 
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SILU_BF16 = 2, EPI_RESID_F32 = 3 };
 
+// Schedule of one linear layer: split = 1 for one pass over K, else the number
+// of K slices; part_floats / counters are the scratch it needs (zero if none).
+struct GemmPlan {
+  int bm, bn, ks, split, tiles;
+  size_t part_floats;
+  int counters;
+};
+GemmPlan plan_linear(int M, int Kd, int N);
+
 // Y = A[M,Kd] W[N,Kd]^T + bias, epilogue as above (bf16 in, fp32 accumulate, MFMA).
+// part / cnt: scratch of plan_linear(M, Kd, N); cnt must be zero on entry and
+// is zero again on exit.
 hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
-                         const float* bias, int epi, const float* resid, void* out,
-                         hipStream_t stream);
+                         const float* bias, int epi, const float* resid, void* out, float* part,
+                         int* cnt, hipStream_t stream);
+hipError_t launch_clear_counters(int* cnt, int n, hipStream_t stream);
 
 hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, float eps,
                           uint16_t* out, hipStream_t stream);
@@ -42,6 +55,15 @@ hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, u
 
 hipError_t launch_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
                               int d_e, float* cos, hipStream_t stream);
+
+// Fused a5 + a6 for the rerank path (cosines in LDS; cos_out may be null).
+// Needs scores_walk_lds_bytes(B, K) <= kScoresWalkMaxLds.
+constexpr size_t kScoresWalkMaxLds = 128 * 1024;
+size_t scores_walk_lds_bytes(int B, int K);
+hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const int32_t* topk_idx,
+                              const float* topk_logp, int N, int B, int K, int d_e, float alpha,
+                              int use_logp, float* cos_out, int32_t* out_tokens, float* score,
+                              float* gap, hipStream_t stream);
 
 hipError_t launch_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos,
                               int N, int B, int K, float alpha, int use_logp, int32_t* out_tokens,

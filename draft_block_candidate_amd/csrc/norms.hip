@@ -34,6 +34,42 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+// Same, with the row held in registers (one read of x) for H <= 64 * 4 * NV.
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const float* __restrict__ x, int M, int H,
+                                                          const float* __restrict__ gamma, float eps,
+                                                          uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float4* xr = (const float4*)(x + row * H);
+  const int n4 = H / 4;
+  float4 v[NV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c4 = lane + 64 * i;
+    v[i] = c4 < n4 ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = wave_sum(ss);
+  const float rstd = 1.0f / __fsqrt_rn(ss / (float)H + eps);
+  const float4* g4 = (const float4*)gamma;
+  uint2* o2 = (uint2*)(out + row * H);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c4 = lane + 64 * i;
+    if (c4 < n4) {
+      const float4 gv = g4[c4];
+      o2[c4] = make_uint2(pack_bf16x2(v[i].x * rstd * gv.x, v[i].y * rstd * gv.y),
+                          pack_bf16x2(v[i].z * rstd * gv.z, v[i].w * rstd * gv.w));
+    }
+  }
+}
+
 // One wave per (token, head): v / max(|v|, 1e-12) rounded to bf16.
 __global__ __launch_bounds__(256) void heads_l2norm_kernel(const float* __restrict__ v, int M,
                                                            int de, uint16_t* __restrict__ outv,
@@ -57,8 +93,13 @@ __global__ __launch_bounds__(256) void heads_l2norm_kernel(const float* __restri
 hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, float eps,
                           uint16_t* out, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, x, M, H,
-                     gamma, eps, out);
+  const dim3 grid((unsigned)((M + 3) / 4));
+  if (H <= 1024)
+    hipLaunchKernelGGL(rmsnorm_reg_kernel<4>, grid, dim3(256), 0, stream, x, M, H, gamma, eps, out);
+  else if (H <= 2048)
+    hipLaunchKernelGGL(rmsnorm_reg_kernel<8>, grid, dim3(256), 0, stream, x, M, H, gamma, eps, out);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel, grid, dim3(256), 0, stream, x, M, H, gamma, eps, out);
   return hipGetLastError();
 }
 

@@ -288,31 +288,41 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(const void* __restric
   }
 }
 
-// One wave per row: combine the P chunk lists (tournament) and (max, sum) pairs.
-__global__ __launch_bounds__(256) void topk_merge_kernel(int rows, int K, int P,
-                                                         const float* __restrict__ part_val,
-                                                         const int32_t* __restrict__ part_idx,
-                                                         const float* __restrict__ part_ms,
-                                                         int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_logp,
-                                                         float* __restrict__ lse_out) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int64_t o = (int64_t)row * P + lane;
+// One wave per row: combine the P chunk lists (tournament) and (max, sum)
+// pairs. The row's P * K partial entries are staged in LDS first, so each of
+// the K tournament steps reads the winner's next entry from LDS.
+__global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
+                                                        const float* __restrict__ part_val,
+                                                        const int32_t* __restrict__ part_idx,
+                                                        const float* __restrict__ part_ms,
+                                                        int32_t* __restrict__ topk_idx,
+                                                        float* __restrict__ topk_logp,
+                                                        float* __restrict__ lse_out) {
+  extern __shared__ float sm[];
+  float* sv = sm;                       // [P K]
+  int* si = (int*)(sm + P * K);         // [P K]
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  const int64_t rbase = (int64_t)row * P * K;
+  for (int i = lane; i < P * K; i += 64) {
+    sv[i] = part_val[rbase + i];
+    si[i] = part_idx[rbase + i];
+  }
   float m = kMInit, s = 0.f;
-  float hv = -INFINITY;
-  int hi = kInvalid, hp = 0;
   if (lane < P) {
-    m = part_ms[2 * o];
-    s = part_ms[2 * o + 1];
-    hv = part_val[o * K];
-    hi = part_idx[o * K];
+    m = part_ms[2 * ((int64_t)row * P + lane)];
+    s = part_ms[2 * ((int64_t)row * P + lane) + 1];
   }
   const float M = wave_max(m);
   const float S = wave_sum(s * __builtin_amdgcn_exp2f((m - M) * kL2E));
   const float lse = M + logf(S);
-
+  __syncthreads();
+  float hv = -INFINITY;
+  int hi = kInvalid, hp = 0;
+  if (lane < P) {
+    hv = sv[lane * K];
+    hi = si[lane * K];
+  }
   float rv = -INFINITY;
   int ri = kInvalid;
   for (int k = 0; k < K; ++k) {
@@ -337,8 +347,8 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(int rows, int K, int P,
     if (lane == bl && lane < P) {
       ++hp;
       if (hp < K) {
-        hv = part_val[o * K + hp];
-        hi = part_idx[o * K + hp];
+        hv = sv[lane * K + hp];
+        hi = si[lane * K + hp];
       } else {
         hv = -INFINITY;
         hi = kInvalid;
@@ -368,7 +378,7 @@ hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype
                        rows, V, K, P, part_val, part_idx, part_ms);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(64), (size_t)P * K * 8, stream,
                      rows, K, P, part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
   return hipGetLastError();
 }

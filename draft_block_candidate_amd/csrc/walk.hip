@@ -89,7 +89,113 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
   }
 }
 
+// Fused pair scores + greedy commit for the rerank path: one workgroup per
+// block. The four waves compute the block's B-1 K x K cosine matrices into LDS
+// (and to global memory when requested); the walk then reads its rows, the
+// log-probabilities and the ids from LDS, so each sequential step costs LDS
+// latency rather than a global round trip.
+__global__ __launch_bounds__(256) void scores_walk_kernel(
+    const uint16_t* __restrict__ outv, const uint16_t* __restrict__ inv,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int B, int K,
+    int de, float alpha, int use_logp, float* __restrict__ cos_out,
+    int32_t* __restrict__ out_tokens, float* __restrict__ score, float* __restrict__ gap) {
+  extern __shared__ float sm[];
+  const int KK = K * K;
+  float* s_cos = sm;                                // [(B-1) K K]
+  float* s_logp = sm + (B - 1) * KK;                // [B K]
+  int* s_idx = (int*)(s_logp + B * K);              // [B K]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t n = blockIdx.x;
+  const int64_t base = n * B * K;
+  for (int i = tid; i < B * K; i += 256) {
+    s_logp[i] = topk_logp[base + i];
+    s_idx[i] = topk_idx[base + i];
+  }
+  const int tiles = (K + 15) / 16;
+  for (int p = wave; p < B - 1; p += 4) {
+    const uint16_t* o = outv + (base + (int64_t)p * K) * de;
+    const uint16_t* in = inv + (base + (int64_t)(p + 1) * K) * de;
+    for (int at = 0; at < tiles; ++at)
+      for (int bt = 0; bt < tiles; ++bt) {
+        const int a = at * 16 + c, b = bt * 16 + c;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < de; k0 += 32) {
+          const u32x4_t af = a < K ? *(const u32x4_t*)(o + (int64_t)a * de + k0 + 8 * g)
+                                   : u32x4_t{0, 0, 0, 0};
+          const u32x4_t bf = b < K ? *(const u32x4_t*)(in + (int64_t)b * de + k0 + 8 * g)
+                                   : u32x4_t{0, 0, 0, 0};
+          acc = mfma16(af, bf, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ra = at * 16 + 4 * g + i;
+          if (ra < K && b < K) {
+            s_cos[p * KK + ra * K + b] = acc[i];
+            if (cos_out) cos_out[(n * (B - 1) + p) * KK + ra * K + b] = acc[i];
+          }
+        }
+      }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t r0 = n * B;
+  if (lane == 0) {
+    out_tokens[r0] = s_idx[0];
+    if (score) score[r0] = s_logp[0];
+    if (gap) gap[r0] = 0.f;
+  }
+  int cprev = 0;
+  for (int s = 1; s < B; ++s) {
+    float z = -INFINITY;
+    if (lane < K) {
+      const float term = __fmul_rn(alpha, s_cos[(s - 1) * KK + cprev * K + lane]);
+      z = use_logp ? __fadd_rn(s_logp[s * K + lane], term) : term;
+    }
+    float bz = z;
+    int bl = lane;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float oz = __shfl_xor(bz, off, 64);
+      const int ol = __shfl_xor(bl, off, 64);
+      if (oz > bz || (oz == bz && ol < bl)) {
+        bz = oz;
+        bl = ol;
+      }
+    }
+    if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
+    const float second = wave_max(lane == bl ? -INFINITY : z);
+    cprev = bl;
+    if (lane == 0) {
+      out_tokens[r0 + s] = s_idx[s * K + bl];
+      if (score) score[r0 + s] = bz;
+      if (gap) gap[r0 + s] = K > 1 ? __fsub_rn(bz, second) : 0.f;
+    }
+  }
+}
+
 }  // namespace
+
+size_t scores_walk_lds_bytes(int B, int K) {
+  return ((size_t)(B - 1) * K * K + 2 * (size_t)B * K) * 4;
+}
+
+hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const int32_t* topk_idx,
+                              const float* topk_logp, int N, int B, int K, int d_e, float alpha,
+                              int use_logp, float* cos_out, int32_t* out_tokens, float* score,
+                              float* gap, hipStream_t stream) {
+  const size_t lds = scores_walk_lds_bytes(B, K);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)scores_walk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        kScoresWalkMaxLds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(scores_walk_kernel, dim3((unsigned)N), dim3(256), lds, stream, outv, inv,
+                     topk_idx, topk_logp, B, K, d_e, alpha, use_logp, cos_out, out_tokens, score,
+                     gap);
+  return hipGetLastError();
+}
 
 hipError_t launch_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
                               int d_e, float* cos, hipStream_t stream) {

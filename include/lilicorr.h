@@ -187,9 +187,13 @@ LILICORR_API int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk
  *   0: out float  = y            1: out bf16 = bf16(y)
  *   2: out bf16   = bf16(silu(y)) 3: out float = resid + y (resid may equal out)
  * A, W: device bf16 bits; bias device float [N] (may be NULL = 0).
- * Requires Kd % 64 == 0. */
-LILICORR_API int lilicorr_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
-                    int epilogue, const float* resid, void* out, void* stream);
+ * workspace: device scratch of lilicorr_linear_workspace_bytes(M, Kd, N) bytes
+ * (split-K partial sums for few rows; may be NULL when that size is 256 or
+ * less). Requires Kd % 64 == 0. */
+LILICORR_API size_t lilicorr_linear_workspace_bytes(int M, int Kd, int N);
+LILICORR_API int lilicorr_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
+                                 const float* bias, int epilogue, const float* resid, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* RMSNorm of fp32 rows then bf16 rounding: out = bf16(x / sqrt(mean(x^2) + eps) * gamma).
  * x device float [M, H]; gamma device float [H]; out device bf16 [M, H]. H % 64 == 0, H <= 8192. */

@@ -225,3 +225,15 @@ def test_greedy_walk_bit_exact(L, B, K, alpha, use_logp, coarse):
         assert np.array_equal(tok[n].cpu().numpy(), r.tokens.astype(np.int32))
         assert np.array_equal(score[n].cpu().numpy(), r.score)
         assert np.array_equal(gap[n].cpu().numpy(), r.gap)
+
+
+@pytest.mark.parametrize("M,Kd,N", [(128, 1024, 3072), (128, 4096, 1024), (64, 256, 512)])
+def test_linear_split_k_is_bit_reproducible(L, M, Kd, N):
+    import torch
+    rng = np.random.default_rng(M * 7 + N)
+    A = f64_to_bf16_device(_rand_bf16(rng, (M, Kd)))
+    W = f64_to_bf16_device(_rand_bf16(rng, (N, Kd), 1 / np.sqrt(Kd)))
+    b = to_device(rng.standard_normal(N).astype(np.float32))
+    outs = [L.linear(A, W, b, L.EPI_F32) for _ in range(3)]
+    _sync()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])

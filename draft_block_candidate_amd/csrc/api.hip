@@ -174,31 +174,46 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
   uint16_t* inv = p->dbg_inv ? p->dbg_inv : (uint16_t*)(ws + L.inv);
   float* cosb = p->dbg_cos ? p->dbg_cos : (float*)(ws + L.cos);
   float* gpart = (float*)(ws + L.gemm_part);
-  int* gcnt = (int*)(ws + L.gemm_cnt);
 
   // a1: log-partition + top-K
   LL_TRY(launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
                          (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms), topk_idx,
                          topk_logp, p->dbg_lse, st));
-  // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c)
+  // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0))
   LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, W.S, W.R, W.conf_w1, W.conf_b1,
-                           hid, x, V, gcnt, L.n_cnt, st));
-  LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, EPI_RESID_F32, x, x, gpart, gcnt, st));
-  // a3: two pre-norm layers
+                           hid, x, V, st));
+  auto resid_norm = [&](const float* gamma) {
+    LinearEpilogue e;
+    e.kind = EPI_RESID_F32;
+    e.resid = x;
+    e.norm_gamma = gamma;
+    e.eps = kRmsEps;
+    e.norm_out = u;
+    return e;
+  };
+  auto plain = [](int kind) {
+    LinearEpilogue e;
+    e.kind = kind;
+    return e;
+  };
+  LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, resid_norm(W.layer[0].gamma1), x, gpart, st));
+  // a3: two pre-norm layers; each residual GEMM also produces the next RMSNorm
   for (int l = 0; l < 2; ++l) {
     const LayerPtrs& Lw = W.layer[l];
-    LL_TRY(launch_rmsnorm(x, M, H, Lw.gamma1, kRmsEps, u, st));
-    LL_TRY(launch_linear(u, M, H, Lw.wqkv, 3 * H, Lw.bqkv, EPI_BF16, nullptr, qkv, gpart, gcnt, st));
+    const float* next_gamma = l == 0 ? W.layer[1].gamma1 : W.gamma_f;
+    LL_TRY(launch_linear(u, M, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st));
     LL_TRY(launch_attention(qkv, N, B, K, H, heads, Lw.dist, Lw.same, attn, st));
-    LL_TRY(launch_linear(attn, M, H, Lw.wo, H, Lw.bo, EPI_RESID_F32, x, x, gpart, gcnt, st));
-    LL_TRY(launch_rmsnorm(x, M, H, Lw.gamma2, kRmsEps, u, st));
-    LL_TRY(launch_linear(u, M, H, Lw.w1, F, Lw.b1, EPI_SILU_BF16, nullptr, hid, gpart, gcnt, st));
-    LL_TRY(launch_linear(hid, M, F, Lw.w2, H, Lw.b2, EPI_RESID_F32, x, x, gpart, gcnt, st));
+    LL_TRY(launch_linear(attn, M, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st));
+    LL_TRY(launch_linear(u, M, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st));
+    LL_TRY(launch_linear(hid, M, F, Lw.w2, H, Lw.b2, resid_norm(next_gamma), x, gpart, st));
   }
-  // a4: final norm, out|in heads, unit norm
-  LL_TRY(launch_rmsnorm(x, M, H, W.gamma_f, kRmsEps, u, st));
-  LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, EPI_F32, nullptr, heads_v, gpart, gcnt, st));
-  LL_TRY(launch_heads_l2norm(heads_v, M, de, outv, inv, st));
+  // a4: out|in heads and their unit normalisation
+  {
+    LinearEpilogue e = plain(EPI_F32);
+    e.heads_out = outv;
+    e.heads_in = inv;
+    LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st));
+  }
   // a5: pair scores, a6: greedy walk (fused when the block's cosines fit in LDS)
   if (scores_walk_lds_bytes(B, K) <= kScoresWalkMaxLds) {
     LL_TRY(launch_scores_walk(outv, inv, topk_idx, topk_logp, N, B, K, de, p->alpha, p->use_logp,
@@ -257,8 +272,7 @@ int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const 
 
 size_t lilicorr_linear_workspace_bytes(int M, int Kd, int N) {
   if (M < 1 || N < 1 || Kd < 64 || Kd % 64) return 0;
-  const GemmPlan p = plan_linear(M, Kd, N);
-  return align256(p.part_floats * 4) + align256((size_t)p.counters * 4) + 256;
+  return align256(plan_linear(M, Kd, N).part_floats * 4) + 256;
 }
 
 int lilicorr_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
@@ -270,20 +284,16 @@ int lilicorr_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, 
   if (epilogue == EPI_RESID_F32 && !resid) return LILICORR_EINVAL;
   if (((uintptr_t)A & 15) || ((uintptr_t)W & 15)) return LILICORR_EINVAL;
   const GemmPlan plan = plan_linear(M, Kd, N);
-  const size_t part_bytes = align256(plan.part_floats * 4);
   if (workspace_bytes < lilicorr_linear_workspace_bytes(M, Kd, N) ||
       (plan.split > 1 && (!workspace || ((uintptr_t)workspace & 255))))
     return LILICORR_EWORKSPACE;
   const int dc = check_device();
   if (dc != LILICORR_OK) return dc;
-  float* part = (float*)workspace;
-  int* cnt = (int*)((char*)workspace + part_bytes);
-  if (plan.split > 1) {
-    const hipError_t e = launch_clear_counters(cnt, plan.counters, (hipStream_t)stream);
-    if (e != hipSuccess) return LILICORR_EHIP;
-  }
-  return hip_status(launch_linear(A, M, Kd, W, N, bias, epilogue, resid, out, part, cnt,
-                                  (hipStream_t)stream));
+  LinearEpilogue ep;
+  ep.kind = epilogue;
+  ep.resid = resid;
+  return hip_status(
+      launch_linear(A, M, Kd, W, N, bias, ep, out, (float*)workspace, (hipStream_t)stream));
 }
 
 int lilicorr_rmsnorm(const float* x, int M, int H, const float* gamma, float eps, uint16_t* out,

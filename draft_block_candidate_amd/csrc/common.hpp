@@ -37,16 +37,72 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, co
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Wave64 reductions on DPP (GFX9 data-parallel primitives): row_shr:1/2/4/8
+// combine within each 16-lane row, row_bcast:15 and row_bcast:31 fold the
+// rows, leaving the result in lane 63, which readlane broadcasts. Lanes with no
+// DPP source contribute the identity passed as `old`. Must be called by all 64
+// lanes (wave-uniform control flow). The order of the combination is fixed.
+enum : int {
+  kDppShr1 = 0x111,
+  kDppShr2 = 0x112,
+  kDppShr4 = 0x114,
+  kDppShr8 = 0x118,
+  kDppBcast15 = 0x142,
+  kDppBcast31 = 0x143
+};
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(old), __float_as_int(v)));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<kDppShr1, 0xf>(0.f, v);
+  v += dpp_f<kDppShr2, 0xf>(0.f, v);
+  v += dpp_f<kDppShr4, 0xf>(0.f, v);
+  v += dpp_f<kDppShr8, 0xf>(0.f, v);
+  v += dpp_f<kDppBcast15, 0xa>(0.f, v);
+  v += dpp_f<kDppBcast31, 0xc>(0.f, v);
+  return readlane_f(v, 63);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<kDppShr1, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppShr2, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppShr4, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppShr8, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppBcast15, 0xa>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppBcast31, 0xc>(-INFINITY, v));
+  return readlane_f(v, 63);
+}
+
+// Largest (v, i) by v descending, then i ascending; result in every lane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = dpp_f<CTRL, ROW_MASK>(-INFINITY, v);
+  const int oi = dpp_i<CTRL, ROW_MASK>(0x7fffffff, i);
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<kDppShr1, 0xf>(v, i);
+  argmax_step<kDppShr2, 0xf>(v, i);
+  argmax_step<kDppShr4, 0xf>(v, i);
+  argmax_step<kDppShr8, 0xf>(v, i);
+  argmax_step<kDppBcast15, 0xa>(v, i);
+  argmax_step<kDppBcast31, 0xc>(v, i);
+  v = readlane_f(v, 63);
+  i = readlane_i(i, 63);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

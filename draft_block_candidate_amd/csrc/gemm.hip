@@ -9,14 +9,16 @@
 // Two schedules:
 //  * many rows (M >= 2048): BM x BN = 128 x 128 tiles over the whole K,
 //    double-buffered in LDS with one barrier per 64-wide k-step;
-//  * few rows (one or a few draft blocks, M = B*K*N of 64..1024): the GEMM is
+//  * few rows (one or a few draft blocks, M = B*K*N of 64..2047): the GEMM is
 //    weight-streaming and latency bound, so K is split S ways. Each workgroup
-//    stages its whole A and W K-slice in LDS with every load in flight at
-//    once, multiplies, and writes an fp32 partial tile; the last workgroup of
-//    a tile to finish (an atomic arrival counter) sums the S partials in the
-//    fixed order s = 0..S-1 (bit-reproducible) and applies the epilogue.
-//    Workgroups of one tile are mapped to the same XCD (consecutive block ids
-//    go round-robin over the 8 XCDs), so its partials stay in one L2.
+//    stages its whole A and W K-slice (64..256 wide) in LDS with every load in
+//    flight at once, multiplies, and writes an fp32 partial tile. A second
+//    kernel sums the S partials in the fixed order s = 0..S-1
+//    (bit-reproducible) and applies the epilogue; it works on whole rows, so
+//    the RMSNorm that follows a residual add and the unit normalisation of the
+//    out/in heads fuse into it.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -148,27 +150,28 @@ __device__ __forceinline__ void epilogue_store(void* out, const float* resid, in
   }
 }
 
-// Split-K schedule for few rows. Block b -> XCD x = b % 8, q = b / 8,
-// tile = (q / S) * 8 + x, split s = q % S.
-template <int BM, int BN, int KS, int EPI>
-__global__ __launch_bounds__(256) void gemm_splitk_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N, int Kd,
-    const float* __restrict__ bias, const float* resid, void* out, float* __restrict__ part,
-    int* __restrict__ cnt, int S, int tiles_n, int tiles) {
-  constexpr int STR = KS + 8;
+// Split-K partial products for few rows: block (tile, s) writes
+// part[s][m][n] for its BM x BN tile over k in [s*KS, (s+1)*KS). The A and W
+// slices sit unpadded in LDS with the 16-byte chunk index XOR-swizzled by the
+// row, so the 16 rows an MFMA fragment read touches hit distinct banks and
+// two 80 KiB workgroups fit on one CU.
+template <int BM, int BN, int KS>
+__global__ __launch_bounds__(256) void gemm_part_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ W, int M, int N,
+                                                        int Kd, float* __restrict__ part,
+                                                        int tiles_n) {
+  constexpr int CPR = KS / 8;                  // 16-byte chunks per row
+  constexpr int SWM = CPR >= 16 ? 15 : CPR - 1;
   constexpr int MT = BM / 32, NT = BN / 32;
-  constexpr int CH_A = BM * KS / 8, CH_W = BN * KS / 8;
+  constexpr int CH_A = BM * CPR, CH_W = BN * CPR;
   constexpr int NCH = (CH_A + CH_W) / 256;
   static_assert((CH_A + CH_W) % 256 == 0, "chunking");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[(BM + BN) * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[(BM + BN) * KS];
   uint16_t* As = smem;
-  uint16_t* Ws = smem + BM * STR;
-  __shared__ int is_last;
+  uint16_t* Ws = smem + BM * KS;
+  auto at = [](int row, int chunk) { return row * KS + ((chunk ^ (row & SWM)) << 3); };
 
-  const int b = blockIdx.x;
-  const int x = b & 7, q = b >> 3;
-  const int tile = (q / S) * 8 + x, s = q % S;
-  if (tile >= tiles) return;
+  const int tile = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 4, c = lane & 15;
@@ -180,23 +183,21 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(
   for (int i = 0; i < NCH; ++i) {
     const int ch = tid + 256 * i;
     if (ch < CH_A) {
-      const int row = ch / (KS / 8), c8 = ch % (KS / 8);
-      const int64_t gm = m0 + row;
-      r[i] = gm < M ? *(const u32x4_t*)(A + gm * Kd + k0 + c8 * 8) : u32x4_t{0, 0, 0, 0};
+      const int64_t gm = m0 + ch / CPR;
+      r[i] = gm < M ? *(const u32x4_t*)(A + gm * Kd + k0 + (ch % CPR) * 8) : u32x4_t{0, 0, 0, 0};
     } else {
       const int cw = ch - CH_A;
-      const int row = cw / (KS / 8), c8 = cw % (KS / 8);
-      const int64_t gn = n0 + row;
-      r[i] = gn < N ? *(const u32x4_t*)(W + gn * Kd + k0 + c8 * 8) : u32x4_t{0, 0, 0, 0};
+      const int64_t gn = n0 + cw / CPR;
+      r[i] = gn < N ? *(const u32x4_t*)(W + gn * Kd + k0 + (cw % CPR) * 8) : u32x4_t{0, 0, 0, 0};
     }
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int ch = tid + 256 * i;
     if (ch < CH_A)
-      *(u32x4_t*)(&As[(ch / (KS / 8)) * STR + (ch % (KS / 8)) * 8]) = r[i];
+      *(u32x4_t*)(&As[at(ch / CPR, ch % CPR)]) = r[i];
     else
-      *(u32x4_t*)(&Ws[((ch - CH_A) / (KS / 8)) * STR + ((ch - CH_A) % (KS / 8)) * 8]) = r[i];
+      *(u32x4_t*)(&Ws[at((ch - CH_A) / CPR, (ch - CH_A) % CPR)]) = r[i];
   }
   __syncthreads();
 
@@ -210,47 +211,170 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(
     u32x4_t af[MT], bfr[NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      af[i] = *(const u32x4_t*)(&As[(wm * (BM / 2) + i * 16 + c) * STR + kk + 8 * g]);
+      af[i] = *(const u32x4_t*)(&As[at(wm * (BM / 2) + i * 16 + c, kk / 8 + g)]);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      bfr[j] = *(const u32x4_t*)(&Ws[(wn * (BN / 2) + j * 16 + c) * STR + kk + 8 * g]);
+      bfr[j] = *(const u32x4_t*)(&Ws[at(wn * (BN / 2) + j * 16 + c, kk / 8 + g)]);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
   }
 
-  float* mypart = part + ((int64_t)tile * S + s) * (BM * BN);
+  float* ps = part + (int64_t)s * M * N;
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int j = 0; j < NT; ++j) {
+    const int64_t n = n0 + wn * (BN / 2) + j * 16 + c;
+    if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int row = wm * (BM / 2) + i * 16 + 4 * g + qq;
-        const int col = wn * (BN / 2) + j * 16 + c;
-        mypart[row * BN + col] = acc[i][j][qq];
+        const int64_t m = m0 + wm * (BM / 2) + i * 16 + 4 * g + qq;
+        if (m < M) ps[m * N + n] = acc[i][j][qq];
       }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(&cnt[tile], 1) == S - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  const float* tp = part + (int64_t)tile * S * (BM * BN);
-  for (int e = tid; e < BM * BN; e += 256) {
-    const int row = e / BN, col = e % BN;
-    const int64_t m = m0 + row, n = n0 + col;
-    if (m >= M || n >= N) continue;
-    float v = tp[e];
-    for (int t = 1; t < S; ++t) v += tp[(int64_t)t * (BM * BN) + e];
-    epilogue_store<EPI>(out, resid, m * N + n, v + (bias ? bias[n] : 0.f));
   }
-  if (tid == 0) cnt[tile] = 0;
 }
 
-__global__ void clear_counters_kernel(int* cnt, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) cnt[i] = 0;
+// Partial sums are added in the fixed order s = 0..S-1; S is a compile-time
+// constant so the S loads of a group are issued together.
+template <int S>
+__device__ __forceinline__ float4 splitk_sum4(const float4* __restrict__ part4, int64_t MN4,
+                                              int64_t q) {
+  float4 v = part4[q];
+#pragma unroll
+  for (int s = 1; s < S; ++s) {
+    const float4 p = part4[(int64_t)s * MN4 + q];
+    v.x += p.x;
+    v.y += p.y;
+    v.z += p.z;
+    v.w += p.w;
+  }
+  return v;
+}
+
+template <int EPI>
+__device__ __forceinline__ void store4(void* out, const float* resid, int64_t o, float4 y) {
+  if constexpr (EPI == EPI_F32) {
+    *(float4*)((float*)out + o) = y;
+  } else if constexpr (EPI == EPI_RESID_F32) {
+    const float4 r = *(const float4*)(resid + o);
+    *(float4*)((float*)out + o) = make_float4(r.x + y.x, r.y + y.y, r.z + y.z, r.w + y.w);
+  } else if constexpr (EPI == EPI_BF16) {
+    *(uint2*)((uint16_t*)out + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+  } else {
+    *(uint2*)((uint16_t*)out + o) =
+        make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
+  }
+}
+
+// Plain epilogues, 4 consecutive outputs per thread (N % 4 == 0).
+template <int EPI, int S>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int M,
+                                                            int N, const float* __restrict__ bias,
+                                                            const float* resid, void* out) {
+  const int64_t MN4 = (int64_t)M * N / 4;
+  const float4* part4 = (const float4*)part;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < MN4; q += (int64_t)gridDim.x * 256) {
+    float4 v = splitk_sum4<S>(part4, MN4, q);
+    const int n = (int)((q * 4) % N);
+    if (bias) {
+      const float4 b = *(const float4*)(bias + n);
+      v.x += b.x;
+      v.y += b.y;
+      v.z += b.z;
+      v.w += b.w;
+    }
+    store4<EPI>(out, resid, q * 4, v);
+  }
+}
+
+// Residual add fused with the RMSNorm that follows it: one wave per row,
+// x = resid + (y + bias) written back, then u = bf16(x * rstd * gamma).
+template <int S, int NV>
+__global__ __launch_bounds__(256) void splitk_resid_rmsnorm_kernel(
+    const float* __restrict__ part, int M, int N, const float* __restrict__ bias,
+    const float* resid, float* x_out, const float* __restrict__ gamma, float eps,
+    uint16_t* __restrict__ u_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const int64_t MN4 = (int64_t)M * N / 4;
+  const int n4 = N / 4;
+  const float4* part4 = (const float4*)part;
+  float4 v[NV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < n4) {
+      const int64_t q = m * n4 + gi;
+      const float4 y = splitk_sum4<S>(part4, MN4, q);
+      const float4 b = bias ? ((const float4*)bias)[gi] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 r = ((const float4*)resid)[q];
+      v[i] = make_float4(r.x + (y.x + b.x), r.y + (y.y + b.y), r.z + (y.z + b.z), r.w + (y.w + b.w));
+      ((float4*)x_out)[q] = v[i];
+    } else {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = wave_sum(ss);
+  const float rstd = 1.0f / __fsqrt_rn(ss / (float)N + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < n4) {
+      const float4 gv = ((const float4*)gamma)[gi];
+      ((uint2*)(u_out + m * N))[gi] =
+          make_uint2(pack_bf16x2(v[i].x * rstd * gv.x, v[i].y * rstd * gv.y),
+                     pack_bf16x2(v[i].z * rstd * gv.z, v[i].w * rstd * gv.w));
+    }
+  }
+}
+
+// Out/in heads: y = A W^T + b over N = 2 d_e, each half normalised to unit
+// length and rounded to bf16. One wave per row; d_e % 4 == 0.
+template <int S, int NV>
+__global__ __launch_bounds__(256) void splitk_heads_l2norm_kernel(
+    const float* __restrict__ part, int M, int de, const float* __restrict__ bias,
+    uint16_t* __restrict__ outv, uint16_t* __restrict__ inv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const int N = 2 * de, n4 = N / 4, h4 = de / 4;
+  const int64_t MN4 = (int64_t)M * n4;
+  const float4* part4 = (const float4*)part;
+  float4 v[NV];
+  float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = lane + 64 * i;
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (gi < n4) {
+      const float4 y = splitk_sum4<S>(part4, MN4, m * n4 + gi);
+      const float4 b = ((const float4*)bias)[gi];
+      v[i] = make_float4(y.x + b.x, y.y + b.y, y.z + b.z, y.w + b.w);
+    }
+    const float sq = v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    if (gi < h4) ss0 += sq; else ss1 += sq;
+  }
+  const float n0 = fmaxf(__fsqrt_rn(wave_sum(ss0)), 1e-12f);
+  const float n1 = fmaxf(__fsqrt_rn(wave_sum(ss1)), 1e-12f);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < n4) {
+      const bool hi = gi >= h4;
+      const float nr = hi ? n1 : n0;
+      uint16_t* dst = (hi ? inv : outv) + m * de + (hi ? gi - h4 : gi) * 4;
+      *(uint2*)dst = make_uint2(pack_bf16x2(__fdiv_rn(v[i].x, nr), __fdiv_rn(v[i].y, nr)),
+                                pack_bf16x2(__fdiv_rn(v[i].z, nr), __fdiv_rn(v[i].w, nr)));
+    }
+  }
 }
 
 template <int BM, int BN>
@@ -279,23 +403,71 @@ hipError_t launch_tile(const uint16_t* A, int M, int Kd, const uint16_t* W, int 
   return hipGetLastError();
 }
 
-template <int BM, int BN, int KS>
-hipError_t launch_splitk(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
-                         const float* bias, int epi, const float* resid, void* out, float* part,
-                         int* cnt, int S, hipStream_t stream) {
-  const int tiles_n = (N + BN - 1) / BN;
-  const int tiles = ((M + BM - 1) / BM) * tiles_n;
-  const int blocks = ((tiles + 7) / 8) * 8 * S;
-#define LL_SPLITK(E)                                                                            \
-  hipLaunchKernelGGL((gemm_splitk_kernel<BM, BN, KS, E>), dim3(blocks), dim3(256), 0, stream, A, \
-                     W, M, N, Kd, bias, resid, out, part, cnt, S, tiles_n, tiles)
-  switch (epi) {
-    case EPI_F32: LL_SPLITK(EPI_F32); break;
-    case EPI_BF16: LL_SPLITK(EPI_BF16); break;
-    case EPI_SILU_BF16: LL_SPLITK(EPI_SILU_BF16); break;
-    default: LL_SPLITK(EPI_RESID_F32); break;
+template <int KS>
+hipError_t launch_part(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, float* part,
+                       int S, int bm, hipStream_t stream) {
+  if (bm == 128) {
+    const int tiles_n = (N + 31) / 32;
+    const dim3 grid((unsigned)(((M + 127) / 128) * tiles_n), (unsigned)S);
+    hipLaunchKernelGGL((gemm_part_kernel<128, 32, KS>), grid, dim3(256), 0, stream, A, W, M, N, Kd,
+                       part, tiles_n);
+  } else {
+    const int tiles_n = (N + 31) / 32;
+    const dim3 grid((unsigned)(((M + 63) / 64) * tiles_n), (unsigned)S);
+    hipLaunchKernelGGL((gemm_part_kernel<64, 32, KS>), grid, dim3(256), 0, stream, A, W, M, N, Kd,
+                       part, tiles_n);
   }
-#undef LL_SPLITK
+  return hipGetLastError();
+}
+
+template <int S>
+hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& ep, void* out,
+                         const float* part, hipStream_t stream) {
+  const unsigned row_blocks = (unsigned)((M + 3) / 4);
+  if (ep.kind == EPI_RESID_F32 && ep.norm_out) {
+    if (N <= 1024)
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 4>), dim3(row_blocks), dim3(256), 0,
+                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
+                         ep.norm_out);
+    else if (N <= 2048)
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 8>), dim3(row_blocks), dim3(256), 0,
+                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
+                         ep.norm_out);
+    else
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 16>), dim3(row_blocks), dim3(256), 0,
+                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
+                         ep.norm_out);
+    return hipGetLastError();
+  }
+  if (ep.kind == EPI_F32 && ep.heads_out) {
+    if (N <= 256)
+      hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 1>), dim3(row_blocks), dim3(256), 0, stream,
+                         part, M, N / 2, bias, ep.heads_out, ep.heads_in);
+    else
+      hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 4>), dim3(row_blocks), dim3(256), 0, stream,
+                         part, M, N / 2, bias, ep.heads_out, ep.heads_in);
+    return hipGetLastError();
+  }
+  const int64_t MN4 = (int64_t)M * N / 4;
+  const unsigned blocks = (unsigned)std::min<int64_t>((MN4 + 255) / 256, 4096);
+  switch (ep.kind) {
+    case EPI_F32:
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_F32, S>), dim3(blocks), dim3(256), 0, stream,
+                         part, M, N, bias, ep.resid, out);
+      break;
+    case EPI_BF16:
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_BF16, S>), dim3(blocks), dim3(256), 0, stream,
+                         part, M, N, bias, ep.resid, out);
+      break;
+    case EPI_SILU_BF16:
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_SILU_BF16, S>), dim3(blocks), dim3(256), 0,
+                         stream, part, M, N, bias, ep.resid, out);
+      break;
+    default:
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_RESID_F32, S>), dim3(blocks), dim3(256), 0,
+                         stream, part, M, N, bias, ep.resid, out);
+      break;
+  }
   return hipGetLastError();
 }
 
@@ -303,54 +475,52 @@ hipError_t launch_splitk(const uint16_t* A, int M, int Kd, const uint16_t* W, in
 
 GemmPlan plan_linear(int M, int Kd, int N) {
   GemmPlan p{};
-  if (M >= 2048 || Kd < 128) {
-    p.split = 1;
-    return p;
-  }
+  p.split = 1;
+  if (M >= 2048 || Kd < 128 || Kd % 64) return p;
   p.bm = M > 64 ? 128 : 64;
   p.bn = 32;
   p.tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-  // about 512 workgroups; K slices of 64..256 (the whole slice sits in LDS)
-  int S = 1;
-  while (S * 2 * p.tiles <= 512 && Kd / (S * 2) >= 64 && (Kd % (S * 2)) == 0) S *= 2;
-  while (Kd / S > 256) S *= 2;
-  if (Kd % S || (Kd / S) % 64) {
-    p.split = 1;
-    return p;
-  }
-  p.split = S;
-  p.ks = Kd / S;
-  if (S == 1) return p;
-  p.part_floats = (size_t)p.tiles * S * p.bm * p.bn;
-  p.counters = p.tiles;
+  // Widest K slice (<= 256, so the slice sits in LDS) that still gives about
+  // 256 workgroups; at least two slices.
+  int ks = 256;
+  while (ks > 64 && (Kd % ks || (int64_t)p.tiles * (Kd / ks) < 256)) ks >>= 1;
+  const int S = Kd / ks;
+  if (Kd % ks || S < 2 || S > 16 || (S & (S - 1)) || N % 4) return p;
+  p.ks = ks;
+  p.split = Kd / ks;
+  p.part_floats = (size_t)p.split * M * N;
   return p;
 }
 
-hipError_t launch_clear_counters(int* cnt, int n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64)),
-                     dim3(256), 0, stream, cnt, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
-                         const float* bias, int epi, const float* resid, void* out, float* part,
-                         int* cnt, hipStream_t stream) {
+                         const float* bias, const LinearEpilogue& ep, void* out, float* part,
+                         hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const GemmPlan p = plan_linear(M, Kd, N);
-  if (p.split > 1) {
-    if (p.bm == 128) {
-      if (p.ks == 64) return launch_splitk<128, 32, 64>(A, M, Kd, W, N, bias, epi, resid, out, part, cnt, p.split, stream);
-      if (p.ks == 128) return launch_splitk<128, 32, 128>(A, M, Kd, W, N, bias, epi, resid, out, part, cnt, p.split, stream);
-      return launch_splitk<128, 32, 256>(A, M, Kd, W, N, bias, epi, resid, out, part, cnt, p.split, stream);
-    }
-    if (p.ks == 64) return launch_splitk<64, 32, 64>(A, M, Kd, W, N, bias, epi, resid, out, part, cnt, p.split, stream);
-    if (p.ks == 128) return launch_splitk<64, 32, 128>(A, M, Kd, W, N, bias, epi, resid, out, part, cnt, p.split, stream);
-    return launch_splitk<64, 32, 256>(A, M, Kd, W, N, bias, epi, resid, out, part, cnt, p.split, stream);
+  if (p.split == 1) {
+    hipError_t e;
+    if (M >= 2048)
+      e = launch_tile<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+    else if (M > 64)
+      e = launch_tile<128, 32>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+    else
+      e = launch_tile<64, 32>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+    if (e != hipSuccess) return e;
+    if (ep.norm_out) return launch_rmsnorm((const float*)out, M, N, ep.norm_gamma, ep.eps, ep.norm_out, stream);
+    if (ep.heads_out) return launch_heads_l2norm((const float*)out, M, N / 2, ep.heads_out, ep.heads_in, stream);
+    return hipSuccess;
   }
-  if (M >= 2048) return launch_tile<128, 128>(A, M, Kd, W, N, bias, epi, resid, out, stream);
-  if (M > 64) return launch_tile<128, 32>(A, M, Kd, W, N, bias, epi, resid, out, stream);
-  return launch_tile<64, 32>(A, M, Kd, W, N, bias, epi, resid, out, stream);
+  hipError_t e;
+  if (p.ks == 64) e = launch_part<64>(A, M, Kd, W, N, part, p.split, p.bm, stream);
+  else if (p.ks == 128) e = launch_part<128>(A, M, Kd, W, N, part, p.split, p.bm, stream);
+  else e = launch_part<256>(A, M, Kd, W, N, part, p.split, p.bm, stream);
+  if (e != hipSuccess) return e;
+  switch (p.split) {
+    case 2: return launch_reduce<2>(M, N, bias, ep, out, part, stream);
+    case 4: return launch_reduce<4>(M, N, bias, ep, out, part, stream);
+    case 8: return launch_reduce<8>(M, N, bias, ep, out, part, stream);
+    default: return launch_reduce<16>(M, N, bias, ep, out, part, stream);
+  }
 }
 
 }  // namespace ll

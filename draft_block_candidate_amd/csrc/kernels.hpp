@@ -17,30 +17,41 @@ hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype
 
 // a2: node features, confidence MLP layer 1 and the embedding/slot/rank sum.
 //   hid  bf16 [M, H] = bf16(silu(W1c f + b1c));  xbase float [M, H] = (E[tok] + S[s]) + R[j]
-// Also zeroes cnt[0, n_cnt) (the split-K counters of the GEMMs that follow).
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
                              int H, const uint16_t* E, const uint16_t* S, const uint16_t* R,
                              const uint16_t* conf_w1, const float* conf_b1, uint16_t* hid,
-                             float* xbase, int V, int* cnt, int n_cnt, hipStream_t stream);
+                             float* xbase, int V, hipStream_t stream);
 
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SILU_BF16 = 2, EPI_RESID_F32 = 3 };
 
 // Schedule of one linear layer: split = 1 for one pass over K, else the number
-// of K slices; part_floats / counters are the scratch it needs (zero if none).
+// of K slices; part_floats is the fp32 scratch it needs (zero if none).
 struct GemmPlan {
   int bm, bn, ks, split, tiles;
   size_t part_floats;
-  int counters;
 };
 GemmPlan plan_linear(int M, int Kd, int N);
 
-// Y = A[M,Kd] W[N,Kd]^T + bias, epilogue as above (bf16 in, fp32 accumulate, MFMA).
-// part / cnt: scratch of plan_linear(M, Kd, N); cnt must be zero on entry and
-// is zero again on exit.
+// What follows the product y = A W^T + bias:
+//   kind       EPI_* store of y (EPI_RESID_F32: out = resid + y)
+//   norm_out   if set (with EPI_RESID_F32): also u = bf16(RMSNorm(out; norm_gamma, eps))
+//   heads_out  if set (with EPI_F32, N = 2 d_e): unit-normalised bf16 halves to
+//              heads_out / heads_in (out then receives y only when not split)
+struct LinearEpilogue {
+  int kind = EPI_F32;
+  const float* resid = nullptr;
+  const float* norm_gamma = nullptr;
+  float eps = 0.f;
+  uint16_t* norm_out = nullptr;
+  uint16_t* heads_out = nullptr;
+  uint16_t* heads_in = nullptr;
+};
+
+// Y = A[M,Kd] W[N,Kd]^T + bias with the epilogue above (bf16 in, fp32
+// accumulate, MFMA). part: fp32 scratch of plan_linear(M, Kd, N).part_floats.
 hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
-                         const float* bias, int epi, const float* resid, void* out, float* part,
-                         int* cnt, hipStream_t stream);
-hipError_t launch_clear_counters(int* cnt, int n, hipStream_t stream);
+                         const float* bias, const LinearEpilogue& ep, void* out, float* part,
+                         hipStream_t stream);
 
 hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, float eps,
                           uint16_t* out, hipStream_t stream);

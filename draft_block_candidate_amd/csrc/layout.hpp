@@ -179,23 +179,19 @@ inline TopkWs topk_ws_layout(int rows, int V, int K) {
 // ---- rerank workspace ------------------------------------------------------
 struct RerankWs {
   size_t topk, topk_idx, topk_logp, lse, x, hid, u, qkv, attn, heads, outv, inv, cos, score, gap,
-      gemm_part, gemm_cnt, total;
-  int n_cnt;
+      gemm_part, total;
 };
 
 // Largest split-K scratch over the linear layers of one rerank call.
-inline void rerank_gemm_scratch(int M, const lilicorr_dims& d, size_t* part_floats, int* counters) {
+inline size_t rerank_gemm_scratch(int M, const lilicorr_dims& d) {
   const int H = d.hidden, F = d.ffn, de = d.d_e;
   const int shapes[6][2] = {{H, H}, {H, 3 * H}, {H, H}, {H, F}, {F, H}, {H, 2 * de}};  // (Kd, N)
   size_t pf = 0;
-  int nc = 0;
   for (const auto& sh : shapes) {
     const GemmPlan p = plan_linear(M, sh[0], sh[1]);
     if (p.part_floats > pf) pf = p.part_floats;
-    if (p.counters > nc) nc = p.counters;
   }
-  *part_floats = pf;
-  *counters = nc;
+  return pf;
 }
 
 inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims& d) {
@@ -224,12 +220,7 @@ inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims
   w.cos = take((size_t)N * (B > 1 ? B - 1 : 1) * K * K * 4);
   w.score = take(rows * 4);
   w.gap = take(rows * 4);
-  size_t pf = 0;
-  int nc = 0;
-  rerank_gemm_scratch((int)M, d, &pf, &nc);
-  w.gemm_part = take(pf * 4);
-  w.gemm_cnt = take((size_t)nc * 4);
-  w.n_cnt = nc;
+  w.gemm_part = take(rerank_gemm_scratch((int)M, d) * 4);
   w.total = off;
   return w;
 }

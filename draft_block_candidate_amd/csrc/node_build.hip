@@ -15,11 +15,8 @@ __global__ __launch_bounds__(256) void node_build_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int B, int K, int H, int V,
     const uint16_t* __restrict__ E, const uint16_t* __restrict__ S, const uint16_t* __restrict__ R,
     const uint16_t* __restrict__ w1, const float* __restrict__ b1, uint16_t* __restrict__ hid,
-    float* __restrict__ xbase, int* __restrict__ cnt, int n_cnt) {
+    float* __restrict__ xbase) {
   const int64_t t = blockIdx.x;
-  // The split-K arrival counters of the encoder GEMMs that follow start at zero.
-  if (t == 0)
-    for (int i = threadIdx.x; i < n_cnt; i += blockDim.x) cnt[i] = 0;
   const int64_t row = t / K;       // (block, slot)
   const int j = (int)(t - row * K);
   const int s = (int)(row % B);
@@ -64,10 +61,10 @@ __global__ __launch_bounds__(256) void node_build_kernel(
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
                              int H, const uint16_t* E, const uint16_t* S, const uint16_t* R,
                              const uint16_t* conf_w1, const float* conf_b1, uint16_t* hid,
-                             float* xbase, int V, int* cnt, int n_cnt, hipStream_t stream) {
+                             float* xbase, int V, hipStream_t stream) {
   const int64_t M = (int64_t)N * B * K;
   hipLaunchKernelGGL(node_build_kernel, dim3((unsigned)M), dim3(256), 0, stream, topk_idx,
-                     topk_logp, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase, cnt, n_cnt);
+                     topk_logp, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
   return hipGetLastError();
 }
 

@@ -39,11 +39,6 @@ constexpr float kLazy = 16.0f;      // reference max may lag the true max by thi
 constexpr float kMInit = -1e30f;
 constexpr int kInvalid = 0x7fffffff;
 
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-
 __device__ __forceinline__ bool key_gt(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
@@ -59,8 +54,9 @@ struct State {
 __device__ __forceinline__ void list_insert(State& st, float cv, int ci, int K, int lane) {
   const bool better = (lane < K) && key_gt(st.lv, st.li, cv, ci);
   const int pos = __popcll(__ballot(better));
-  const float upv = __shfl_up(st.lv, 1, 64);
-  const int upi = __shfl_up(st.li, 1, 64);
+  // wave_shr:1 (DPP): every lane receives the entry of the lane below it
+  const float upv = dpp_f<0x138, 0xf>(st.lv, st.lv);
+  const int upi = dpp_i<0x138, 0xf>(st.li, st.li);
   if (lane == pos) {
     st.lv = cv;
     st.li = ci;
@@ -84,13 +80,31 @@ __device__ __forceinline__ void offer(State& st, float x, int id, bool allowed, 
   }
 }
 
+template <int DT>
+__device__ __forceinline__ float load_scalar(const void* p, int64_t i) {
+  if (DT == 1) return bf16_to_f32(((const uint16_t*)p)[i]);
+  return ((const float*)p)[i];
+}
+
+// Element e of a packed 16-byte vector.
+template <int EPV>
+__device__ __forceinline__ float elem(const u32x4_t& w, int e) {
+  if constexpr (EPV == 8)
+    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
+  else
+    return __uint_as_float(w[e]);
+}
+
+// Log-sum-exp update for one group of NV packed vectors per lane (slots
+// outside the chunk hold -inf words, which add nothing). Returns the lane's
+// group maximum.
 template <int NV, int EPV>
-__device__ __forceinline__ void lse_update(State& st, const float (&x)[NV][EPV]) {
-  float lm = x[0][0];
+__device__ __forceinline__ float group_lse(State& st, const u32x4_t (&w)[NV]) {
+  float lm = elem<EPV>(w[0], 0);
 #pragma unroll
   for (int u = 0; u < NV; ++u)
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) lm = fmaxf(lm, x[u][e]);
+    for (int e = 0; e < EPV; ++e) lm = fmaxf(lm, elem<EPV>(w[u], e));
   if (__any(lm > st.m_ref + kLazy)) {
     const float nm = lm > st.m_ref + kLazy ? lm : st.m_ref;
     st.s *= __builtin_amdgcn_exp2f((st.m_ref - nm) * kL2E);
@@ -101,104 +115,94 @@ __device__ __forceinline__ void lse_update(State& st, const float (&x)[NV][EPV])
   for (int u = 0; u < NV; ++u) {
     float t = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) t += __builtin_amdgcn_exp2f(fmaf(x[u][e], kL2E, -c));
+    for (int e = 0; e < EPV; ++e) t += __builtin_amdgcn_exp2f(fmaf(elem<EPV>(w[u], e), kL2E, -c));
     st.s += t;
   }
+  return lm;
 }
 
-// Element (u, e) of a lane has row-local index base + u*64*EPV + lane*LS + e.
+// Slow path over a group stashed in this wave's LDS area (vector slot u of
+// lane l at stash[u * 64 + l]). Element (u, e) of a lane has row-local index
+// base + (u * 64 + lane) * LS + e; -inf elements are outside the row.
 template <int NV, int EPV, int LS>
-__device__ __forceinline__ int elem_idx(int base, int u, int e, int lane, float x) {
-  return x == -INFINITY ? kInvalid : base + u * 64 * EPV + lane * LS + e;
-}
-
-// Exact pass over a group: every element that beats the threshold is offered.
-template <int NV, int EPV, int LS>
-__device__ __forceinline__ void group_exact(State& st, const float (&x)[NV][EPV], int base, int excl, int K,
-                            int lane) {
+__device__ __forceinline__ void group_slow(State& st, const u32x4_t* stash, int base, bool seed,
+                                           int K, int lane) {
+  int excl = -1;
+  if (seed) {
+    // the 64 lanes' best elements, bitonic-sorted (descending key); the first
+    // K seed the list, so the threshold starts at the K-th best lane maximum
+    float bv = -INFINITY;
+    int bi = kInvalid;
+    for (int u = 0; u < NV; ++u) {
+      const u32x4_t w = stash[u * 64 + lane];
 #pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float x = elem<EPV>(w, e);
+        const int id = base + (u * 64 + lane) * LS + e;
+        if (x != -INFINITY && key_gt(x, id, bv, bi)) {
+          bv = x;
+          bi = id;
+        }
+      }
+    }
+    float sv = bv;
+    int si = bi;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const float ov = __shfl_xor(sv, j, 64);
+        const int oi = __shfl_xor(si, j, 64);
+        const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
+        const bool mine_better = key_gt(sv, si, ov, oi);
+        if (keep_better != mine_better) {
+          sv = ov;
+          si = oi;
+        }
+      }
+    }
+    st.lv = lane < K ? sv : -INFINITY;
+    st.li = lane < K ? si : kInvalid;
+    st.th_v = readlane_f(st.lv, K - 1);
+    st.th_i = readlane_i(st.li, K - 1);
+    excl = bi;
+  }
   for (int u = 0; u < NV; ++u) {
-    float vm = x[u][0];
+    const u32x4_t w = stash[u * 64 + lane];
+    float vm = -INFINITY;
 #pragma unroll
-    for (int e = 1; e < EPV; ++e) vm = fmaxf(vm, x[u][e]);
+    for (int e = 0; e < EPV; ++e) vm = fmaxf(vm, elem<EPV>(w, e));
     if (!__any(vm >= st.th_v)) continue;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      const int id = elem_idx<NV, EPV, LS>(base, u, e, lane, x[u][e]);
-      offer(st, x[u][e], id, id != excl, K, lane);
+      const float x = elem<EPV>(w, e);
+      const int id = x == -INFINITY ? kInvalid : base + (u * 64 + lane) * LS + e;
+      offer(st, x, id, id != excl, K, lane);
     }
   }
-}
-
-// Seed the list from a group: sort the 64 lanes' best elements (bitonic,
-// descending by key), keep the first K, then offer the rest of the group.
-template <int NV, int EPV, int LS>
-__device__ __forceinline__ void group_seed(State& st, const float (&x)[NV][EPV], int base, int K, int lane) {
-  float bv = -INFINITY;
-  int bi = kInvalid;
-#pragma unroll
-  for (int u = 0; u < NV; ++u)
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      const int id = elem_idx<NV, EPV, LS>(base, u, e, lane, x[u][e]);
-      if (key_gt(x[u][e], id, bv, bi)) {
-        bv = x[u][e];
-        bi = id;
-      }
-    }
-  float sv = bv;
-  int si = bi;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float ov = __shfl_xor(sv, j, 64);
-      const int oi = __shfl_xor(si, j, 64);
-      const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
-      const bool mine_better = key_gt(sv, si, ov, oi);
-      if (keep_better != mine_better) {
-        sv = ov;
-        si = oi;
-      }
-    }
-  }
-  st.lv = lane < K ? sv : -INFINITY;
-  st.li = lane < K ? si : kInvalid;
-  st.th_v = readlane_f(st.lv, K - 1);
-  st.th_i = readlane_i(st.li, K - 1);
-  group_exact<NV, EPV, LS>(st, x, base, bi, K, lane);
-}
-
-template <int DT>
-__device__ __forceinline__ float load_scalar(const void* p, int64_t i) {
-  if (DT == 1) return bf16_to_f32(((const uint16_t*)p)[i]);
-  return ((const float*)p)[i];
 }
 
 template <int EPV>
 __device__ __forceinline__ void unpack(const u32x4_t& w, float (&x)[EPV]) {
-  if constexpr (EPV == 8) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      x[2 * d] = __uint_as_float(w[d] << 16);
-      x[2 * d + 1] = __uint_as_float(w[d] & 0xFFFF0000u);
-    }
-  } else {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) x[d] = __uint_as_float(w[d]);
-  }
+  for (int e = 0; e < EPV; ++e) x[e] = elem<EPV>(w, e);
 }
 
 // One wave per (row, chunk). DT: 0 = fp32 logits, 1 = bf16 logits.
 template <int DT, int NV>
-__global__ __launch_bounds__(256) void topk_partial_kernel(const void* __restrict__ logits,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_partial_kernel(const void* __restrict__ logits,
                                                            int rows, int V, int K, int P,
                                                            float* __restrict__ part_val,
                                                            int32_t* __restrict__ part_idx,
                                                            float* __restrict__ part_ms) {
   constexpr int EPV = DT == 1 ? 8 : 4;
+  // a 32-bit word holding -inf in every element
+  constexpr uint32_t kNegInfWord = DT == 1 ? 0xFF80FF80u : 0xFF800000u;
+  __shared__ u32x4_t stash_all[4][NV * 64];
   const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wid = threadIdx.x >> 6;
+  u32x4_t* stash = stash_all[wid];
+  const int g = blockIdx.x * 4 + wid;
   const int row = g / P, unit = g - (g / P) * P;
   if (row >= rows) return;
 
@@ -223,52 +227,77 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(const void* __restric
   st.th_i = kInvalid;
   bool seeded = false;
 
-  // Head: elements before the first aligned vector (owned by chunk 0). It is
-  // merged in after the list is seeded, with exact compares.
-  auto do_edge = [&](int64_t start, int len) {
-    float xe[1][EPV];
+  // Head / tail elements (fewer than EPV, or a row shorter than two vectors):
+  // one element per lane in slot (u = 0, e = 0), through the same slow path.
+  auto do_edge = [&](int64_t start, int len) __attribute__((always_inline)) {
+    const float x = lane < len ? load_scalar<DT>(logits, start + lane) : -INFINITY;
+    u32x4_t w = {0, 0, 0, 0};
+    if constexpr (EPV == 8)
+      w[0] = (__float_as_uint(x) >> 16) | 0xFF800000u;  // element 0 (exact), element 1 = -inf
+    else
+      w[0] = __float_as_uint(x);
+    w[1] = w[2] = w[3] = kNegInfWord;
+    u32x4_t wg[NV];
+    wg[0] = w;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) xe[0][e] = -INFINITY;
-    if (lane < len) xe[0][0] = load_scalar<DT>(logits, start + lane);
-    lse_update<1, EPV>(st, xe);
-    if (!seeded) {
-      group_seed<1, EPV, 1>(st, xe, (int)(start - rs), K, lane);
-      seeded = true;
-    } else {
-      group_exact<1, EPV, 1>(st, xe, (int)(start - rs), -1, K, lane);
-    }
+    for (int u = 1; u < NV; ++u) wg[u] = u32x4_t{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
+    group_lse<NV, EPV>(st, wg);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) stash[u * 64 + lane] = wg[u];
+    __builtin_amdgcn_wave_barrier();
+    group_slow<NV, EPV, 1>(st, stash, (int)(start - rs), !seeded, K, lane);
+    __builtin_amdgcn_wave_barrier();
+    seeded = true;
   };
 
   bool head_pending = unit == 0 && head_len > 0;
-  for (int64_t v = vb; v < ve; v += 64 * NV) {
-    float x[NV][EPV];
+  // Interior vectors [vb, ve), 64 * NV per iteration. Loads are unconditional
+  // (indices clamped into the chunk) so all NV of an iteration issue back to
+  // back, and the next iteration's loads are in flight while the current one
+  // is consumed. Only the final partial iteration has invalid slots.
+  auto load_group = [&](int64_t v, u32x4_t (&w)[NV]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int64_t vi = v + u * 64 + lane;
-      if (vi < ve) {
-        const u32x4_t w = __builtin_nontemporal_load(vbase + vi);
-        unpack<EPV>(w, x[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) x[u][e] = -INFINITY;
-      }
+      int64_t vi = v + u * 64 + lane;
+      vi = vi < ve ? vi : ve - 1;
+      w[u] = __builtin_nontemporal_load(vbase + vi);
     }
-    const int base = (int)(a0 - rs + v * EPV);
-    lse_update<NV, EPV>(st, x);
-    if (!seeded) {
-      group_seed<NV, EPV, EPV>(st, x, base, K, lane);
-      seeded = true;
-    } else {
-      float lm = x[0][0];
+  };
+  auto consume = [&](u32x4_t (&w)[NV], int64_t v) __attribute__((always_inline)) {
+    if (v + 64 * NV > ve) {
+      // last, partial iteration: slots past the chunk end read as -inf
 #pragma unroll
       for (int u = 0; u < NV; ++u)
+        if (v + u * 64 + lane >= ve) w[u] = u32x4_t{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
+    }
+    const float lm = group_lse<NV, EPV>(st, w);
+    if (!seeded || __any(lm > st.th_v)) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) lm = fmaxf(lm, x[u][e]);
-      if (__any(lm > st.th_v)) group_exact<NV, EPV, EPV>(st, x, base, -1, K, lane);
+      for (int u = 0; u < NV; ++u) stash[u * 64 + lane] = w[u];
+      __builtin_amdgcn_wave_barrier();
+      group_slow<NV, EPV, EPV>(st, stash, (int)(a0 - rs + v * EPV), !seeded, K, lane);
+      __builtin_amdgcn_wave_barrier();
+      seeded = true;
     }
     if (head_pending) {
       do_edge(rs, head_len);
       head_pending = false;
+    }
+  };
+  if (vb < ve) {
+    u32x4_t wa[NV], wb[NV];
+    int64_t v = vb;
+    load_group(v, wa);
+    while (true) {
+      const int64_t v1 = v + 64 * NV;
+      if (v1 < ve) load_group(v1, wb);
+      consume(wa, v);
+      if (v1 >= ve) break;
+      const int64_t v2 = v1 + 64 * NV;
+      if (v2 < ve) load_group(v2, wa);
+      consume(wb, v1);
+      if (v2 >= ve) break;
+      v = v2;
     }
   }
   if (head_pending) do_edge(rs, head_len);
@@ -326,20 +355,12 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
   float rv = -INFINITY;
   int ri = kInvalid;
   for (int k = 0; k < K; ++k) {
-    // wave argmax of the heads by (value desc, index asc); keys are unique
+    // wave argmax of the heads by (value desc, index asc); the winner is the
+    // lowest lane holding that key (keys are unique except exhausted lists)
     float bv = hv;
-    int bi = hi, bl = lane;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      const int ol = __shfl_xor(bl, off, 64);
-      if (key_gt(ov, oi, bv, bi) || (ov == bv && oi == bi && ol < bl)) {
-        bv = ov;
-        bi = oi;
-        bl = ol;
-      }
-    }
+    int bi = hi;
+    wave_argmax(bv, bi);
+    const int bl = __ffsll((long long)__ballot(hv == bv && hi == bi)) - 1;
     if (lane == k) {
       rv = bv;
       ri = bi;

@@ -69,15 +69,7 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
     }
     float bz = z;
     int bl = lane;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float oz = __shfl_xor(bz, off, 64);
-      const int ol = __shfl_xor(bl, off, 64);
-      if (oz > bz || (oz == bz && ol < bl)) {
-        bz = oz;
-        bl = ol;
-      }
-    }
+    wave_argmax(bz, bl);
     if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
     const float second = wave_max(lane == bl ? -INFINITY : z);
     cprev = bl;
@@ -154,15 +146,7 @@ __global__ __launch_bounds__(256) void scores_walk_kernel(
     }
     float bz = z;
     int bl = lane;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float oz = __shfl_xor(bz, off, 64);
-      const int ol = __shfl_xor(bl, off, 64);
-      if (oz > bz || (oz == bz && ol < bl)) {
-        bz = oz;
-        bl = ol;
-      }
-    }
+    wave_argmax(bz, bl);
     if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
     const float second = wave_max(lane == bl ? -INFINITY : z);
     cprev = bl;

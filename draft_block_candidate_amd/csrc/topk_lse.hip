@@ -7,24 +7,30 @@
 //
 // Design for gfx950 (the PR's Triton kernel pre-selects whole tiles; here the
 // unit of work is one wave64 streaming a contiguous chunk of a row):
-//  * each lane issues NV 16-byte non-temporal loads per iteration (coalesced:
-//    64 lanes read 1 KiB contiguous per load);
-//  * the log-partition is an online sum of exp2 terms against a lazily raised
-//    per-lane reference max (raised only when a value exceeds it by 16), so
-//    the common path is one fma + one v_exp_f32 + one add per element;
+//  * each lane issues NV 16-byte non-temporal buffer loads per group (64 lanes
+//    read 1 KiB contiguous per load); the next group is always in flight
+//    while the current one is consumed;
+//  * the log-partition is a per-lane sum of exp(x - ref) against a
+//    wave-uniform reference max that is raised only when a term exceeds 2^23,
+//    so the common path per element is unpack, fma, v_exp_f32 and add;
+//  * the same exponential terms gate the top-K: the largest term of each
+//    lane's vector is compared with exp(threshold - ref), so the streaming
+//    pass adds only a max3 per three terms and one compare per vector;
 //  * the running top-K is a sorted list held one entry per lane (lane k holds
-//    the k-th best key). An element can only enter if it beats entry K-1, the
-//    wave-uniform threshold; the per-iteration test is one compare of each
-//    lane's running max against it, so insertions (K ln(n/K) of them for n
-//    streamed elements in random order) are the only slow path;
-//  * the list is seeded from the first iteration by a 64-lane bitonic sort of
-//    the lanes' best elements, so it starts at a tight threshold;
-//  * chunks of one row are merged by a second kernel (one wave per row: a
-//    K-step tournament over the chunks' sorted lists plus the log-sum-exp
-//    combination of the chunks' (max, sum) pairs).
-// Exactness: the streamed order is ascending in vocabulary index, so a value
-// equal to the threshold never beats it in the fast test; everything that
-// reaches the slow path is compared on the full (value, index) key.
+//    the k-th best key); the threshold is entry K-1. Groups that pass the gate
+//    are scanned element position by element position (one ballot each) and
+//    candidates are inserted on the full (value, id) key; insertions number
+//    about K ln(n/K) for n streamed elements in random order;
+//  * the list is seeded from the first group by a 64-lane bitonic sort of the
+//    lanes' best elements, so it starts at a tight threshold;
+//  * a row split over several chunks is merged by a second kernel (one wave
+//    per row: a K-step tournament over the chunks' sorted lists plus the
+//    log-sum-exp combination of the chunks' (max, sum) pairs); a row that is
+//    one chunk is written directly.
+// Exactness: the gate can only let extra elements through (its slack covers
+// the rounding of the exponential); every element that reaches the scan is
+// decided on the full (value, id) key, and the top-K of a set under a total
+// order does not depend on the order the elements are offered in.
 #include <cmath>
 
 #include "common.hpp"
@@ -35,21 +41,43 @@ namespace ll {
 namespace {
 
 constexpr float kL2E = 1.4426950408889634f;
-constexpr float kLazy = 16.0f;      // reference max may lag the true max by this much
+// A term exp(x - ref) above 2^23 (x more than ~15.9 above the reference)
+// triggers a rebase of the reference to the group maximum.
+constexpr float kRebase = 8388608.0f;
 constexpr float kMInit = -1e30f;
+// The top-K gate compares exp(x - ref) with exp(threshold - ref) scaled down
+// by this factor, so that rounding of the exponential (a few ulp) can only
+// let extra elements through, never drop one.
+constexpr float kGateSlack = 0.99998474f;   // 1 - 2^-16
 constexpr int kInvalid = 0x7fffffff;
+// Buffer descriptor word 3 for raw (untyped) loads on gfx9-family targets.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: non-temporal (streamed once).
+constexpr int kLoadNonTemporal = 2;
 
 __device__ __forceinline__ bool key_gt(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
 struct State {
-  float m_ref, s;   // per lane: reference max and sum of exp(x - m_ref)
+  float ref;        // wave-uniform reference max (kMInit until a finite value is seen)
+  float nc;         // -ref * log2(e)
+  float s;          // per lane: sum of exp(x - ref)
   float lv;         // list entry of this lane (lanes >= K hold -inf)
   int li;
   float th_v;       // wave-uniform threshold = list entry K-1
   int th_i;
+  float p_th;       // wave-uniform gate: exp(th_v - ref) * kGateSlack
+  bool seeded;
 };
+
+__device__ __forceinline__ float exp_term(float x, float nc) {
+  return __builtin_amdgcn_exp2f(fmaf(x, kL2E, nc));
+}
+
+__device__ __forceinline__ void update_gate(State& st) {
+  st.p_th = exp_term(st.th_v, st.nc) * kGateSlack;
+}
 
 __device__ __forceinline__ void list_insert(State& st, float cv, int ci, int K, int lane) {
   const bool better = (lane < K) && key_gt(st.lv, st.li, cv, ci);
@@ -68,18 +96,6 @@ __device__ __forceinline__ void list_insert(State& st, float cv, int ci, int K, 
   st.th_i = readlane_i(st.li, K - 1);
 }
 
-// Offer one element slot of every lane to the list (exact key compare).
-__device__ __forceinline__ void offer(State& st, float x, int id, bool allowed, int K, int lane) {
-  uint64_t mask = __ballot(allowed && key_gt(x, id, st.th_v, st.th_i));
-  while (mask) {
-    const int l = __ffsll((long long)mask) - 1;
-    mask &= mask - 1;
-    const float cv = readlane_f(x, l);
-    const int ci = readlane_i(id, l);
-    if (key_gt(cv, ci, st.th_v, st.th_i)) list_insert(st, cv, ci, K, lane);
-  }
-}
-
 template <int DT>
 __device__ __forceinline__ float load_scalar(const void* p, int64_t i) {
   if (DT == 1) return bf16_to_f32(((const uint16_t*)p)[i]);
@@ -95,97 +111,153 @@ __device__ __forceinline__ float elem(const u32x4_t& w, int e) {
     return __uint_as_float(w[e]);
 }
 
-// Log-sum-exp update for one group of NV packed vectors per lane (slots
-// outside the chunk hold -inf words, which add nothing). Returns the lane's
-// group maximum.
+// exp(x - ref) summed over a group of NV packed vectors per lane (-inf
+// padding words add nothing); pm[u] receives the lane's largest term of
+// vector slot u, t the lane's sum.
 template <int NV, int EPV>
-__device__ __forceinline__ float group_lse(State& st, const u32x4_t (&w)[NV]) {
-  float lm = elem<EPV>(w[0], 0);
+__device__ __forceinline__ void lse_pass(float nc, const u32x4_t (&w)[NV], float& t, float (&pm)[NV]) {
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    float a = exp_term(elem<EPV>(w[u], 0), nc);
+    float m = a;
+#pragma unroll
+    for (int e = 1; e < EPV; ++e) {
+      const float p = exp_term(elem<EPV>(w[u], e), nc);
+      a += p;
+      m = fmaxf(m, p);
+    }
+    t = u == 0 ? a : t + a;
+    pm[u] = m;
+  }
+}
+
+// A copy of a group that the compiler cannot relate to the original, so that
+// the rarely taken paths unpack their own elements instead of keeping the
+// streaming pass's unpacked values alive in registers.
+template <int NV>
+__device__ __forceinline__ void opaque_copy(const u32x4_t (&w)[NV], u32x4_t (&c)[NV]) {
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    c[u] = w[u];
+    asm volatile("" : "+v"(c[u]));
+  }
+}
+
+// Raise the reference to the group maximum and recompute the group's terms.
+template <int NV, int EPV>
+__device__ __forceinline__ void rebase(State& st, const u32x4_t (&w0)[NV], float& t, float (&pm)[NV]) {
+  u32x4_t w[NV];
+  opaque_copy<NV>(w0, w);
+  float m = -INFINITY;
 #pragma unroll
   for (int u = 0; u < NV; ++u)
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) lm = fmaxf(lm, elem<EPV>(w[u], e));
-  if (__any(lm > st.m_ref + kLazy)) {
-    const float nm = lm > st.m_ref + kLazy ? lm : st.m_ref;
-    st.s *= __builtin_amdgcn_exp2f((st.m_ref - nm) * kL2E);
-    st.m_ref = nm;
+    for (int e = 0; e < EPV; ++e) m = fmaxf(m, elem<EPV>(w[u], e));
+  const float nm = fmaxf(st.ref, wave_max(m));
+  if (nm > st.ref) {
+    st.s *= __builtin_amdgcn_exp2f((st.ref - nm) * kL2E);
+    st.ref = nm;
+    st.nc = -nm * kL2E;
+    update_gate(st);
   }
-  const float c = st.m_ref * kL2E;
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    float t = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) t += __builtin_amdgcn_exp2f(fmaf(elem<EPV>(w[u], e), kL2E, -c));
-    st.s += t;
-  }
-  return lm;
+  lse_pass<NV, EPV>(st.nc, w, t, pm);
 }
 
-// Slow path over a group stashed in this wave's LDS area (vector slot u of
-// lane l at stash[u * 64 + l]). Element (u, e) of a lane has row-local index
-// base + (u * 64 + lane) * LS + e; -inf elements are outside the row.
+// Seed the list from a group: the 64 lanes' best elements, bitonic-sorted
+// (descending key); the first K become the list. Returns this lane's best id
+// (already offered, to be skipped by the candidate scan).
 template <int NV, int EPV, int LS>
-__device__ __forceinline__ void group_slow(State& st, const u32x4_t* stash, int base, bool seed,
-                                           int K, int lane) {
-  int excl = -1;
-  if (seed) {
-    // the 64 lanes' best elements, bitonic-sorted (descending key); the first
-    // K seed the list, so the threshold starts at the K-th best lane maximum
-    float bv = -INFINITY;
-    int bi = kInvalid;
-    for (int u = 0; u < NV; ++u) {
-      const u32x4_t w = stash[u * 64 + lane];
+__device__ __forceinline__ int seed_list(State& st, const u32x4_t (&w)[NV], int base, int K, int lane) {
+  float bv = -INFINITY;
+  int bi = kInvalid;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float x = elem<EPV>(w, e);
-        const int id = base + (u * 64 + lane) * LS + e;
-        if (x != -INFINITY && key_gt(x, id, bv, bi)) {
-          bv = x;
-          bi = id;
-        }
-      }
-    }
-    float sv = bv;
-    int si = bi;
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        const float ov = __shfl_xor(sv, j, 64);
-        const int oi = __shfl_xor(si, j, 64);
-        const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
-        const bool mine_better = key_gt(sv, si, ov, oi);
-        if (keep_better != mine_better) {
-          sv = ov;
-          si = oi;
-        }
-      }
-    }
-    st.lv = lane < K ? sv : -INFINITY;
-    st.li = lane < K ? si : kInvalid;
-    st.th_v = readlane_f(st.lv, K - 1);
-    st.th_i = readlane_i(st.li, K - 1);
-    excl = bi;
-  }
-  for (int u = 0; u < NV; ++u) {
-    const u32x4_t w = stash[u * 64 + lane];
-    float vm = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) vm = fmaxf(vm, elem<EPV>(w, e));
-    if (!__any(vm >= st.th_v)) continue;
+  for (int u = 0; u < NV; ++u)
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      const float x = elem<EPV>(w, e);
-      const int id = x == -INFINITY ? kInvalid : base + (u * 64 + lane) * LS + e;
-      offer(st, x, id, id != excl, K, lane);
+      // a lane's ids increase with (u, e): strict > keeps the lowest id of a tie
+      const float x = elem<EPV>(w[u], e);
+      if (x > bv) {
+        bv = x;
+        bi = base + (u * 64 + lane) * LS + e;
+      }
+    }
+  float sv = bv;
+  int si = bi;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float ov = __shfl_xor(sv, j, 64);
+      const int oi = __shfl_xor(si, j, 64);
+      const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
+      const bool mine_better = key_gt(sv, si, ov, oi);
+      if (keep_better != mine_better) {
+        sv = ov;
+        si = oi;
+      }
     }
   }
+  st.lv = lane < K ? sv : -INFINITY;
+  st.li = lane < K ? si : kInvalid;
+  st.th_v = readlane_f(st.lv, K - 1);
+  st.th_i = readlane_i(st.li, K - 1);
+  st.seeded = true;
+  return bi;
 }
 
-template <int EPV>
-__device__ __forceinline__ void unpack(const u32x4_t& w, float (&x)[EPV]) {
+// Top-K update from a group whose terms passed the gate somewhere. For each
+// vector slot that may hold an element >= threshold, each element position e
+// is tested in all lanes at once; the lanes that pass are visited one at a
+// time and decided on the full (value, id) key.
+// Element (u, e) of lane l has row-local id base + (u * 64 + l) * LS + e.
+template <int NV, int EPV, int LS>
+__device__ __forceinline__ void topk_pass(State& st, const u32x4_t (&w0)[NV], const float (&pm)[NV],
+                                          int base, int K, int lane) {
+  u32x4_t w[NV];
+  opaque_copy<NV>(w0, w);
+  int excl = -1;
+  if (!st.seeded) {
+    excl = seed_list<NV, EPV, LS>(st, w, base, K, lane);
+    update_gate(st);
+  }
 #pragma unroll
-  for (int e = 0; e < EPV; ++e) x[e] = elem<EPV>(w, e);
+  for (int u = 0; u < NV; ++u) {
+    if (!__any(pm[u] >= st.p_th)) continue;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const float x = elem<EPV>(w[u], e);
+      // logits are finite: -inf elements are padding and never enter
+      uint64_t mask = __ballot(x >= fmaxf(st.th_v, -3.402823466e38f));
+      while (mask) {
+        const int l = __ffsll((long long)mask) - 1;
+        mask &= mask - 1;
+        const float cv = readlane_f(x, l);
+        const int ci = base + (u * 64 + l) * LS + e;
+        if (ci != readlane_i(excl, l) && key_gt(cv, ci, st.th_v, st.th_i))
+          list_insert(st, cv, ci, K, lane);
+      }
+    }
+  }
+  update_gate(st);
+}
+
+// One group: log-partition terms, then the gated top-K update.
+template <int NV, int EPV, int LS>
+__device__ __forceinline__ void consume_group(State& st, const u32x4_t (&w)[NV], int base, int K,
+                                              int lane) {
+  float t, pm[NV];
+  lse_pass<NV, EPV>(st.nc, w, t, pm);
+  float pmax = pm[0];
+#pragma unroll
+  for (int u = 1; u < NV; ++u) pmax = fmaxf(pmax, pm[u]);
+  if (__any(pmax > kRebase)) {
+    rebase<NV, EPV>(st, w, t, pm);
+    pmax = pm[0];
+#pragma unroll
+    for (int u = 1; u < NV; ++u) pmax = fmaxf(pmax, pm[u]);
+  }
+  st.s += t;
+  if (!st.seeded || __any(pmax >= st.p_th)) topk_pass<NV, EPV, LS>(st, w, pm, base, K, lane);
 }
 
 // One wave per (row, chunk). DT: 0 = fp32 logits, 1 = bf16 logits.
@@ -194,14 +266,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
                                                            int rows, int V, int K, int P,
                                                            float* __restrict__ part_val,
                                                            int32_t* __restrict__ part_idx,
-                                                           float* __restrict__ part_ms) {
+                                                           float* __restrict__ part_ms,
+                                                           int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_logp,
+                                                           float* __restrict__ lse_out) {
   constexpr int EPV = DT == 1 ? 8 : 4;
   // a 32-bit word holding -inf in every element
   constexpr uint32_t kNegInfWord = DT == 1 ? 0xFF80FF80u : 0xFF800000u;
-  __shared__ u32x4_t stash_all[4][NV * 64];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  u32x4_t* stash = stash_all[wid];
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x * 4 + wid;
   const int row = g / P, unit = g - (g / P) * P;
   if (row >= rows) return;
@@ -212,107 +285,96 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     a0 = re;
     a1 = re;
   }
-  const int64_t nv = (a1 - a0) / EPV;
-  const int64_t cv = (nv + P - 1) / P;
-  const int64_t vb = min(nv, (int64_t)unit * cv), ve = min(nv, vb + cv);
+  // vector indices relative to the row's first aligned vector (< 2^31)
+  const int nv = (int)((a1 - a0) / EPV);
+  const int cv = (nv + P - 1) / P;
+  const int vb = min(nv, unit * cv), ve = min(nv, vb + cv);
   const u32x4_t* vbase = (const u32x4_t*)logits + a0 / EPV;
   const int head_len = (int)(a0 - rs), tail_len = (int)(re - a1);
 
   State st;
-  st.m_ref = kMInit;
+  st.ref = kMInit;
+  st.nc = -kMInit * kL2E;
   st.s = 0.f;
   st.lv = -INFINITY;
   st.li = kInvalid;
   st.th_v = -INFINITY;
   st.th_i = kInvalid;
-  bool seeded = false;
+  st.p_th = 0.f;
+  st.seeded = false;
 
-  // Head / tail elements (fewer than EPV, or a row shorter than two vectors):
-  // one element per lane in slot (u = 0, e = 0), through the same slow path.
-  auto do_edge = [&](int64_t start, int len) __attribute__((always_inline)) {
-    const float x = lane < len ? load_scalar<DT>(logits, start + lane) : -INFINITY;
-    u32x4_t w = {0, 0, 0, 0};
-    if constexpr (EPV == 8)
-      w[0] = (__float_as_uint(x) >> 16) | 0xFF800000u;  // element 0 (exact), element 1 = -inf
-    else
-      w[0] = __float_as_uint(x);
-    w[1] = w[2] = w[3] = kNegInfWord;
-    u32x4_t wg[NV];
-    wg[0] = w;
+  // Interior vectors [vb, ve), 64 * NV per group, read with buffer loads
+  // through a per-group descriptor whose range ends at the chunk end: a load
+  // past it returns zero without touching memory, so every load is issued
+  // unconditionally, the loop body is straight-line and the next group's
+  // loads stay in flight while the current group is consumed. Only the final
+  // partial group has padding slots (set to -inf below).
+  auto load_group = [&](int v, u32x4_t (&w)[NV]) __attribute__((always_inline)) {
+    const int bytes = max(0, ve - v) * 16;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + v), 0, bytes, kBufferWord3);
 #pragma unroll
-    for (int u = 1; u < NV; ++u) wg[u] = u32x4_t{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
-    group_lse<NV, EPV>(st, wg);
-#pragma unroll
-    for (int u = 0; u < NV; ++u) stash[u * 64 + lane] = wg[u];
-    __builtin_amdgcn_wave_barrier();
-    group_slow<NV, EPV, 1>(st, stash, (int)(start - rs), !seeded, K, lane);
-    __builtin_amdgcn_wave_barrier();
-    seeded = true;
+    for (int u = 0; u < NV; ++u)
+      w[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u * 64 + lane) * 16, 0, kLoadNonTemporal);
   };
-
-  bool head_pending = unit == 0 && head_len > 0;
-  // Interior vectors [vb, ve), 64 * NV per iteration. Loads are unconditional
-  // (indices clamped into the chunk) so all NV of an iteration issue back to
-  // back, and the next iteration's loads are in flight while the current one
-  // is consumed. Only the final partial iteration has invalid slots.
-  auto load_group = [&](int64_t v, u32x4_t (&w)[NV]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      int64_t vi = v + u * 64 + lane;
-      vi = vi < ve ? vi : ve - 1;
-      w[u] = __builtin_nontemporal_load(vbase + vi);
-    }
-  };
-  auto consume = [&](u32x4_t (&w)[NV], int64_t v) __attribute__((always_inline)) {
+  auto consume = [&](u32x4_t (&w)[NV], int v) __attribute__((always_inline)) {
     if (v + 64 * NV > ve) {
-      // last, partial iteration: slots past the chunk end read as -inf
 #pragma unroll
       for (int u = 0; u < NV; ++u)
         if (v + u * 64 + lane >= ve) w[u] = u32x4_t{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
     }
-    const float lm = group_lse<NV, EPV>(st, w);
-    if (!seeded || __any(lm > st.th_v)) {
-#pragma unroll
-      for (int u = 0; u < NV; ++u) stash[u * 64 + lane] = w[u];
-      __builtin_amdgcn_wave_barrier();
-      group_slow<NV, EPV, EPV>(st, stash, (int)(a0 - rs + v * EPV), !seeded, K, lane);
-      __builtin_amdgcn_wave_barrier();
-      seeded = true;
-    }
-    if (head_pending) {
-      do_edge(rs, head_len);
-      head_pending = false;
-    }
+    consume_group<NV, EPV, EPV>(st, w, (int)(a0 - rs) + v * EPV, K, lane);
   };
   if (vb < ve) {
     u32x4_t wa[NV], wb[NV];
-    int64_t v = vb;
+    int v = vb;
     load_group(v, wa);
     while (true) {
-      const int64_t v1 = v + 64 * NV;
-      if (v1 < ve) load_group(v1, wb);
+      load_group(v + 64 * NV, wb);
       consume(wa, v);
-      if (v1 >= ve) break;
-      const int64_t v2 = v1 + 64 * NV;
-      if (v2 < ve) load_group(v2, wa);
-      consume(wb, v1);
-      if (v2 >= ve) break;
-      v = v2;
+      if (v + 64 * NV >= ve) break;
+      load_group(v + 128 * NV, wa);
+      consume(wb, v + 64 * NV);
+      if (v + 128 * NV >= ve) break;
+      v += 128 * NV;
     }
   }
-  if (head_pending) do_edge(rs, head_len);
+
+  // Head / tail elements (fewer than EPV each, or a row too short for an
+  // aligned vector): one element per lane, as a one-vector group whose
+  // element 0 is the lane's element.
+  auto do_edge = [&](int64_t start, int len) __attribute__((always_inline)) {
+    const float x = lane < len ? load_scalar<DT>(logits, start + lane) : -INFINITY;
+    u32x4_t w1[1];
+    w1[0] = u32x4_t{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
+    if constexpr (EPV == 8)
+      w1[0][0] = (__float_as_uint(x) >> 16) | 0xFF800000u;  // element 0 exact, element 1 = -inf
+    else
+      w1[0][0] = __float_as_uint(x);
+    consume_group<1, EPV, 1>(st, w1, (int)(start - rs), K, lane);
+  };
+  if (unit == 0 && head_len > 0) do_edge(rs, head_len);
   if (unit == P - 1 && tail_len > 0) do_edge(a1, tail_len);
 
+  const float S = wave_sum(st.s);
+  if (P == 1) {
+    // the row is one chunk: its sorted list is the answer
+    const float lse = st.ref + logf(S);
+    if (lane < K) {
+      topk_idx[(int64_t)row * K + lane] = st.li;
+      topk_logp[(int64_t)row * K + lane] = __fsub_rn(st.lv, lse);
+    }
+    if (lse_out != nullptr && lane == 0) lse_out[row] = lse;
+    return;
+  }
   // Chunk outputs: sorted list and (reference max, sum) of the wave.
   const int64_t o = (int64_t)row * P + unit;
   if (lane < K) {
     part_val[o * K + lane] = st.lv;
     part_idx[o * K + lane] = st.li;
   }
-  const float M = wave_max(st.m_ref);
-  const float S = wave_sum(st.s * __builtin_amdgcn_exp2f((st.m_ref - M) * kL2E));
   if (lane == 0) {
-    part_ms[2 * o] = M;
+    part_ms[2 * o] = st.ref;
     part_ms[2 * o + 1] = S;
   }
 }
@@ -393,12 +455,12 @@ hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype
   const unsigned blocks = (unsigned)((waves + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL((topk_partial_kernel<1, 4>), dim3(blocks), dim3(256), 0, stream, logits,
-                       rows, V, K, P, part_val, part_idx, part_ms);
+                       rows, V, K, P, part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
   else
     hipLaunchKernelGGL((topk_partial_kernel<0, 4>), dim3(blocks), dim3(256), 0, stream, logits,
-                       rows, V, K, P, part_val, part_idx, part_ms);
+                       rows, V, K, P, part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || P == 1) return e;
   hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(64), (size_t)P * K * 8, stream,
                      rows, K, P, part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
   return hipGetLastError();

@@ -11,6 +11,15 @@ V = 151,936 bf16 logits with three spikes per slot, K = 8, encoder width 1024,
 Logits are resident in HBM before timing; consecutive steps rotate over
 enough logits buffers (>= 768 MiB in total) that each step reads its logits
 cold, not from the 256 MiB Infinity Cache. Prints one JSON line.
+
+Per-stage times come from the library's stage-timing events (two events
+recorded on the library's stream around one stage of a lilicorr_rerank
+call). The dominant stage is found in untimed steps; in the timed steps it is
+bracketed by its own event pair every step, and `roofline` divides that
+stage's algorithmic bytes or flops by the mean bracketed duration. `traffic`
+is the HBM bytes per launch from a committed rocprofv3 counter summary
+(profiles/traffic_<workload>_<stage>.md), reported only while the kernel
+sources still hash to the value recorded there.
 """
 from __future__ import annotations
 
@@ -38,30 +47,27 @@ def parse():
     ap.add_argument("--workload", default="c1_qwen3_8b")
     ap.add_argument("--tier", type=int, default=0)
     ap.add_argument("--rotate-mib", type=float, default=768.0)
-    ap.add_argument("--probe-reps", type=int, default=50)
+    ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
+    ap.add_argument("--copy-probe-mib", type=float, default=0.0,
+                    help="after the run, stream this many MiB through a plain copy kernel three "
+                         "times (the known-size reference for HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, both with --copy-probe-mib) into HBM bytes per stage launch")
     return ap.parse_args()
-
-
-def event_time_ms(fn, reps, stream):
-    import torch
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(reps):
-        fn()
-    stop.record(stream)
-    stop.synchronize()
-    return start.elapsed_time(stop) / reps
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(blocks are independent; see DESIGN.md for how it would shard)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path here "
+              "(draft blocks are independent; the path would shard by blocks)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -87,6 +93,7 @@ def main():
     ws = L.Workspace(w.num_blocks, w.slots, w.vocab, w.topk, dims, device=dev)
     out = torch.empty((w.num_blocks, w.slots), dtype=torch.int32, device=dev)
     N, B, V, K = w.num_blocks, w.slots, w.vocab, w.topk
+    H, F, de = w.hidden, w.ffn, w.d_e
     ldt = L.BF16 if w.dtype == "bf16" else L.F32
     params = [L.make_params(N, ldt, weights, ws, w.alpha, True) for _ in range(1)]
     lib = L.lib()
@@ -127,93 +134,87 @@ def main():
             graphs[gstate["i"] % nbuf].replay()
             gstate["i"] += 1
 
+    # ---- per-stage durations, measured in the pipeline with the library's
+    # stage events (a few untimed steps per stage)
+    stage_names = stage_table(w)
+    stage_ms = {}
+
+    def new_event():
+        # torch creates the HIP event on its first record; the library then
+        # re-records the same handle
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    # each stage is bracketed in stage_reps consecutive steps with no host
+    # synchronisation between them, as in the timed region
+    cal = [(new_event(), new_event()) for _ in range(args.stage_reps)]
+    for sid in stage_names:
+        for i in range(args.stage_reps):
+            set_timing(params[0], sid, cal[i][0], cal[i][1])
+            step()
+        cal[-1][1].synchronize()
+        stage_ms[sid] = sum(a.elapsed_time(b) for a, b in cal) / args.stage_reps
+    set_timing(params[0], None)
+    dom_sid = max(stage_ms, key=lambda k: stage_ms[k])
+
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
+    # ---- timed region: K steps; the dominant stage is bracketed by its own
+    # event pair in every step (not in graph mode, where the step is replayed)
+    pairs = [(new_event(), new_event()) for _ in range(args.steps)] if not args.graph else []
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
-    ms = event_time_ms(run, args.steps, stream)
-    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        if pairs:
+            set_timing(params[0], dom_sid, pairs[i][0], pairs[i][1])
+        run()
+    stop.record(stream)
+    stop.synchronize()
     wall = time.perf_counter() - t_wall
+    set_timing(params[0], None)
+    ms = start.elapsed_time(stop) / args.steps
     value = N / (ms * 1e-3)
+    if pairs:
+        dom_ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+        dom_src = "live: stage events in every timed step"
+    else:
+        dom_ms = stage_ms[dom_sid]
+        dom_src = "stage events in untimed eager steps (graph mode)"
 
-    # ---- live per-kernel probes (same kernels through the component entry points)
-    M = N * B * K
-    H, F, de = w.hidden, w.ffn, w.d_e
-    probes = {}
-    tk = {"i": 0}
-    nb = len(bufs)
-    rows = N * B
-
-    def topk_probe():
-        b = bufs[tk["i"] % nb]
-        tk["i"] += 1
-        L.topk_lse(b.view(rows, V), K)
-
-    # allocation inside topk_lse happens through torch's caching allocator; warm it
-    topk_probe()
-    torch.cuda.synchronize()
-    t_topk = event_time_ms(topk_probe, args.probe_reps, stream)
-    topk_bytes = rows * V * esize + rows * (8 * K + 4)
-    probes["topk_lse"] = {"ms": t_topk, "launches_per_step": 1, "bytes": topk_bytes, "flops": 0}
-
-    g = torch.Generator(device="cpu").manual_seed(0)
-    def rnd(shape, scale=1.0):
-        return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16).to(dev)
-    shapes = {
-        "linear_conf_w2": (M, H, H, L.EPI_RESID_F32, 1),
-        "linear_qkv": (M, H, 3 * H, L.EPI_BF16, 2),
-        "linear_o": (M, H, H, L.EPI_RESID_F32, 2),
-        "linear_ffn1": (M, H, F, L.EPI_SILU_BF16, 2),
-        "linear_ffn2": (M, F, H, L.EPI_RESID_F32, 2),
-        "linear_heads": (M, H, 2 * de, L.EPI_F32, 1),
-    }
-    for name, (m, kd, n, epi, cnt) in shapes.items():
-        A = rnd((m, kd))
-        Wt = rnd((n, kd), 1 / math.sqrt(kd))
-        bias = torch.zeros(n, dtype=torch.float32, device=dev)
-        resid = torch.zeros((m, n), dtype=torch.float32, device=dev)
-        lws = torch.empty(max(256, int(lib.lilicorr_linear_workspace_bytes(m, kd, n))), dtype=torch.uint8,
-                          device=dev)
-        fn = lambda: L.linear(A, Wt, bias, epi, resid if epi == L.EPI_RESID_F32 else None, lws)
-        fn()
-        torch.cuda.synchronize()
-        t = event_time_ms(fn, args.probe_reps, stream)
-        out_b = 4 if epi in (L.EPI_F32, L.EPI_RESID_F32) else 2
-        nbytes = m * kd * 2 + n * kd * 2 + n * 4 + m * n * out_b + (m * n * 4 if epi == L.EPI_RESID_F32 else 0)
-        probes[name] = {"ms": t, "launches_per_step": cnt, "bytes": nbytes, "flops": 2 * m * n * kd}
-    qkv = rnd((M, 3 * H))
-    dist = torch.zeros((w.heads, 127), dtype=torch.float32, device=dev)
-    same = torch.zeros((w.heads,), dtype=torch.float32, device=dev)
-    fn = lambda: L.lattice_attention(qkv, N, B, K, H, w.heads, dist, same)
-    fn()
-    torch.cuda.synchronize()
-    T = B * K
-    probes["lattice_attention"] = {"ms": event_time_ms(fn, args.probe_reps, stream), "launches_per_step": 2,
-                                   "bytes": M * 3 * H * 2 + M * H * 2,
-                                   "flops": 4 * N * w.heads * T * T * (H // w.heads)}
-
-    for p in probes.values():
-        p["ms_per_step"] = p["ms"] * p["launches_per_step"]
-    dom_name = max(probes, key=lambda k: probes[k]["ms_per_step"])
-    dom = probes[dom_name]
-    intensity = dom["flops"] / max(dom["bytes"], 1)
+    dom = stage_names[dom_sid]
+    work = stage_work(w, dom_sid)
+    intensity = work["flops"] / max(work["bytes"], 1)
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if dom["flops"] and intensity >= ridge:
-        achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    if work["flops"] and intensity >= ridge:
+        achieved = work["flops"] / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:
-        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        achieved = work["bytes"] / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = dom_name
+    roof["traffic"] = counter_traffic(w.name, dom)
+    roof["kernel"] = dom
+    roof["us_per_launch"] = dom_ms * 1e3
+    roof["duration_source"] = dom_src
+    roof["algorithmic"] = {"bytes": work["bytes"], "flops": work["flops"]}
 
-    enc_flops = sum(p["flops"] * p["launches_per_step"] for k, p in probes.items() if k != "topk_lse")
-    enc_ms = sum(p["ms_per_step"] for k, p in probes.items() if k != "topk_lse")
-    stages = {k: {"us": round(p["ms"] * 1e3, 3), "per_step": p["launches_per_step"],
-                  "GB_s": round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1),
-                  "TFLOP_s": round(p["flops"] / (p["ms"] * 1e-3) / 1e12, 2)} for k, p in probes.items()}
-    topk_gbs = topk_bytes / (t_topk * 1e-3) / 1e9
+    stages = {}
+    enc_flops = enc_ms = 0.0
+    for sid, name in stage_names.items():
+        wk = stage_work(w, sid)
+        t = stage_ms[sid]
+        stages[name] = {"us": round(t * 1e3, 2), "GB_s": round(wk["bytes"] / (t * 1e-3) / 1e9, 1),
+                        "TFLOP_s": round(wk["flops"] / (t * 1e-3) / 1e12, 2)}
+        if sid not in (0, 14):
+            enc_flops += wk["flops"]
+            enc_ms += t
+    topk_w = stage_work(w, 0)
+    topk_gbs = topk_w["bytes"] / (stage_ms[0] * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -234,8 +235,8 @@ def main():
                    "graph": bool(args.graph), "rotating_logits_buffers": nbuf},
         "roofline": roof,
         "topk_hbm": {"achieved_GB_s": topk_gbs, "frac": topk_gbs / PEAK_HBM_GBS},
-        "encoder_mfma": {"achieved_TFLOP_s": enc_flops / (enc_ms * 1e-3) / 1e12 if enc_ms else None,
-                         "frac": (enc_flops / (enc_ms * 1e-3) / 1e12) / PEAK_BF16_TFLOPS if enc_ms else None},
+        "encoder_mfma": {"achieved_TFLOP_s": enc_flops / (enc_ms * 1e-3) / 1e12,
+                         "frac": enc_flops / (enc_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "stages": stages,
         "wall_s_timed": wall,
     }
@@ -243,6 +244,204 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    if args.copy_probe_mib > 0:
+        n = int(args.copy_probe_mib * 2 ** 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)    # reads and writes n * 4 bytes once each
+        torch.cuda.synchronize()
+
+
+def set_timing(params, sid, begin=None, end=None):
+    """Point the library's stage-timing events at (begin, end) for stage sid."""
+    import ctypes
+    if sid is None:
+        params.timing_begin = None
+        params.timing_end = None
+        params.timing_stage = 0
+        return
+    params.timing_stage = sid
+    params.timing_begin = ctypes.c_void_p(begin.cuda_event)
+    params.timing_end = ctypes.c_void_p(end.cuda_event)
+
+
+def stage_table(w):
+    """lilicorr_stage id -> name (layer stages of layer l at base + 5 l)."""
+    names = {0: "topk_lse", 1: "node_build", 2: "linear_conf_w2"}
+    for l in range(2):
+        for j, n in enumerate(["linear_qkv", "lattice_attention", "linear_o", "linear_ffn1", "linear_ffn2"]):
+            names[3 + j + 5 * l] = f"{n}.l{l}"
+    names[13] = "linear_heads"
+    names[14] = "scores_walk"
+    return names
+
+
+def stage_work(w, sid):
+    """Algorithmic bytes and flops of one stage for one call over the workload."""
+    N, B, V, K = w.num_blocks, w.slots, w.vocab, w.topk
+    H, F, de, h = w.hidden, w.ffn, w.d_e, w.heads
+    rows, T = N * B, B * K
+    M = rows * K
+    es = 2 if w.dtype == "bf16" else 4
+
+    def lin(kd, n, a_b, out_b, resid=False, norm_out=False):
+        by = M * kd * a_b + n * kd * 2 + n * 4 + M * n * out_b
+        if resid:
+            by += M * n * 4          # residual read (the write is out_b)
+        if norm_out:
+            by += M * n * 2          # bf16 RMSNorm output
+        return {"bytes": by, "flops": 2 * M * n * kd}
+
+    layer = sid - 3
+    if sid == 0:
+        return {"bytes": rows * V * es + rows * (8 * K + 4), "flops": 0}
+    if sid == 1:   # E rows, S/R tables, first confidence layer; writes x (f32), hid (bf16)
+        return {"bytes": M * H * 2 + 2 * 64 * H * 2 + H * (5 * 2 + 4) + M * 8 + M * H * (4 + 2),
+                "flops": 2 * M * H * 5 + 4 * M * H}
+    if sid == 2:
+        return lin(H, H, 2, 4, resid=True, norm_out=True)
+    if 3 <= sid <= 12:
+        j = layer % 5
+        if j == 0:
+            return lin(H, 3 * H, 2, 2)
+        if j == 1:
+            return {"bytes": M * 3 * H * 2 + M * H * 2 + h * 128 * 4,
+                    "flops": 4 * N * h * T * T * (H // h)}
+        if j == 2:
+            return lin(H, H, 2, 4, resid=True, norm_out=True)
+        if j == 3:
+            return lin(H, F, 2, 2)
+        return lin(F, H, 2, 4, resid=True, norm_out=True)
+    if sid == 13:
+        return lin(H, 2 * de, 2, 2)
+    return {"bytes": 2 * M * de * 2 + rows * K * 8 + rows * 4,
+            "flops": 2 * N * (B - 1) * K * K * de}
+
+
+def counter_traffic(workload, stage):
+    """HBM bytes per launch of a stage from the committed rocprofv3 counter
+    summary of this workload, if the kernel sources are unchanged since the
+    counters were taken; else None."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"^csrc_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m_h or m_h.group(1) != csrc_sha256():
+        return None
+    m = re.search(r"^\|\s*" + re.escape(stage) + r"\s*\|\s*(\d+)\s*\|", text, re.M)
+    return int(m.group(1)) if m else None
+
+
+# Kernel roles, by name, for splitting a step's dispatch sequence into stages.
+_GEMM_MAIN = ("gemm_kernel", "gemm_part_kernel")
+_GEMM_TAIL = ("splitk_", "rmsnorm", "heads_l2norm")
+_LINEAR_ORDER = ["linear_conf_w2"] + [f"{n}.l{l}" for l in range(2)
+                                      for n in ("linear_qkv", "linear_o", "linear_ffn1", "linear_ffn2")] \
+    + ["linear_heads"]
+
+
+def split_step_stages(names):
+    """Stage name for each kernel of one step's dispatch sequence."""
+    out, lin, att = [], 0, 0
+    for n in names:
+        if "topk_" in n:
+            out.append("topk_lse")
+        elif "node_build" in n:
+            out.append("node_build")
+        elif "attention_kernel" in n:
+            out.append(f"lattice_attention.l{att}")
+            att += 1
+        elif any(k in n for k in _GEMM_MAIN):
+            out.append(_LINEAR_ORDER[lin])
+            lin += 1
+        elif any(k in n for k in _GEMM_TAIL):
+            out.append(_LINEAR_ORDER[lin - 1])
+        elif "scores_walk" in n or "pair_scores" in n or "greedy_walk" in n:
+            out.append("scores_walk")
+        else:
+            out.append(None)
+    return out
+
+
+def read_counter_csv(d, counter):
+    """(dispatch id, kernel name, value) rows of one counter from a rocprofv3 CSV directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    rows = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            prev = rows.get(key)
+            val = float(r["Counter_Value"]) + (prev[2] if prev else 0.0)
+            rows[key] = (key, r["Kernel_Name"], val)
+    return [rows[k] for k in sorted(rows)]
+
+
+def summarize_counters(args):
+    """Per-stage HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs."""
+    scale = {}
+    per_stage = {}
+    for counter, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_counters):
+        rows = read_counter_csv(d, counter)
+        copy = [v for _, n, v in rows if "neg_kernel" in n or "neg" in n.split("<")[0]]
+        ref_kib = args.copy_probe_mib * 1024
+        if not copy or ref_kib <= 0:
+            raise SystemExit("the counter runs need --copy-probe-mib and its copy kernel")
+        scale[counter] = ref_kib / (sum(copy[-3:]) / len(copy[-3:]))
+        # steps: from each top-K dispatch to the next scores/walk dispatch
+        names = [n for _, n, _ in rows]
+        i = 0
+        while i < len(rows):
+            if "topk_partial" not in names[i]:
+                i += 1
+                continue
+            j = i
+            while j < len(rows) and not ("scores_walk" in names[j] or "greedy_walk" in names[j]):
+                j += 1
+            if j >= len(rows):
+                break
+            seq = rows[i:j + 1]
+            step_sum = {}
+            for (_, n, v), st in zip(seq, split_step_stages([n for _, n, _ in seq])):
+                if st is not None:
+                    step_sum[st] = step_sum.get(st, 0.0) + v
+            for st, v in step_sum.items():
+                per_stage.setdefault(st, {}).setdefault(counter, []).append(v)
+            i = j + 1
+    w = args.workload
+    print(f"# HBM traffic per stage launch: {w}\n")
+    print("Counters: rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch), one run each,")
+    print("scaled by what the same counter reads for a plain copy kernel of known size")
+    print(f"({args.copy_probe_mib:g} MiB read and written by torch.neg):")
+    print(f"FETCH_SIZE scale {scale['FETCH_SIZE']:.4f}, WRITE_SIZE scale {scale['WRITE_SIZE']:.4f}.\n")
+    print(f"csrc_sha256: {csrc_sha256()}\n")
+    print("| stage | HBM bytes per launch (fetch + write) | fetch bytes | write bytes | steps |")
+    print("|---|---|---|---|---|")
+    for st, c in per_stage.items():
+        f = c.get("FETCH_SIZE", [])
+        wr = c.get("WRITE_SIZE", [])
+        f_b = sum(f) / max(1, len(f)) * 1024 * scale["FETCH_SIZE"]
+        w_b = sum(wr) / max(1, len(wr)) * 1024 * scale["WRITE_SIZE"]
+        print(f"| {st} | {int(round(f_b + w_b))} | {int(round(f_b))} | {int(round(w_b))} | {len(f)} |")
+
+
+def csrc_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "draft_block_candidate_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
 
 
 def cpu_baseline(w, host, seconds):

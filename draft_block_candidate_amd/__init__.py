@@ -18,6 +18,10 @@ LIB_PATH = os.path.join(_PKG, "liblilicorr.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EWEIGHTS, EHIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 EPI_F32, EPI_BF16, EPI_SILU_BF16, EPI_RESID_F32 = 0, 1, 2, 3
+# lilicorr_stage values (per-layer stages of layer l: base + 5*l)
+STAGE_TOPK, STAGE_NODE, STAGE_CONF_LINEAR = 0, 1, 2
+STAGE_QKV, STAGE_ATTENTION, STAGE_O, STAGE_FFN1, STAGE_FFN2 = 3, 4, 5, 6, 7
+STAGE_HEADS, STAGE_SCORES_WALK, STAGE_COUNT = 13, 14, 15
 ABI_VERSION = 1
 MAX_SLOTS, MAX_TOPK, MAX_LATTICE = 64, 64, 512
 
@@ -51,7 +55,9 @@ class Params(ctypes.Structure):
                 ("dbg_topk_idx", ctypes.c_void_p), ("dbg_topk_logp", ctypes.c_void_p),
                 ("dbg_lse", ctypes.c_void_p), ("dbg_outv", ctypes.c_void_p),
                 ("dbg_inv", ctypes.c_void_p), ("dbg_cos", ctypes.c_void_p),
-                ("dbg_score", ctypes.c_void_p), ("dbg_gap", ctypes.c_void_p)]
+                ("dbg_score", ctypes.c_void_p), ("dbg_gap", ctypes.c_void_p),
+                ("timing_stage", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
+                ("timing_end", ctypes.c_void_p)]
 
 
 _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -242,8 +248,12 @@ def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool 
 
 def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
              weights_desc: WeightsDesc | None, workspace_ptr: int, workspace_nbytes: int,
-             out_ptr: int, abi_version: int = ABI_VERSION, use_logp: int = 1) -> int:
-    """Host-only argument check of rerank (no GPU needed); returns the status code."""
+             out_ptr: int, abi_version: int = ABI_VERSION, use_logp: int = 1,
+             timing: tuple[int, int, int] | None = None) -> int:
+    """Host-only argument check of rerank (no GPU needed); returns the status code.
+
+    timing = (stage, begin_event, end_event) as plain integers (handles are
+    only checked for presence here)."""
     p = Params()
     p.abi_version = abi_version
     p.num_blocks = N
@@ -253,6 +263,8 @@ def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
     p.weights = ctypes.pointer(weights_desc) if weights_desc is not None else None
     p.workspace = ctypes.c_void_p(workspace_ptr)
     p.workspace_bytes = workspace_nbytes
+    if timing is not None:
+        p.timing_stage, p.timing_begin, p.timing_end = timing[0], timing[1] or None, timing[2] or None
     return int(lib().lilicorr_validate(ctypes.c_void_p(logits_ptr), B, V, K, ctypes.byref(p),
                                        ctypes.c_void_p(out_ptr)))
 

@@ -142,6 +142,9 @@ int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_pa
   const size_t need = rerank_ws_layout(p->num_blocks, B, V, K, w->dims).total;
   if (!p->workspace || p->workspace_bytes < need || ((uintptr_t)p->workspace & 255))
     return LILICORR_EWORKSPACE;
+  if ((p->timing_begin == nullptr) != (p->timing_end == nullptr)) return LILICORR_EINVAL;
+  if (p->timing_begin && (p->timing_stage < 0 || p->timing_stage >= LILICORR_STAGE_COUNT))
+    return LILICORR_EINVAL;
   return LILICORR_OK;
 }
 
@@ -174,14 +177,27 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
   uint16_t* inv = p->dbg_inv ? p->dbg_inv : (uint16_t*)(ws + L.inv);
   float* cosb = p->dbg_cos ? p->dbg_cos : (float*)(ws + L.cos);
   float* gpart = (float*)(ws + L.gemm_part);
+  // optional events around one stage (measurement only)
+  const bool timing = p->timing_begin != nullptr;
+  auto mark = [&](int stage, bool end) -> hipError_t {
+    if (!timing || stage != p->timing_stage) return hipSuccess;
+    return hipEventRecord((hipEvent_t)(end ? p->timing_end : p->timing_begin), st);
+  };
+#define LL_STAGE(stage, ...)          \
+  do {                                \
+    LL_TRY(mark((stage), false));     \
+    __VA_ARGS__;                      \
+    LL_TRY(mark((stage), true));      \
+  } while (0)
 
   // a1: log-partition + top-K
-  LL_TRY(launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
+  LL_STAGE(LILICORR_STAGE_TOPK, LL_TRY(launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
                          (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms), topk_idx,
-                         topk_logp, p->dbg_lse, st));
+                         topk_logp, p->dbg_lse, st)));
   // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0))
-  LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, W.S, W.R, W.conf_w1, W.conf_b1,
-                           hid, x, V, st));
+  LL_STAGE(LILICORR_STAGE_NODE,
+           LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, W.S, W.R, W.conf_w1,
+                                    W.conf_b1, hid, x, V, st)));
   auto resid_norm = [&](const float* gamma) {
     LinearEpilogue e;
     e.kind = EPI_RESID_F32;
@@ -196,25 +212,35 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
     e.kind = kind;
     return e;
   };
-  LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, resid_norm(W.layer[0].gamma1), x, gpart, st));
+  LL_STAGE(LILICORR_STAGE_CONF_LINEAR,
+           LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, resid_norm(W.layer[0].gamma1),
+                                x, gpart, st)));
   // a3: two pre-norm layers; each residual GEMM also produces the next RMSNorm
   for (int l = 0; l < 2; ++l) {
     const LayerPtrs& Lw = W.layer[l];
     const float* next_gamma = l == 0 ? W.layer[1].gamma1 : W.gamma_f;
-    LL_TRY(launch_linear(u, M, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st));
-    LL_TRY(launch_attention(qkv, N, B, K, H, heads, Lw.dist, Lw.same, attn, st));
-    LL_TRY(launch_linear(attn, M, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st));
-    LL_TRY(launch_linear(u, M, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st));
-    LL_TRY(launch_linear(hid, M, F, Lw.w2, H, Lw.b2, resid_norm(next_gamma), x, gpart, st));
+    const int s0 = 5 * l;
+    LL_STAGE(LILICORR_STAGE_QKV + s0,
+             LL_TRY(launch_linear(u, M, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st)));
+    LL_STAGE(LILICORR_STAGE_ATTENTION + s0,
+             LL_TRY(launch_attention(qkv, N, B, K, H, heads, Lw.dist, Lw.same, attn, st)));
+    LL_STAGE(LILICORR_STAGE_O + s0,
+             LL_TRY(launch_linear(attn, M, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
+    LL_STAGE(LILICORR_STAGE_FFN1 + s0,
+             LL_TRY(launch_linear(u, M, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st)));
+    LL_STAGE(LILICORR_STAGE_FFN2 + s0,
+             LL_TRY(launch_linear(hid, M, F, Lw.w2, H, Lw.b2, resid_norm(next_gamma), x, gpart, st)));
   }
   // a4: out|in heads and their unit normalisation
   {
     LinearEpilogue e = plain(EPI_F32);
     e.heads_out = outv;
     e.heads_in = inv;
-    LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st));
+    LL_STAGE(LILICORR_STAGE_HEADS,
+             LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st)));
   }
   // a5: pair scores, a6: greedy walk (fused when the block's cosines fit in LDS)
+  LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, false));
   if (scores_walk_lds_bytes(B, K) <= kScoresWalkMaxLds) {
     LL_TRY(launch_scores_walk(outv, inv, topk_idx, topk_logp, N, B, K, de, p->alpha, p->use_logp,
                               p->dbg_cos, out_tokens, p->dbg_score, p->dbg_gap, st));
@@ -223,6 +249,8 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
     LL_TRY(launch_greedy_walk(topk_idx, topk_logp, cosb, N, B, K, p->alpha, p->use_logp,
                               out_tokens, p->dbg_score, p->dbg_gap, st));
   }
+  LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, true));
+#undef LL_STAGE
   return LILICORR_OK;
 }
 

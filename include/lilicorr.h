@@ -81,6 +81,22 @@ typedef struct {
   size_t bytes;    /* size of the blob at dev */
 } lilicorr_weights;
 
+/* Stages of lilicorr_rerank, for the optional timing events below. The five
+ * per-layer stages of layer l are LILICORR_STAGE_QKV + 5*l .. FFN2 + 5*l. */
+typedef enum {
+  LILICORR_STAGE_TOPK = 0,         /* fused log-partition + top-K (and its chunk merge) */
+  LILICORR_STAGE_NODE = 1,         /* embedding gathers + first confidence-MLP layer */
+  LILICORR_STAGE_CONF_LINEAR = 2,  /* second confidence-MLP layer, residual, RMSNorm */
+  LILICORR_STAGE_QKV = 3,          /* layer 0: fused q|k|v projection */
+  LILICORR_STAGE_ATTENTION = 4,    /* layer 0: lattice attention */
+  LILICORR_STAGE_O = 5,            /* layer 0: output projection, residual, RMSNorm */
+  LILICORR_STAGE_FFN1 = 6,         /* layer 0: first FFN linear + SiLU */
+  LILICORR_STAGE_FFN2 = 7,         /* layer 0: second FFN linear, residual, RMSNorm */
+  LILICORR_STAGE_HEADS = 13,       /* out|in heads + unit normalisation */
+  LILICORR_STAGE_SCORES_WALK = 14, /* pair scores + greedy walk */
+  LILICORR_STAGE_COUNT = 15
+} lilicorr_stage;
+
 typedef struct {
   uint32_t abi_version;            /* must be LILICORR_ABI_VERSION */
   int32_t num_blocks;              /* N independent draft blocks (>= 1) */
@@ -107,6 +123,14 @@ typedef struct {
   float* dbg_cos;
   float* dbg_score;
   float* dbg_gap;
+  /* Optional timing of one stage (measurement only). When timing_begin and
+   * timing_end are both non-NULL (hipEvent_t handles created by the caller),
+   * they are recorded on `stream` right before the first and right after the
+   * last kernel of stage `timing_stage` (a lilicorr_stage value, < COUNT).
+   * Both NULL: nothing is recorded and timing_stage is ignored. */
+  int32_t timing_stage;
+  void* timing_begin;
+  void* timing_end;
 } lilicorr_params;
 
 /* The whole reranking path (LiLiCorr paper, Section 3.5 "Single-pass

@@ -60,7 +60,7 @@ DIMS = L.EncoderDims(64, 2, 256, 32)
 def _good(**over):
     args = dict(logits_ptr=1 << 20, N=1, B=16, V=1024, K=4, logits_dtype=L.F32, vocab=1024,
                 dims=DIMS, wptr=1 << 24, wbytes=None, ws=1 << 28, wsbytes=None, out=1 << 12,
-                abi=L.ABI_VERSION, use_logp=1, weights=True)
+                abi=L.ABI_VERSION, use_logp=1, weights=True, timing=None)
     args.update(over)
     wb = args["wbytes"] if args["wbytes"] is not None else L.weights_bytes(args["dims"], args["vocab"])
     desc = L.WeightsDesc(args["dims"].c(), args["vocab"], 42, ctypes.c_void_p(args["wptr"]), wb) if args["weights"] else None
@@ -68,7 +68,7 @@ def _good(**over):
     if wsb is None:
         wsb = L.workspace_bytes(args["N"], args["B"], args["V"], args["K"], DIMS)
     return L.validate(args["logits_ptr"], args["N"], args["B"], args["V"], args["K"], args["logits_dtype"],
-                      desc, args["ws"], wsb, args["out"], args["abi"], args["use_logp"])
+                      desc, args["ws"], wsb, args["out"], args["abi"], args["use_logp"], args["timing"])
 
 
 @pytest.mark.parametrize("over,code", [
@@ -97,6 +97,12 @@ def _good(**over):
     ({"ws": 0}, L.EWORKSPACE),
     ({"wsbytes": 100}, L.EWORKSPACE),
     ({"ws": (1 << 28) + 64}, L.EWORKSPACE),
+    ({"timing": (L.STAGE_FFN2, 0x1000, 0x2000)}, L.OK),             # stage timing events
+    ({"timing": (L.STAGE_SCORES_WALK, 0x1000, 0x2000)}, L.OK),
+    ({"timing": (L.STAGE_COUNT, 0x1000, 0x2000)}, L.EINVAL),       # no such stage
+    ({"timing": (-1, 0x1000, 0x2000)}, L.EINVAL),
+    ({"timing": (L.STAGE_TOPK, 0x1000, 0)}, L.EINVAL),             # one event only
+    ({"timing": (99, 0, 0)}, L.OK),                                # no events: stage ignored
 ])
 def test_validate_status_codes(over, code):
     assert _good(**over) == code

@@ -134,6 +134,10 @@ def main():
             graphs[gstate["i"] % nbuf].replay()
             gstate["i"] += 1
 
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
     # ---- per-stage durations, measured in the pipeline with the library's
     # stage events (a few untimed steps per stage)
     stage_names = stage_table(w)

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   const uint16_t* blk = qkv + n * T * H3;
   const int q = blockIdx.x * 64 + wave * 16 + c;   // this lane's query
   const bool q_ok = q < T;
-  const int slot_q = q_ok ? q / K : 0;
+  const int qc = min(q, T - 1);   // rows past the lattice compute a copy, never stored
+  const int slot_q = qc / K;
 
   if (tid < 127) bias_tab[tid] = dist[h * 127 + tid];
   const float same_h = same[h];
@@ -52,8 +53,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   u32x4_t qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = q_ok ? *(const u32x4_t*)(blk + (int64_t)q * H3 + h * DH + ks * 32 + 8 * g)
-                  : u32x4_t{0, 0, 0, 0};
+    qf[ks] = *(const u32x4_t*)(blk + (int64_t)qc * H3 + h * DH + ks * 32 + 8 * g);
 
   // V chunk loader (32 keys x DH, 16 bytes per thread-slot); chunk 0 is issued
   // now so its latency overlaps the score computation.
@@ -64,10 +64,10 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
     for (int i = 0; i < VCH; ++i) {
       const int v = tid + 256 * i;
       const int key = v / (DH / 8), d8 = v % (DH / 8);
-      const int kg = ch * 32 + key;
-      vreg[i] = (v < 32 * DH / 8 && kg < T)
-                    ? *(const u32x4_t*)(blk + (int64_t)kg * H3 + 2 * H + h * DH + d8 * 8)
-                    : u32x4_t{0, 0, 0, 0};
+      // keys past the lattice read its last token (probability 0 there)
+      const int kg = min(ch * 32 + key, T - 1);
+      if (v < 32 * DH / 8)
+        vreg[i] = *(const u32x4_t*)(blk + (int64_t)kg * H3 + 2 * H + h * DH + d8 * 8);
     }
   };
   load_v(0);
@@ -82,12 +82,11 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
       for (int i = 0; i < 4; ++i) s[kt][i] = -INFINITY;
       continue;
     }
-    const int krow = kt * 16 + c;   // A operand row = key
+    const int krow = min(kt * 16 + c, T - 1);   // A operand row = key (past T: masked below)
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4_t kf = krow < T ? *(const u32x4_t*)(blk + (int64_t)krow * H3 + H + h * DH + ks * 32 + 8 * g)
-                                  : u32x4_t{0, 0, 0, 0};
+      const u32x4_t kf = *(const u32x4_t*)(blk + (int64_t)krow * H3 + H + h * DH + ks * 32 + 8 * g);
       acc = mfma16(kf, qf[ks], acc);
     }
 #pragma unroll
@@ -173,6 +172,182 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   }
 }
 
+// Resident variant for lattices of up to 256 tokens: one workgroup of eight
+// waves per (head, block) loads the block's K (row-major, 16-byte chunks
+// XOR-swizzled by key) and V (transposed, [d][key]) into LDS once, with every
+// global load in flight together, and the waves then loop over the block's
+// 16-query tiles (wave w takes tiles w, w+8, ...). Per tile: S^T = K Q^T with
+// the key tiles as independent MFMA chains, exact row max,
+// P~ = bf16(exp(s - max)), O^T = V^T P~^T, O / l. K and V are read from HBM
+// once per (block, head). V is fetched key-fastest so that each transposed
+// 2-byte LDS store instruction covers 64 consecutive keys of one d row.
+template <int TMAX, int DH>
+__global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
+                                                            int K, int H,
+                                                            const float* __restrict__ dist,
+                                                            const float* __restrict__ same,
+                                                            uint16_t* __restrict__ out) {
+  constexpr int NW = 8;           // waves per workgroup
+  constexpr int KT = TMAX / 16;   // 16-key tiles
+  constexpr int KS = DH / 32;     // MFMA k-steps over d_h
+  constexpr int DT = DH / 16;     // 16-wide d tiles of the output
+  constexpr int CPR = DH / 8;     // 16-byte chunks per K row
+  constexpr int VS = TMAX + 8;    // bf16 per transposed-V row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[TMAX * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VS];
+  __shared__ float bias_tab[128];
+  // K chunk (key, c) lives at chunk c ^ swz(key) of its row
+  auto kat = [](int key, int c) {
+    const int sw = CPR >= 8 ? (key & 7) : ((key >> 1) & (CPR - 1));
+    return key * DH + ((c ^ sw) << 3);
+  };
+
+  const int T = B * K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int h = blockIdx.x;
+  const int64_t n = blockIdx.y;
+  const int64_t H3 = 3 * (int64_t)H;
+  const uint16_t* blk = qkv + n * T * H3;
+
+  if (tid < 127) bias_tab[tid] = dist[h * 127 + tid];
+  const float same_h = same[h];
+  // K (chunk-fastest) and V (key-fastest) of this head, all loads issued
+  // before any store. Rows past the lattice are read from its last token
+  // (a conditional load would serialise the loads): their keys are masked to
+  // -inf and their values meet probability 0.
+  constexpr int TOT = TMAX * CPR;                     // 16-byte chunks of each of K and V
+  constexpr int NCH = (TOT + 64 * NW - 1) / (64 * NW);   // per thread
+  constexpr bool EXACT = TOT % (64 * NW) == 0;
+  u32x4_t kr[NCH], vr[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int ch = min(tid + 64 * NW * i, TOT - 1);
+    const int kk = min(ch / CPR, T - 1), kc = ch % CPR;
+    kr[i] = *(const u32x4_t*)(blk + (int64_t)kk * H3 + H + h * DH + kc * 8);
+    const int vk = min(ch % TMAX, T - 1), vc = ch / TMAX;
+    vr[i] = *(const u32x4_t*)(blk + (int64_t)vk * H3 + 2 * H + h * DH + vc * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int ch = tid + 64 * NW * i;
+    if (!EXACT && ch >= TOT) break;
+    *(u32x4_t*)(&Ks[kat(ch / CPR, ch % CPR)]) = kr[i];
+    const int vk = ch % TMAX, vc = ch / TMAX;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Vt[(vc * 8 + 2 * e) * VS + vk] = (uint16_t)(vr[i][e] & 0xFFFF);
+      Vt[(vc * 8 + 2 * e + 1) * VS + vk] = (uint16_t)(vr[i][e] >> 16);
+    }
+  }
+  __syncthreads();
+
+  const float scale = 1.0f / __fsqrt_rn((float)DH);
+  const int nkt = (T + 15) / 16, nch = (T + 31) / 32;
+  const int ntile = (T + 15) / 16;
+  for (int qt = wave; qt < ntile; qt += NW) {
+    const int q = qt * 16 + c;   // this lane's query
+    const bool q_ok = q < T;
+    const int qc = min(q, T - 1);   // rows past the lattice compute a copy, never stored
+    const int slot_q = qc / K;
+    u32x4_t qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *(const u32x4_t*)(blk + (int64_t)qc * H3 + h * DH + ks * 32 + 8 * g);
+    // S^T tiles: key tiles are independent accumulation chains
+    f32x4_t acc[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt >= nkt) continue;
+        const u32x4_t kf = *(const u32x4_t*)(&Ks[kat(kt * 16 + c, ks * 4 + g)]);
+        acc[kt] = mfma16(kf, qf[ks], acc[kt]);
+      }
+    }
+    float s[KT][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt * 16 + 4 * g + i;
+        float v = -INFINITY;
+        if (kt < nkt && key < T) {
+          const int slot_k = key / K;
+          v = acc[kt][i] * scale + bias_tab[slot_k - slot_q + 63];
+          if (slot_k == slot_q) v += same_h;
+        }
+        s[kt][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float lsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __expf(s[kt][i] - mx);
+        s[kt][i] = p;
+        lsum += p;
+      }
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+
+    f32x4_t oacc[DT];
+#pragma unroll
+    for (int d = 0; d < DT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // k-slot j of lane group g stands for key 32*ch + 4g + j (j < 4) or
+    // 32*ch + 16 + 4g + (j - 4) (j >= 4), matching the score layout
+#pragma unroll
+    for (int ch = 0; ch < KT / 2; ++ch) {
+      if (ch >= nch) break;
+      u32x4_t pb;
+      pb[0] = pack_bf16x2(s[2 * ch][0], s[2 * ch][1]);
+      pb[1] = pack_bf16x2(s[2 * ch][2], s[2 * ch][3]);
+      pb[2] = pack_bf16x2(s[2 * ch + 1][0], s[2 * ch + 1][1]);
+      pb[3] = pack_bf16x2(s[2 * ch + 1][2], s[2 * ch + 1][3]);
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const uint16_t* vrow = &Vt[(d * 16 + c) * VS + ch * 32];
+        const u32x2_t lo = *(const u32x2_t*)(vrow + 4 * g);
+        const u32x2_t hi = *(const u32x2_t*)(vrow + 16 + 4 * g);
+        const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[d] = mfma16(va, pb, oacc[d]);
+      }
+    }
+    if (q_ok) {
+      const float inv = 1.0f / lsum;
+      uint16_t* orow = out + (n * T + q) * (int64_t)H + h * DH;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const uint32_t w0 = pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv);
+        const uint32_t w1 = pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv);
+        *(uint2*)(orow + d * 16 + 4 * g) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+template <int TMAX>
+hipError_t launch_res(int dh, const uint16_t* qkv, int N, int B, int K, int H, int heads,
+                      const float* dist, const float* same, uint16_t* out, hipStream_t stream) {
+  const dim3 grid((unsigned)heads, (unsigned)N);
+  if (dh == 32)
+    hipLaunchKernelGGL((attention_res_kernel<TMAX, 32>), grid, dim3(512), 0, stream, qkv, B, K, H,
+                       dist, same, out);
+  else if (dh == 64)
+    hipLaunchKernelGGL((attention_res_kernel<TMAX, 64>), grid, dim3(512), 0, stream, qkv, B, K, H,
+                       dist, same, out);
+  else
+    hipLaunchKernelGGL((attention_res_kernel<TMAX, 128>), grid, dim3(512), 0, stream, qkv, B, K, H,
+                       dist, same, out);
+  return hipGetLastError();
+}
+
 template <int TMAX>
 hipError_t launch_dh(int dh, const uint16_t* qkv, int N, int B, int K, int H, int heads,
                      const float* dist, const float* same, uint16_t* out, hipStream_t stream) {
@@ -196,9 +371,9 @@ hipError_t launch_attention(const uint16_t* qkv, int N, int B, int K, int H, int
                             const float* dist, const float* same, uint16_t* out,
                             hipStream_t stream) {
   const int T = B * K, dh = H / heads;
-  if (T <= 64) return launch_dh<64>(dh, qkv, N, B, K, H, heads, dist, same, out, stream);
-  if (T <= 128) return launch_dh<128>(dh, qkv, N, B, K, H, heads, dist, same, out, stream);
-  if (T <= 256) return launch_dh<256>(dh, qkv, N, B, K, H, heads, dist, same, out, stream);
+  if (T <= 64) return launch_res<64>(dh, qkv, N, B, K, H, heads, dist, same, out, stream);
+  if (T <= 128) return launch_res<128>(dh, qkv, N, B, K, H, heads, dist, same, out, stream);
+  if (T <= 256) return launch_res<256>(dh, qkv, N, B, K, H, heads, dist, same, out, stream);
   return launch_dh<512>(dh, qkv, N, B, K, H, heads, dist, same, out, stream);
 }
 

@@ -117,7 +117,8 @@ def _rand_bf16(rng, shape, scale=1.0):
 
 
 @pytest.mark.parametrize("M,Kd,N", [(64, 64, 32), (100, 256, 96), (128, 1024, 3072), (300, 1024, 1024),
-                                    (2100, 512, 200), (4096, 1024, 4096), (128, 4096, 1024)])
+                                    (2100, 512, 200), (4096, 1024, 4096), (128, 4096, 1024),
+                                    (8192, 1024, 4096), (33000, 256, 1000), (6000, 192, 640)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
 def test_linear(L, M, Kd, N, epi):
     import torch
@@ -162,7 +163,8 @@ def test_rmsnorm(L, M, H):
 
 @pytest.mark.parametrize("N,B,K,heads,dh", [(1, 16, 4, 2, 32), (2, 16, 8, 8, 128), (1, 16, 16, 8, 128),
                                             (1, 16, 32, 16, 128), (3, 5, 3, 2, 64), (1, 1, 1, 1, 32),
-                                            (2, 7, 9, 4, 32), (1, 64, 8, 2, 64)])
+                                            (2, 7, 9, 4, 32), (1, 64, 8, 2, 64), (2, 25, 8, 4, 64),
+                                            (3, 10, 13, 2, 128)])
 def test_lattice_attention(L, N, B, K, heads, dh):
     rng = np.random.default_rng(N * 1000 + B * 10 + K)
     H = heads * dh

@@ -6,9 +6,12 @@
 // v_mfma_f32_16x16x32_bf16 tiles. Epilogues fuse the bias, the bf16 rounding,
 // SiLU and the fp32 residual add of the pre-norm transformer.
 //
-// Two schedules:
-//  * many rows (M >= 2048): BM x BN = 128 x 128 tiles over the whole K,
-//    double-buffered in LDS with one barrier per 64-wide k-step;
+// Three schedules:
+//  * many rows and at least 256 tiles of 256 x 256: the DMA-pipelined kernel
+//    below (32 x 32 x 16 MFMA, 128 x 128 per wave, four LDS stages filled by
+//    direct global-to-LDS loads, LDS-staged coalesced epilogue);
+//  * other many-row shapes (M >= 2048): BM x BN = 128 x 128 tiles over the
+//    whole K, double-buffered in LDS with one barrier per 64-wide k-step;
 //  * few rows (one or a few draft blocks, M = B*K*N of 64..2047): the GEMM is
 //    weight-streaming and latency bound, so K is split S ways. Each workgroup
 //    stages its whole A and W K-slice (64..256 wide) in LDS with every load in
@@ -135,6 +138,179 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
       }
     }
   }
+}
+
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Many-row GEMM, 256 x 256 tiles on 32 x 32 x 16 MFMA. Four waves in a 2 x 2
+// grid each hold a 128 x 128 fp32 accumulator block (in AGPRs), so every
+// 16-byte fragment read from LDS feeds four MFMAs. K advances 32 per stage
+// through four LDS stages that global_load_lds fills directly (no register
+// staging), three stages ahead of the one being multiplied; each wave waits
+// only for its own stage loads (vmcnt) and a bare s_barrier then makes the
+// stage visible, so the loads behind it stay in flight. Within a stage the
+// next k-step's fragment reads are interleaved with the current MFMAs. Stage
+// rows are 64 bytes with the 16-byte chunk XOR-swizzled by (row >> 1) & 3, so
+// a fragment read touches every bank once. Workgroups are dealt to the XCDs
+// round-robin; the tile order is remapped so that each XCD runs a contiguous
+// run of tiles and shares their A row panels in its L2. The epilogue moves
+// each wave's block out through LDS in 32-row slices as 16-byte stores.
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dma_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N, int Kd,
+    const float* __restrict__ bias, const float* resid, void* out, int tiles_n, int ntiles) {
+  constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
+  constexpr int WM = 128, WN = 128, MT = 4, NT = 4;
+  constexpr int STAGE = (BM + BN) * BK;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
+
+  const int wg = blockIdx.x;
+  const int q = ntiles / 8, r = ntiles % 8, x = wg % 8;
+  const int t = x * q + min(x, r) + wg / 8;
+  if (t >= ntiles) return;
+  const int64_t m0 = (int64_t)(t / tiles_n) * BM, n0 = (int64_t)(t % tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // Stage loads: each wave issues 4 A and 4 W instructions of 1 KiB; instruction
+  // j (0..15 over the workgroup) covers tile rows 16 j .. 16 j + 15, and its lane
+  // i fills LDS slot i (row 16 j + i / 4, chunk' = i % 4), which holds chunk
+  // chunk' ^ ((row >> 1) & 3) of that row. Rows past the matrix are clamped.
+  const uint16_t* srcA[4];
+  const uint16_t* srcW[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = wave * 4 + u;
+    const int row = 16 * j + lane / 4;
+    const int chunk = (lane % 4) ^ ((row >> 1) & 3);
+    srcA[u] = A + min(m0 + row, (int64_t)M - 1) * Kd + chunk * 8;
+    srcW[u] = W + min(n0 + row, (int64_t)N - 1) * Kd + chunk * 8;
+  }
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    uint16_t* st = smem + (kt % NS) * STAGE;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = wave * 4 + u;
+      __builtin_amdgcn_global_load_lds((const void*)(srcA[u] + k0),
+                                       (__attribute__((address_space(3))) void*)(st + j * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = wave * 4 + u;
+      __builtin_amdgcn_global_load_lds((const void*)(srcW[u] + k0),
+                                       (__attribute__((address_space(3))) void*)(st + BM * BK + j * 512), 16, 0, 0);
+    }
+  };
+  auto fat = [](int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 3)) << 3); };
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = Kd / BK;
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt are done once at most those of the stages
+    // issued after it (up to two, eight instructions each) are outstanding
+    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
+    else if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    // every wave has finished stage kt - 1, so its buffer takes stage kt + 3
+    if (kt + 3 < nk) issue(kt + 3);
+    const uint16_t* as = smem + (kt % NS) * STAGE;
+    const uint16_t* ws = as + BM * BK;
+    u32x4_t fa[2][MT], fb[2][NT];
+    auto rd = [&](int ks, int slot) __attribute__((always_inline)) {
+      const int ch = ks * 2 + hi;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[slot][i] = *(const u32x4_t*)(&as[fat(wm * WM + i * 32 + l32, ch)]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) fb[slot][j] = *(const u32x4_t*)(&ws[fat(wn * WN + j * 32 + l32, ch)]);
+    };
+    rd(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) rd(ks + 1, (ks + 1) & 1);   // next k-step's fragments in flight
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma32(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
+      if (ks + 1 < BK / 16) {
+        // two MFMAs, then one fragment read, eight times
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Epilogue through LDS: each wave owns a slice and moves its 128 x 128
+  // block out 32 rows at a time as full rows of 16-byte stores (N % 4 == 0,
+  // so a 4-column chunk is entirely inside or outside the matrix).
+  __syncthreads();   // every wave is done reading the pipeline stages
+  constexpr int ES = 128 + 4;
+  float* stg = (float*)smem + wave * (32 * ES + 64);
+  const int64_t col0 = n0 + wn * WN;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        stg[(8 * (e >> 2) + 4 * hi + (e & 3)) * ES + j * 32 + l32] = acc[i][j][e];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int ch = lane + 64 * u, rr = ch >> 5, c4 = (ch & 31) * 4;
+      const int64_t m = m0 + wm * WM + i * 32 + rr;
+      const int64_t n = col0 + c4;
+      if (m >= M || n >= N) continue;
+      float4 y = *(const float4*)(&stg[rr * ES + c4]);
+      if (bias) {
+        const float4 bv = *(const float4*)(bias + n);
+        y.x += bv.x; y.y += bv.y; y.z += bv.z; y.w += bv.w;
+      }
+      const int64_t o = m * N + n;
+      if constexpr (EPI == EPI_F32) {
+        *(float4*)((float*)out + o) = y;
+      } else if constexpr (EPI == EPI_BF16) {
+        *(uint2*)((uint16_t*)out + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+      } else if constexpr (EPI == EPI_SILU_BF16) {
+        *(uint2*)((uint16_t*)out + o) =
+            make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
+      } else {
+        const float4 rv = *(const float4*)(resid + o);
+        *(float4*)((float*)out + o) = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int EPI>
+hipError_t launch_dma(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
+                      const float* resid, void* out, hipStream_t stream) {
+  const int tiles_n = (N + 255) / 256;
+  const int ntiles = ((M + 255) / 256) * tiles_n;
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3((unsigned)ntiles), dim3(256), 0, stream, A, W, M, N,
+                     Kd, bias, resid, out, tiles_n, ntiles);
+  return hipGetLastError();
 }
 
 template <int EPI>
@@ -499,7 +675,17 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
   const GemmPlan p = plan_linear(M, Kd, N);
   if (p.split == 1) {
     hipError_t e;
-    if (M >= 2048)
+    const auto al16 = [](const void* ptr) { return ((uintptr_t)ptr & 15) == 0; };
+    const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    if (M >= 2048 && tiles256 >= 256 && Kd % 32 == 0 && N % 4 == 0 && al16(out) &&
+        (bias == nullptr || al16(bias)) && (ep.resid == nullptr || al16(ep.resid))) {
+      switch (ep.kind) {
+        case EPI_F32: e = launch_dma<EPI_F32>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
+        case EPI_BF16: e = launch_dma<EPI_BF16>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
+        case EPI_SILU_BF16: e = launch_dma<EPI_SILU_BF16>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
+        default: e = launch_dma<EPI_RESID_F32>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
+      }
+    } else if (M >= 2048)
       e = launch_tile<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     else if (M > 64)
       e = launch_tile<128, 32>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);

@@ -158,12 +158,18 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
 // round-robin; the tile order is remapped so that each XCD runs a contiguous
 // run of tiles and shares their A row panels in its L2. The epilogue moves
 // each wave's block out through LDS in 32-row slices as 16-byte stores.
-template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dma_kernel(
+// s_waitcnt immediate for "at most v vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited).
+constexpr int waitcnt_vm(int v) { return (v & 15) | ((v >> 4) << 14) | 0x70 | 0xF00; }
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM * BN >= 32768 ? 1 : 2, BM * BN >= 32768 ? 1 : 2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N, int Kd,
     const float* __restrict__ bias, const float* resid, void* out, int tiles_n, int ntiles) {
-  constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
-  constexpr int WM = 128, WN = 128, MT = 4, NT = 4;
+  constexpr int BK = 32, NS = 4;
+  constexpr int WM = BM / 2, WN = BN / 2, MT = WM / 32, NT = WN / 32;
+  constexpr int UA = BM / 64, UW = BN / 64;   // 1 KiB stage-load instructions per wave
+  constexpr int PER = UA + UW;                 // per wave per stage
   constexpr int STAGE = (BM + BN) * BK;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
 
@@ -176,35 +182,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // Stage loads: each wave issues 4 A and 4 W instructions of 1 KiB; instruction
-  // j (0..15 over the workgroup) covers tile rows 16 j .. 16 j + 15, and its lane
-  // i fills LDS slot i (row 16 j + i / 4, chunk' = i % 4), which holds chunk
-  // chunk' ^ ((row >> 1) & 3) of that row. Rows past the matrix are clamped.
-  const uint16_t* srcA[4];
-  const uint16_t* srcW[4];
+  // Stage loads: instruction j of A (0 .. BM/16 - 1 over the workgroup) covers
+  // tile rows 16 j .. 16 j + 15, and its lane i fills LDS slot i (row
+  // 16 j + i / 4, chunk' = i % 4), which holds chunk chunk' ^ ((row >> 1) & 3)
+  // of that row; likewise for W. Rows past the matrix are clamped.
+  const uint16_t* srcA[UA];
+  const uint16_t* srcW[UW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = wave * 4 + u;
-    const int row = 16 * j + lane / 4;
+  for (int u = 0; u < UA; ++u) {
+    const int row = 16 * (wave * UA + u) + lane / 4;
     const int chunk = (lane % 4) ^ ((row >> 1) & 3);
     srcA[u] = A + min(m0 + row, (int64_t)M - 1) * Kd + chunk * 8;
+  }
+#pragma unroll
+  for (int u = 0; u < UW; ++u) {
+    const int row = 16 * (wave * UW + u) + lane / 4;
+    const int chunk = (lane % 4) ^ ((row >> 1) & 3);
     srcW[u] = W + min(n0 + row, (int64_t)N - 1) * Kd + chunk * 8;
   }
   auto issue = [&](int kt) __attribute__((always_inline)) {
     uint16_t* st = smem + (kt % NS) * STAGE;
     const int k0 = kt * BK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = wave * 4 + u;
+    for (int u = 0; u < UA; ++u)
       __builtin_amdgcn_global_load_lds((const void*)(srcA[u] + k0),
-                                       (__attribute__((address_space(3))) void*)(st + j * 512), 16, 0, 0);
-    }
+                                       (__attribute__((address_space(3))) void*)(st + (wave * UA + u) * 512),
+                                       16, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = wave * 4 + u;
+    for (int u = 0; u < UW; ++u)
       __builtin_amdgcn_global_load_lds((const void*)(srcW[u] + k0),
-                                       (__attribute__((address_space(3))) void*)(st + BM * BK + j * 512), 16, 0, 0);
-    }
+                                       (__attribute__((address_space(3))) void*)(st + BM * BK + (wave * UW + u) * 512),
+                                       16, 0, 0);
   };
   auto fat = [](int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 3)) << 3); };
 
@@ -222,10 +230,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (nk > 2) issue(2);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of stage kt are done once at most those of the stages
-    // issued after it (up to two, eight instructions each) are outstanding
-    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
-    else if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+    // issued after it (up to two, PER instructions each) are outstanding
+    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER));
+    else if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
     // every wave has finished stage kt - 1, so its buffer takes stage kt + 3
     if (kt + 3 < nk) issue(kt + 3);
@@ -249,10 +257,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = mfma32(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
       if (ks + 1 < BK / 16) {
-        // two MFMAs, then one fragment read, eight times
+        // MFMAs and the next k-step's fragment reads, interleaved
+        constexpr int RD = MT + NT, G = MT * NT, PERRD = G / RD > 0 ? G / RD : 1;
 #pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        for (int r2 = 0; r2 < RD; ++r2) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PERRD, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
@@ -260,11 +269,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   }
 
-  // Epilogue through LDS: each wave owns a slice and moves its 128 x 128
-  // block out 32 rows at a time as full rows of 16-byte stores (N % 4 == 0,
-  // so a 4-column chunk is entirely inside or outside the matrix).
+  // Epilogue through LDS: each wave owns a slice and moves its WM x WN block
+  // out 32 rows at a time as full rows of 16-byte stores (N % 4 == 0, so a
+  // 4-column chunk is entirely inside or outside the matrix).
   __syncthreads();   // every wave is done reading the pipeline stages
-  constexpr int ES = 128 + 4;
+  constexpr int ES = WN + 4;          // floats per staged row (16-byte pad)
+  constexpr int CPRW = WN / 4;        // 4-column chunks per row
+  static_assert(4 * (32 * ES + 64) * 4 <= NS * STAGE * 2, "epilogue staging fits");
   float* stg = (float*)smem + wave * (32 * ES + 64);
   const int64_t col0 = n0 + wn * WN;
 #pragma unroll
@@ -276,8 +287,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         stg[(8 * (e >> 2) + 4 * hi + (e & 3)) * ES + j * 32 + l32] = acc[i][j][e];
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int ch = lane + 64 * u, rr = ch >> 5, c4 = (ch & 31) * 4;
+    for (int u = 0; u < 32 * CPRW / 64; ++u) {
+      const int ch = lane + 64 * u, rr = ch / CPRW, c4 = (ch % CPRW) * 4;
       const int64_t m = m0 + wm * WM + i * 32 + rr;
       const int64_t n = col0 + c4;
       if (m >= M || n >= N) continue;
@@ -303,13 +314,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-template <int EPI>
+template <int BM, int BN>
 hipError_t launch_dma(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
-                      const float* resid, void* out, hipStream_t stream) {
-  const int tiles_n = (N + 255) / 256;
-  const int ntiles = ((M + 255) / 256) * tiles_n;
-  hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3((unsigned)ntiles), dim3(256), 0, stream, A, W, M, N,
-                     Kd, bias, resid, out, tiles_n, ntiles);
+                      int epi, const float* resid, void* out, hipStream_t stream) {
+  const int tiles_n = (N + BN - 1) / BN;
+  const int ntiles = ((M + BM - 1) / BM) * tiles_n;
+  const dim3 grid((unsigned)ntiles);
+  switch (epi) {
+    case EPI_F32:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_F32>), grid, dim3(256), 0, stream, A, W, M, N,
+                         Kd, bias, resid, out, tiles_n, ntiles);
+      break;
+    case EPI_BF16:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_BF16>), grid, dim3(256), 0, stream, A, W, M, N,
+                         Kd, bias, resid, out, tiles_n, ntiles);
+      break;
+    case EPI_SILU_BF16:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_SILU_BF16>), grid, dim3(256), 0, stream, A, W,
+                         M, N, Kd, bias, resid, out, tiles_n, ntiles);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_RESID_F32>), grid, dim3(256), 0, stream, A, W,
+                         M, N, Kd, bias, resid, out, tiles_n, ntiles);
+      break;
+  }
   return hipGetLastError();
 }
 
@@ -676,15 +704,16 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
   if (p.split == 1) {
     hipError_t e;
     const auto al16 = [](const void* ptr) { return ((uintptr_t)ptr & 15) == 0; };
-    const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (M >= 2048 && tiles256 >= 256 && Kd % 32 == 0 && N % 4 == 0 && al16(out) &&
-        (bias == nullptr || al16(bias)) && (ep.resid == nullptr || al16(ep.resid))) {
-      switch (ep.kind) {
-        case EPI_F32: e = launch_dma<EPI_F32>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
-        case EPI_BF16: e = launch_dma<EPI_BF16>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
-        case EPI_SILU_BF16: e = launch_dma<EPI_SILU_BF16>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
-        default: e = launch_dma<EPI_RESID_F32>(A, M, Kd, W, N, bias, ep.resid, out, stream); break;
-      }
+    const auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (M >= 2048 && Kd % 32 == 0 && N % 4 == 0 && al16(out) && (bias == nullptr || al16(bias)) &&
+        (ep.resid == nullptr || al16(ep.resid))) {
+      // the largest tile that still gives every CU work
+      if (tiles(256, 256) >= 256)
+        e = launch_dma<256, 256>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+      else if (tiles(256, 128) >= 256)
+        e = launch_dma<256, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+      else
+        e = launch_dma<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     } else if (M >= 2048)
       e = launch_tile<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     else if (M > 64)

@@ -340,7 +340,7 @@ def counter_traffic(workload, stage):
 
 
 # Kernel roles, by name, for splitting a step's dispatch sequence into stages.
-_GEMM_MAIN = ("gemm_kernel", "gemm_part_kernel")
+_GEMM_MAIN = ("gemm_kernel", "gemm_part_kernel", "gemm_dma_kernel", "gemm_fullk_kernel")
 _GEMM_TAIL = ("splitk_", "rmsnorm", "heads_l2norm")
 _LINEAR_ORDER = ["linear_conf_w2"] + [f"{n}.l{l}" for l in range(2)
                                       for n in ("linear_qkv", "linear_o", "linear_ffn1", "linear_ffn2")] \
@@ -349,13 +349,14 @@ _LINEAR_ORDER = ["linear_conf_w2"] + [f"{n}.l{l}" for l in range(2)
 
 def split_step_stages(names):
     """Stage name for each kernel of one step's dispatch sequence."""
+    import re
     out, lin, att = [], 0, 0
     for n in names:
         if "topk_" in n:
             out.append("topk_lse")
         elif "node_build" in n:
             out.append("node_build")
-        elif "attention_kernel" in n:
+        elif re.search(r"attention_\w*kernel", n):
             out.append(f"lattice_attention.l{att}")
             att += 1
         elif any(k in n for k in _GEMM_MAIN):

@@ -13,12 +13,49 @@
 namespace ll {
 namespace {
 
+// One K x K cosine matrix (rows of o against rows of in, d_e wide) by one
+// wave, 16 x 16 MFMA tiles; emit(ra, b, value) receives every in-range entry.
+// Rows past K are clamped to row K - 1 (their results are never emitted), so
+// every load is unconditional and a 256-wide slice of d is loaded ahead of
+// its MFMAs (conditional loads would be serialised).
+template <typename Emit>
+__device__ __forceinline__ void pair_matrix(const uint16_t* __restrict__ o,
+                                            const uint16_t* __restrict__ in, int K, int de,
+                                            int lane, Emit emit) {
+  const int g = lane >> 4, c = lane & 15;
+  const int tiles = (K + 15) / 16;
+  for (int at = 0; at < tiles; ++at)
+    for (int bt = 0; bt < tiles; ++bt) {
+      const int a = min(at * 16 + c, K - 1), b = min(bt * 16 + c, K - 1);
+      const uint16_t* ar = o + (int64_t)a * de + 8 * g;
+      const uint16_t* br = in + (int64_t)b * de + 8 * g;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < de; k0 += 256) {
+        u32x4_t af[8], bf[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          if (k0 + ks * 32 < de) {
+            af[ks] = *(const u32x4_t*)(ar + k0 + ks * 32);
+            bf[ks] = *(const u32x4_t*)(br + k0 + ks * 32);
+          }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          if (k0 + ks * 32 < de) acc = mfma16(af[ks], bf[ks], acc);
+      }
+      const int bc = bt * 16 + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = at * 16 + 4 * g + i;
+        if (ra < K && bc < K) emit(ra, bc, acc[i]);
+      }
+    }
+}
+
 __global__ __launch_bounds__(256) void pair_scores_kernel(const uint16_t* __restrict__ outv,
                                                           const uint16_t* __restrict__ inv, int N,
                                                           int B, int K, int de,
                                                           float* __restrict__ cos) {
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, c = lane & 15;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)N * (B - 1)) return;
   const int64_t n = pair / (B - 1);
@@ -26,24 +63,7 @@ __global__ __launch_bounds__(256) void pair_scores_kernel(const uint16_t* __rest
   const uint16_t* o = outv + ((n * B + s - 1) * K) * (int64_t)de;
   const uint16_t* in = inv + ((n * B + s) * K) * (int64_t)de;
   float* dst = cos + pair * K * K;
-  const int tiles = (K + 15) / 16;
-  for (int at = 0; at < tiles; ++at)
-    for (int bt = 0; bt < tiles; ++bt) {
-      const int a = at * 16 + c, b = bt * 16 + c;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < de; k0 += 32) {
-        const u32x4_t af = a < K ? *(const u32x4_t*)(o + (int64_t)a * de + k0 + 8 * g)
-                                 : u32x4_t{0, 0, 0, 0};
-        const u32x4_t bf = b < K ? *(const u32x4_t*)(in + (int64_t)b * de + k0 + 8 * g)
-                                 : u32x4_t{0, 0, 0, 0};
-        acc = mfma16(af, bf, acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra = at * 16 + 4 * g + i;
-        if (ra < K && b < K) dst[ra * K + b] = acc[i];
-      }
-    }
+  pair_matrix(o, in, K, de, lane, [&](int ra, int b, float v) { dst[ra * K + b] = v; });
 }
 
 __global__ __launch_bounds__(256) void greedy_walk_kernel(
@@ -82,11 +102,11 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
 }
 
 // Fused pair scores + greedy commit for the rerank path: one workgroup per
-// block. The four waves compute the block's B-1 K x K cosine matrices into LDS
+// block. The eight waves compute the block's B-1 K x K cosine matrices into LDS
 // (and to global memory when requested); the walk then reads its rows, the
 // log-probabilities and the ids from LDS, so each sequential step costs LDS
 // latency rather than a global round trip.
-__global__ __launch_bounds__(256) void scores_walk_kernel(
+__global__ __launch_bounds__(512) void scores_walk_kernel(
     const uint16_t* __restrict__ outv, const uint16_t* __restrict__ inv,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int B, int K,
     int de, float alpha, int use_logp, float* __restrict__ cos_out,
@@ -97,37 +117,20 @@ __global__ __launch_bounds__(256) void scores_walk_kernel(
   float* s_logp = sm + (B - 1) * KK;                // [B K]
   int* s_idx = (int*)(s_logp + B * K);              // [B K]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c = lane & 15;
   const int64_t n = blockIdx.x;
   const int64_t base = n * B * K;
-  for (int i = tid; i < B * K; i += 256) {
+  for (int i = tid; i < B * K; i += blockDim.x) {
     s_logp[i] = topk_logp[base + i];
     s_idx[i] = topk_idx[base + i];
   }
-  const int tiles = (K + 15) / 16;
-  for (int p = wave; p < B - 1; p += 4) {
+  const int nw = blockDim.x >> 6;
+  for (int p = wave; p < B - 1; p += nw) {
     const uint16_t* o = outv + (base + (int64_t)p * K) * de;
     const uint16_t* in = inv + (base + (int64_t)(p + 1) * K) * de;
-    for (int at = 0; at < tiles; ++at)
-      for (int bt = 0; bt < tiles; ++bt) {
-        const int a = at * 16 + c, b = bt * 16 + c;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < de; k0 += 32) {
-          const u32x4_t af = a < K ? *(const u32x4_t*)(o + (int64_t)a * de + k0 + 8 * g)
-                                   : u32x4_t{0, 0, 0, 0};
-          const u32x4_t bf = b < K ? *(const u32x4_t*)(in + (int64_t)b * de + k0 + 8 * g)
-                                   : u32x4_t{0, 0, 0, 0};
-          acc = mfma16(af, bf, acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ra = at * 16 + 4 * g + i;
-          if (ra < K && b < K) {
-            s_cos[p * KK + ra * K + b] = acc[i];
-            if (cos_out) cos_out[(n * (B - 1) + p) * KK + ra * K + b] = acc[i];
-          }
-        }
-      }
+    pair_matrix(o, in, K, de, lane, [&](int ra, int b, float v) {
+      s_cos[p * KK + ra * K + b] = v;
+      if (cos_out) cos_out[(n * (B - 1) + p) * KK + ra * K + b] = v;
+    });
   }
   __syncthreads();
   if (wave != 0) return;
@@ -148,7 +151,8 @@ __global__ __launch_bounds__(256) void scores_walk_kernel(
     int bl = lane;
     wave_argmax(bz, bl);
     if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
-    const float second = wave_max(lane == bl ? -INFINITY : z);
+    // the runner-up is only needed for the optional gap output
+    const float second = gap ? wave_max(lane == bl ? -INFINITY : z) : 0.f;
     cprev = bl;
     if (lane == 0) {
       out_tokens[r0 + s] = s_idx[s * K + bl];
@@ -175,7 +179,7 @@ hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const i
                         kScoresWalkMaxLds);
     attr_set = true;
   }
-  hipLaunchKernelGGL(scores_walk_kernel, dim3((unsigned)N), dim3(256), lds, stream, outv, inv,
+  hipLaunchKernelGGL(scores_walk_kernel, dim3((unsigned)N), dim3(512), lds, stream, outv, inv,
                      topk_idx, topk_logp, B, K, d_e, alpha, use_logp, cos_out, out_tokens, score,
                      gap);
   return hipGetLastError();

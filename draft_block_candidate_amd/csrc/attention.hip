@@ -210,6 +210,15 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
   const int64_t H3 = 3 * (int64_t)H;
   const uint16_t* blk = qkv + n * T * H3;
 
+  // Query fragments of this wave's first tile, issued before the staging
+  // loads so that their latency overlaps them.
+  u32x4_t qf0[KS];
+  {
+    const int qc = min(wave * 16 + c, T - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf0[ks] = *(const u32x4_t*)(blk + (int64_t)qc * H3 + h * DH + ks * 32 + 8 * g);
+  }
   if (tid < 127) bias_tab[tid] = dist[h * 127 + tid];
   const float same_h = same[h];
   // K (chunk-fastest) and V (key-fastest) of this head, all loads issued
@@ -243,30 +252,41 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
   __syncthreads();
 
   const float scale = 1.0f / __fsqrt_rn((float)DH);
-  const int nkt = (T + 15) / 16, nch = (T + 31) / 32;
+  // slot of a token: (t * kmul) >> 16 equals t / K for t < 1024 and K <= 64
+  const unsigned kmul = (65536u + K - 1) / K;
   const int ntile = (T + 15) / 16;
   for (int qt = wave; qt < ntile; qt += NW) {
     const int q = qt * 16 + c;   // this lane's query
     const bool q_ok = q < T;
     const int qc = min(q, T - 1);   // rows past the lattice compute a copy, never stored
-    const int slot_q = qc / K;
+    const int slot_q = (int)(((unsigned)qc * kmul) >> 16);
     u32x4_t qf[KS];
+    if (qt == wave) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = *(const u32x4_t*)(blk + (int64_t)qc * H3 + h * DH + ks * 32 + 8 * g);
-    // S^T tiles: key tiles are independent accumulation chains
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = qf0[ks];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = *(const u32x4_t*)(blk + (int64_t)qc * H3 + h * DH + ks * 32 + 8 * g);
+    }
+    // S^T tiles: key tiles are independent accumulation chains. Every tile of
+    // TMAX is computed (rows past the lattice hold copies of its last token
+    // and are masked below), so the loop has no branches and a k-step's LDS
+    // reads are all issued before its MFMAs.
     f32x4_t acc[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t kf[KT];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        if (kt >= nkt) continue;
-        const u32x4_t kf = *(const u32x4_t*)(&Ks[kat(kt * 16 + c, ks * 4 + g)]);
-        acc[kt] = mfma16(kf, qf[ks], acc[kt]);
-      }
+      for (int kt = 0; kt < KT; ++kt) kf[kt] = *(const u32x4_t*)(&Ks[kat(kt * 16 + c, ks * 4 + g)]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = mfma16(kf[kt], qf[ks], acc[kt]);
+      __builtin_amdgcn_sched_barrier(0);   // keep each k-step's reads with it
     }
+    // masking by select: the bias-table reads use a clamped slot and are
+    // unconditional (a read under a per-element branch is waited for inside it)
     float s[KT][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -274,12 +294,10 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kt * 16 + 4 * g + i;
-        float v = -INFINITY;
-        if (kt < nkt && key < T) {
-          const int slot_k = key / K;
-          v = acc[kt][i] * scale + bias_tab[slot_k - slot_q + 63];
-          if (slot_k == slot_q) v += same_h;
-        }
+        const int slot_k = (int)(((unsigned)min(key, T - 1) * kmul) >> 16);
+        float v = acc[kt][i] * scale + bias_tab[slot_k - slot_q + 63];
+        v = slot_k == slot_q ? v + same_h : v;
+        v = key < T ? v : -INFINITY;
         s[kt][i] = v;
         mx = fmaxf(mx, v);
       }
@@ -302,9 +320,9 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
     for (int d = 0; d < DT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // k-slot j of lane group g stands for key 32*ch + 4g + j (j < 4) or
     // 32*ch + 16 + 4g + (j - 4) (j >= 4), matching the score layout
+    // chunks past the lattice carry probability 0 against finite values
 #pragma unroll
     for (int ch = 0; ch < KT / 2; ++ch) {
-      if (ch >= nch) break;
       u32x4_t pb;
       pb[0] = pack_bf16x2(s[2 * ch][0], s[2 * ch][1]);
       pb[1] = pack_bf16x2(s[2 * ch][2], s[2 * ch][3]);
@@ -318,6 +336,7 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
         const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
         oacc[d] = mfma16(va, pb, oacc[d]);
       }
+      __builtin_amdgcn_sched_barrier(0);   // bound the V reads in flight
     }
     if (q_ok) {
       const float inv = 1.0f / lsum;

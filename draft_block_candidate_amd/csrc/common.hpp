@@ -87,14 +87,15 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Largest (v, i) by v descending, then i ascending; result in every lane.
+// Written with non-short-circuit operators and selects: a branchy form
+// compiles to exec-mask updates whose hazards stall every step.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ void argmax_step(float& v, int& i) {
   const float ov = dpp_f<CTRL, ROW_MASK>(-INFINITY, v);
   const int oi = dpp_i<CTRL, ROW_MASK>(0x7fffffff, i);
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
+  const bool take = (ov > v) | ((ov == v) & (oi < i));
+  v = take ? ov : v;
+  i = take ? oi : i;
 }
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step<kDppShr1, 0xf>(v, i);

@@ -112,28 +112,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ 
     __syncthreads();
   }
 
-  // Epilogue: lane holds rows 4g+q, column c of every 16 x 16 tile.
+  // Epilogue: lane holds rows 4g+q, column c of every 16 x 16 tile. Bias and
+  // residual addresses are clamped so their loads are unconditional; only the
+  // stores are predicated.
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int64_t n = n0 + wn * (BN / 2) + j * 16 + c;
-    if (n >= N) continue;
-    const float bv = bias ? bias[n] : 0.f;
+    const int64_t nc = min(n, (int64_t)N - 1);
+    const float bv = bias ? bias[nc] : 0.f;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t m = m0 + wm * (BM / 2) + i * 16 + 4 * g + q;
-        if (m >= M) continue;
+        const bool ok = m < M && n < N;
         const float y = acc[i][j][q] + bv;
         const int64_t o = m * N + n;
         if constexpr (EPI == EPI_F32) {
-          ((float*)out)[o] = y;
+          if (ok) ((float*)out)[o] = y;
         } else if constexpr (EPI == EPI_BF16) {
-          ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(y);
+          if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(y);
         } else if constexpr (EPI == EPI_SILU_BF16) {
-          ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(silu(y));
+          if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(silu(y));
         } else {
-          ((float*)out)[o] = resid[o] + y;
+          const float r = resid[min(m, (int64_t)M - 1) * N + nc];
+          if (ok) ((float*)out)[o] = r + y;
         }
       }
     }
@@ -162,13 +165,15 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited).
 constexpr int waitcnt_vm(int v) { return (v & 15) | ((v >> 4) << 14) | 0x70 | 0xF00; }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM * BN >= 32768 ? 1 : 2, BM * BN >= 32768 ? 1 : 2))) void gemm_dma_kernel(
+template <int BM, int BN, int EPI, int NW = 4>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN * 4 / NW >= 32768 ? 1 : 2, BM * BN * 4 / NW >= 32768 ? 1 : 2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N, int Kd,
     const float* __restrict__ bias, const float* resid, void* out, int tiles_n, int ntiles) {
   constexpr int BK = 32, NS = 4;
-  constexpr int WM = BM / 2, WN = BN / 2, MT = WM / 32, NT = WN / 32;
-  constexpr int UA = BM / 64, UW = BN / 64;   // 1 KiB stage-load instructions per wave
+  constexpr int WGN = NW / 2;                  // waves: 2 x WGN grid
+  constexpr int WM = BM / 2, WN = BN / WGN, MT = WM / 32, NT = WN / 32;
+  constexpr int UA = BM / 16 / NW, UW = BN / 16 / NW;   // 1 KiB stage-load instructions per wave
+  static_assert(UA >= 1 && UW >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "stage loads");
   constexpr int PER = UA + UW;                 // per wave per stage
   constexpr int STAGE = (BM + BN) * BK;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM * BN >= 
   if (t >= ntiles) return;
   const int64_t m0 = (int64_t)(t / tiles_n) * BM, n0 = (int64_t)(t % tiles_n) * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Stage loads: instruction j of A (0 .. BM/16 - 1 over the workgroup) covers
@@ -275,9 +280,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM * BN >= 
   __syncthreads();   // every wave is done reading the pipeline stages
   constexpr int ES = WN + 4;          // floats per staged row (16-byte pad)
   constexpr int CPRW = WN / 4;        // 4-column chunks per row
-  static_assert(4 * (32 * ES + 64) * 4 <= NS * STAGE * 2, "epilogue staging fits");
+  static_assert(NW * (32 * ES + 64) * 4 <= NS * STAGE * 2, "epilogue staging fits");
+  static_assert(64 % CPRW == 0, "a lane keeps one column chunk");
   float* stg = (float*)smem + wave * (32 * ES + 64);
-  const int64_t col0 = n0 + wn * WN;
+  // A lane stores the same 4-column chunk in every row it handles, so its
+  // bias is loaded once. Loads never sit behind the row/column predicate
+  // (the residual address is clamped instead): a load under a branch is
+  // waited for before the branch closes, serialising the whole epilogue.
+  const int c4 = (lane % CPRW) * 4;
+  const int64_t n = n0 + wn * WN + c4;
+  const bool col_ok = n < N;
+  const int64_t nc = min(n, (int64_t)N - 4);
+  float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (bias) bv = *(const float4*)(bias + nc);
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -288,53 +303,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM * BN >= 
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int u = 0; u < 32 * CPRW / 64; ++u) {
-      const int ch = lane + 64 * u, rr = ch / CPRW, c4 = (ch % CPRW) * 4;
+      const int rr = (lane + 64 * u) / CPRW;
       const int64_t m = m0 + wm * WM + i * 32 + rr;
-      const int64_t n = col0 + c4;
-      if (m >= M || n >= N) continue;
+      const bool ok = col_ok && m < M;
       float4 y = *(const float4*)(&stg[rr * ES + c4]);
-      if (bias) {
-        const float4 bv = *(const float4*)(bias + n);
-        y.x += bv.x; y.y += bv.y; y.z += bv.z; y.w += bv.w;
-      }
+      y.x += bv.x; y.y += bv.y; y.z += bv.z; y.w += bv.w;
       const int64_t o = m * N + n;
       if constexpr (EPI == EPI_F32) {
-        *(float4*)((float*)out + o) = y;
+        if (ok) *(float4*)((float*)out + o) = y;
       } else if constexpr (EPI == EPI_BF16) {
-        *(uint2*)((uint16_t*)out + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+        if (ok) *(uint2*)((uint16_t*)out + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
       } else if constexpr (EPI == EPI_SILU_BF16) {
-        *(uint2*)((uint16_t*)out + o) =
-            make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
+        if (ok)
+          *(uint2*)((uint16_t*)out + o) =
+              make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
       } else {
-        const float4 rv = *(const float4*)(resid + o);
-        *(float4*)((float*)out + o) = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
+        const float4 rv = *(const float4*)(resid + min(m, (int64_t)M - 1) * N + nc);
+        if (ok) *(float4*)((float*)out + o) = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NW = 4>
 hipError_t launch_dma(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
                       int epi, const float* resid, void* out, hipStream_t stream) {
   const int tiles_n = (N + BN - 1) / BN;
   const int ntiles = ((M + BM - 1) / BM) * tiles_n;
-  const dim3 grid((unsigned)ntiles);
+  const dim3 grid((unsigned)ntiles), block(64 * NW);
   switch (epi) {
     case EPI_F32:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_F32>), grid, dim3(256), 0, stream, A, W, M, N,
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_F32, NW>), grid, block, 0, stream, A, W, M, N,
                          Kd, bias, resid, out, tiles_n, ntiles);
       break;
     case EPI_BF16:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_BF16>), grid, dim3(256), 0, stream, A, W, M, N,
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_BF16, NW>), grid, block, 0, stream, A, W, M, N,
                          Kd, bias, resid, out, tiles_n, ntiles);
       break;
     case EPI_SILU_BF16:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_SILU_BF16>), grid, dim3(256), 0, stream, A, W,
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_SILU_BF16, NW>), grid, block, 0, stream, A, W,
                          M, N, Kd, bias, resid, out, tiles_n, ntiles);
       break;
     default:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_RESID_F32>), grid, dim3(256), 0, stream, A, W,
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_RESID_F32, NW>), grid, block, 0, stream, A, W,
                          M, N, Kd, bias, resid, out, tiles_n, ntiles);
       break;
   }
@@ -382,18 +394,23 @@ __global__ __launch_bounds__(256) void gemm_part_kernel(const uint16_t* __restri
   const int64_t m0 = (int64_t)(tile / tiles_n) * BM, n0 = (int64_t)(tile % tiles_n) * BN;
   const int64_t k0 = (int64_t)s * KS;
 
+  // Every load is issued unconditionally (rows past the matrix are clamped to
+  // its last row; their products land in rows that are never stored), so all
+  // of them are in flight together: one memory round trip per workgroup.
   u32x4_t r[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int ch = tid + 256 * i;
-    if (ch < CH_A) {
-      const int64_t gm = m0 + ch / CPR;
-      r[i] = gm < M ? *(const u32x4_t*)(A + gm * Kd + k0 + (ch % CPR) * 8) : u32x4_t{0, 0, 0, 0};
+    const uint16_t* src;
+    if (ch < CH_A) {   // uniform per i: CH_A is a multiple of 256
+      const int64_t gm = min(m0 + ch / CPR, (int64_t)M - 1);
+      src = A + gm * Kd + k0 + (ch % CPR) * 8;
     } else {
       const int cw = ch - CH_A;
-      const int64_t gn = n0 + cw / CPR;
-      r[i] = gn < N ? *(const u32x4_t*)(W + gn * Kd + k0 + (cw % CPR) * 8) : u32x4_t{0, 0, 0, 0};
+      const int64_t gn = min(n0 + cw / CPR, (int64_t)N - 1);
+      src = W + gn * Kd + k0 + (cw % CPR) * 8;
     }
+    r[i] = *(const u32x4_t*)src;
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -425,18 +442,102 @@ __global__ __launch_bounds__(256) void gemm_part_kernel(const uint16_t* __restri
       for (int j = 0; j < NT; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
   }
 
+  // The tile goes out through LDS (row-major, 4-float pad) as 16-byte row
+  // stores; N % 4 == 0, so a 4-column chunk is entirely inside or outside.
+  constexpr int ES = BN + 4;
+  static_assert(BM * ES * 4 <= (BM + BN) * KS * 2, "epilogue staging fits");
+  __syncthreads();   // every wave is done with the A and W slices
+  float* stg = (float*)smem;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        stg[(wm * (BM / 2) + i * 16 + 4 * g + qq) * ES + wn * (BN / 2) + j * 16 + c] = acc[i][j][qq];
+  __syncthreads();
   float* ps = part + (int64_t)s * M * N;
+  constexpr int C4 = BN / 4;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int64_t n = n0 + wn * (BN / 2) + j * 16 + c;
-    if (n >= N) continue;
+  for (int u = 0; u < BM * C4 / 256; ++u) {
+    const int idx = tid + 256 * u, row = idx / C4, c4 = (idx % C4) * 4;
+    const int64_t m = m0 + row, n = n0 + c4;
+    if (m < M && n < N) *(float4*)(ps + m * N + n) = *(const float4*)(&stg[row * ES + c4]);
+  }
+}
+
+// Few-row linear (M <= 128): one workgroup of eight waves per 16 output
+// columns over the whole of K, so there are no split-K partials and the
+// epilogue is fused. Wave w owns rows 16 w .. 16 w + 15 and loads its A rows
+// straight into MFMA fragments (an A element is used once per workgroup, so
+// staging it would buy nothing); the 16 W rows, shared by the eight waves, go
+// through LDS per 1024-wide K chunk with the 16-byte chunk index XOR-swizzled
+// by the row, so a fragment read touches every bank once. Every load is
+// unconditional (indices clamped; k-steps past K get a zero A fragment, rows
+// and columns past the matrix are computed and not stored), so one K chunk
+// costs one memory round trip.
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
+                                                          const uint16_t* __restrict__ W, int M,
+                                                          int N, int Kd,
+                                                          const float* __restrict__ bias,
+                                                          const float* resid, void* out) {
+  constexpr int KC = 1024, CPR = KC / 8, KSTEPS = KC / 32;
+  constexpr int WCH = 16 * CPR / 512;   // W chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[16 * KC];
+  auto wat = [](int row, int ch) { return row * KC + ((ch ^ (row & 15)) << 3); };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t arow = min(wave * 16 + c, M - 1);
+  const uint16_t* ap = A + arow * Kd + 8 * g;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < Kd; k0 += KC) {
+    const int kc = min(KC, Kd - k0);   // a multiple of 32
+    u32x4_t wr[WCH];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < WCH; ++i) {
+      const int ch = tid + 512 * i, row = ch / CPR, cc = min(ch % CPR, kc / 8 - 1);
+      const int64_t wrow = min(n0 + row, (int64_t)N - 1);
+      wr[i] = *(const u32x4_t*)(W + wrow * Kd + k0 + cc * 8);
+    }
+    u32x4_t af[KSTEPS];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int64_t m = m0 + wm * (BM / 2) + i * 16 + 4 * g + qq;
-        if (m < M) ps[m * N + n] = acc[i][j][qq];
-      }
+    for (int ks = 0; ks < KSTEPS; ++ks) af[ks] = *(const u32x4_t*)(ap + k0 + min(ks * 32, kc - 32));
+    if (k0 > 0) __syncthreads();   // every wave is done with the previous chunk
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int ch = tid + 512 * i;
+      *(u32x4_t*)(&Ws[wat(ch / CPR, ch % CPR)]) = wr[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4_t a = ks * 32 < kc ? af[ks] : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t wf = *(const u32x4_t*)(&Ws[wat(c, ks * 4 + g)]);
+      acc = mfma16(a, wf, acc);
+    }
+  }
+  // acc[i]: row 16 w + 4 g + i, column n0 + c
+  const int64_t n = n0 + c, nc = min(n, (int64_t)N - 1);
+  const float bv = bias ? bias[nc] : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = wave * 16 + 4 * g + i;
+    const bool ok = m < M && n < N;
+    const float y = acc[i] + bv;
+    const int64_t o = m * N + n;
+    if constexpr (EPI == EPI_F32) {
+      if (ok) ((float*)out)[o] = y;
+    } else if constexpr (EPI == EPI_BF16) {
+      if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(y);
+    } else if constexpr (EPI == EPI_SILU_BF16) {
+      if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(silu(y));
+    } else {
+      const float r = resid[min(m, (int64_t)M - 1) * N + nc];
+      if (ok) ((float*)out)[o] = r + y;
+    }
   }
 }
 
@@ -506,37 +607,43 @@ __global__ __launch_bounds__(256) void splitk_resid_rmsnorm_kernel(
   const int64_t MN4 = (int64_t)M * N / 4;
   const int n4 = N / 4;
   const float4* part4 = (const float4*)part;
+  // Loads use clamped indices and are unconditional, so the NV column groups'
+  // partials, bias and residual are all in flight at once; only the stores
+  // and the sum are predicated.
   float4 v[NV];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int gi = lane + 64 * i;
-    if (gi < n4) {
-      const int64_t q = m * n4 + gi;
-      const float4 y = splitk_sum4<S>(part4, MN4, q);
-      const float4 b = bias ? ((const float4*)bias)[gi] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 r = ((const float4*)resid)[q];
-      v[i] = make_float4(r.x + (y.x + b.x), r.y + (y.y + b.y), r.z + (y.z + b.z), r.w + (y.w + b.w));
-      ((float4*)x_out)[q] = v[i];
-    } else {
-      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    const int gc = min(gi, n4 - 1);
+    const int64_t q = m * n4 + gc;
+    const float4 y = splitk_sum4<S>(part4, MN4, q);
+    const float4 b = bias ? ((const float4*)bias)[gc] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 r = ((const float4*)resid)[q];
+    v[i] = make_float4(r.x + (y.x + b.x), r.y + (y.y + b.y), r.z + (y.z + b.z), r.w + (y.w + b.w));
+    if (gi >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < n4) ((float4*)x_out)[m * n4 + gi] = v[i];
     ss = fmaf(v[i].x, v[i].x, ss);
     ss = fmaf(v[i].y, v[i].y, ss);
     ss = fmaf(v[i].z, v[i].z, ss);
     ss = fmaf(v[i].w, v[i].w, ss);
   }
+  float4 gv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) gv[i] = ((const float4*)gamma)[min(lane + 64 * i, n4 - 1)];
   ss = wave_sum(ss);
   const float rstd = 1.0f / __fsqrt_rn(ss / (float)N + eps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int gi = lane + 64 * i;
-    if (gi < n4) {
-      const float4 gv = ((const float4*)gamma)[gi];
+    if (gi < n4)
       ((uint2*)(u_out + m * N))[gi] =
-          make_uint2(pack_bf16x2(v[i].x * rstd * gv.x, v[i].y * rstd * gv.y),
-                     pack_bf16x2(v[i].z * rstd * gv.z, v[i].w * rstd * gv.w));
-    }
+          make_uint2(pack_bf16x2(v[i].x * rstd * gv[i].x, v[i].y * rstd * gv[i].y),
+                     pack_bf16x2(v[i].z * rstd * gv[i].z, v[i].w * rstd * gv[i].w));
   }
 }
 
@@ -557,12 +664,15 @@ __global__ __launch_bounds__(256) void splitk_heads_l2norm_kernel(
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int gi = lane + 64 * i;
-    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (gi < n4) {
-      const float4 y = splitk_sum4<S>(part4, MN4, m * n4 + gi);
-      const float4 b = ((const float4*)bias)[gi];
-      v[i] = make_float4(y.x + b.x, y.y + b.y, y.z + b.z, y.w + b.w);
-    }
+    const int gc = min(gi, n4 - 1);   // clamped: loads stay unconditional
+    const float4 y = splitk_sum4<S>(part4, MN4, m * n4 + gc);
+    const float4 b = ((const float4*)bias)[gc];
+    v[i] = make_float4(y.x + b.x, y.y + b.y, y.z + b.z, y.w + b.w);
+    if (gi >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = lane + 64 * i;
     const float sq = v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
     if (gi < h4) ss0 += sq; else ss1 += sq;
   }
@@ -677,6 +787,35 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
 
 }  // namespace
 
+hipError_t launch_skinny(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
+                         const float* bias, int epi, const float* resid, void* out,
+                         hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 15) / 16));
+  switch (epi) {
+    case EPI_F32:
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_F32>), grid, dim3(512), 0, stream, A, W, M, N, Kd,
+                         bias, resid, out);
+      break;
+    case EPI_BF16:
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_BF16>), grid, dim3(512), 0, stream, A, W, M, N, Kd,
+                         bias, resid, out);
+      break;
+    case EPI_SILU_BF16:
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_SILU_BF16>), grid, dim3(512), 0, stream, A, W, M,
+                         N, Kd, bias, resid, out);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_RESID_F32>), grid, dim3(512), 0, stream, A, W, M,
+                         N, Kd, bias, resid, out);
+      break;
+  }
+  return hipGetLastError();
+}
+
+bool uses_skinny(int M, int Kd, int N) {
+  return M <= 128 && Kd % 32 == 0 && (N + 15) / 16 >= 128;
+}
+
 GemmPlan plan_linear(int M, int Kd, int N) {
   GemmPlan p{};
   p.split = 1;
@@ -700,6 +839,10 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
                          const float* bias, const LinearEpilogue& ep, void* out, float* part,
                          hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  // Few rows and enough 16-column tiles to occupy the GPU: one pass over K
+  // with the epilogue fused (row-wide epilogues need whole rows: not here).
+  if (uses_skinny(M, Kd, N) && ep.norm_out == nullptr && ep.heads_out == nullptr)
+    return launch_skinny(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
   const GemmPlan p = plan_linear(M, Kd, N);
   if (p.split == 1) {
     hipError_t e;

@@ -31,6 +31,9 @@ struct GemmPlan {
   size_t part_floats;
 };
 GemmPlan plan_linear(int M, int Kd, int N);
+// True when launch_linear runs the product as one few-row pass over K
+// (no split-K scratch) for epilogues that need no whole rows.
+bool uses_skinny(int M, int Kd, int N);
 
 // What follows the product y = A W^T + bias:
 //   kind       EPI_* store of y (EPI_RESID_F32: out = resid + y)

@@ -55,8 +55,10 @@ constexpr int kBufferWord3 = 0x00020000;
 // Cache-policy operand of a buffer load: non-temporal (streamed once).
 constexpr int kLoadNonTemporal = 2;
 
+// Non-short-circuit form, so lane-varying uses compile to selects rather
+// than exec-mask branches.
 __device__ __forceinline__ bool key_gt(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+  return (av > bv) | ((av == bv) & (ai < bi));
 }
 
 struct State {
@@ -85,13 +87,10 @@ __device__ __forceinline__ void list_insert(State& st, float cv, int ci, int K, 
   // wave_shr:1 (DPP): every lane receives the entry of the lane below it
   const float upv = dpp_f<0x138, 0xf>(st.lv, st.lv);
   const int upi = dpp_i<0x138, 0xf>(st.li, st.li);
-  if (lane == pos) {
-    st.lv = cv;
-    st.li = ci;
-  } else if (lane > pos && lane < K) {
-    st.lv = upv;
-    st.li = upi;
-  }
+  const bool here = lane == pos;
+  const bool shift = (lane > pos) & (lane < K);
+  st.lv = here ? cv : (shift ? upv : st.lv);
+  st.li = here ? ci : (shift ? upi : st.li);
   st.th_v = readlane_f(st.lv, K - 1);
   st.th_i = readlane_i(st.li, K - 1);
 }
@@ -165,7 +164,8 @@ __device__ __forceinline__ void rebase(State& st, const u32x4_t (&w0)[NV], float
 
 // Seed the list from a group: the 64 lanes' best elements, bitonic-sorted
 // (descending key); the first K become the list. Returns this lane's best id
-// (already offered, to be skipped by the candidate scan).
+// (to be skipped by the candidate scan: inside the list it would be a
+// duplicate, outside it fails the strict key test anyway).
 template <int NV, int EPV, int LS>
 __device__ __forceinline__ int seed_list(State& st, const u32x4_t (&w)[NV], int base, int K, int lane) {
   float bv = -INFINITY;
@@ -176,10 +176,9 @@ __device__ __forceinline__ int seed_list(State& st, const u32x4_t (&w)[NV], int 
     for (int e = 0; e < EPV; ++e) {
       // a lane's ids increase with (u, e): strict > keeps the lowest id of a tie
       const float x = elem<EPV>(w[u], e);
-      if (x > bv) {
-        bv = x;
-        bi = base + (u * 64 + lane) * LS + e;
-      }
+      const bool better = x > bv;
+      bv = better ? x : bv;
+      bi = better ? base + (u * 64 + lane) * LS + e : bi;
     }
   float sv = bv;
   int si = bi;
@@ -190,11 +189,9 @@ __device__ __forceinline__ int seed_list(State& st, const u32x4_t (&w)[NV], int 
       const float ov = __shfl_xor(sv, j, 64);
       const int oi = __shfl_xor(si, j, 64);
       const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
-      const bool mine_better = key_gt(sv, si, ov, oi);
-      if (keep_better != mine_better) {
-        sv = ov;
-        si = oi;
-      }
+      const bool swap = keep_better != key_gt(sv, si, ov, oi);
+      sv = swap ? ov : sv;
+      si = swap ? oi : si;
     }
   }
   st.lv = lane < K ? sv : -INFINITY;
@@ -226,15 +223,16 @@ __device__ __forceinline__ void topk_pass(State& st, const u32x4_t (&w0)[NV], co
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
       const float x = elem<EPV>(w[u], e);
-      // logits are finite: -inf elements are padding and never enter
-      uint64_t mask = __ballot(x >= fmaxf(st.th_v, -3.402823466e38f));
+      const int id = base + (u * 64 + lane) * LS + e;
+      // logits are finite: -inf elements are padding and never enter; an
+      // element already placed by the seeding is dropped here
+      uint64_t mask = __ballot((x >= fmaxf(st.th_v, -3.402823466e38f)) & (id != excl));
       while (mask) {
         const int l = __ffsll((long long)mask) - 1;
         mask &= mask - 1;
         const float cv = readlane_f(x, l);
         const int ci = base + (u * 64 + l) * LS + e;
-        if (ci != readlane_i(excl, l) && key_gt(cv, ci, st.th_v, st.th_i))
-          list_insert(st, cv, ci, K, lane);
+        if (key_gt(cv, ci, st.th_v, st.th_i)) list_insert(st, cv, ci, K, lane);
       }
     }
   }
@@ -395,25 +393,44 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
   const int64_t rbase = (int64_t)row * P * K;
-  for (int i = lane; i < P * K; i += 64) {
-    sv[i] = part_val[rbase + i];
-    si[i] = part_idx[rbase + i];
+  const int n = P * K;
+  // Eight entries per lane per batch, every load issued before the first
+  // is used (indices clamped to the row, duplicates written twice with the
+  // same value), so staging costs one memory round trip per 512 entries.
+  for (int i0 = 0; i0 < n; i0 += 512) {
+    float bv[8];
+    int bi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = min(i0 + j * 64 + lane, n - 1);
+      bv[j] = part_val[rbase + i];
+      bi[j] = part_idx[rbase + i];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = min(i0 + j * 64 + lane, n - 1);
+      sv[i] = bv[j];
+      si[i] = bi[j];
+    }
   }
-  float m = kMInit, s = 0.f;
-  if (lane < P) {
-    m = part_ms[2 * ((int64_t)row * P + lane)];
-    s = part_ms[2 * ((int64_t)row * P + lane) + 1];
+  const int pl = min(lane, P - 1);
+  float m = part_ms[2 * ((int64_t)row * P + pl)];
+  float s = part_ms[2 * ((int64_t)row * P + pl) + 1];
+  if (lane >= P) {
+    m = kMInit;
+    s = 0.f;
   }
   const float M = wave_max(m);
   const float S = wave_sum(s * __builtin_amdgcn_exp2f((m - M) * kL2E));
   const float lse = M + logf(S);
   __syncthreads();
-  float hv = -INFINITY;
-  int hi = kInvalid, hp = 0;
-  if (lane < P) {
-    hv = sv[lane * K];
-    hi = si[lane * K];
-  }
+  // Lane p < P walks chunk p's sorted list; hp is its read position. Every
+  // step is straight-line (selects, a clamped LDS read in every lane).
+  const bool live = lane < P;
+  const int lb = min(lane, P - 1) * K;
+  float hv = live ? sv[lb] : -INFINITY;
+  int hi = live ? si[lb] : kInvalid;
+  int hp = 0;
   float rv = -INFINITY;
   int ri = kInvalid;
   for (int k = 0; k < K; ++k) {
@@ -422,21 +439,16 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
     float bv = hv;
     int bi = hi;
     wave_argmax(bv, bi);
-    const int bl = __ffsll((long long)__ballot(hv == bv && hi == bi)) - 1;
-    if (lane == k) {
-      rv = bv;
-      ri = bi;
-    }
-    if (lane == bl && lane < P) {
-      ++hp;
-      if (hp < K) {
-        hv = sv[lane * K + hp];
-        hi = si[lane * K + hp];
-      } else {
-        hv = -INFINITY;
-        hi = kInvalid;
-      }
-    }
+    const int bl = __ffsll((long long)__ballot((hv == bv) & (hi == bi))) - 1;
+    rv = lane == k ? bv : rv;
+    ri = lane == k ? bi : ri;
+    const bool adv = (lane == bl) & live;
+    hp += adv ? 1 : 0;
+    const float nv = sv[lb + min(hp, K - 1)];
+    const int ni = si[lb + min(hp, K - 1)];
+    const bool more = hp < K;
+    hv = adv ? (more ? nv : -INFINITY) : hv;
+    hi = adv ? (more ? ni : kInvalid) : hi;
   }
   if (lane < K) {
     topk_idx[(int64_t)row * K + lane] = ri;

@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 // once per (block, head). V is fetched key-fastest so that each transposed
 // 2-byte LDS store instruction covers 64 consecutive keys of one d row.
 template <int TMAX, int DH>
-__global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
                                                             int K, int H,
                                                             const float* __restrict__ dist,
                                                             const float* __restrict__ same,
@@ -283,11 +283,22 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
       for (int kt = 0; kt < KT; ++kt) kf[kt] = *(const u32x4_t*)(&Ks[kat(kt * 16 + c, ks * 4 + g)]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) acc[kt] = mfma16(kf[kt], qf[ks], acc[kt]);
+      __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);
       __builtin_amdgcn_sched_barrier(0);   // keep each k-step's reads with it
     }
-    // masking by select: the bias-table reads use a clamped slot and are
-    // unconditional (a read under a per-element branch is waited for inside it)
+    // Masking by select: the bias-table reads use a clamped slot, are
+    // unconditional (a read under a per-element branch is waited for inside
+    // it) and are issued together in a region of their own.
     float s[KT][4];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot_k = (int)(((unsigned)min(kt * 16 + 4 * g + i, T - 1) * kmul) >> 16);
+        s[kt][i] = bias_tab[slot_k - slot_q + 63];
+      }
+    __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
       for (int i = 0; i < 4; ++i) {
         const int key = kt * 16 + 4 * g + i;
         const int slot_k = (int)(((unsigned)min(key, T - 1) * kmul) >> 16);
-        float v = acc[kt][i] * scale + bias_tab[slot_k - slot_q + 63];
+        float v = acc[kt][i] * scale + s[kt][i];
         v = slot_k == slot_q ? v + same_h : v;
         v = key < T ? v : -INFINITY;
         s[kt][i] = v;
@@ -328,14 +339,20 @@ __global__ __launch_bounds__(512) void attention_res_kernel(const uint16_t* __re
       pb[1] = pack_bf16x2(s[2 * ch][2], s[2 * ch][3]);
       pb[2] = pack_bf16x2(s[2 * ch + 1][0], s[2 * ch + 1][1]);
       pb[3] = pack_bf16x2(s[2 * ch + 1][2], s[2 * ch + 1][3]);
+      // all of the chunk's V^T fragment reads are issued before its MFMAs
+      u32x4_t va[DT];
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         const uint16_t* vrow = &Vt[(d * 16 + c) * VS + ch * 32];
         const u32x2_t lo = *(const u32x2_t*)(vrow + 4 * g);
         const u32x2_t hi = *(const u32x2_t*)(vrow + 16 + 4 * g);
-        const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[d] = mfma16(va, pb, oacc[d]);
+        va[d] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
       }
+#pragma unroll
+      for (int d = 0; d < DT; ++d) oacc[d] = mfma16(va[d], pb, oacc[d]);
+      // schedule: the chunk's LDS reads first, then its MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);
       __builtin_amdgcn_sched_barrier(0);   // bound the V reads in flight
     }
     if (q_ok) {

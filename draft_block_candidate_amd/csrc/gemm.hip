@@ -1,25 +1,28 @@
 // Linear layers of the candidate encoder on CDNA4 MFMA (bf16 in, fp32 acc).
 //
 // Y[M, N] = A[M, Kd] . W[N, Kd]^T + bias, both operands K-contiguous, so every
-// MFMA operand fragment is one 16-byte LDS read. Four waves per workgroup in a
-// 2 x 2 arrangement; each wave owns a (BM/2) x (BN/2) patch of 16 x 16
-// v_mfma_f32_16x16x32_bf16 tiles. Epilogues fuse the bias, the bf16 rounding,
-// SiLU and the fp32 residual add of the pre-norm transformer.
+// MFMA operand fragment is one 16-byte LDS read. Epilogues fuse the bias, the
+// bf16 rounding, SiLU and the fp32 residual add of the pre-norm transformer.
 //
-// Three schedules:
-//  * many rows and at least 256 tiles of 256 x 256: the DMA-pipelined kernel
-//    below (32 x 32 x 16 MFMA, 128 x 128 per wave, four LDS stages filled by
-//    direct global-to-LDS loads, LDS-staged coalesced epilogue);
-//  * other many-row shapes (M >= 2048): BM x BN = 128 x 128 tiles over the
-//    whole K, double-buffered in LDS with one barrier per 64-wide k-step;
-//  * few rows (one or a few draft blocks, M = B*K*N of 64..2047): the GEMM is
-//    weight-streaming and latency bound, so K is split S ways. Each workgroup
-//    stages its whole A and W K-slice (64..256 wide) in LDS with every load in
-//    flight at once, multiplies, and writes an fp32 partial tile. A second
-//    kernel sums the S partials in the fixed order s = 0..S-1
-//    (bit-reproducible) and applies the epilogue; it works on whole rows, so
-//    the RMSNorm that follows a residual add and the unit normalisation of the
-//    out/in heads fuse into it.
+// Schedules:
+//  * many rows (M >= 2048): the DMA-pipelined kernel (32 x 32 x 16 MFMA, four
+//    LDS stages filled by direct global-to-LDS loads, LDS-staged coalesced
+//    epilogue) with the largest of 256 x 256, 256 x 128 and 128 x 128 tiles
+//    that still gives every CU a tile; eight waves (two per SIMD) for the
+//    two large tiles, four for 128 x 128;
+//  * many rows that the DMA kernel cannot take (K not a multiple of 32,
+//    misaligned operands): 128 x 128 tiles over the whole K, double-buffered
+//    in LDS, four waves in a 2 x 2 arrangement of 16 x 16 MFMA tiles;
+//  * few rows (M <= 128) and at least 128 tiles of 16 columns: one DMA-
+//    pipelined pass over K per 16-column tile with the epilogue fused;
+//  * other few-row shapes (one or a few draft blocks, M = B*K*N of 64..2047):
+//    the GEMM is weight-streaming and latency bound, so K is split S ways.
+//    Each workgroup stages its whole A and W K-slice (64..256 wide) in LDS
+//    with every load in flight at once, multiplies, and writes an fp32
+//    partial tile. A second kernel sums the S partials in the fixed order
+//    s = 0..S-1 (bit-reproducible) and applies the epilogue; it works on
+//    whole rows, so the RMSNorm that follows a residual add and the unit
+//    normalisation of the out/in heads fuse into it.
 #include <algorithm>
 
 #include "common.hpp"
@@ -148,9 +151,10 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Many-row GEMM, 256 x 256 tiles on 32 x 32 x 16 MFMA. Four waves in a 2 x 2
-// grid each hold a 128 x 128 fp32 accumulator block (in AGPRs), so every
-// 16-byte fragment read from LDS feeds four MFMAs. K advances 32 per stage
+// Many-row GEMM on 32 x 32 x 16 MFMA, BM x BN tiles. NW waves in a
+// 2 x (NW / 2) grid each hold a (BM / 2) x (2 BN / NW) fp32 accumulator block
+// (with four waves and 256 x 256 tiles, 128 x 128: every 16-byte fragment
+// read from LDS feeds four MFMAs). K advances 32 per stage
 // through four LDS stages that global_load_lds fills directly (no register
 // staging), three stages ahead of the one being multiplied; each wave waits
 // only for its own stage loads (vmcnt) and a bare s_barrier then makes the
@@ -466,79 +470,103 @@ __global__ __launch_bounds__(256) void gemm_part_kernel(const uint16_t* __restri
   }
 }
 
-// Few-row linear (M <= 128): one workgroup of eight waves per 16 output
+// Few-row linear (M <= 128): one workgroup of four waves per 16 output
 // columns over the whole of K, so there are no split-K partials and the
-// epilogue is fused. Wave w owns rows 16 w .. 16 w + 15 and loads its A rows
-// straight into MFMA fragments (an A element is used once per workgroup, so
-// staging it would buy nothing); the 16 W rows, shared by the eight waves, go
-// through LDS per 1024-wide K chunk with the 16-byte chunk index XOR-swizzled
-// by the row, so a fragment read touches every bank once. Every load is
-// unconditional (indices clamped; k-steps past K get a zero A fragment, rows
-// and columns past the matrix are computed and not stored), so one K chunk
-// costs one memory round trip.
+// epilogue is fused. Every workgroup streams all of A, so the kernel is bound
+// by how fast A reaches each CU: A and the 16 W rows go through LDS in
+// 128-wide K stages by global_load_lds, three stages ahead of the one being
+// multiplied; each DMA instruction moves four whole 256-byte row segments
+// (full cache lines), with the 16-byte chunk index XOR-swizzled by the row so
+// that fragment reads touch every bank once. Wave w multiplies rows
+// 32 w .. 32 w + 31 (two 16-row MFMA tiles) against the 16 columns. Rows and
+// columns past the matrix are clamped on load and never stored.
 template <int EPI>
-__global__ __launch_bounds__(512) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W, int M,
                                                           int N, int Kd,
                                                           const float* __restrict__ bias,
                                                           const float* resid, void* out) {
-  constexpr int KC = 1024, CPR = KC / 8, KSTEPS = KC / 32;
-  constexpr int WCH = 16 * CPR / 512;   // W chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[16 * KC];
-  auto wat = [](int row, int ch) { return row * KC + ((ch ^ (row & 15)) << 3); };
+  constexpr int BM = 128, BN = 16, BK = 128, NS = 4;
+  constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
+  constexpr int NI = STAGE / 512;              // 1 KiB DMA instructions per stage (36)
+  constexpr int PER = NI / 4;                  // per wave (9)
+  static_assert(NI % 4 == 0, "stage split");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t arow = min(wave * 16 + c, M - 1);
-  const uint16_t* ap = A + arow * Kd + 8 * g;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < Kd; k0 += KC) {
-    const int kc = min(KC, Kd - k0);   // a multiple of 32
-    u32x4_t wr[WCH];
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+
+  // Instruction j of a stage fills elements [512 j, 512 j + 512): rows
+  // 4 j .. 4 j + 3 of the stage (A rows first, then the W rows); lane i
+  // fills row 4 j + i / 16, slot i % 16, which holds chunk (i % 16) ^ (row & 15).
+  const uint16_t* src[PER];
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int ch = tid + 512 * i, row = ch / CPR, cc = min(ch % CPR, kc / 8 - 1);
-      const int64_t wrow = min(n0 + row, (int64_t)N - 1);
-      wr[i] = *(const u32x4_t*)(W + wrow * Kd + k0 + cc * 8);
-    }
-    u32x4_t af[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) af[ks] = *(const u32x4_t*)(ap + k0 + min(ks * 32, kc - 32));
-    if (k0 > 0) __syncthreads();   // every wave is done with the previous chunk
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int ch = tid + 512 * i;
-      *(u32x4_t*)(&Ws[wat(ch / CPR, ch % CPR)]) = wr[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4_t a = ks * 32 < kc ? af[ks] : u32x4_t{0u, 0u, 0u, 0u};
-      const u32x4_t wf = *(const u32x4_t*)(&Ws[wat(c, ks * 4 + g)]);
-      acc = mfma16(a, wf, acc);
-    }
+  for (int u = 0; u < PER; ++u) {
+    const int j = wave * PER + u, row = 4 * j + lane / 16;
+    const int chunk = (lane % 16) ^ (row & 15);
+    src[u] = row < BM ? A + (int64_t)min(row, M - 1) * Kd + chunk * 8
+                      : W + min(n0 + (row - BM), (int64_t)N - 1) * Kd + chunk * 8;
   }
-  // acc[i]: row 16 w + 4 g + i, column n0 + c
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    uint16_t* st = smem + (kt % NS) * STAGE;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      __builtin_amdgcn_global_load_lds((const void*)(src[u] + kt * BK),
+                                       (__attribute__((address_space(3))) void*)(st + (wave * PER + u) * 512),
+                                       16, 0, 0);
+  };
+  auto at = [](int row, int chunk) { return row * BK + ((chunk ^ (row & 15)) << 3); };
+
+  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const int nk = Kd / BK;
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt are done once at most those of the
+    // stages issued after it are outstanding; the barrier makes them visible
+    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER));
+    else if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    // every wave is done with stage kt - 1, whose buffer takes stage kt + 3
+    if (kt + 3 < nk) issue(kt + 3);
+    const uint16_t* st = smem + (kt % NS) * STAGE;
+    u32x4_t fa[BK / 32][2], fw[BK / 32];
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[ks][i] = *(const u32x4_t*)(&st[at(wave * 32 + i * 16 + c, ks * 4 + g)]);
+      fw[ks] = *(const u32x4_t*)(&st[at(BM + c, ks * 4 + g)]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] = mfma16(fa[ks][i], fw[ks], acc[i]);
+  }
+  // acc[i][q]: row 32 w + 16 i + 4 g + q, column n0 + c
   const int64_t n = n0 + c, nc = min(n, (int64_t)N - 1);
   const float bv = bias ? bias[nc] : 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = wave * 16 + 4 * g + i;
-    const bool ok = m < M && n < N;
-    const float y = acc[i] + bv;
-    const int64_t o = m * N + n;
-    if constexpr (EPI == EPI_F32) {
-      if (ok) ((float*)out)[o] = y;
-    } else if constexpr (EPI == EPI_BF16) {
-      if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(y);
-    } else if constexpr (EPI == EPI_SILU_BF16) {
-      if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(silu(y));
-    } else {
-      const float r = resid[min(m, (int64_t)M - 1) * N + nc];
-      if (ok) ((float*)out)[o] = r + y;
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t m = wave * 32 + i * 16 + 4 * g + q;
+      const bool ok = m < M && n < N;
+      const float y = acc[i][q] + bv;
+      const int64_t o = m * N + n;
+      if constexpr (EPI == EPI_F32) {
+        if (ok) ((float*)out)[o] = y;
+      } else if constexpr (EPI == EPI_BF16) {
+        if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(y);
+      } else if constexpr (EPI == EPI_SILU_BF16) {
+        if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(silu(y));
+      } else {
+        const float r = resid[min(m, (int64_t)M - 1) * N + nc];
+        if (ok) ((float*)out)[o] = r + y;
+      }
     }
-  }
 }
 
 // Partial sums are added in the fixed order s = 0..S-1; S is a compile-time
@@ -793,19 +821,19 @@ hipError_t launch_skinny(const uint16_t* A, int M, int Kd, const uint16_t* W, in
   const dim3 grid((unsigned)((N + 15) / 16));
   switch (epi) {
     case EPI_F32:
-      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_F32>), grid, dim3(512), 0, stream, A, W, M, N, Kd,
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_F32>), grid, dim3(256), 0, stream, A, W, M, N, Kd,
                          bias, resid, out);
       break;
     case EPI_BF16:
-      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_BF16>), grid, dim3(512), 0, stream, A, W, M, N, Kd,
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_BF16>), grid, dim3(256), 0, stream, A, W, M, N, Kd,
                          bias, resid, out);
       break;
     case EPI_SILU_BF16:
-      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_SILU_BF16>), grid, dim3(512), 0, stream, A, W, M,
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_SILU_BF16>), grid, dim3(256), 0, stream, A, W, M,
                          N, Kd, bias, resid, out);
       break;
     default:
-      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_RESID_F32>), grid, dim3(512), 0, stream, A, W, M,
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI_RESID_F32>), grid, dim3(256), 0, stream, A, W, M,
                          N, Kd, bias, resid, out);
       break;
   }
@@ -813,7 +841,7 @@ hipError_t launch_skinny(const uint16_t* A, int M, int Kd, const uint16_t* W, in
 }
 
 bool uses_skinny(int M, int Kd, int N) {
-  return M <= 128 && Kd % 32 == 0 && (N + 15) / 16 >= 128;
+  return M <= 128 && Kd % 128 == 0 && (N + 15) / 16 >= 128;
 }
 
 GemmPlan plan_linear(int M, int Kd, int N) {
@@ -851,12 +879,15 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
     if (M >= 2048 && Kd % 32 == 0 && N % 4 == 0 && al16(out) && (bias == nullptr || al16(bias)) &&
         (ep.resid == nullptr || al16(ep.resid))) {
       // the largest tile that still gives every CU work
+      // (eight waves, two per SIMD, for the large tiles: each wave then owns a
+      // 128 x 64 or 128 x 32 block, and one wave's barrier wait overlaps the
+      // other's MFMAs)
       if (tiles(256, 256) >= 256)
-        e = launch_dma<256, 256>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+        e = launch_dma<256, 256, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
       else if (tiles(256, 128) >= 256)
-        e = launch_dma<256, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+        e = launch_dma<256, 128, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
       else
-        e = launch_dma<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+        e = launch_dma<128, 128, 4>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     } else if (M >= 2048)
       e = launch_tile<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     else if (M > 64)

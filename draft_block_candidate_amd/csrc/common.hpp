@@ -97,6 +97,19 @@ __device__ __forceinline__ void argmax_step(float& v, int& i) {
   v = take ? ov : v;
   i = take ? oi : i;
 }
+// Argmax over lanes 0 .. n - 1 only (n = 16, 32 or 64); fewer DPP steps for
+// small n. Result in every lane.
+__device__ __forceinline__ void lanes_argmax(float& v, int& i, int n) {
+  argmax_step<kDppShr1, 0xf>(v, i);
+  argmax_step<kDppShr2, 0xf>(v, i);
+  argmax_step<kDppShr4, 0xf>(v, i);
+  argmax_step<kDppShr8, 0xf>(v, i);
+  if (n > 16) argmax_step<kDppBcast15, 0xa>(v, i);
+  if (n > 32) argmax_step<kDppBcast31, 0xc>(v, i);
+  const int last = n > 32 ? 63 : (n > 16 ? 31 : 15);
+  v = readlane_f(v, last);
+  i = readlane_i(i, last);
+}
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step<kDppShr1, 0xf>(v, i);
   argmax_step<kDppShr2, 0xf>(v, i);

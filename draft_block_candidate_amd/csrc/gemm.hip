@@ -622,52 +622,56 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-// Residual add fused with the RMSNorm that follows it: one wave per row,
+// Residual add fused with the RMSNorm that follows it: one 256-thread
+// workgroup per row (few rows here, so the row is spread over four waves),
 // x = resid + (y + bias) written back, then u = bf16(x * rstd * gamma).
+// Thread t holds the 4-column groups t, t + 256, ...; the sum of squares is
+// reduced per wave, then over the four waves in a fixed order.
 template <int S, int NV>
 __global__ __launch_bounds__(256) void splitk_resid_rmsnorm_kernel(
     const float* __restrict__ part, int M, int N, const float* __restrict__ bias,
     const float* resid, float* x_out, const float* __restrict__ gamma, float eps,
     uint16_t* __restrict__ u_out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m = blockIdx.x;
   const int64_t MN4 = (int64_t)M * N / 4;
   const int n4 = N / 4;
   const float4* part4 = (const float4*)part;
-  // Loads use clamped indices and are unconditional, so the NV column groups'
-  // partials, bias and residual are all in flight at once; only the stores
-  // and the sum are predicated.
-  float4 v[NV];
-  float ss = 0.f;
+  // Loads use clamped indices and are unconditional, so every column group's
+  // partials, bias, residual and gamma are in flight at once; only the
+  // stores and the sum are predicated.
+  float4 v[NV], gv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int gi = lane + 64 * i;
+    const int gi = tid + 256 * i;
     const int gc = min(gi, n4 - 1);
     const int64_t q = m * n4 + gc;
     const float4 y = splitk_sum4<S>(part4, MN4, q);
     const float4 b = bias ? ((const float4*)bias)[gc] : make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 r = ((const float4*)resid)[q];
+    gv[i] = ((const float4*)gamma)[gc];
     v[i] = make_float4(r.x + (y.x + b.x), r.y + (y.y + b.y), r.z + (y.z + b.z), r.w + (y.w + b.w));
     if (gi >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int gi = lane + 64 * i;
+    const int gi = tid + 256 * i;
     if (gi < n4) ((float4*)x_out)[m * n4 + gi] = v[i];
     ss = fmaf(v[i].x, v[i].x, ss);
     ss = fmaf(v[i].y, v[i].y, ss);
     ss = fmaf(v[i].z, v[i].z, ss);
     ss = fmaf(v[i].w, v[i].w, ss);
   }
-  float4 gv[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) gv[i] = ((const float4*)gamma)[min(lane + 64 * i, n4 - 1)];
   ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  ss = ((red[0] + red[1]) + red[2]) + red[3];
   const float rstd = 1.0f / __fsqrt_rn(ss / (float)N + eps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int gi = lane + 64 * i;
+    const int gi = tid + 256 * i;
     if (gi < n4)
       ((uint2*)(u_out + m * N))[gi] =
           make_uint2(pack_bf16x2(v[i].x * rstd * gv[i].x, v[i].y * rstd * gv[i].y),
@@ -768,15 +772,15 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
   const unsigned row_blocks = (unsigned)((M + 3) / 4);
   if (ep.kind == EPI_RESID_F32 && ep.norm_out) {
     if (N <= 1024)
-      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 4>), dim3(row_blocks), dim3(256), 0,
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 1>), dim3((unsigned)M), dim3(256), 0,
                          stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
                          ep.norm_out);
     else if (N <= 2048)
-      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 8>), dim3(row_blocks), dim3(256), 0,
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 2>), dim3((unsigned)M), dim3(256), 0,
                          stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
                          ep.norm_out);
     else
-      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 16>), dim3(row_blocks), dim3(256), 0,
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 4>), dim3((unsigned)M), dim3(256), 0,
                          stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
                          ep.norm_out);
     return hipGetLastError();

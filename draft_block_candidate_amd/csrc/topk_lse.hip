@@ -438,7 +438,7 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
     // lowest lane holding that key (keys are unique except exhausted lists)
     float bv = hv;
     int bi = hi;
-    wave_argmax(bv, bi);
+    lanes_argmax(bv, bi, P <= 16 ? 16 : (P <= 32 ? 32 : 64));   // lanes >= P hold -inf
     const int bl = __ffsll((long long)__ballot((hv == bv) & (hi == bi))) - 1;
     rv = lane == k ? bv : rv;
     ri = lane == k ? bi : ri;

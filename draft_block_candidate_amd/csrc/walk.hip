@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
     }
     float bz = z;
     int bl = lane;
-    wave_argmax(bz, bl);
+    lanes_argmax(bz, bl, K <= 16 ? 16 : (K <= 32 ? 32 : 64));   // lanes >= K hold -inf
     if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
     const float second = wave_max(lane == bl ? -INFINITY : z);
     cprev = bl;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
     }
     float bz = z;
     int bl = lane;
-    wave_argmax(bz, bl);
+    lanes_argmax(bz, bl, K <= 16 ? 16 : (K <= 32 ? 32 : 64));   // lanes >= K hold -inf
     if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
     // the runner-up is only needed for the optional gap output
     const float second = gap ? wave_max(lane == bl ? -INFINITY : z) : 0.f;

@@ -97,6 +97,17 @@ __device__ __forceinline__ void argmax_step(float& v, int& i) {
   v = take ? ov : v;
   i = take ? oi : i;
 }
+// Maximum over lanes 0 .. n - 1 only (n = 16, 32 or 64); result in every lane.
+__device__ __forceinline__ float lanes_max(float v, int n) {
+  v = fmaxf(v, dpp_f<kDppShr1, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppShr2, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppShr4, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppShr8, 0xf>(-INFINITY, v));
+  if (n > 16) v = fmaxf(v, dpp_f<kDppBcast15, 0xa>(-INFINITY, v));
+  if (n > 32) v = fmaxf(v, dpp_f<kDppBcast31, 0xc>(-INFINITY, v));
+  return readlane_f(v, n > 32 ? 63 : (n > 16 ? 31 : 15));
+}
+
 // Argmax over lanes 0 .. n - 1 only (n = 16, 32 or 64); fewer DPP steps for
 // small n. Result in every lane.
 __device__ __forceinline__ void lanes_argmax(float& v, int& i, int n) {

@@ -74,11 +74,11 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
   const int64_t r0 = n * B;
-  if (lane == 0) {
-    out_tokens[r0] = topk_idx[r0 * K];
-    if (score) score[r0] = topk_logp[r0 * K];
-    if (gap) gap[r0] = 0.f;
-  }
+  // as in the fused kernel: winner by max then lowest lane of the ballot;
+  // step s's results are kept in lane s and written after the loop
+  const int width = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
+  int choice = 0;
+  float my_score = topk_logp[r0 * K], my_gap = 0.f;
   int cprev = 0;
   for (int s = 1; s < B; ++s) {
     float z = -INFINITY;
@@ -87,17 +87,19 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
       const float term = __fmul_rn(alpha, cs);
       z = use_logp ? __fadd_rn(topk_logp[(r0 + s) * K + lane], term) : term;
     }
-    float bz = z;
-    int bl = lane;
-    lanes_argmax(bz, bl, K <= 16 ? 16 : (K <= 32 ? 32 : 64));   // lanes >= K hold -inf
-    if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
-    const float second = wave_max(lane == bl ? -INFINITY : z);
+    const float bz = lanes_max(z, width);
+    int bl = __ffsll((long long)__ballot(z == bz)) - 1;
+    if (bl < 0 || bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
+    const float second = gap ? wave_max(lane == bl ? -INFINITY : z) : 0.f;
+    choice = lane == s ? bl : choice;
+    my_score = lane == s ? bz : my_score;
+    my_gap = lane == s ? (K > 1 ? __fsub_rn(bz, second) : 0.f) : my_gap;
     cprev = bl;
-    if (lane == 0) {
-      out_tokens[r0 + s] = topk_idx[(r0 + s) * K + bl];
-      if (score) score[r0 + s] = bz;
-      if (gap) gap[r0 + s] = K > 1 ? __fsub_rn(bz, second) : 0.f;
-    }
+  }
+  if (lane < B) {
+    out_tokens[r0 + lane] = topk_idx[(r0 + lane) * K + choice];
+    if (score) score[r0 + lane] = my_score;
+    if (gap) gap[r0 + lane] = my_gap;
   }
 }
 
@@ -134,12 +136,15 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
   }
   __syncthreads();
   if (wave != 0) return;
+  // The walk. Lane j scores candidate j; the winner is the largest score and,
+  // among equal ones, the lowest lane (a max, then the lowest lane of the
+  // ballot of lanes holding it). Step s's choice, score and gap are kept in
+  // lane s, so the sequential part carries only the LDS read of the previous
+  // choice's cosine row; tokens and outputs are written after the loop.
   const int64_t r0 = n * B;
-  if (lane == 0) {
-    out_tokens[r0] = s_idx[0];
-    if (score) score[r0] = s_logp[0];
-    if (gap) gap[r0] = 0.f;
-  }
+  const int width = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
+  int choice = 0;
+  float my_score = s_logp[0], my_gap = 0.f;
   int cprev = 0;
   for (int s = 1; s < B; ++s) {
     float z = -INFINITY;
@@ -147,18 +152,20 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
       const float term = __fmul_rn(alpha, s_cos[(s - 1) * KK + cprev * K + lane]);
       z = use_logp ? __fadd_rn(s_logp[s * K + lane], term) : term;
     }
-    float bz = z;
-    int bl = lane;
-    lanes_argmax(bz, bl, K <= 16 ? 16 : (K <= 32 ? 32 : 64));   // lanes >= K hold -inf
-    if (bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
+    const float bz = lanes_max(z, width);
+    int bl = __ffsll((long long)__ballot(z == bz)) - 1;
+    if (bl < 0 || bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
     // the runner-up is only needed for the optional gap output
     const float second = gap ? wave_max(lane == bl ? -INFINITY : z) : 0.f;
+    choice = lane == s ? bl : choice;
+    my_score = lane == s ? bz : my_score;
+    my_gap = lane == s ? (K > 1 ? __fsub_rn(bz, second) : 0.f) : my_gap;
     cprev = bl;
-    if (lane == 0) {
-      out_tokens[r0 + s] = s_idx[s * K + bl];
-      if (score) score[r0 + s] = bz;
-      if (gap) gap[r0 + s] = K > 1 ? __fsub_rn(bz, second) : 0.f;
-    }
+  }
+  if (lane < B) {
+    out_tokens[r0 + lane] = s_idx[lane * K + choice];
+    if (score) score[r0 + lane] = my_score;
+    if (gap) gap[r0 + lane] = my_gap;
   }
 }
 

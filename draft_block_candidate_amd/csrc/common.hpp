@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 
 #define LL_WAVE 64
@@ -76,14 +77,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return readlane_f(v, 63);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<kDppShr1, 0xf>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppShr2, 0xf>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppShr4, 0xf>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppShr8, 0xf>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppBcast15, 0xa>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppBcast31, 0xc>(-INFINITY, v));
-  return readlane_f(v, 63);
+// Order-preserving map of a float to a signed int (and back): for non-NaN
+// values, a < b exactly when key(a) < key(b) (with -0 below +0). Maxima are
+// taken on the keys so that each DPP step is one integer max, which the
+// compiler folds into a v_max_i32 with a DPP operand.
+__device__ __forceinline__ int fkey(float x) {
+  const int i = __float_as_int(x);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float fkey_inv(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
+
+__device__ __forceinline__ float wave_max(float x) {
+  int v = fkey(x);
+  v = max(v, dpp_i<kDppShr1, 0xf>(INT_MIN, v));
+  v = max(v, dpp_i<kDppShr2, 0xf>(INT_MIN, v));
+  v = max(v, dpp_i<kDppShr4, 0xf>(INT_MIN, v));
+  v = max(v, dpp_i<kDppShr8, 0xf>(INT_MIN, v));
+  v = max(v, dpp_i<kDppBcast15, 0xa>(INT_MIN, v));
+  v = max(v, dpp_i<kDppBcast31, 0xc>(INT_MIN, v));
+  return fkey_inv(readlane_i(v, 63));
 }
 
 // Largest (v, i) by v descending, then i ascending; result in every lane.
@@ -98,14 +110,15 @@ __device__ __forceinline__ void argmax_step(float& v, int& i) {
   i = take ? oi : i;
 }
 // Maximum over lanes 0 .. n - 1 only (n = 16, 32 or 64); result in every lane.
-__device__ __forceinline__ float lanes_max(float v, int n) {
-  v = fmaxf(v, dpp_f<kDppShr1, 0xf>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppShr2, 0xf>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppShr4, 0xf>(-INFINITY, v));
-  v = fmaxf(v, dpp_f<kDppShr8, 0xf>(-INFINITY, v));
-  if (n > 16) v = fmaxf(v, dpp_f<kDppBcast15, 0xa>(-INFINITY, v));
-  if (n > 32) v = fmaxf(v, dpp_f<kDppBcast31, 0xc>(-INFINITY, v));
-  return readlane_f(v, n > 32 ? 63 : (n > 16 ? 31 : 15));
+__device__ __forceinline__ float lanes_max(float x, int n) {
+  int v = fkey(x);
+  v = max(v, dpp_i<kDppShr1, 0xf>(INT_MIN, v));
+  v = max(v, dpp_i<kDppShr2, 0xf>(INT_MIN, v));
+  v = max(v, dpp_i<kDppShr4, 0xf>(INT_MIN, v));
+  v = max(v, dpp_i<kDppShr8, 0xf>(INT_MIN, v));
+  if (n > 16) v = max(v, dpp_i<kDppBcast15, 0xa>(INT_MIN, v));
+  if (n > 32) v = max(v, dpp_i<kDppBcast31, 0xc>(INT_MIN, v));
+  return fkey_inv(readlane_i(v, n > 32 ? 63 : (n > 16 ? 31 : 15)));
 }
 
 // Argmax over lanes 0 .. n - 1 only (n = 16, 32 or 64); fewer DPP steps for

@@ -297,8 +297,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
   const int64_t nc = min(n, (int64_t)N - 4);
   float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
   if (bias) bv = *(const float4*)(bias + nc);
+  // Residual epilogue: the residual rows of slice i + 1 are loaded while
+  // slice i is staged and stored (double-buffered), so the reads overlap.
+  constexpr int U = 32 * CPRW / 64;
+  float4 rbuf[2][EPI == EPI_RESID_F32 ? U : 1];
+  auto load_resid = [&](int i, float4 (&r)[EPI == EPI_RESID_F32 ? U : 1]) __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_RESID_F32) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t m = m0 + wm * WM + i * 32 + (lane + 64 * u) / CPRW;
+        r[u] = *(const float4*)(resid + min(m, (int64_t)M - 1) * N + nc);
+      }
+    }
+  };
+  load_resid(0, rbuf[0]);
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
+    if (i + 1 < MT) load_resid(i + 1, rbuf[(i + 1) & 1]);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -306,7 +321,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
         stg[(8 * (e >> 2) + 4 * hi + (e & 3)) * ES + j * 32 + l32] = acc[i][j][e];
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < 32 * CPRW / 64; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int rr = (lane + 64 * u) / CPRW;
       const int64_t m = m0 + wm * WM + i * 32 + rr;
       const bool ok = col_ok && m < M;
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
           *(uint2*)((uint16_t*)out + o) =
               make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
       } else {
-        const float4 rv = *(const float4*)(resid + min(m, (int64_t)M - 1) * N + nc);
+        const float4 rv = rbuf[i & 1][u];
         if (ok) *(float4*)((float*)out + o) = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
       }
     }

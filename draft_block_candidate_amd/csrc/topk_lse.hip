@@ -213,13 +213,25 @@ __device__ __forceinline__ void topk_pass(State& st, const u32x4_t (&w0)[NV], co
   u32x4_t w[NV];
   opaque_copy<NV>(w0, w);
   int excl = -1;
-  if (!st.seeded) {
+  const bool seeding = !st.seeded;
+  if (seeding) {
     excl = seed_list<NV, EPV, LS>(st, w, base, K, lane);
     update_gate(st);
   }
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
-    if (!__any(pm[u] >= st.p_th)) continue;
+    if (seeding) {
+      // right after seeding every slot holding a seed passes the exp gate, so
+      // count the elements that can still enter instead
+      const float th = fmaxf(st.th_v, -3.402823466e38f);
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e)
+        c += (elem<EPV>(w[u], e) >= th) & (base + (u * 64 + lane) * LS + e != excl);
+      if (!__any(c > 0)) continue;
+    } else if (!__any(pm[u] >= st.p_th)) {
+      continue;
+    }
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
       const float x = elem<EPV>(w[u], e);
@@ -433,13 +445,14 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
   int hp = 0;
   float rv = -INFINITY;
   int ri = kInvalid;
+  const int width = P <= 16 ? 16 : (P <= 32 ? 32 : 64);   // lanes >= P hold -inf
   for (int k = 0; k < K; ++k) {
-    // wave argmax of the heads by (value desc, index asc); the winner is the
-    // lowest lane holding that key (keys are unique except exhausted lists)
-    float bv = hv;
-    int bi = hi;
-    lanes_argmax(bv, bi, P <= 16 ? 16 : (P <= 32 ? 32 : 64));   // lanes >= P hold -inf
-    const int bl = __ffsll((long long)__ballot((hv == bv) & (hi == bi))) - 1;
+    // Winner by (value desc, id asc): chunk p covers a contiguous id range
+    // below chunk p + 1's, so among equal values the lowest lane holds the
+    // lowest id, and a max plus the lowest lane of the ballot decides it.
+    const float bv = lanes_max(hv, width);
+    const int bl = __ffsll((long long)__ballot(hv == bv)) - 1;
+    const int bi = readlane_i(hi, bl);
     rv = lane == k ? bv : rv;
     ri = lane == k ? bi : ri;
     const bool adv = (lane == bl) & live;

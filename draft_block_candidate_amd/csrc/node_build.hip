@@ -10,49 +10,96 @@
 namespace ll {
 namespace {
 
-// One block per token; each thread owns 4 consecutive columns.
+// One block per TPB tokens; thread t owns the 4-column groups t, t + 256, ...
+// (CG of them). The first-layer weights and biases of a thread's columns are
+// loaded once per block and kept in registers; the tokens' embedding, slot
+// and rank rows are all loaded before any is used.
+template <int CG, int TPB>
 __global__ __launch_bounds__(256) void node_build_kernel(
-    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int B, int K, int H, int V,
-    const uint16_t* __restrict__ E, const uint16_t* __restrict__ S, const uint16_t* __restrict__ R,
-    const uint16_t* __restrict__ w1, const float* __restrict__ b1, uint16_t* __restrict__ hid,
-    float* __restrict__ xbase) {
-  const int64_t t = blockIdx.x;
-  const int64_t row = t / K;       // (block, slot)
-  const int j = (int)(t - row * K);
-  const int s = (int)(row % B);
-  int64_t tok = topk_idx[t];
-  if (tok < 0 || tok >= V) tok = 0;  // ids come from the top-K stage; never read outside E
-  const float lp = topk_logp[t];
-  const float lp0 = topk_logp[row * K];
-  float f[5];
-  f[0] = lp;
-  f[1] = expf(lp);
-  f[2] = __fsub_rn(lp, lp0);
-  f[3] = K > 1 ? __fdiv_rn((float)j, (float)(K - 1)) : 0.f;
-  f[4] = j == 0 ? 1.f : 0.f;
-  const uint2* e4 = (const uint2*)(E + tok * H);
-  const uint2* s4 = (const uint2*)(S + (int64_t)s * H);
-  const uint2* r4 = (const uint2*)(R + (int64_t)j * H);
-  for (int c4 = threadIdx.x; c4 < H / 4; c4 += blockDim.x) {
-    const uint2 ev = e4[c4], sv = s4[c4], rv = r4[c4];
-    float xb[4], hz[4];
-    const uint32_t ew[2] = {ev.x, ev.y}, sw[2] = {sv.x, sv.y}, rw[2] = {rv.x, rv.y};
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int64_t M, int B,
+    int K, int H, int V, const uint16_t* __restrict__ E, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ R, const uint16_t* __restrict__ w1, const float* __restrict__ b1,
+    uint16_t* __restrict__ hid, float* __restrict__ xbase) {
+  const int tid = threadIdx.x;
+  const int h4 = H / 4;
+  // this thread's columns: w1 rows are 5 bf16 (10 bytes), so the 4 columns of
+  // a group are 40 contiguous bytes
+  float wv[CG][4][5], bv[CG][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t sh = (q & 1) ? 16 : 0;
-      const float a = bf16_to_f32((ew[q >> 1] >> sh) & 0xFFFF);
-      const float b = bf16_to_f32((sw[q >> 1] >> sh) & 0xFFFF);
-      const float c = bf16_to_f32((rw[q >> 1] >> sh) & 0xFFFF);
-      xb[q] = __fadd_rn(__fadd_rn(a, b), c);
-      const int col = c4 * 4 + q;
-      const uint16_t* wr = w1 + (int64_t)col * 5;
-      float z = 0.f;
+  for (int g = 0; g < CG; ++g) {
+    const int c4 = min(tid + 256 * g, h4 - 1);
+    const uint2* wp = (const uint2*)(w1 + (int64_t)c4 * 20);
+    uint32_t wr[10];
 #pragma unroll
-      for (int i = 0; i < 5; ++i) z = fmaf(bf16_to_f32(wr[i]), f[i], z);
-      hz[q] = silu(z + b1[col]);
+    for (int i = 0; i < 5; ++i) {
+      const uint2 u = wp[i];
+      wr[2 * i] = u.x;
+      wr[2 * i + 1] = u.y;
     }
-    ((float4*)(xbase + t * H))[c4] = make_float4(xb[0], xb[1], xb[2], xb[3]);
-    ((uint2*)(hid + t * H))[c4] = make_uint2(pack_bf16x2(hz[0], hz[1]), pack_bf16x2(hz[2], hz[3]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int h = q * 5 + i;   // bf16 index within the 20
+        wv[g][q][i] = bf16_to_f32((wr[h >> 1] >> ((h & 1) * 16)) & 0xFFFF);
+      }
+    const float4 b = ((const float4*)b1)[c4];
+    bv[g][0] = b.x; bv[g][1] = b.y; bv[g][2] = b.z; bv[g][3] = b.w;
+  }
+  // the block's tokens (clamped; the ones past M are computed, not stored)
+  int64_t tk[TPB];
+  uint2 ev[TPB][CG], sv[TPB][CG], rv[TPB][CG];
+  float f[TPB][5];
+#pragma unroll
+  for (int u = 0; u < TPB; ++u) {
+    const int64_t t = min((int64_t)blockIdx.x * TPB + u, M - 1);
+    tk[u] = t;
+    const int64_t row = t / K;       // (block, slot)
+    const int j = (int)(t - row * K);
+    const int s = (int)(row % B);
+    int64_t tok = topk_idx[t];
+    if (tok < 0 || tok >= V) tok = 0;  // ids come from the top-K stage; never read outside E
+    const float lp = topk_logp[t];
+    const float lp0 = topk_logp[row * K];
+    f[u][0] = lp;
+    f[u][1] = expf(lp);
+    f[u][2] = __fsub_rn(lp, lp0);
+    f[u][3] = K > 1 ? __fdiv_rn((float)j, (float)(K - 1)) : 0.f;
+    f[u][4] = j == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+      const int c4 = min(tid + 256 * g, h4 - 1);
+      ev[u][g] = ((const uint2*)(E + tok * H))[c4];
+      sv[u][g] = ((const uint2*)(S + (int64_t)s * H))[c4];
+      rv[u][g] = ((const uint2*)(R + (int64_t)j * H))[c4];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPB; ++u) {
+    const bool tok_ok = (int64_t)blockIdx.x * TPB + u < M;
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+      const int c4 = tid + 256 * g;
+      const uint32_t ew[2] = {ev[u][g].x, ev[u][g].y}, sw[2] = {sv[u][g].x, sv[u][g].y},
+                     rw[2] = {rv[u][g].x, rv[u][g].y};
+      float xb[4], hz[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sh = (q & 1) ? 16 : 0;
+        const float a = bf16_to_f32((ew[q >> 1] >> sh) & 0xFFFF);
+        const float b = bf16_to_f32((sw[q >> 1] >> sh) & 0xFFFF);
+        const float c = bf16_to_f32((rw[q >> 1] >> sh) & 0xFFFF);
+        xb[q] = __fadd_rn(__fadd_rn(a, b), c);
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) z = fmaf(wv[g][q][i], f[u][i], z);
+        hz[q] = silu(z + bv[g][q]);
+      }
+      if (tok_ok && c4 < h4) {
+        ((float4*)(xbase + tk[u] * H))[c4] = make_float4(xb[0], xb[1], xb[2], xb[3]);
+        ((uint2*)(hid + tk[u] * H))[c4] = make_uint2(pack_bf16x2(hz[0], hz[1]), pack_bf16x2(hz[2], hz[3]));
+      }
+    }
   }
 }
 
@@ -63,8 +110,31 @@ hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, in
                              const uint16_t* conf_w1, const float* conf_b1, uint16_t* hid,
                              float* xbase, int V, hipStream_t stream) {
   const int64_t M = (int64_t)N * B * K;
-  hipLaunchKernelGGL(node_build_kernel, dim3((unsigned)M), dim3(256), 0, stream, topk_idx,
-                     topk_logp, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+  // few tokens: one per block (more blocks in flight); many: eight per block
+  // (four for the widest rows, to bound the registers)
+  if (M < 4096) {
+    const dim3 grid((unsigned)M);
+    if (H <= 1024)
+      hipLaunchKernelGGL((node_build_kernel<1, 1>), grid, dim3(256), 0, stream, topk_idx, topk_logp,
+                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+    else if (H <= 2048)
+      hipLaunchKernelGGL((node_build_kernel<2, 1>), grid, dim3(256), 0, stream, topk_idx, topk_logp,
+                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+    else
+      hipLaunchKernelGGL((node_build_kernel<4, 1>), grid, dim3(256), 0, stream, topk_idx, topk_logp,
+                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+  } else {
+    const dim3 grid8((unsigned)((M + 7) / 8)), grid4((unsigned)((M + 3) / 4));
+    if (H <= 1024)
+      hipLaunchKernelGGL((node_build_kernel<1, 8>), grid8, dim3(256), 0, stream, topk_idx, topk_logp,
+                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+    else if (H <= 2048)
+      hipLaunchKernelGGL((node_build_kernel<2, 8>), grid8, dim3(256), 0, stream, topk_idx, topk_logp,
+                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+    else
+      hipLaunchKernelGGL((node_build_kernel<4, 4>), grid4, dim3(256), 0, stream, topk_idx, topk_logp,
+                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+  }
   return hipGetLastError();
 }
 

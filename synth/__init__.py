@@ -61,8 +61,12 @@ WORKLOADS = {
     # Entropy sweep: 64 blocks per temperature tier, K = 32, wider encoder.
     "entropy_k32": Workload("entropy_k32", 64, 16, 151936, 32, 2048, 16, 8192, 256,
                             "bf16", "tempered", temperatures=(0.3, 1.0, 3.0)),
+    # Odd shapes for the test suite: an odd token count above 4096 (the
+    # many-token node-build path with a ragged last block), 15 slots, a width
+    # above 2048 and d_h = 128.
+    "odd_h2560": Workload("odd_h2560", 41, 15, 4096, 7, 2560, 20, 512, 128, "bf16", "spiked"),
 }
-WORKLOADS_ORDER = ["tiny", "c1_qwen3_8b", "c32", "c256_k16", "entropy_k32"]
+WORKLOADS_ORDER = ["tiny", "c1_qwen3_8b", "c32", "c256_k16", "entropy_k32", "odd_h2560"]
 
 
 def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:

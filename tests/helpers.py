@@ -40,15 +40,17 @@ def assert_within(g, o, tol=TOL, what=""):
                              f"gpu {[float(g[tuple(b)]) for b in bad]} oracle {[float(o[tuple(b)]) for b in bad]}")
 
 
-def assert_scores(g, o, what="", alpha=1.0):
-    """Cosines / step scores: COS_FRACTION within TOL, all within the bf16 bound."""
+def assert_scores(g, o, what="", alpha=1.0, fraction=COS_FRACTION):
+    """Cosines / step scores: a fraction (COS_FRACTION unless a case states its
+    own, derived from the float32 drift of its shape) within TOL, all within the
+    bf16 bound."""
     g = np.asarray(g, dtype=np.float64).ravel()
     o = np.asarray(o, dtype=np.float64).ravel()
     err = np.abs(g - o)
     hard = TOL * np.maximum(1.0, np.abs(o)) + abs(alpha) * COS_HARD
     assert np.all(err <= hard), f"{what}: max error {err.max()} beyond the bf16 bound"
     n_bad = int((~within(g, o)).sum())
-    allowed = max(1, int((1.0 - COS_FRACTION) * err.size))
+    allowed = max(1, int((1.0 - fraction) * err.size))
     assert n_bad <= allowed, f"{what}: {n_bad} of {err.size} outside {TOL} (allowed {allowed})"
     return {"n": int(err.size), "over_tol": n_bad, "max": float(err.max()),
             "p999": float(np.percentile(err, 99.9)) if err.size else 0.0}

@@ -117,6 +117,7 @@ def _rand_bf16(rng, shape, scale=1.0):
 
 
 @pytest.mark.parametrize("M,Kd,N", [(64, 64, 32), (100, 256, 96), (128, 1024, 3072), (300, 1024, 1024),
+                                    (100, 1024, 2100), (128, 2048, 2048),
                                     (2100, 512, 200), (4096, 1024, 4096), (128, 4096, 1024),
                                     (8192, 1024, 4096), (33000, 256, 1000), (6000, 192, 640),
                                     (64, 1024, 256), (50, 512, 1000), (128, 768, 4096), (7, 256, 48),

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from helpers import (assert_within, assert_scores, bf16_to_f64, to_device, oracle_weights,
-                     device_weights, compare_walk, oracle_step_scores, TOL)
+                     device_weights, compare_walk, oracle_step_scores, TOL, COS_FRACTION)
 import synth
 import oracle
 
@@ -37,7 +37,12 @@ CASES = [
     ("entropy_k32", 0, [0]),
     ("entropy_k32", 1, [31]),
     ("entropy_k32", 2, [63]),
+    ("odd_h2560", 0, [0, 40]),
 ]
+# The wide odd shape (H = 2560) cascades more bf16 rounding flips: an
+# independent float32 build of the encoder already misses TOL on ~0.15 % of its
+# cosines (tests/test_tolerance_derivation.py), so its fraction is 0.995.
+COS_FRACTION_OF = {"odd_h2560": 0.995}
 
 
 def run_case(L, name, tier, sample, alpha=None, use_logp=True):
@@ -74,9 +79,10 @@ def run_case(L, name, tier, sample, alpha=None, use_logp=True):
         if not ex:
             assert np.array_equal(gtok, r.tokens.astype(np.int32)), f"block {b}: tokens"
     if g_cos:
+        frac = COS_FRACTION_OF.get(name, COS_FRACTION)
         sc = assert_scores(np.concatenate([c.ravel() for c in g_cos]),
-                           np.concatenate([c.ravel() for c in o_cos]), f"{name} cos", 1.0)
-        sz = assert_scores(np.concatenate(g_z), np.concatenate(o_z), f"{name} step scores", alpha)
+                           np.concatenate([c.ravel() for c in o_cos]), f"{name} cos", 1.0, frac)
+        sz = assert_scores(np.concatenate(g_z), np.concatenate(o_z), f"{name} step scores", alpha, frac)
         print(f"[scores] {name} tier {tier}: cos {sc} step {sz}", flush=True)
     if excused:
         print(f"[excused] {name} tier {tier}: {excused}", flush=True)

@@ -92,3 +92,23 @@ def test_float32_build_drifts_to_the_bar_but_not_past_the_bound():
         worst = max(worst, d.max())
         assert np.mean(o32 != r.outv) > 0.05      # the cascade reaches the stored vectors
     assert 5e-4 < worst < COS_HARD
+
+
+def test_float32_drift_rate_of_the_wide_odd_shape():
+    """The wide odd shape (H = 2560, 15 slots, K = 7) drifts more: the float32
+    build misses 1e-3 on more than 0.1 % of its cosines (the bar of the main
+    workloads), still inside the bf16 bound; its GPU case uses fraction 0.995."""
+    w = synth.WORKLOADS["odd_h2560"]
+    host = synth.make_logits(w)
+    ow = oracle.OracleWeights(oracle.Dims(w.hidden, w.heads, w.ffn, w.d_e), w.vocab, synth.WEIGHTS_SEED)
+    bad = total = 0
+    worst = 0.0
+    for b in (0, 1):
+        r = oracle.rerank_block(host[b], w.topk, ow, 1.0)
+        o32, i32 = encoder_float32(r.idx, r.logp, ow, w.topk)
+        d = np.abs(pair_scores(o32, i32).astype(np.float64) - r.cos)
+        bad += int((d > 1e-3 * np.maximum(1.0, np.abs(r.cos))).sum())
+        total += d.size
+        worst = max(worst, d.max())
+    assert 0.001 < bad / total < 0.005
+    assert worst < COS_HARD

@@ -173,14 +173,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 }
 
 // Resident variant for lattices of up to 256 tokens: one workgroup of eight
-// waves per (head, block) loads the block's K (row-major, 16-byte chunks
-// XOR-swizzled by key) and V (transposed, [d][key]) into LDS once, with every
-// global load in flight together, and the waves then loop over the block's
-// 16-query tiles (wave w takes tiles w, w+8, ...). Per tile: S^T = K Q^T with
-// the key tiles as independent MFMA chains, exact row max,
-// P~ = bf16(exp(s - max)), O^T = V^T P~^T, O / l. K and V are read from HBM
-// once per (block, head). V is fetched key-fastest so that each transposed
-// 2-byte LDS store instruction covers 64 consecutive keys of one d row.
+// waves per (head, block) loads the block's K and V (row-major, 16-byte
+// chunks XOR-swizzled by key) into LDS once, with every global load in flight
+// together, and the waves then loop over the block's 16-query tiles (wave w
+// takes tiles w, w+8, ...). Per tile: S^T = K Q^T with the key tiles as
+// independent MFMA chains, exact row max, P~ = bf16(exp(s - max)),
+// O^T = V^T P~^T with V^T fragments read by ds_read_b64_tr_b16, O / l. K and V
+// are read from HBM once per (block, head).
 template <int TMAX, int DH>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
                                                             int K, int H,
@@ -191,16 +190,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KT = TMAX / 16;   // 16-key tiles
   constexpr int KS = DH / 32;     // MFMA k-steps over d_h
   constexpr int DT = DH / 16;     // 16-wide d tiles of the output
-  constexpr int CPR = DH / 8;     // 16-byte chunks per K row
-  constexpr int VS = TMAX + 8;    // bf16 per transposed-V row (16-byte pad)
+  constexpr int CPR = DH / 8;     // 16-byte chunks per K or V row
+  constexpr int SWM = DT - 1;     // V d-tile swizzle mask
   __shared__ __attribute__((aligned(16))) uint16_t Ks[TMAX * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[TMAX * DH];
   __shared__ float bias_tab[128];
   // K chunk (key, c) lives at chunk c ^ swz(key) of its row
   auto kat = [](int key, int c) {
     const int sw = CPR >= 8 ? (key & 7) : ((key >> 1) & (CPR - 1));
     return key * DH + ((c ^ sw) << 3);
   };
+  // V row-major; chunk c (8 columns) of row key sits in 32-byte d tile
+  // ((c >> 1) ^ key) & SWM, so transposed fragment reads spread over the banks
+  auto cat = [](int key, int c) { return key * DH + (((((c >> 1) ^ key) & SWM) << 1 | (c & 1)) << 3); };
 
   const int T = B * K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if (tid < 127) bias_tab[tid] = dist[h * 127 + tid];
   const float same_h = same[h];
-  // K (chunk-fastest) and V (key-fastest) of this head, all loads issued
+  // K and V of this head (row-major, 16-byte chunks), all loads issued
   // before any store. Rows past the lattice are read from its last token
   // (a conditional load would serialise the loads): their keys are masked to
   // -inf and their values meet probability 0.
@@ -234,20 +236,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int ch = min(tid + 64 * NW * i, TOT - 1);
     const int kk = min(ch / CPR, T - 1), kc = ch % CPR;
     kr[i] = *(const u32x4_t*)(blk + (int64_t)kk * H3 + H + h * DH + kc * 8);
-    const int vk = min(ch % TMAX, T - 1), vc = ch / TMAX;
-    vr[i] = *(const u32x4_t*)(blk + (int64_t)vk * H3 + 2 * H + h * DH + vc * 8);
+    vr[i] = *(const u32x4_t*)(blk + (int64_t)kk * H3 + 2 * H + h * DH + kc * 8);
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int ch = tid + 64 * NW * i;
     if (!EXACT && ch >= TOT) break;
     *(u32x4_t*)(&Ks[kat(ch / CPR, ch % CPR)]) = kr[i];
-    const int vk = ch % TMAX, vc = ch / TMAX;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Vt[(vc * 8 + 2 * e) * VS + vk] = (uint16_t)(vr[i][e] & 0xFFFF);
-      Vt[(vc * 8 + 2 * e + 1) * VS + vk] = (uint16_t)(vr[i][e] >> 16);
-    }
+    *(u32x4_t*)(&Vs[cat(ch / CPR, ch % CPR)]) = vr[i];
   }
   __syncthreads();
 
@@ -339,19 +335,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pb[1] = pack_bf16x2(s[2 * ch][2], s[2 * ch][3]);
       pb[2] = pack_bf16x2(s[2 * ch + 1][0], s[2 * ch + 1][1]);
       pb[3] = pack_bf16x2(s[2 * ch + 1][2], s[2 * ch + 1][3]);
-      // all of the chunk's V^T fragment reads are issued before its MFMAs
+      // V^T fragments by ds_read_b64_tr_b16: within each 16-lane group,
+      // source lane s addresses key k0 + s / 4, columns 4 (s % 4) .. + 3 of
+      // the d tile, and output lane i receives keys k0 .. k0 + 3 of column i
+      // (the MFMA A-operand layout); all of the chunk's reads are issued
+      // before its MFMAs
       u32x4_t va[DT];
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
-        const uint16_t* vrow = &Vt[(d * 16 + c) * VS + ch * 32];
-        const u32x2_t lo = *(const u32x2_t*)(vrow + 4 * g);
-        const u32x2_t hi = *(const u32x2_t*)(vrow + 16 + 4 * g);
-        va[d] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        const int k_lo = 32 * ch + 4 * g + c / 4, k_hi = k_lo + 16;
+        const int c8 = 2 * d + (c & 3) / 2, off = 4 * (c & 1);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(&Vs[cat(k_lo, c8) + off]));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(&Vs[cat(k_hi, c8) + off]));
+        const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+        va[d] = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
       }
 #pragma unroll
       for (int d = 0; d < DT; ++d) oacc[d] = mfma16(va[d], pb, oacc[d]);
       // schedule: the chunk's LDS reads first, then its MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);
       __builtin_amdgcn_sched_barrier(0);   // bound the V reads in flight
     }
@@ -476,19 +480,40 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
             const u32x4_t kf = *(const u32x4_t*)(&lb[cat((kt0 + j) * 16 + c, ks * 4 + g)]);
             acc[j] = mfma16(kf, qf[ks], acc[j]);
           }
+        if (K % 16 == 0) {
+          // every 16-key tile lies in one slot: one table read per tile, no
+          // per-element branch (a read under one is waited for inside it)
+          float bt[4];
+          int st[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
-            float x = -INFINITY;
-            if (key < T) {
-              const int slot_k = (int)(((unsigned)key * kmul) >> 16);
-              x = acc[j][i] * scale + bias_tab[slot_k - slot_q + 63];
-              if (slot_k == slot_q) x += same_h;
-            }
-            v[j][i] = x;
+          for (int j = 0; j < 4; ++j) {
+            st[j] = (int)(((unsigned)min((kt0 + j) * 16 + zb, T - 1) * kmul) >> 16);
+            bt[j] = bias_tab[st[j] - slot_q + 63];
           }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
+              float x = acc[j][i] * scale + bt[j];
+              x = st[j] == slot_q ? x + same_h : x;
+              v[j][i] = key < T ? x : -INFINITY;
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
+              float x = -INFINITY;
+              if (key < T) {
+                const int slot_k = (int)(((unsigned)key * kmul) >> 16);
+                x = acc[j][i] * scale + bias_tab[slot_k - slot_q + 63];
+                if (slot_k == slot_q) x += same_h;
+              }
+              v[j][i] = x;
+            }
+        }
       };
       // pass 1: exact row max; pass 2 recomputes the identical scores (the
       // full strip would not fit in registers beside P~) and forms P~

@@ -9,6 +9,8 @@
 #define LL_WAVE 64
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -28,8 +30,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two floats to packed bfloat16 (lo in bits 15:0), round to nearest even:
+// one v_cvt_pk_bf16_f32, the same rounding as f32_to_bf16 for finite values.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // 16x16x32 bf16 MFMA on gfx950: acc += A(16x32) * B(32x16).
@@ -147,6 +151,8 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU with the hardware exponential and reciprocal (v_exp_f32, v_rcp_f32;
+// about 1 ulp each): the result is rounded to bfloat16 by every caller.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 }  // namespace ll

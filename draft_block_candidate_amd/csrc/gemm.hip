@@ -24,6 +24,7 @@
 //    whole rows, so the RMSNorm that follows a residual add and the unit
 //    normalisation of the out/in heads fuse into it.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -160,8 +161,11 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
 // only for its own stage loads (vmcnt) and a bare s_barrier then makes the
 // stage visible, so the loads behind it stay in flight. Within a stage the
 // next k-step's fragment reads are interleaved with the current MFMAs. Stage
-// rows are 64 bytes with the 16-byte chunk XOR-swizzled by (row >> 1) & 3, so
-// a fragment read touches every bank once. Workgroups are dealt to the XCDs
+// rows are 64 bytes with the 16-byte chunk XOR-swizzled by (row >> 2) & 3:
+// LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, all 64 banks) at a
+// time, and the 16 rows those lanes read then start on 16 distinct 4-bank
+// groups (swizzling by (row >> 1) & 3 left rows r and r + 8 on one group,
+// a two-way conflict on every read). Workgroups are dealt to the XCDs
 // round-robin; the tile order is remapped so that each XCD runs a contiguous
 // run of tiles and shares their A row panels in its L2. The epilogue moves
 // each wave's block out through LDS in 32-row slices as 16-byte stores.
@@ -209,20 +213,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
 
   // Stage loads: instruction j of A (0 .. BM/16 - 1 over the workgroup) covers
   // tile rows 16 j .. 16 j + 15, and its lane i fills LDS slot i (row
-  // 16 j + i / 4, chunk' = i % 4), which holds chunk chunk' ^ ((row >> 1) & 3)
+  // 16 j + i / 4, chunk' = i % 4), which holds chunk chunk' ^ ((row >> 2) & 3)
   // of that row; likewise for W. Rows past the matrix are clamped.
   const uint16_t* srcA[UA];
   const uint16_t* srcW[UW];
 #pragma unroll
   for (int u = 0; u < UA; ++u) {
     const int row = 16 * (wave * UA + u) + lane / 4;
-    const int chunk = (lane % 4) ^ ((row >> 1) & 3);
+    const int chunk = (lane % 4) ^ ((row >> 2) & 3);
     srcA[u] = A + min(m0 + row, (int64_t)M - 1) * Kd + chunk * 8;
   }
 #pragma unroll
   for (int u = 0; u < UW; ++u) {
     const int row = 16 * (wave * UW + u) + lane / 4;
-    const int chunk = (lane % 4) ^ ((row >> 1) & 3);
+    const int chunk = (lane % 4) ^ ((row >> 2) & 3);
     srcW[u] = W + min(n0 + row, (int64_t)N - 1) * Kd + chunk * 8;
   }
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
                                        (__attribute__((address_space(3))) void*)(st + BM * BK + (wave * UW + u) * 512),
                                        16, 0, 0);
   };
-  auto fat = [](int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 3)) << 3); };
+  auto fat = [](int row, int chunk) { return row * BK + ((chunk ^ ((row >> 2) & 3)) << 3); };
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -326,39 +330,52 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
       }
     }
   };
-  load_resid(0, rbuf[0]);
+  // Whole tiles (the wave-uniform common case) store with no predicate at
+  // all: a predicated store sits in its own exec branch, and the wait the
+  // compiler puts at its head (for a bias or residual load that may still be
+  // outstanding on the skipped path) also waits for every earlier store.
+  const bool full = m0 + BM <= M && n0 + BN <= N;
+  auto slices = [&](auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    load_resid(0, rbuf[0]);
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    if (i + 1 < MT) load_resid(i + 1, rbuf[(i + 1) & 1]);
+    for (int i = 0; i < MT; ++i) {
+      if (i + 1 < MT) load_resid(i + 1, rbuf[(i + 1) & 1]);
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        stg[(8 * (e >> 2) + 4 * hi + (e & 3)) * ES + j * 32 + l32] = acc[i][j][e];
-    __builtin_amdgcn_wave_barrier();
+        for (int e = 0; e < 16; ++e)
+          stg[(8 * (e >> 2) + 4 * hi + (e & 3)) * ES + j * 32 + l32] = acc[i][j][e];
+      __builtin_amdgcn_wave_barrier();
+      float4 ys[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int rr = (lane + 64 * u) / CPRW;
-      const int64_t m = m0 + wm * WM + i * 32 + rr;
-      const bool ok = col_ok && m < M;
-      float4 y = *(const float4*)(&stg[rr * ES + c4]);
-      y.x += bv.x; y.y += bv.y; y.z += bv.z; y.w += bv.w;
-      const int64_t o = m * N + n;
-      if constexpr (EPI == EPI_F32) {
-        if (ok) *(float4*)((float*)out + o) = y;
-      } else if constexpr (EPI == EPI_BF16) {
-        if (ok) *(uint2*)((uint16_t*)out + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
-      } else if constexpr (EPI == EPI_SILU_BF16) {
-        if (ok)
-          *(uint2*)((uint16_t*)out + o) =
-              make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
-      } else {
-        const float4 rv = rbuf[i & 1][u];
-        if (ok) *(float4*)((float*)out + o) = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
+      for (int u = 0; u < U; ++u) ys[u] = *(const float4*)(&stg[((lane + 64 * u) / CPRW) * ES + c4]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int rr = (lane + 64 * u) / CPRW;
+        const int64_t m = m0 + wm * WM + i * 32 + rr;
+        const bool ok = FULL || (col_ok && m < M);
+        float4 y = ys[u];
+        y.x += bv.x; y.y += bv.y; y.z += bv.z; y.w += bv.w;
+        const int64_t o = m * N + n;
+        if constexpr (EPI == EPI_F32) {
+          if (ok) *(float4*)((float*)out + o) = y;
+        } else if constexpr (EPI == EPI_BF16) {
+          if (ok) *(uint2*)((uint16_t*)out + o) = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+        } else if constexpr (EPI == EPI_SILU_BF16) {
+          if (ok)
+            *(uint2*)((uint16_t*)out + o) =
+                make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
+        } else {
+          const float4 rv = rbuf[i & 1][u];
+          if (ok) *(float4*)((float*)out + o) = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
+        }
       }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
-  }
+  };
+  if (full) slices(std::true_type{});
+  else slices(std::false_type{});
 }
 
 template <int BM, int BN, int NW = 4>

@@ -195,9 +195,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) uint16_t Ks[TMAX * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[TMAX * DH];
   __shared__ float bias_tab[128];
-  // K chunk (key, c) lives at chunk c ^ swz(key) of its row
+  // K chunk (key, c) lives at chunk c ^ swz(key) of its row. A 16-byte LDS
+  // read is served 16 lanes (256 bytes, all 64 banks) at a time, and a K
+  // fragment read has those lanes on 16 consecutive keys at one chunk, so the
+  // swizzle gives them 16 distinct 16-byte bank groups: 256 / (16 CPR) rows
+  // share a 256-byte line, and the key's line index picks the chunk.
   auto kat = [](int key, int c) {
-    const int sw = CPR >= 8 ? (key & 7) : ((key >> 1) & (CPR - 1));
+    constexpr int RPL = CPR >= 16 ? 1 : 16 / CPR;   // rows per 256-byte line
+    const int sw = (key / RPL) & (CPR >= 16 ? 15 : CPR - 1);
     return key * DH + ((c ^ sw) << 3);
   };
   // V row-major; chunk c (8 columns) of row key sits in 32-byte d tile

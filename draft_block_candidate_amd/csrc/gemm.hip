@@ -347,15 +347,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
         for (int e = 0; e < 16; ++e)
           stg[(8 * (e >> 2) + 4 * hi + (e & 3)) * ES + j * 32 + l32] = acc[i][j][e];
       __builtin_amdgcn_wave_barrier();
-      float4 ys[U];
+      // the slice's staged values are read together, except in the residual
+      // epilogue, whose double-buffered residual rows leave no registers
+      constexpr int UY = EPI == EPI_RESID_F32 ? 1 : U;
+      float4 ys[UY];
+      if constexpr (UY > 1) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) ys[u] = *(const float4*)(&stg[((lane + 64 * u) / CPRW) * ES + c4]);
+        for (int u = 0; u < U; ++u) ys[u] = *(const float4*)(&stg[((lane + 64 * u) / CPRW) * ES + c4]);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int rr = (lane + 64 * u) / CPRW;
         const int64_t m = m0 + wm * WM + i * 32 + rr;
         const bool ok = FULL || (col_ok && m < M);
-        float4 y = ys[u];
+        float4 y = UY > 1 ? ys[u % UY] : *(const float4*)(&stg[rr * ES + c4]);
         y.x += bv.x; y.y += bv.y; y.z += bv.z; y.w += bv.w;
         const int64_t o = m * N + n;
         if constexpr (EPI == EPI_F32) {

@@ -935,11 +935,13 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
     const auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (M >= 2048 && Kd % 32 == 0 && N % 4 == 0 && al16(out) && (bias == nullptr || al16(bias)) &&
         (ep.resid == nullptr || al16(ep.resid))) {
-      // the largest tile that still gives every CU work
+      // the largest tile that still gives (nearly) every CU work
       // (eight waves, two per SIMD, for the large tiles: each wave then owns a
       // 128 x 64 or 128 x 32 block, and one wave's barrier wait overlaps the
-      // other's MFMAs)
-      if (tiles(256, 256) >= 256)
+      // other's MFMAs). Three quarters of the CUs busy with 256 x 256 tiles
+      // beat all of them with 256 x 128 ones (QKV at 4,096 rows: 36 against
+      // 43 us).
+      if (tiles(256, 256) >= 192)
         e = launch_dma<256, 256, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
       else if (tiles(256, 128) >= 256)
         e = launch_dma<256, 128, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);

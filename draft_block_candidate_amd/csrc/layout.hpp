@@ -147,7 +147,7 @@ inline WeightPtrs weight_ptrs(const lilicorr_weights& w) {
 // kTopkMinChunk elements, and at most 64 chunks per row (the merge assigns one
 // lane per chunk).
 constexpr int kTopkTargetWaves = 4096;
-constexpr int64_t kTopkMinChunk = 4096;
+constexpr int64_t kTopkMinChunk = 2048;
 
 inline int topk_chunks_per_row(int rows, int V) {
   int64_t want = (kTopkTargetWaves + rows - 1) / rows;

@@ -105,9 +105,9 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
 
 // Fused pair scores + greedy commit for the rerank path: one workgroup per
 // block. The eight waves compute the block's B-1 K x K cosine matrices into LDS
-// (and to global memory when requested); the walk then reads its rows, the
-// log-probabilities and the ids from LDS, so each sequential step costs LDS
-// latency rather than a global round trip.
+// (and to global memory when requested), then tabulate the walk's decision for
+// every (slot, previous candidate) pair; the sequential part is one LDS lookup
+// per slot.
 __global__ __launch_bounds__(512) void scores_walk_kernel(
     const uint16_t* __restrict__ outv, const uint16_t* __restrict__ inv,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int B, int K,
@@ -118,6 +118,9 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
   float* s_cos = sm;                                // [(B-1) K K]
   float* s_logp = sm + (B - 1) * KK;                // [B K]
   int* s_idx = (int*)(s_logp + B * K);              // [B K]
+  int* s_tc = s_idx + B * K;                        // [(B-1) K] walk table: choice
+  float* s_tz = (float*)(s_tc + (B - 1) * K);       // [(B-1) K] its score
+  float* s_tg = s_tz + (B - 1) * K;                 // [(B-1) K] its gap
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = blockIdx.x;
   const int64_t base = n * B * K;
@@ -135,32 +138,66 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
     });
   }
   __syncthreads();
+  // Walk table: for every slot s >= 1 and every candidate c of slot s - 1, the
+  // choice the walk makes at s when it stands on c, with its score and the
+  // gap to the runner-up. Entries are independent, so all threads build them;
+  // the largest score wins and the lowest index breaks a tie. The arithmetic
+  // is the walk's own (fl32, no contraction), so the table holds exactly the
+  // decisions the walk takes.
+  const int NE = (B - 1) * K;
+  for (int e = tid; e < NE; e += blockDim.x) {
+    const int s = e / K + 1, cp = e - (s - 1) * K;
+    const float* crow = s_cos + (s - 1) * KK + cp * K;
+    const float* lrow = s_logp + s * K;
+    float best = -INFINITY, second = -INFINITY;
+    int bj = K;
+    // neighbouring entries start their scans at different j (their rows are
+    // K floats apart, so equal j would hit a few LDS banks); the comparison
+    // is on the full (score, lower index) key, so the order does not matter
+    // (eight at a time, all eight pairs of reads issued before any is used)
+    for (int jj0 = 0; jj0 < K; jj0 += 8) {
+      float cv[8], lv[8];
+      int jv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int j = cp + min(jj0 + u, K - 1);
+        j = j >= K ? j - K : j;
+        jv[u] = j;
+        cv[u] = crow[j];
+        lv[u] = lrow[j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float term = __fmul_rn(alpha, cv[u]);
+        const float z = use_logp ? __fadd_rn(lv[u], term) : term;
+        const int j = jv[u];
+        const bool better = (jj0 + u < K) & ((z > best) | ((z == best) & (j < bj)));
+        second = (jj0 + u < K) ? (better ? best : fmaxf(second, z)) : second;
+        best = better ? z : best;
+        bj = better ? j : bj;
+      }
+    }
+    s_tc[e] = bj < K ? bj : 0;   // bj == K only if every score is NaN; keeps the walk in range
+    s_tz[e] = best;
+    s_tg[e] = K > 1 ? __fsub_rn(best, second) : 0.f;
+  }
+  __syncthreads();
   if (wave != 0) return;
-  // The walk. Lane j scores candidate j; the winner is the largest score and,
-  // among equal ones, the lowest lane (a max, then the lowest lane of the
-  // ballot of lanes holding it). Step s's choice, score and gap are kept in
-  // lane s, so the sequential part carries only the LDS read of the previous
-  // choice's cosine row; tokens and outputs are written after the loop.
+  // The walk proper: one table lookup per slot, starting from slot 0's top
+  // candidate. Step s's choice, score and gap are kept in lane s and written
+  // after the loop.
   const int64_t r0 = n * B;
-  const int width = K <= 16 ? 16 : (K <= 32 ? 32 : 64);
   int choice = 0;
   float my_score = s_logp[0], my_gap = 0.f;
-  int cprev = 0;
+  int c = 0;
   for (int s = 1; s < B; ++s) {
-    float z = -INFINITY;
-    if (lane < K) {
-      const float term = __fmul_rn(alpha, s_cos[(s - 1) * KK + cprev * K + lane]);
-      z = use_logp ? __fadd_rn(s_logp[s * K + lane], term) : term;
-    }
-    const float bz = lanes_max(z, width);
-    int bl = __ffsll((long long)__ballot(z == bz)) - 1;
-    if (bl < 0 || bl >= K) bl = 0;  // only reachable with non-finite scores; keeps every index in range
-    // the runner-up is only needed for the optional gap output
-    const float second = gap ? wave_max(lane == bl ? -INFINITY : z) : 0.f;
-    choice = lane == s ? bl : choice;
-    my_score = lane == s ? bz : my_score;
-    my_gap = lane == s ? (K > 1 ? __fsub_rn(bz, second) : 0.f) : my_gap;
-    cprev = bl;
+    const int e = (s - 1) * K + c;
+    const int nc = s_tc[e];
+    const float z = s_tz[e], gz = s_tg[e];
+    choice = lane == s ? nc : choice;
+    my_score = lane == s ? z : my_score;
+    my_gap = lane == s ? gz : my_gap;
+    c = nc;
   }
   if (lane < B) {
     out_tokens[r0 + lane] = s_idx[lane * K + choice];
@@ -172,7 +209,7 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
 }  // namespace
 
 size_t scores_walk_lds_bytes(int B, int K) {
-  return ((size_t)(B - 1) * K * K + 2 * (size_t)B * K) * 4;
+  return ((size_t)(B - 1) * K * K + 2 * (size_t)B * K + 3 * (size_t)(B - 1) * K) * 4;
 }
 
 hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const int32_t* topk_idx,

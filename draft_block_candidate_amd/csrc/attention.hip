@@ -180,13 +180,12 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 // independent MFMA chains, exact row max, P~ = bf16(exp(s - max)),
 // O^T = V^T P~^T with V^T fragments read by ds_read_b64_tr_b16, O / l. K and V
 // are read from HBM once per (block, head).
-template <int TMAX, int DH>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
+template <int TMAX, int DH, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
                                                             int K, int H,
                                                             const float* __restrict__ dist,
                                                             const float* __restrict__ same,
                                                             uint16_t* __restrict__ out) {
-  constexpr int NW = 8;           // waves per workgroup
   constexpr int KT = TMAX / 16;   // 16-key tiles
   constexpr int KS = DH / 32;     // MFMA k-steps over d_h
   constexpr int DT = DH / 16;     // 16-wide d tiles of the output
@@ -217,11 +216,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t H3 = 3 * (int64_t)H;
   const uint16_t* blk = qkv + n * T * H3;
 
+  // The block's query tiles are dealt to the gridDim.z workgroups of this
+  // (head, block) and, within one, to its waves: tile qt0 + j * qstep.
+  const int qt0 = blockIdx.z * NW + wave, qstep = NW * gridDim.z;
   // Query fragments of this wave's first tile, issued before the staging
   // loads so that their latency overlaps them.
   u32x4_t qf0[KS];
   {
-    const int qc = min(wave * 16 + c, T - 1);
+    const int qc = min(qt0 * 16 + c, T - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf0[ks] = *(const u32x4_t*)(blk + (int64_t)qc * H3 + h * DH + ks * 32 + 8 * g);
@@ -256,13 +258,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // slot of a token: (t * kmul) >> 16 equals t / K for t < 1024 and K <= 64
   const unsigned kmul = (65536u + K - 1) / K;
   const int ntile = (T + 15) / 16;
-  for (int qt = wave; qt < ntile; qt += NW) {
+  for (int qt = qt0; qt < ntile; qt += qstep) {
     const int q = qt * 16 + c;   // this lane's query
     const bool q_ok = q < T;
     const int qc = min(q, T - 1);   // rows past the lattice compute a copy, never stored
     const int slot_q = (int)(((unsigned)qc * kmul) >> 16);
     u32x4_t qf[KS];
-    if (qt == wave) {
+    if (qt == qt0) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = qf0[ks];
     } else {
@@ -610,16 +612,22 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
 template <int TMAX>
 hipError_t launch_res(int dh, const uint16_t* qkv, int N, int B, int K, int H, int heads,
                       const float* dist, const float* same, uint16_t* out, hipStream_t stream) {
-  const dim3 grid((unsigned)heads, (unsigned)N);
+  // Up to 128 tokens: two four-wave workgroups per (head, block), each with
+  // half of the query tiles (every wave reads all of K and V from LDS, so
+  // fewer waves per CU means less LDS traffic per CU); larger lattices: one
+  // eight-wave workgroup.
+  constexpr int NW = TMAX <= 128 ? 4 : 8;
+  const int ntile = (B * K + 15) / 16;
+  const dim3 grid((unsigned)heads, (unsigned)N, TMAX <= 128 && ntile > NW ? 2u : 1u);
   if (dh == 32)
-    hipLaunchKernelGGL((attention_res_kernel<TMAX, 32>), grid, dim3(512), 0, stream, qkv, B, K, H,
-                       dist, same, out);
+    hipLaunchKernelGGL((attention_res_kernel<TMAX, 32, NW>), grid, dim3(64 * NW), 0, stream, qkv, B,
+                       K, H, dist, same, out);
   else if (dh == 64)
-    hipLaunchKernelGGL((attention_res_kernel<TMAX, 64>), grid, dim3(512), 0, stream, qkv, B, K, H,
-                       dist, same, out);
+    hipLaunchKernelGGL((attention_res_kernel<TMAX, 64, NW>), grid, dim3(64 * NW), 0, stream, qkv, B,
+                       K, H, dist, same, out);
   else
-    hipLaunchKernelGGL((attention_res_kernel<TMAX, 128>), grid, dim3(512), 0, stream, qkv, B, K, H,
-                       dist, same, out);
+    hipLaunchKernelGGL((attention_res_kernel<TMAX, 128, NW>), grid, dim3(64 * NW), 0, stream, qkv, B,
+                       K, H, dist, same, out);
   return hipGetLastError();
 }
 

@@ -156,8 +156,8 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
 // 2 x (NW / 2) grid each hold a (BM / 2) x (2 BN / NW) fp32 accumulator block
 // (with four waves and 256 x 256 tiles, 128 x 128: every 16-byte fragment
 // read from LDS feeds four MFMAs). K advances 32 per stage
-// through four LDS stages that global_load_lds fills directly (no register
-// staging), three stages ahead of the one being multiplied; each wave waits
+// through four or five LDS stages that global_load_lds fills directly (no
+// register staging), NS - 1 stages ahead of the one being multiplied; each wave waits
 // only for its own stage loads (vmcnt) and a bare s_barrier then makes the
 // stage visible, so the loads behind it stay in flight. Within a stage the
 // next k-step's fragment reads are interleaved with the current MFMAs. Stage
@@ -177,7 +177,9 @@ template <int BM, int BN, int EPI, int NW = 4>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN * 4 / NW >= 32768 ? 1 : 2, BM * BN * 4 / NW >= 32768 ? 1 : 2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N, int Kd,
     const float* __restrict__ bias, const float* resid, void* out, int tiles_n, int ntiles) {
-  constexpr int BK = 32, NS = 4;
+  // stages in LDS: five for 256 x 256 tiles (all 160 KiB: one more stage of
+  // loads in flight, 1-3 % faster than four), four otherwise
+  constexpr int BK = 32, NS = BM == 256 && BN == 256 ? 5 : 4;
   constexpr int WGN = NW / 2;                  // waves: 2 x WGN grid
   constexpr int WM = BM / 2, WN = BN / WGN, MT = WM / 32, NT = WN / 32;
   constexpr int UA = BM / 16 / NW, UW = BN / 16 / NW;   // 1 KiB stage-load instructions per wave
@@ -254,18 +256,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = Kd / BK;
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of stage kt are done once at most those of the stages
-    // issued after it (up to two, PER instructions each) are outstanding
-    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER));
-    else if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER));
+    // issued after it (up to NS - 2, PER instructions each) are outstanding
+    const int after = min(NS - 2, nk - 1 - kt);
+    if (NS >= 5 && after >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * PER));
+    else if (after >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    // every wave has finished stage kt - 1, so its buffer takes stage kt + 3
-    if (kt + 3 < nk) issue(kt + 3);
+    // every wave has finished stage kt - 1, so its buffer takes stage kt + NS - 1
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
     const uint16_t* as = smem + (kt % NS) * STAGE;
     const uint16_t* ws = as + BM * BK;
     u32x4_t fa[2][MT], fb[2][NT];

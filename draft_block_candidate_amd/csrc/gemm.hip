@@ -155,17 +155,17 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
 // Many-row GEMM on 32 x 32 x 16 MFMA, BM x BN tiles. NW waves in a
 // 2 x (NW / 2) grid each hold a (BM / 2) x (2 BN / NW) fp32 accumulator block
 // (with four waves and 256 x 256 tiles, 128 x 128: every 16-byte fragment
-// read from LDS feeds four MFMAs). K advances 32 per stage
-// through four or five LDS stages that global_load_lds fills directly (no
+// read from LDS feeds four MFMAs). K advances 64 per stage
+// through two or three LDS stages that global_load_lds fills directly (no
 // register staging), NS - 1 stages ahead of the one being multiplied; each wave waits
 // only for its own stage loads (vmcnt) and a bare s_barrier then makes the
 // stage visible, so the loads behind it stay in flight. Within a stage the
 // next k-step's fragment reads are interleaved with the current MFMAs. Stage
-// rows are 64 bytes with the 16-byte chunk XOR-swizzled by (row >> 2) & 3:
+// rows are 128 bytes with the 16-byte chunk XOR-swizzled by (row >> 1) & 7:
 // LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, all 64 banks) at a
-// time, and the 16 rows those lanes read then start on 16 distinct 4-bank
-// groups (swizzling by (row >> 1) & 3 left rows r and r + 8 on one group,
-// a two-way conflict on every read). Workgroups are dealt to the XCDs
+// time; the 16 rows those lanes read pair up on the two halves of the banks
+// (row parity) and the swizzle gives the 8 rows of each half 8 distinct
+// chunks, so every read touches each bank once. Workgroups are dealt to the XCDs
 // round-robin; the tile order is remapped so that each XCD runs a contiguous
 // run of tiles and shares their A row panels in its L2. The epilogue moves
 // each wave's block out through LDS in 32-row slices as 16-byte stores.
@@ -177,13 +177,16 @@ template <int BM, int BN, int EPI, int NW = 4>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN * 4 / NW >= 32768 ? 1 : 2, BM * BN * 4 / NW >= 32768 ? 1 : 2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N, int Kd,
     const float* __restrict__ bias, const float* resid, void* out, int tiles_n, int ntiles) {
-  // stages in LDS: five for 256 x 256 tiles (all 160 KiB: one more stage of
-  // loads in flight, 1-3 % faster than four), four otherwise
-  constexpr int BK = 32, NS = BM == 256 && BN == 256 ? 5 : 4;
+  // K advances 64 per stage, so a stage row is one whole 128-byte line of A or
+  // W (10-17 % faster than 32 per stage, whose load instructions each touched
+  // half of 16 lines). Stages in LDS: three for 256 x 128 tiles (144 KiB), two
+  // otherwise (128 KiB for 256 x 256; 64 KiB for 128 x 128, two workgroups per CU).
+  constexpr int BK = 64, NS = BM == 256 && BN == 128 ? 3 : 2;
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;   // 16-byte chunks per stage row; rows per load instruction
   constexpr int WGN = NW / 2;                  // waves: 2 x WGN grid
   constexpr int WM = BM / 2, WN = BN / WGN, MT = WM / 32, NT = WN / 32;
-  constexpr int UA = BM / 16 / NW, UW = BN / 16 / NW;   // 1 KiB stage-load instructions per wave
-  static_assert(UA >= 1 && UW >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "stage loads");
+  constexpr int UA = BM / RPI / NW, UW = BN / RPI / NW;   // 1 KiB stage-load instructions per wave
+  static_assert(UA >= 1 && UW >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "stage loads");
   constexpr int PER = UA + UW;                 // per wave per stage
   constexpr int STAGE = (BM + BN) * BK;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
@@ -213,22 +216,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
   const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // Stage loads: instruction j of A (0 .. BM/16 - 1 over the workgroup) covers
-  // tile rows 16 j .. 16 j + 15, and its lane i fills LDS slot i (row
-  // 16 j + i / 4, chunk' = i % 4), which holds chunk chunk' ^ ((row >> 2) & 3)
-  // of that row; likewise for W. Rows past the matrix are clamped.
+  // Stage loads: instruction j of A (0 .. BM/8 - 1 over the workgroup) covers
+  // tile rows 8 j .. 8 j + 7, and its lane i fills LDS slot i (row 8 j + i / 8,
+  // chunk' = i % 8), which holds chunk chunk' ^ ((row >> 1) & 7) of that row;
+  // likewise for W. Rows past the matrix are clamped.
   const uint16_t* srcA[UA];
   const uint16_t* srcW[UW];
 #pragma unroll
   for (int u = 0; u < UA; ++u) {
-    const int row = 16 * (wave * UA + u) + lane / 4;
-    const int chunk = (lane % 4) ^ ((row >> 2) & 3);
+    const int row = RPI * (wave * UA + u) + lane / CPR;
+    const int chunk = (lane % CPR) ^ ((row >> 1) & 7);
     srcA[u] = A + min(m0 + row, (int64_t)M - 1) * Kd + chunk * 8;
   }
 #pragma unroll
   for (int u = 0; u < UW; ++u) {
-    const int row = 16 * (wave * UW + u) + lane / 4;
-    const int chunk = (lane % 4) ^ ((row >> 2) & 3);
+    const int row = RPI * (wave * UW + u) + lane / CPR;
+    const int chunk = (lane % CPR) ^ ((row >> 1) & 7);
     srcW[u] = W + min(n0 + row, (int64_t)N - 1) * Kd + chunk * 8;
   }
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
                                        (__attribute__((address_space(3))) void*)(st + BM * BK + (wave * UW + u) * 512),
                                        16, 0, 0);
   };
-  auto fat = [](int row, int chunk) { return row * BK + ((chunk ^ ((row >> 2) & 3)) << 3); };
+  auto fat = [](int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); };
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -937,7 +940,7 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
     hipError_t e;
     const auto al16 = [](const void* ptr) { return ((uintptr_t)ptr & 15) == 0; };
     const auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (M >= 2048 && Kd % 32 == 0 && N % 4 == 0 && al16(out) && (bias == nullptr || al16(bias)) &&
+    if (M >= 2048 && Kd % 64 == 0 && N % 4 == 0 && al16(out) && (bias == nullptr || al16(bias)) &&
         (ep.resid == nullptr || al16(ep.resid))) {
       // the largest tile that still gives (nearly) every CU work
       // (eight waves, two per SIMD, for the large tiles: each wave then owns a

@@ -21,6 +21,11 @@ Parity status per part (pins live in the test suite, marked ``not gpu``):
     torch build from library routines. The trained head of the paper is not
     published, so no printed value pins the encoder's outputs.
   * synthetic weights: pinned to the published SplitMix64 test vector.
+  * exact best path (paper, Appendix E): pinned (brute force over every path
+    of tiny lattices, hand-worked fixtures, never below the greedy total).
+  * sampled commit (PR, opt-in sampling): pinned (hand-worked draws at an
+    exact boundary, chi-square of draw frequencies against scipy's softmax,
+    greedy rows equal to the greedy walk, vanishing temperature).
 """
 
 from .bf16 import round_bf16, bf16_bits_to_f64, f64_to_bf16_bits  # noqa: F401
@@ -29,4 +34,5 @@ from .topk_lse import topk_lse_row, topk_lse  # noqa: F401
 from .encoder import encode_block  # noqa: F401
 from .scores import pair_scores  # noqa: F401
 from .walk import greedy_walk, WalkResult  # noqa: F401
+from .paths import best_path, sample_path, path_total, PathResult, SampleResult  # noqa: F401
 from .rerank import rerank_block, BlockResult  # noqa: F401

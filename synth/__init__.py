@@ -144,3 +144,21 @@ def make_random_logits(rows: int, vocab: int, dtype: str, seed: int,
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(scale)).astype(np.float32)
     return x if dtype == "f32" else f32_to_bf16_bits_rne(x)
+
+
+def make_uniforms(num_blocks: int, slots: int, seed: int) -> np.ndarray:
+    """The sampled commit's random draws, passed to both sides as input:
+    float32 [N, B] uniform in [0, 1) from default_rng(seed).random."""
+    return np.random.default_rng(seed).random((num_blocks, slots), dtype=np.float32)
+
+
+def make_temperatures(num_blocks: int, seed: int, greedy_every: int = 4) -> np.ndarray:
+    """Per-block sampling temperatures, float32 [N]: every greedy_every-th block
+    (block 0 first) is a greedy row (T = 0); the others draw T uniformly from
+    [0.5, 1.5) (the pages serve requests at their own temperature, T = 1
+    in their measurement)."""
+    rng = np.random.default_rng(seed)
+    t = rng.uniform(0.5, 1.5, size=num_blocks).astype(np.float32)
+    if greedy_every > 0:
+        t[::greedy_every] = 0.0
+    return t

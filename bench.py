@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
+    ap.add_argument("--rule", default="greedy", choices=["greedy", "exact", "sample"],
+                    help="commit rule: greedy walk (default), exact best path, or sampled commit "
+                         "(seeded per-block temperatures and per-slot uniforms)")
     ap.add_argument("--copy-probe-mib", type=float, default=0.0,
                     help="after the run, stream this many MiB through a plain copy kernel three "
                          "times (the known-size reference for HBM byte counters)")
@@ -95,7 +98,13 @@ def main():
     N, B, V, K = w.num_blocks, w.slots, w.vocab, w.topk
     H, F, de = w.hidden, w.ffn, w.d_e
     ldt = L.BF16 if w.dtype == "bf16" else L.F32
-    params = [L.make_params(N, ldt, weights, ws, w.alpha, True) for _ in range(1)]
+    rule_kw = {}
+    if args.rule == "sample":
+        rule_kw = {"temperature": torch.from_numpy(synth.make_temperatures(N, seed=1)).to(dev),
+                   "uniforms": torch.from_numpy(synth.make_uniforms(N, B, seed=2)).to(dev),
+                   "proposal": torch.empty((N, B, K), dtype=torch.float32, device=dev)}
+    params = [L.make_params(N, ldt, weights, ws, w.alpha, True, rule=args.rule, **rule_kw)
+              for _ in range(1)]
     lib = L.lib()
     state = {"i": 0}
 
@@ -236,7 +245,7 @@ def main():
         "config": {"workload": w.name, "num_blocks": N, "slots": B, "vocab": V, "topk": K,
                    "hidden": H, "heads": w.heads, "ffn": F, "d_e": de, "alpha": w.alpha,
                    "logits": f"{w.dtype} {w.recipe}", "weights": "seeded random (SplitMix64)",
-                   "graph": bool(args.graph), "rotating_logits_buffers": nbuf},
+                   "graph": bool(args.graph), "rotating_logits_buffers": nbuf, "rule": args.rule},
         "roofline": roof,
         "topk_hbm": {"achieved_GB_s": topk_gbs, "frac": topk_gbs / PEAK_HBM_GBS},
         "encoder_mfma": {"achieved_TFLOP_s": enc_flops / (enc_ms * 1e-3) / 1e12,
@@ -246,7 +255,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, args.rule)
     print(json.dumps(result), flush=True)
     if args.copy_probe_mib > 0:
         n = int(args.copy_probe_mib * 2 ** 20) // 4
@@ -449,8 +458,9 @@ def csrc_sha256():
     return h.hexdigest()
 
 
-def cpu_baseline(w, host, seconds):
-    """The oracle, untuned, on this host: repeated passes over the workload's blocks."""
+def cpu_baseline(w, host, seconds, rule="greedy"):
+    """The oracle, untuned, on this host: repeated passes over the workload's blocks
+    with the same commit rule (and, for sampling, the same temperatures and draws)."""
     import oracle
     import synth
     try:
@@ -459,11 +469,18 @@ def cpu_baseline(w, host, seconds):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     ow = oracle.OracleWeights(oracle.Dims(w.hidden, w.heads, w.ffn, w.d_e), w.vocab, synth.WEIGHTS_SEED)
-    oracle.rerank_block(host[0], w.topk, ow, w.alpha)   # generates the weights: excluded
+    temps = synth.make_temperatures(w.num_blocks, seed=1)
+    unif = synth.make_uniforms(w.num_blocks, w.slots, seed=2)
+
+    def one(b):
+        return oracle.rerank_block(host[b], w.topk, ow, w.alpha, rule=rule, temperature=float(temps[b]),
+                                   uniforms=unif[b])
+
+    one(0)   # generates the weights: excluded
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.rerank_block(host[n % host.shape[0]], w.topk, ow, w.alpha)
+        one(n % host.shape[0])
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or n >= 100000:

@@ -22,7 +22,10 @@ EPI_F32, EPI_BF16, EPI_SILU_BF16, EPI_RESID_F32 = 0, 1, 2, 3
 STAGE_TOPK, STAGE_NODE, STAGE_CONF_LINEAR = 0, 1, 2
 STAGE_QKV, STAGE_ATTENTION, STAGE_O, STAGE_FFN1, STAGE_FFN2 = 3, 4, 5, 6, 7
 STAGE_HEADS, STAGE_SCORES_WALK, STAGE_COUNT = 13, 14, 15
-ABI_VERSION = 1
+ABI_VERSION = 2
+# commit rules (lilicorr_rule)
+RULE_GREEDY, RULE_EXACT, RULE_SAMPLE = 0, 1, 2
+_RULES = {"greedy": RULE_GREEDY, "exact": RULE_EXACT, "sample": RULE_SAMPLE}
 MAX_SLOTS, MAX_TOPK, MAX_LATTICE = 64, 64, 512
 
 
@@ -57,7 +60,9 @@ class Params(ctypes.Structure):
                 ("dbg_inv", ctypes.c_void_p), ("dbg_cos", ctypes.c_void_p),
                 ("dbg_score", ctypes.c_void_p), ("dbg_gap", ctypes.c_void_p),
                 ("timing_stage", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
-                ("timing_end", ctypes.c_void_p)]
+                ("timing_end", ctypes.c_void_p),
+                ("rule", ctypes.c_int32), ("temperature", ctypes.c_void_p),
+                ("uniforms", ctypes.c_void_p), ("proposal", ctypes.c_void_p)]
 
 
 _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -74,6 +79,9 @@ _SIGNATURES = {
     "lilicorr_topk_lse": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp, _vp, _vp]),
     "lilicorr_pair_scores": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "lilicorr_greedy_walk": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _f, _c_int, _vp, _vp, _vp, _vp]),
+    "lilicorr_best_path": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _f, _c_int, _vp, _vp, _vp]),
+    "lilicorr_sample_path": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _f, _c_int, _vp, _vp, _vp, _vp,
+                                      _vp, _vp]),
     "lilicorr_linear_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "lilicorr_linear": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "lilicorr_rmsnorm": (_c_int, [_vp, _c_int, _c_int, _vp, _f, _vp, _vp]),
@@ -201,8 +209,13 @@ class Workspace:
 
 
 def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1.0, use_logp=True,
-                stream=None, dbg=None) -> Params:
+                stream=None, dbg=None, rule: str = "greedy", temperature=None, uniforms=None,
+                proposal=None) -> Params:
     p = Params()
+    p.rule = _RULES[rule]
+    p.temperature = _ptr(temperature)
+    p.uniforms = _ptr(uniforms)
+    p.proposal = _ptr(proposal)
     p.abi_version = ABI_VERSION
     p.num_blocks = N
     p.logits_dtype = logits_dtype
@@ -218,8 +231,12 @@ def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1
 
 
 def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool = True,
-           workspace: Workspace | None = None, debug: bool = False, out=None):
-    """Rerank [N, B, V] device logits; returns int32 tokens [N, B] (and debug tensors)."""
+           workspace: Workspace | None = None, debug: bool = False, out=None, rule: str = "greedy",
+           temperature=None, uniforms=None, proposal=None):
+    """Rerank [N, B, V] device logits; returns int32 tokens [N, B] (and debug tensors).
+
+    rule: "greedy", "exact" or "sample" (then temperature [N] and uniforms [N, B]
+    float32 device tensors are required; proposal [N, B, K] float32 is optional)."""
     torch = _torch()
     _require_cuda(logits, "logits")
     N, B, V = logits.shape
@@ -241,7 +258,8 @@ def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool 
             "score": torch.empty((N, B), dtype=torch.float32, device=dev),
             "gap": torch.empty((N, B), dtype=torch.float32, device=dev),
         }
-    p = make_params(N, _logits_dtype(logits), weights, workspace, alpha, use_logp, dbg=dbg)
+    p = make_params(N, _logits_dtype(logits), weights, workspace, alpha, use_logp, dbg=dbg, rule=rule,
+                    temperature=temperature, uniforms=uniforms, proposal=proposal)
     _check(lib().lilicorr_rerank(_ptr(logits), B, V, K, ctypes.byref(p), _ptr(out)), "rerank")
     return (out, dbg) if debug else out
 
@@ -249,7 +267,8 @@ def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool 
 def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
              weights_desc: WeightsDesc | None, workspace_ptr: int, workspace_nbytes: int,
              out_ptr: int, abi_version: int = ABI_VERSION, use_logp: int = 1,
-             timing: tuple[int, int, int] | None = None) -> int:
+             timing: tuple[int, int, int] | None = None, rule: int = RULE_GREEDY,
+             temperature_ptr: int = 0, uniforms_ptr: int = 0) -> int:
     """Host-only argument check of rerank (no GPU needed); returns the status code.
 
     timing = (stage, begin_event, end_event) as plain integers (handles are
@@ -263,6 +282,9 @@ def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
     p.weights = ctypes.pointer(weights_desc) if weights_desc is not None else None
     p.workspace = ctypes.c_void_p(workspace_ptr)
     p.workspace_bytes = workspace_nbytes
+    p.rule = rule
+    p.temperature = ctypes.c_void_p(temperature_ptr)
+    p.uniforms = ctypes.c_void_p(uniforms_ptr)
     if timing is not None:
         p.timing_stage, p.timing_begin, p.timing_end = timing[0], timing[1] or None, timing[2] or None
     return int(lib().lilicorr_validate(ctypes.c_void_p(logits_ptr), B, V, K, ctypes.byref(p),
@@ -310,6 +332,34 @@ def greedy_walk(topk_idx, topk_logp, cos, alpha: float = 1.0, use_logp: bool = T
                                       1 if use_logp else 0, _ptr(out), _ptr(score), _ptr(gap), _stream()),
            "greedy_walk")
     return out, score, gap
+
+
+def best_path(topk_idx, topk_logp, cos, alpha: float = 1.0, use_logp: bool = True):
+    """Exact best path over given scores; returns (tokens int32 [N,B], score float32 [N,B])."""
+    torch = _torch()
+    N, B, K = topk_idx.shape
+    dev = topk_idx.device
+    out = torch.empty((N, B), dtype=torch.int32, device=dev)
+    score = torch.empty((N, B), dtype=torch.float32, device=dev)
+    _check(lib().lilicorr_best_path(_ptr(topk_idx), _ptr(topk_logp), _ptr(cos), N, B, K, alpha,
+                                    1 if use_logp else 0, _ptr(out), _ptr(score), _stream()), "best_path")
+    return out, score
+
+
+def sample_path(topk_idx, topk_logp, cos, temperature, uniforms, alpha: float = 1.0,
+                use_logp: bool = True):
+    """Sampled commit over given scores; returns (tokens int32 [N,B],
+    proposal float32 [N,B,K], score float32 [N,B])."""
+    torch = _torch()
+    N, B, K = topk_idx.shape
+    dev = topk_idx.device
+    out = torch.empty((N, B), dtype=torch.int32, device=dev)
+    prop = torch.empty((N, B, K), dtype=torch.float32, device=dev)
+    score = torch.empty((N, B), dtype=torch.float32, device=dev)
+    _check(lib().lilicorr_sample_path(_ptr(topk_idx), _ptr(topk_logp), _ptr(cos), N, B, K, alpha,
+                                      1 if use_logp else 0, _ptr(temperature), _ptr(uniforms), _ptr(out),
+                                      _ptr(prop), _ptr(score), _stream()), "sample_path")
+    return out, prop, score
 
 
 def linear(A, W, bias=None, epilogue: int = EPI_F32, resid=None, workspace=None):

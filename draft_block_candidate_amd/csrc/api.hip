@@ -54,6 +54,30 @@ int check_device() {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LILICORR_OK : LILICORR_EHIP; }
 
+CommitRule commit_rule(const lilicorr_params& p) {
+  CommitRule r;
+  r.kind = p.rule;
+  r.alpha = p.alpha;
+  r.use_logp = p.use_logp;
+  r.temperature = p.temperature;
+  r.uniforms = p.uniforms;
+  r.proposal = p.proposal;
+  return r;
+}
+
+// Shared checks of the stand-alone commit entry points that run the fused
+// kernel on given cosines (its LDS holds one block's B-1 K x K matrices).
+int commit_args_ok(const int32_t* topk_idx, const float* topk_logp, const float* cos, int N, int B,
+                   int K, int use_logp, const int32_t* out_tokens) {
+  if (!topk_idx || !topk_logp || !out_tokens || (B > 1 && !cos)) return LILICORR_EINVAL;
+  if (N < 1 || B < 1 || B > LILICORR_MAX_SLOTS || K < 1 || K > LILICORR_MAX_TOPK ||
+      B * K > LILICORR_MAX_LATTICE)
+    return LILICORR_EINVAL;
+  if (use_logp != 0 && use_logp != 1) return LILICORR_EINVAL;
+  if (scores_walk_lds_bytes(B, K) > kScoresWalkMaxLds) return LILICORR_EUNSUPPORTED;
+  return LILICORR_OK;
+}
+
 #define LL_TRY(expr)                                \
   do {                                              \
     hipError_t _e = (expr);                         \
@@ -142,6 +166,10 @@ int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_pa
   const size_t need = rerank_ws_layout(p->num_blocks, B, V, K, w->dims).total;
   if (!p->workspace || p->workspace_bytes < need || ((uintptr_t)p->workspace & 255))
     return LILICORR_EWORKSPACE;
+  if (p->rule != LILICORR_RULE_GREEDY && p->rule != LILICORR_RULE_EXACT &&
+      p->rule != LILICORR_RULE_SAMPLE)
+    return LILICORR_EINVAL;
+  if (p->rule == LILICORR_RULE_SAMPLE && (!p->temperature || !p->uniforms)) return LILICORR_EINVAL;
   if ((p->timing_begin == nullptr) != (p->timing_end == nullptr)) return LILICORR_EINVAL;
   if (p->timing_begin && (p->timing_stage < 0 || p->timing_stage >= LILICORR_STAGE_COUNT))
     return LILICORR_EINVAL;
@@ -175,7 +203,6 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
   float* heads_v = (float*)(ws + L.heads);
   uint16_t* outv = p->dbg_outv ? p->dbg_outv : (uint16_t*)(ws + L.outv);
   uint16_t* inv = p->dbg_inv ? p->dbg_inv : (uint16_t*)(ws + L.inv);
-  float* cosb = p->dbg_cos ? p->dbg_cos : (float*)(ws + L.cos);
   float* gpart = (float*)(ws + L.gemm_part);
   // optional events around one stage (measurement only)
   const bool timing = p->timing_begin != nullptr;
@@ -239,16 +266,12 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
     LL_STAGE(LILICORR_STAGE_HEADS,
              LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st)));
   }
-  // a5: pair scores, a6: greedy walk (fused when the block's cosines fit in LDS)
+  // a5: pair scores, a6: the commit (one fused kernel: B * K <= 512 keeps the
+  // block's cosines within the kernel's LDS budget)
   LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, false));
-  if (scores_walk_lds_bytes(B, K) <= kScoresWalkMaxLds) {
-    LL_TRY(launch_scores_walk(outv, inv, topk_idx, topk_logp, N, B, K, de, p->alpha, p->use_logp,
-                              p->dbg_cos, out_tokens, p->dbg_score, p->dbg_gap, st));
-  } else {
-    LL_TRY(launch_pair_scores(outv, inv, N, B, K, de, cosb, st));
-    LL_TRY(launch_greedy_walk(topk_idx, topk_logp, cosb, N, B, K, p->alpha, p->use_logp,
-                              out_tokens, p->dbg_score, p->dbg_gap, st));
-  }
+  LL_TRY(launch_scores_walk(outv, inv, nullptr, topk_idx, topk_logp, N, B, K, de,
+                            commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score, p->dbg_gap,
+                            st));
   LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, true));
 #undef LL_STAGE
   return LILICORR_OK;
@@ -296,6 +319,41 @@ int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const 
   if (dc != LILICORR_OK) return dc;
   return hip_status(launch_greedy_walk(topk_idx, topk_logp, cos, N, B, K, alpha, use_logp,
                                        out_tokens, score, gap, (hipStream_t)stream));
+}
+
+int lilicorr_best_path(const int32_t* topk_idx, const float* topk_logp, const float* cos, int N,
+                       int B, int K, float alpha, int use_logp, int32_t* out_tokens, float* score,
+                       void* stream) {
+  const int a = commit_args_ok(topk_idx, topk_logp, cos, N, B, K, use_logp, out_tokens);
+  if (a != LILICORR_OK) return a;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  CommitRule r;
+  r.kind = RULE_EXACT;
+  r.alpha = alpha;
+  r.use_logp = use_logp;
+  return hip_status(launch_scores_walk(nullptr, nullptr, cos, topk_idx, topk_logp, N, B, K, 0, r,
+                                       nullptr, out_tokens, score, nullptr, (hipStream_t)stream));
+}
+
+int lilicorr_sample_path(const int32_t* topk_idx, const float* topk_logp, const float* cos, int N,
+                         int B, int K, float alpha, int use_logp, const float* temperature,
+                         const float* uniforms, int32_t* out_tokens, float* proposal, float* score,
+                         void* stream) {
+  const int a = commit_args_ok(topk_idx, topk_logp, cos, N, B, K, use_logp, out_tokens);
+  if (a != LILICORR_OK) return a;
+  if (!temperature || !uniforms) return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  CommitRule r;
+  r.kind = RULE_SAMPLE;
+  r.alpha = alpha;
+  r.use_logp = use_logp;
+  r.temperature = temperature;
+  r.uniforms = uniforms;
+  r.proposal = proposal;
+  return hip_status(launch_scores_walk(nullptr, nullptr, cos, topk_idx, topk_logp, N, B, K, 0, r,
+                                       nullptr, out_tokens, score, nullptr, (hipStream_t)stream));
 }
 
 size_t lilicorr_linear_workspace_bytes(int M, int Kd, int N) {

@@ -70,14 +70,26 @@ hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, u
 hipError_t launch_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
                               int d_e, float* cos, hipStream_t stream);
 
-// Fused a5 + a6 for the rerank path (cosines in LDS; cos_out may be null).
+// Commit rule of a6: greedy walk, exact best path, or sampled commit.
+enum CommitKind { RULE_GREEDY = 0, RULE_EXACT = 1, RULE_SAMPLE = 2 };
+struct CommitRule {
+  int kind = RULE_GREEDY;
+  float alpha = 1.f;
+  int use_logp = 1;
+  const float* temperature = nullptr;  // [N] (RULE_SAMPLE; T <= 0: greedy row)
+  const float* uniforms = nullptr;     // [N, B] in [0, 1) (RULE_SAMPLE)
+  float* proposal = nullptr;           // [N, B, K] (RULE_SAMPLE; may be null)
+};
+
+// Fused a5 + a6 (cosines in LDS; cos_out may be null). With cos_in set, the
+// cosines [N, B-1, K, K] are read instead of computed (outv/inv unused).
 // Needs scores_walk_lds_bytes(B, K) <= kScoresWalkMaxLds.
 constexpr size_t kScoresWalkMaxLds = 128 * 1024;
 size_t scores_walk_lds_bytes(int B, int K);
-hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const int32_t* topk_idx,
-                              const float* topk_logp, int N, int B, int K, int d_e, float alpha,
-                              int use_logp, float* cos_out, int32_t* out_tokens, float* score,
-                              float* gap, hipStream_t stream);
+hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const float* cos_in,
+                              const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
+                              int d_e, const CommitRule& rule, float* cos_out, int32_t* out_tokens,
+                              float* score, float* gap, hipStream_t stream);
 
 hipError_t launch_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos,
                               int N, int B, int K, float alpha, int use_logp, int32_t* out_tokens,

@@ -178,8 +178,7 @@ inline TopkWs topk_ws_layout(int rows, int V, int K) {
 
 // ---- rerank workspace ------------------------------------------------------
 struct RerankWs {
-  size_t topk, topk_idx, topk_logp, lse, x, hid, u, qkv, attn, heads, outv, inv, cos, score, gap,
-      gemm_part, total;
+  size_t topk, topk_idx, topk_logp, x, hid, u, qkv, attn, heads, outv, inv, gemm_part, total;
 };
 
 // Largest split-K scratch over the linear layers of one rerank call.
@@ -208,7 +207,6 @@ inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims
   w.topk = take(topk_ws_layout((int)rows, V, K).total);
   w.topk_idx = take(rows * K * 4);
   w.topk_logp = take(rows * K * 4);
-  w.lse = take(rows * 4);
   w.x = take(M * H * 4);
   w.hid = take(M * (F > H ? F : H) * 2);
   w.u = take(M * H * 2);
@@ -217,9 +215,6 @@ inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims
   w.heads = take(M * 2 * de * 4);
   w.outv = take(M * de * 2);
   w.inv = take(M * de * 2);
-  w.cos = take((size_t)N * (B > 1 ? B - 1 : 1) * K * K * 4);
-  w.score = take(rows * 4);
-  w.gap = take(rows * 4);
   w.gemm_part = take(rerank_gemm_scratch((int)M, d) * 4);
   w.total = off;
   return w;

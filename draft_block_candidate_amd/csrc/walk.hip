@@ -1,4 +1,4 @@
-// Pair scores and the greedy commit.
+// Pair scores and the commit rules.
 //
 // Pair scores (LiLiCorr paper, Eq. (1) and Section 3.5): for every adjacent
 // slot pair, cos_s = out_{s-1} . in_s^T over unit vectors, one K x K product
@@ -7,6 +7,11 @@
 // Greedy commit (Eq. (8); ties to the lower index as in the SGLang PR,
 // "Why the custom kernels"): one wave per block, lane j scores candidate j.
 // Only the walk is sequential, over slots.
+//
+// Exact best path (Appendix E, Eq. (12)) and sampled commit (SGLang PR,
+// "Sampling the committed path (opt-in)"): further rules of the fused kernel,
+// with the same per-step score z_s(i, j) = fl32(logp[s][j] + fl32(alpha *
+// cos_s[i][j])).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -103,24 +108,35 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
   }
 }
 
-// Fused pair scores + greedy commit for the rerank path: one workgroup per
-// block. The eight waves compute the block's B-1 K x K cosine matrices into LDS
-// (and to global memory when requested), then tabulate the walk's decision for
-// every (slot, previous candidate) pair; the sequential part is one LDS lookup
-// per slot.
+// Pair scores + commit for the rerank path: one workgroup per block. The
+// eight waves compute the block's B-1 K x K cosine matrices into LDS (and to
+// global memory when requested), or copy them from cos_in when the scores are
+// given. Then, by rule:
+//   RULE_GREEDY  tabulate the walk's decision for every (slot, previous
+//                candidate) pair; the sequential part is one LDS lookup per slot
+//   RULE_EXACT   the highest-scoring path (LiLiCorr paper, Appendix E, Eq. (12))
+//                by dynamic programming in wave 0, then the predecessor trace-back
+//   RULE_SAMPLE  (SGLang PR, opt-in sampled commit) tabulate, for every (slot,
+//                previous candidate) pair, the draw from softmax(z / T) with the
+//                slot's input uniform, then walk the table; blocks with T <= 0
+//                take the greedy table (the greedy path, bit for bit)
+template <int RULE>
 __global__ __launch_bounds__(512) void scores_walk_kernel(
     const uint16_t* __restrict__ outv, const uint16_t* __restrict__ inv,
-    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int B, int K,
-    int de, float alpha, int use_logp, float* __restrict__ cos_out,
-    int32_t* __restrict__ out_tokens, float* __restrict__ score, float* __restrict__ gap) {
+    const float* __restrict__ cos_in, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_logp, int B, int K, int de, float alpha, int use_logp,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms,
+    float* __restrict__ proposal, float* __restrict__ cos_out, int32_t* __restrict__ out_tokens,
+    float* __restrict__ score, float* __restrict__ gap) {
   extern __shared__ float sm[];
   const int KK = K * K;
   float* s_cos = sm;                                // [(B-1) K K]
   float* s_logp = sm + (B - 1) * KK;                // [B K]
   int* s_idx = (int*)(s_logp + B * K);              // [B K]
-  int* s_tc = s_idx + B * K;                        // [(B-1) K] walk table: choice
-  float* s_tz = (float*)(s_tc + (B - 1) * K);       // [(B-1) K] its score
-  float* s_tg = s_tz + (B - 1) * K;                 // [(B-1) K] its gap
+  int* s_tc = s_idx + B * K;                        // [(B-1) K] table: choice (EXACT: predecessor)
+  float* s_tz = (float*)(s_tc + (B - 1) * K);       // [(B-1) K] its score (SAMPLE: the row max)
+  float* s_tg = s_tz + (B - 1) * K;                 // [(B-1) K] its gap (SAMPLE: the row's exp sum)
+  int* s_path = (int*)(s_tg + (B - 1) * K);         // [B] committed candidates
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = blockIdx.x;
   const int64_t base = n * B * K;
@@ -129,103 +145,210 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
     s_idx[i] = topk_idx[base + i];
   }
   const int nw = blockDim.x >> 6;
-  for (int p = wave; p < B - 1; p += nw) {
-    const uint16_t* o = outv + (base + (int64_t)p * K) * de;
-    const uint16_t* in = inv + (base + (int64_t)(p + 1) * K) * de;
-    pair_matrix(o, in, K, de, lane, [&](int ra, int b, float v) {
-      s_cos[p * KK + ra * K + b] = v;
-      if (cos_out) cos_out[(n * (B - 1) + p) * KK + ra * K + b] = v;
-    });
+  if (cos_in) {
+    const float* src = cos_in + n * (int64_t)(B - 1) * KK;
+    for (int i = tid; i < (B - 1) * KK; i += blockDim.x) s_cos[i] = src[i];
+  } else {
+    for (int p = wave; p < B - 1; p += nw) {
+      const uint16_t* o = outv + (base + (int64_t)p * K) * de;
+      const uint16_t* in = inv + (base + (int64_t)(p + 1) * K) * de;
+      pair_matrix(o, in, K, de, lane, [&](int ra, int b, float v) {
+        s_cos[p * KK + ra * K + b] = v;
+        if (cos_out) cos_out[(n * (B - 1) + p) * KK + ra * K + b] = v;
+      });
+    }
   }
   __syncthreads();
-  // Walk table: for every slot s >= 1 and every candidate c of slot s - 1, the
-  // choice the walk makes at s when it stands on c, with its score and the
-  // gap to the runner-up. Entries are independent, so all threads build them;
-  // the largest score wins and the lowest index breaks a tie. The arithmetic
-  // is the walk's own (fl32, no contraction), so the table holds exactly the
-  // decisions the walk takes.
+  // z_s(i, j): the walk's own arithmetic (fl32, no contraction)
+  auto zval = [&](int s, int i, int j) {
+    const float term = __fmul_rn(alpha, s_cos[(s - 1) * KK + i * K + j]);
+    return use_logp ? __fadd_rn(s_logp[s * K + j], term) : term;
+  };
+  const float T = RULE == RULE_SAMPLE ? temperature[n] : 0.f;
+  const bool draw = RULE == RULE_SAMPLE && T > 0.f;   // uniform over the workgroup
+  const float inv_t = draw ? 1.0f / T : 0.f;
   const int NE = (B - 1) * K;
-  for (int e = tid; e < NE; e += blockDim.x) {
-    const int s = e / K + 1, cp = e - (s - 1) * K;
-    const float* crow = s_cos + (s - 1) * KK + cp * K;
-    const float* lrow = s_logp + s * K;
-    float best = -INFINITY, second = -INFINITY;
-    int bj = K;
-    // neighbouring entries start their scans at different j (their rows are
-    // K floats apart, so equal j would hit a few LDS banks); the comparison
-    // is on the full (score, lower index) key, so the order does not matter
-    // (eight at a time, all eight pairs of reads issued before any is used)
-    for (int jj0 = 0; jj0 < K; jj0 += 8) {
-      float cv[8], lv[8];
-      int jv[8];
+  if (RULE == RULE_GREEDY || (RULE == RULE_SAMPLE && !draw)) {
+    // Walk table: for every slot s >= 1 and every candidate c of slot s - 1,
+    // the choice the walk makes at s when it stands on c, with its score and
+    // the gap to the runner-up. Entries are independent, so all threads build
+    // them; the largest score wins and the lowest index breaks a tie.
+    for (int e = tid; e < NE; e += blockDim.x) {
+      const int s = e / K + 1, cp = e - (s - 1) * K;
+      const float* crow = s_cos + (s - 1) * KK + cp * K;
+      const float* lrow = s_logp + s * K;
+      float best = -INFINITY, second = -INFINITY;
+      int bj = K;
+      // neighbouring entries start their scans at different j (their rows are
+      // K floats apart, so equal j would hit a few LDS banks); the comparison
+      // is on the full (score, lower index) key, so the order does not matter
+      // (eight at a time, all eight pairs of reads issued before any is used)
+      for (int jj0 = 0; jj0 < K; jj0 += 8) {
+        float cv[8], lv[8];
+        int jv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        int j = cp + min(jj0 + u, K - 1);
-        j = j >= K ? j - K : j;
-        jv[u] = j;
-        cv[u] = crow[j];
-        lv[u] = lrow[j];
+        for (int u = 0; u < 8; ++u) {
+          int j = cp + min(jj0 + u, K - 1);
+          j = j >= K ? j - K : j;
+          jv[u] = j;
+          cv[u] = crow[j];
+          lv[u] = lrow[j];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float term = __fmul_rn(alpha, cv[u]);
+          const float z = use_logp ? __fadd_rn(lv[u], term) : term;
+          const int j = jv[u];
+          const bool better = (jj0 + u < K) & ((z > best) | ((z == best) & (j < bj)));
+          second = (jj0 + u < K) ? (better ? best : fmaxf(second, z)) : second;
+          best = better ? z : best;
+          bj = better ? j : bj;
+        }
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float term = __fmul_rn(alpha, cv[u]);
-        const float z = use_logp ? __fadd_rn(lv[u], term) : term;
-        const int j = jv[u];
-        const bool better = (jj0 + u < K) & ((z > best) | ((z == best) & (j < bj)));
-        second = (jj0 + u < K) ? (better ? best : fmaxf(second, z)) : second;
-        best = better ? z : best;
-        bj = better ? j : bj;
+      s_tc[e] = bj < K ? bj : 0;   // bj == K only if every score is NaN; keeps the walk in range
+      s_tz[e] = best;
+      s_tg[e] = K > 1 ? __fsub_rn(best, second) : 0.f;
+    }
+  } else if (draw) {
+    // Sample table: the row maximum m, the float32 sum S of e_j =
+    // exp((z_j - m) / T) in ascending j, and the draw: the number of
+    // cumulative sums C_j <= u_s * S (the smallest j whose cumulative
+    // probability exceeds u_s), at most K - 1.
+    for (int e = tid; e < NE; e += blockDim.x) {
+      const int s = e / K + 1, cp = e - (s - 1) * K;
+      float m = -INFINITY;
+      for (int j = 0; j < K; ++j) m = fmaxf(m, zval(s, cp, j));
+      float S = 0.f;
+      for (int j = 0; j < K; ++j) S = __fadd_rn(S, __expf(__fmul_rn(__fsub_rn(zval(s, cp, j), m), inv_t)));
+      const float target = __fmul_rn(uniforms[n * B + s], S);
+      float C = 0.f;
+      int cnt = 0;
+      for (int j = 0; j < K; ++j) {
+        C = __fadd_rn(C, __expf(__fmul_rn(__fsub_rn(zval(s, cp, j), m), inv_t)));
+        cnt += C <= target ? 1 : 0;
+      }
+      s_tc[e] = min(cnt, K - 1);
+      s_tz[e] = m;
+      s_tg[e] = S;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t r0 = n * B;
+    int choice = 0;
+    float my_score = s_logp[0], my_gap = 0.f;
+    if (RULE == RULE_EXACT) {
+      // G in lane j: the best float32 total of a path ending at candidate j of
+      // slot s (left-to-right sums); s_tc[(s-2) K + j] its predecessor. The
+      // predecessor scan runs i upward and keeps the first maximum.
+      const int j = lane < K ? lane : K - 1;
+      float G = (lane < K && B > 1) ? zval(1, 0, j) : -INFINITY;
+      for (int s = 2; s < B; ++s) {
+        float best = -INFINITY;
+        int bi = 0;
+        const float lj = s_logp[s * K + j];
+        const float* ccol = s_cos + (s - 1) * KK + j;
+        for (int i = 0; i < K; ++i) {
+          const float term = __fmul_rn(alpha, ccol[i * K]);
+          const float z = use_logp ? __fadd_rn(lj, term) : term;
+          const float cand = __fadd_rn(readlane_f(G, i), z);
+          const bool better = cand > best;
+          best = better ? cand : best;
+          bi = better ? i : bi;
+        }
+        if (lane < K) s_tc[(s - 2) * K + lane] = bi;
+        G = lane < K ? best : -INFINITY;
+      }
+      if (B > 1) {
+        // best final candidate, lowest index on a tie, then the trace-back
+        float gv = G;
+        int c = lane;
+        lanes_argmax(gv, c, K <= 16 ? 16 : (K <= 32 ? 32 : 64));
+        c = c < K ? c : 0;
+        choice = lane == B - 1 ? c : choice;
+        for (int s = B - 1; s >= 2; --s) {
+          c = s_tc[(s - 2) * K + c];
+          choice = lane == s - 1 ? c : choice;
+        }
+      }
+    } else {
+      // the walk proper: one table lookup per slot, starting from slot 0's top
+      // candidate; step s's results are kept in lane s and written after the loop
+      int c = 0;
+      for (int s = 1; s < B; ++s) {
+        const int e = (s - 1) * K + c;
+        const int nc = s_tc[e];
+        choice = lane == s ? nc : choice;
+        if (RULE == RULE_GREEDY || !draw) {
+          my_score = lane == s ? s_tz[e] : my_score;
+          my_gap = lane == s ? s_tg[e] : my_gap;
+        }
+        c = nc;
       }
     }
-    s_tc[e] = bj < K ? bj : 0;   // bj == K only if every score is NaN; keeps the walk in range
-    s_tz[e] = best;
-    s_tg[e] = K > 1 ? __fsub_rn(best, second) : 0.f;
+    if (RULE == RULE_EXACT || draw) {
+      // score of the committed candidate at each slot along the path
+      const int prev = __shfl(choice, lane > 0 ? lane - 1 : 0);
+      if (lane >= 1 && lane < B) my_score = zval(lane, prev, choice);
+    }
+    if (lane < B) {
+      out_tokens[r0 + lane] = s_idx[lane * K + choice];
+      if (score) score[r0 + lane] = my_score;
+      if (gap) gap[r0 + lane] = my_gap;
+      s_path[lane] = choice;
+    }
   }
-  __syncthreads();
-  if (wave != 0) return;
-  // The walk proper: one table lookup per slot, starting from slot 0's top
-  // candidate. Step s's choice, score and gap are kept in lane s and written
-  // after the loop.
-  const int64_t r0 = n * B;
-  int choice = 0;
-  float my_score = s_logp[0], my_gap = 0.f;
-  int c = 0;
-  for (int s = 1; s < B; ++s) {
-    const int e = (s - 1) * K + c;
-    const int nc = s_tc[e];
-    const float z = s_tz[e], gz = s_tg[e];
-    choice = lane == s ? nc : choice;
-    my_score = lane == s ? z : my_score;
-    my_gap = lane == s ? gz : my_gap;
-    c = nc;
-  }
-  if (lane < B) {
-    out_tokens[r0 + lane] = s_idx[lane * K + choice];
-    if (score) score[r0 + lane] = my_score;
-    if (gap) gap[r0 + lane] = my_gap;
+  if (RULE == RULE_SAMPLE && proposal) {
+    // the distribution each slot was drawn from: softmax(z / T) of the row the
+    // path stood on (one-hot for slot 0 and for greedy rows)
+    __syncthreads();
+    for (int t = tid; t < B * K; t += blockDim.x) {
+      const int s = t / K, j = t - s * K;
+      float q;
+      if (s == 0 || !draw) {
+        q = j == s_path[s] ? 1.f : 0.f;
+      } else {
+        const int cp = s_path[s - 1], e = (s - 1) * K + cp;
+        q = __expf(__fmul_rn(__fsub_rn(zval(s, cp, j), s_tz[e]), inv_t)) / s_tg[e];
+      }
+      proposal[base + t] = q;
+    }
   }
 }
 
 }  // namespace
 
 size_t scores_walk_lds_bytes(int B, int K) {
-  return ((size_t)(B - 1) * K * K + 2 * (size_t)B * K + 3 * (size_t)(B - 1) * K) * 4;
+  return ((size_t)(B - 1) * K * K + 2 * (size_t)B * K + 3 * (size_t)(B - 1) * K + B) * 4;
 }
 
-hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const int32_t* topk_idx,
-                              const float* topk_logp, int N, int B, int K, int d_e, float alpha,
-                              int use_logp, float* cos_out, int32_t* out_tokens, float* score,
-                              float* gap, hipStream_t stream) {
+hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const float* cos_in,
+                              const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
+                              int d_e, const CommitRule& rule, float* cos_out, int32_t* out_tokens,
+                              float* score, float* gap, hipStream_t stream) {
   const size_t lds = scores_walk_lds_bytes(B, K);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)scores_walk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        kScoresWalkMaxLds);
+    hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_GREEDY>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
+    hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_EXACT>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
+    hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_SAMPLE>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
     attr_set = true;
   }
-  hipLaunchKernelGGL(scores_walk_kernel, dim3((unsigned)N), dim3(512), lds, stream, outv, inv,
-                     topk_idx, topk_logp, B, K, d_e, alpha, use_logp, cos_out, out_tokens, score,
-                     gap);
+#define LL_SW(R)                                                                                  \
+  hipLaunchKernelGGL(scores_walk_kernel<R>, dim3((unsigned)N), dim3(512), lds, stream, outv, inv, \
+                     cos_in, topk_idx, topk_logp, B, K, d_e, rule.alpha, rule.use_logp,           \
+                     rule.temperature, rule.uniforms, rule.proposal, cos_out, out_tokens, score,  \
+                     gap)
+  if (rule.kind == RULE_EXACT)
+    LL_SW(RULE_EXACT);
+  else if (rule.kind == RULE_SAMPLE)
+    LL_SW(RULE_SAMPLE);
+  else
+    LL_SW(RULE_GREEDY);
+#undef LL_SW
   return hipGetLastError();
 }
 

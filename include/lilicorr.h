@@ -44,7 +44,7 @@ extern "C" {
 #define LILICORR_API
 #endif
 
-#define LILICORR_ABI_VERSION 1u
+#define LILICORR_ABI_VERSION 2u
 #define LILICORR_MAX_SLOTS 64     /* B: slots per block */
 #define LILICORR_MAX_TOPK 64      /* K: candidates per slot (one per wave lane) */
 #define LILICORR_MAX_LATTICE 512  /* T = B*K tokens per block */
@@ -59,6 +59,21 @@ typedef enum {
 } lilicorr_status;
 
 typedef enum { LILICORR_F32 = 0, LILICORR_BF16 = 1 } lilicorr_dtype;
+
+/* Commit rule of the last step (all three score a step alike:
+ * z_s(i, j) = fl32(logp[s][j] + fl32(alpha * cos_s[i][j])), or fl32(alpha * cos_s[i][j])
+ * when use_logp = 0; slot 0 commits its top candidate, c_0 = 0).
+ *   GREEDY  LiLiCorr paper, Section 3.5, Eq. (8): c_s = lowest j maximising z_s(c_{s-1}, j).
+ *   EXACT   Appendix E, Eq. (12): the path maximising g(c) = sum_s z_s(c_{s-1}, c_s), summed
+ *           left to right in fp32 and found by dynamic programming; every maximum (best
+ *           predecessor, best final candidate) takes the lowest index, so among equal totals
+ *           the path smallest when read from the last slot backward is returned.
+ *   SAMPLE  SGLang PR, "Sampling the committed path (opt-in)": block n draws slot s from
+ *           softmax(z_s(c_{s-1}, .) / T_n) by inverse CDF with the caller's uniform u[n, s]:
+ *           c_s = number of cumulative sums C_j <= u * S (S the fp32 sum of the exps in
+ *           ascending j), at most K - 1. Blocks with T_n <= 0 are greedy rows: the GREEDY
+ *           path bit for bit, with one-hot proposals. */
+typedef enum { LILICORR_RULE_GREEDY = 0, LILICORR_RULE_EXACT = 1, LILICORR_RULE_SAMPLE = 2 } lilicorr_rule;
 
 /* Encoder geometry. LiLiCorr paper, Appendix A "Architecture" and Table 4:
  * a two-layer bidirectional transformer of width `hidden` with `heads`
@@ -131,10 +146,20 @@ typedef struct {
   int32_t timing_stage;
   void* timing_begin;
   void* timing_end;
+  /* Commit rule (lilicorr_rule). For LILICORR_RULE_SAMPLE:
+   *   temperature  device float [N]     per-block temperature (<= 0: greedy row), required
+   *   uniforms     device float [N, B]  draws in [0, 1), slot 0 unused, required
+   *   proposal     device float [N, B, K] distribution each slot was drawn from (may be NULL)
+   * Other rules ignore the three pointers. dbg_score then holds z along the committed path;
+   * dbg_gap is the runner-up gap for greedy steps and 0 for exact or drawn steps. */
+  int32_t rule;
+  const float* temperature;
+  const float* uniforms;
+  float* proposal;
 } lilicorr_params;
 
 /* The whole reranking path (LiLiCorr paper, Section 3.5 "Single-pass
- * decoding"; spec commit rule with alpha, see greedy_walk below).
+ * decoding"; commit by p->rule, see lilicorr_rule).
  *   logits      device, [N, B, V] row-major (V contiguous), dtype p->logits_dtype
  *   B, V, K     slots per block (1..64), vocabulary (K..2^31-1), candidates (1..64), B*K <= 512
  *   out_tokens  device int32 [N, B]: committed vocabulary id per slot
@@ -205,6 +230,25 @@ LILICORR_API int lilicorr_pair_scores(const uint16_t* outv, const uint16_t* inv,
 LILICORR_API int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos, int N,
                          int B, int K, float alpha, int use_logp, int32_t* out_tokens,
                          float* score, float* gap, void* stream);
+
+/* Exact best path over given scores (LiLiCorr paper, Appendix E, Eq. (12); LILICORR_RULE_EXACT).
+ *   topk_idx int32 / topk_logp float [N,B,K], cos float [N,B-1,K,K] (device)
+ *   out_tokens int32 [N,B]; score float [N,B] (device, may be NULL): z along the path.
+ * B * K <= 512. Errors: EINVAL, EUNSUPPORTED, EHIP. */
+LILICORR_API int lilicorr_best_path(const int32_t* topk_idx, const float* topk_logp, const float* cos,
+                                    int N, int B, int K, float alpha, int use_logp,
+                                    int32_t* out_tokens, float* score, void* stream);
+
+/* Sampled commit over given scores (SGLang PR, "Sampling the committed path (opt-in)" and
+ * lilicorr_sample_path; LILICORR_RULE_SAMPLE). Arguments as lilicorr_best_path, plus
+ *   temperature device float [N] (<= 0: greedy row), uniforms device float [N,B] in [0, 1),
+ *   proposal device float [N,B,K] (may be NULL): softmax(z / T) each slot was drawn from.
+ * B * K <= 512. Errors: EINVAL, EUNSUPPORTED, EHIP. */
+LILICORR_API int lilicorr_sample_path(const int32_t* topk_idx, const float* topk_logp,
+                                      const float* cos, int N, int B, int K, float alpha,
+                                      int use_logp, const float* temperature,
+                                      const float* uniforms, int32_t* out_tokens, float* proposal,
+                                      float* score, void* stream);
 
 /* One linear layer on MFMA: Y[M,N] = A[M,Kd] . W[N,Kd]^T + bias[N], bf16
  * inputs, fp32 accumulation, then the epilogue:

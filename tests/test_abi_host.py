@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("lilicorr_rerank", "lilicorr_validate", "lilicorr_workspace_bytes",
                  "lilicorr_weights_bytes", "lilicorr_weights_init", "lilicorr_strerror",
-                 "lilicorr_topk_lse", "lilicorr_greedy_walk", "lilicorr_pair_scores"):
+                 "lilicorr_topk_lse", "lilicorr_greedy_walk", "lilicorr_pair_scores",
+                 "lilicorr_best_path", "lilicorr_sample_path"):
         assert must in names
 
 
@@ -60,7 +61,8 @@ DIMS = L.EncoderDims(64, 2, 256, 32)
 def _good(**over):
     args = dict(logits_ptr=1 << 20, N=1, B=16, V=1024, K=4, logits_dtype=L.F32, vocab=1024,
                 dims=DIMS, wptr=1 << 24, wbytes=None, ws=1 << 28, wsbytes=None, out=1 << 12,
-                abi=L.ABI_VERSION, use_logp=1, weights=True, timing=None)
+                abi=L.ABI_VERSION, use_logp=1, weights=True, timing=None, rule=L.RULE_GREEDY,
+                temp=0, unif=0)
     args.update(over)
     wb = args["wbytes"] if args["wbytes"] is not None else L.weights_bytes(args["dims"], args["vocab"])
     desc = L.WeightsDesc(args["dims"].c(), args["vocab"], 42, ctypes.c_void_p(args["wptr"]), wb) if args["weights"] else None
@@ -68,14 +70,15 @@ def _good(**over):
     if wsb is None:
         wsb = L.workspace_bytes(args["N"], args["B"], args["V"], args["K"], DIMS)
     return L.validate(args["logits_ptr"], args["N"], args["B"], args["V"], args["K"], args["logits_dtype"],
-                      desc, args["ws"], wsb, args["out"], args["abi"], args["use_logp"], args["timing"])
+                      desc, args["ws"], wsb, args["out"], args["abi"], args["use_logp"], args["timing"],
+                      args["rule"], args["temp"], args["unif"])
 
 
 @pytest.mark.parametrize("over,code", [
     ({}, L.OK),
     ({"logits_ptr": 0}, L.EINVAL),
     ({"out": 0}, L.EINVAL),
-    ({"abi": 2}, L.EINVAL),
+    ({"abi": 1}, L.EINVAL),                                        # layout before the commit rules
     ({"N": 0}, L.EINVAL),
     ({"B": 0}, L.EINVAL),
     ({"B": 65}, L.EINVAL),
@@ -103,6 +106,14 @@ def _good(**over):
     ({"timing": (-1, 0x1000, 0x2000)}, L.EINVAL),
     ({"timing": (L.STAGE_TOPK, 0x1000, 0)}, L.EINVAL),             # one event only
     ({"timing": (99, 0, 0)}, L.OK),                                # no events: stage ignored
+    ({"rule": L.RULE_EXACT}, L.OK),
+    ({"rule": L.RULE_EXACT, "temp": 0x3000}, L.OK),                # sampling inputs ignored
+    ({"rule": 3}, L.EINVAL),
+    ({"rule": -1}, L.EINVAL),
+    ({"rule": L.RULE_SAMPLE, "temp": 0x3000, "unif": 0x4000}, L.OK),
+    ({"rule": L.RULE_SAMPLE}, L.EINVAL),                           # temperatures and uniforms required
+    ({"rule": L.RULE_SAMPLE, "temp": 0x3000}, L.EINVAL),
+    ({"rule": L.RULE_SAMPLE, "unif": 0x4000}, L.EINVAL),
 ])
 def test_validate_status_codes(over, code):
     assert _good(**over) == code

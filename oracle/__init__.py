@@ -23,6 +23,8 @@ Parity status per part (pins live in the test suite, marked ``not gpu``):
   * synthetic weights: pinned to the published SplitMix64 test vector.
   * exact best path (paper, Appendix E): pinned (brute force over every path
     of tiny lattices, hand-worked fixtures, never below the greedy total).
+  * vocabulary-sharded top-K / log-partition: pinned (equal to the unsplit
+    definition for any shard count, ties across shard boundaries, constant rows).
   * sampled commit (PR, opt-in sampling): pinned (hand-worked draws at an
     exact boundary, chi-square of draw frequencies against scipy's softmax,
     greedy rows equal to the greedy walk, vanishing temperature).
@@ -34,5 +36,6 @@ from .topk_lse import topk_lse_row, topk_lse  # noqa: F401
 from .encoder import encode_block  # noqa: F401
 from .scores import pair_scores  # noqa: F401
 from .walk import greedy_walk, WalkResult  # noqa: F401
+from .sharded import shard_bounds, shard_partial, merge_partials, topk_lse_sharded_row  # noqa: F401
 from .paths import best_path, sample_path, path_total, PathResult, SampleResult  # noqa: F401
 from .rerank import rerank_block, BlockResult  # noqa: F401

@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--rule", default="greedy", choices=["greedy", "exact", "sample"],
                     help="commit rule: greedy walk (default), exact best path, or sampled commit "
                          "(seeded per-block temperatures and per-slot uniforms)")
+    ap.add_argument("--topk-shards", type=int, default=0,
+                    help="also time the vocabulary-sharded top-K at G shards: one shard's kernel on its "
+                         "[rows, V/G] slice (cold, rotating copies) and the merge of G shard outputs")
     ap.add_argument("--copy-probe-mib", type=float, default=0.0,
                     help="after the run, stream this many MiB through a plain copy kernel three "
                          "times (the known-size reference for HBM byte counters)")
@@ -254,6 +257,10 @@ def main():
         "wall_s_timed": wall,
     }
 
+    if args.topk_shards > 0:
+        result["topk_sharded"] = bench_topk_shards(L, w, bufs[0].view(N * B, V), args.topk_shards,
+                                                   args.rotate_mib, max(args.steps, 20), stream)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, args.rule)
     print(json.dumps(result), flush=True)
@@ -264,6 +271,57 @@ def main():
         for _ in range(3):
             torch.neg(src, out=dst)    # reads and writes n * 4 bytes once each
         torch.cuda.synchronize()
+
+
+def bench_topk_shards(L, w, logits2d, G, rotate_mib, reps, stream):
+    """Time the split-vocabulary top-K: the shard kernel on one shard's slice
+    (the work one GPU of a G-way tensor-parallel head does) and the merge of the
+    G shard outputs, each bracketed by events on the library's stream."""
+    import math
+    import torch
+    rows, V = logits2d.shape
+    K = w.topk
+    dev = logits2d.device
+    # contiguous split of the vocabulary, the first V % G shards one longer
+    base, extra = divmod(V, G)
+    edges = [0]
+    for g in range(G):
+        edges.append(edges[-1] + base + (1 if g < extra else 0))
+    bounds = list(zip(edges[:-1], edges[1:]))
+    val = torch.empty((G, rows, K), dtype=torch.float32, device=dev)
+    idx = torch.empty((G, rows, K), dtype=torch.int32, device=dev)
+    ms = torch.empty((G, rows, 2), dtype=torch.float32, device=dev)
+    for g, (lo, hi) in enumerate(bounds):
+        L.topk_shard(logits2d[:, lo:hi].contiguous(), K, lo, out=(val[g], idx[g], ms[g]))
+    lo, hi = bounds[0]
+    sl = logits2d[:, lo:hi].contiguous()
+    nrot = max(1, math.ceil(rotate_mib * 2 ** 20 / (sl.numel() * sl.element_size())))
+    slices = [sl] + [sl.clone() for _ in range(nrot - 1)]
+    nbytes = int(L.lib().lilicorr_topk_shard_workspace_bytes(rows, hi - lo, K))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    outs = (torch.empty((rows, K), dtype=torch.float32, device=dev),
+            torch.empty((rows, K), dtype=torch.int32, device=dev),
+            torch.empty((rows, 2), dtype=torch.float32, device=dev))
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    shard_us = timed(lambda i: L.topk_shard(slices[i % nrot], K, lo, out=outs, workspace=ws))
+    merge_us = timed(lambda i: L.topk_merge(val, idx, ms))
+    by = rows * (hi - lo) * logits2d.element_size()
+    return {"shards": G, "shard_shape": [rows, hi - lo], "shard_us": shard_us,
+            "shard_GB_s": by / (shard_us * 1e-6) / 1e9, "shard_frac": by / (shard_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "merge_us": merge_us, "note": "one shard's kernel (cold input) and the merge of G shard "
+                                          "outputs; the all-gather between GPUs is not run (one GPU)"}
 
 
 def set_timing(params, sid, begin=None, end=None):

@@ -77,6 +77,10 @@ _SIGNATURES = {
     "lilicorr_strerror": (ctypes.c_char_p, [_c_int]),
     "lilicorr_topk_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "lilicorr_topk_lse": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp, _vp, _vp]),
+    "lilicorr_topk_shard_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "lilicorr_topk_shard": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp, _vp,
+                                     _vp]),
+    "lilicorr_topk_merge": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "lilicorr_pair_scores": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "lilicorr_greedy_walk": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _f, _c_int, _vp, _vp, _vp, _vp]),
     "lilicorr_best_path": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _f, _c_int, _vp, _vp, _vp]),
@@ -306,6 +310,43 @@ def topk_lse(logits2d, K: int):
     _check(lib().lilicorr_topk_lse(_ptr(logits2d), rows, V, K, _logits_dtype(logits2d), _ptr(ws), nbytes,
                                    _ptr(idx), _ptr(logp), _ptr(lse), _stream()), "topk_lse")
     return idx, logp, lse
+
+
+def topk_shard(logits2d, K: int, id_offset: int, out=None, workspace=None):
+    """One shard of a split vocabulary: [rows, V_shard] device logits holding ids
+    id_offset.. -> (values f32 [rows, K], global ids i32 [rows, K], (m, s) f32 [rows, 2]).
+    out: optional (values, ids, ms) views to write into (e.g. slices of stacked buffers)."""
+    torch = _torch()
+    _require_cuda(logits2d, "logits")
+    rows, V = logits2d.shape
+    dev = logits2d.device
+    nbytes = int(lib().lilicorr_topk_shard_workspace_bytes(rows, V, K))
+    if nbytes == 0:
+        raise LilicorrError(EINVAL, "topk_shard_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = (torch.empty((rows, K), dtype=torch.float32, device=dev),
+               torch.empty((rows, K), dtype=torch.int32, device=dev),
+               torch.empty((rows, 2), dtype=torch.float32, device=dev))
+    val, idx, ms = out
+    _check(lib().lilicorr_topk_shard(_ptr(logits2d), rows, V, K, _logits_dtype(logits2d), id_offset,
+                                     _ptr(workspace), workspace.numel(), _ptr(val), _ptr(idx), _ptr(ms),
+                                     _stream()), "topk_shard")
+    return val, idx, ms
+
+
+def topk_merge(val, idx, ms):
+    """Merge stacked shard outputs [G, rows, K] / [G, rows, 2] -> (ids, logp, lse)."""
+    torch = _torch()
+    G, rows, K = val.shape
+    dev = val.device
+    tidx = torch.empty((rows, K), dtype=torch.int32, device=dev)
+    logp = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _check(lib().lilicorr_topk_merge(_ptr(val), _ptr(idx), _ptr(ms), G, rows, K, _ptr(tidx), _ptr(logp),
+                                     _ptr(lse), _stream()), "topk_merge")
+    return tidx, logp, lse
 
 
 def pair_scores(outv, inv):

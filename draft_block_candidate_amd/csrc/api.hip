@@ -296,6 +296,42 @@ int lilicorr_topk_lse(const void* logits, int rows, int V, int K, int dtype, voi
                                     topk_idx, topk_logp, lse, (hipStream_t)stream));
 }
 
+size_t lilicorr_topk_shard_workspace_bytes(int rows, int V_shard, int K) {
+  return lilicorr_topk_workspace_bytes(rows, V_shard, K);
+}
+
+int lilicorr_topk_shard(const void* logits, int rows, int V_shard, int K, int dtype, int id_offset,
+                        void* workspace, size_t workspace_bytes, float* part_val,
+                        int32_t* part_idx, float* part_ms, void* stream) {
+  if (!logits || !part_val || !part_idx || !part_ms) return LILICORR_EINVAL;
+  if (rows < 1 || K < 1 || K > LILICORR_MAX_TOPK || V_shard < K) return LILICORR_EINVAL;
+  if ((int64_t)rows * 64 > ((int64_t)1 << 31)) return LILICORR_EINVAL;
+  if (id_offset < 0 || (int64_t)id_offset + V_shard > (int64_t)INT32_MAX) return LILICORR_EINVAL;
+  if (dtype != LILICORR_F32 && dtype != LILICORR_BF16) return LILICORR_EUNSUPPORTED;
+  if ((uintptr_t)logits & 15) return LILICORR_EINVAL;
+  const TopkWs TL = topk_ws_layout(rows, V_shard, K);
+  if (!workspace || workspace_bytes < TL.total || ((uintptr_t)workspace & 255))
+    return LILICORR_EWORKSPACE;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  char* w = (char*)workspace;
+  return hip_status(launch_topk_shard(logits, rows, V_shard, K, dtype, id_offset,
+                                      (float*)(w + TL.part_val), (int32_t*)(w + TL.part_idx),
+                                      (float*)(w + TL.part_ms), part_val, part_idx, part_ms,
+                                      (hipStream_t)stream));
+}
+
+int lilicorr_topk_merge(const float* part_val, const int32_t* part_idx, const float* part_ms, int G,
+                        int rows, int K, int32_t* topk_idx, float* topk_logp, float* lse,
+                        void* stream) {
+  if (!part_val || !part_idx || !part_ms || !topk_idx || !topk_logp) return LILICORR_EINVAL;
+  if (G < 1 || G > 64 || rows < 1 || K < 1 || K > LILICORR_MAX_TOPK) return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  return hip_status(launch_topk_merge_shards(G, rows, K, part_val, part_idx, part_ms, topk_idx,
+                                             topk_logp, lse, (hipStream_t)stream));
+}
+
 int lilicorr_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K, int d_e,
                          float* cos, void* stream) {
   if (!outv || !inv || !cos) return LILICORR_EINVAL;

@@ -15,6 +15,20 @@ hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype
                            int32_t* part_idx, float* part_ms, int32_t* topk_idx, float* topk_logp,
                            float* lse, hipStream_t stream);
 
+// a1 over one shard of a split vocabulary: the shard's [rows, V] slice holds
+// ids id_offset .. id_offset + V - 1. Outputs per row the shard's K best
+// (value, global id) pairs and its (max, sum of exp(x - max)) pair:
+// out_val/out_idx [rows, K], out_ms [rows, 2]; part_* are chunk scratch of
+// topk_ws_layout(rows, V, K).
+hipError_t launch_topk_shard(const void* logits, int rows, int V, int K, int dtype, int id_offset,
+                             float* part_val, int32_t* part_idx, float* part_ms, float* out_val,
+                             int32_t* out_idx, float* out_ms, hipStream_t stream);
+// Merge of G shard outputs stacked [G, rows, K] / [G, rows, 2] (shards in
+// ascending order of their id ranges) into topk_idx, topk_logp, lse.
+hipError_t launch_topk_merge_shards(int G, int rows, int K, const float* val, const int32_t* idx,
+                                    const float* ms, int32_t* topk_idx, float* topk_logp,
+                                    float* lse, hipStream_t stream);
+
 // a2: node features, confidence MLP layer 1 and the embedding/slot/rank sum.
 //   hid  bf16 [M, H] = bf16(silu(W1c f + b1c));  xbase float [M, H] = (E[tok] + S[s]) + R[j]
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,

@@ -146,7 +146,10 @@ inline WeightPtrs weight_ptrs(const lilicorr_weights& w) {
 // chunks to give the GPU about kTopkTargetWaves waves, each chunk at least
 // kTopkMinChunk elements, and at most 64 chunks per row (the merge assigns one
 // lane per chunk).
-constexpr int kTopkTargetWaves = 4096;
+#ifndef LL_TOPK_TARGET_WAVES
+#define LL_TOPK_TARGET_WAVES 4096
+#endif
+constexpr int kTopkTargetWaves = LL_TOPK_TARGET_WAVES;
 constexpr int64_t kTopkMinChunk = 2048;
 
 inline int topk_chunks_per_row(int rows, int V) {

@@ -274,6 +274,7 @@ __device__ __forceinline__ void consume_group(State& st, const u32x4_t (&w)[NV],
 template <int DT, int NV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_partial_kernel(const void* __restrict__ logits,
                                                            int rows, int V, int K, int P,
+                                                           int id_offset, int final_out,
                                                            float* __restrict__ part_val,
                                                            int32_t* __restrict__ part_idx,
                                                            float* __restrict__ part_ms,
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (unit == P - 1 && tail_len > 0) do_edge(a1, tail_len);
 
   const float S = wave_sum(st.s);
-  if (P == 1) {
+  if (P == 1 && final_out) {
     // the row is one chunk: its sorted list is the answer
     const float lse = st.ref + logf(S);
     if (lane < K) {
@@ -377,11 +378,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     if (lse_out != nullptr && lane == 0) lse_out[row] = lse;
     return;
   }
-  // Chunk outputs: sorted list and (reference max, sum) of the wave.
+  // Chunk outputs: sorted list (ids shifted to the caller's numbering) and
+  // (reference max, sum) of the wave.
   const int64_t o = (int64_t)row * P + unit;
   if (lane < K) {
     part_val[o * K + lane] = st.lv;
-    part_idx[o * K + lane] = st.li;
+    part_idx[o * K + lane] = st.li == kInvalid ? kInvalid : st.li + id_offset;
   }
   if (lane == 0) {
     part_ms[2 * o] = st.ref;
@@ -391,8 +393,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 
 // One wave per row: combine the P chunk lists (tournament) and (max, sum)
 // pairs. The row's P * K partial entries are staged in LDS first, so each of
-// the K tournament steps reads the winner's next entry from LDS.
-__global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
+// the K tournament steps reads the winner's next entry from LDS. Entry k of
+// list p of a row sits at p * sp + row * sr + k (values and ids) and its
+// (max, sum) pair at 2 * (p * mp + row * mr): the chunks of one row are
+// [rows, P, K]; the shards of a split vocabulary are [P, rows, K]. Lists must
+// be in ascending order of their id ranges. PARTIAL_OUT writes the merged
+// list and the combined (max, sum) pair instead of (ids, logp, lse).
+template <bool PARTIAL_OUT>
+__global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P, int64_t sp, int64_t sr,
+                                                        int64_t mp, int64_t mr,
                                                         const float* __restrict__ part_val,
                                                         const int32_t* __restrict__ part_idx,
                                                         const float* __restrict__ part_ms,
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
   int* si = (int*)(sm + P * K);         // [P K]
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
-  const int64_t rbase = (int64_t)row * P * K;
+  const int64_t rbase = (int64_t)row * sr;
   const int n = P * K;
   // Eight entries per lane per batch, every load issued before the first
   // is used (indices clamped to the row, duplicates written twice with the
@@ -415,8 +424,13 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = min(i0 + j * 64 + lane, n - 1);
-      bv[j] = part_val[rbase + i];
-      bi[j] = part_idx[rbase + i];
+      int64_t a = rbase + i;         // lists of a row contiguous (sp == K)
+      if (sp != K) {
+        const int p = i / K;
+        a = rbase + p * sp + (i - p * K);
+      }
+      bv[j] = part_val[a];
+      bi[j] = part_idx[a];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -426,8 +440,8 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
     }
   }
   const int pl = min(lane, P - 1);
-  float m = part_ms[2 * ((int64_t)row * P + pl)];
-  float s = part_ms[2 * ((int64_t)row * P + pl) + 1];
+  float m = part_ms[2 * (pl * mp + row * mr)];
+  float s = part_ms[2 * (pl * mp + row * mr) + 1];
   if (lane >= P) {
     m = kMInit;
     s = 0.f;
@@ -463,6 +477,18 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
     hv = adv ? (more ? nv : -INFINITY) : hv;
     hi = adv ? (more ? ni : kInvalid) : hi;
   }
+  if (PARTIAL_OUT) {
+    // topk_logp receives the merged values, lse_out the (max, sum) pair
+    if (lane < K) {
+      topk_idx[(int64_t)row * K + lane] = ri;
+      topk_logp[(int64_t)row * K + lane] = rv;
+    }
+    if (lane == 0) {
+      lse_out[2 * (int64_t)row] = M;
+      lse_out[2 * (int64_t)row + 1] = S;
+    }
+    return;
+  }
   if (lane < K) {
     topk_idx[(int64_t)row * K + lane] = ri;
     topk_logp[(int64_t)row * K + lane] = __fsub_rn(rv, lse);
@@ -472,22 +498,61 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P,
 
 }  // namespace
 
-hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype, float* part_val,
-                           int32_t* part_idx, float* part_ms, int32_t* topk_idx, float* topk_logp,
-                           float* lse, hipStream_t stream) {
-  const int P = topk_chunks_per_row(rows, V);
+namespace {
+
+hipError_t launch_partial(const void* logits, int rows, int V, int K, int dtype, int P, int id_offset,
+                          int final_out, float* part_val, int32_t* part_idx, float* part_ms,
+                          int32_t* topk_idx, float* topk_logp, float* lse, hipStream_t stream) {
   const int64_t waves = (int64_t)rows * P;
   const unsigned blocks = (unsigned)((waves + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL((topk_partial_kernel<1, 4>), dim3(blocks), dim3(256), 0, stream, logits,
-                       rows, V, K, P, part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
+                       rows, V, K, P, id_offset, final_out, part_val, part_idx, part_ms, topk_idx,
+                       topk_logp, lse);
   else
     hipLaunchKernelGGL((topk_partial_kernel<0, 4>), dim3(blocks), dim3(256), 0, stream, logits,
-                       rows, V, K, P, part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
-  hipError_t e = hipGetLastError();
+                       rows, V, K, P, id_offset, final_out, part_val, part_idx, part_ms, topk_idx,
+                       topk_logp, lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype, float* part_val,
+                           int32_t* part_idx, float* part_ms, int32_t* topk_idx, float* topk_logp,
+                           float* lse, hipStream_t stream) {
+  const int P = topk_chunks_per_row(rows, V);
+  hipError_t e = launch_partial(logits, rows, V, K, dtype, P, 0, 1, part_val, part_idx, part_ms,
+                                topk_idx, topk_logp, lse, stream);
   if (e != hipSuccess || P == 1) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(64), (size_t)P * K * 8, stream,
-                     rows, K, P, part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
+  hipLaunchKernelGGL(topk_merge_kernel<false>, dim3((unsigned)rows), dim3(64), (size_t)P * K * 8,
+                     stream, rows, K, P, (int64_t)K, (int64_t)P * K, (int64_t)1, (int64_t)P,
+                     part_val, part_idx, part_ms, topk_idx, topk_logp, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_shard(const void* logits, int rows, int V, int K, int dtype, int id_offset,
+                             float* part_val, int32_t* part_idx, float* part_ms, float* out_val,
+                             int32_t* out_idx, float* out_ms, hipStream_t stream) {
+  const int P = topk_chunks_per_row(rows, V);
+  if (P == 1)   // one chunk per row: its list and (max, sum) are the shard's output
+    return launch_partial(logits, rows, V, K, dtype, 1, id_offset, 0, out_val, out_idx, out_ms,
+                          nullptr, nullptr, nullptr, stream);
+  hipError_t e = launch_partial(logits, rows, V, K, dtype, P, id_offset, 0, part_val, part_idx,
+                                part_ms, nullptr, nullptr, nullptr, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_kernel<true>, dim3((unsigned)rows), dim3(64), (size_t)P * K * 8,
+                     stream, rows, K, P, (int64_t)K, (int64_t)P * K, (int64_t)1, (int64_t)P,
+                     part_val, part_idx, part_ms, out_idx, out_val, out_ms);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_merge_shards(int G, int rows, int K, const float* val, const int32_t* idx,
+                                    const float* ms, int32_t* topk_idx, float* topk_logp,
+                                    float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_merge_kernel<false>, dim3((unsigned)rows), dim3(64), (size_t)G * K * 8,
+                     stream, rows, K, G, (int64_t)rows * K, (int64_t)K, (int64_t)rows, (int64_t)1,
+                     val, idx, ms, topk_idx, topk_logp, lse);
   return hipGetLastError();
 }
 

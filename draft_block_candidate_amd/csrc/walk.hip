@@ -329,12 +329,12 @@ hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const f
   const size_t lds = scores_walk_lds_bytes(B, K);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_GREEDY>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
-    hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_EXACT>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
-    hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_SAMPLE>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
+    (void)hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_GREEDY>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
+    (void)hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_EXACT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
+    (void)hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_SAMPLE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
     attr_set = true;
   }
 #define LL_SW(R)                                                                                  \

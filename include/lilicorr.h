@@ -215,6 +215,34 @@ LILICORR_API int lilicorr_topk_lse(const void* logits, int rows, int V, int K, i
                       size_t workspace_bytes, int32_t* topk_idx, float* topk_logp, float* lse,
                       void* stream);
 
+/* Top-K of a vocabulary split across shards (a tensor-parallel LM head; the SGLang PR's
+ * top-K + log-partition of "Why the custom kernels" for tp > 1): each shard reduces its
+ * slice, then one merge over the shards' outputs gives lilicorr_topk_lse's result for
+ * the whole rows (ids exactly; lse and logp to float32 rounding).
+ *
+ * Shard side. logits device [rows, V_shard] holds vocabulary ids id_offset ..
+ * id_offset + V_shard - 1 of each row (K <= V_shard). Outputs (device, caller-owned):
+ *   part_val  float [rows, K]  the slice's K best values, (value desc, id asc)
+ *   part_idx  int32 [rows, K]  their global ids (id_offset added)
+ *   part_ms   float [rows, 2]  (m, s): a reference m and s = sum_v exp(x_v - m) in fp32,
+ *                              so the slice's log-partition is m + log s
+ *   workspace device, >= lilicorr_topk_shard_workspace_bytes(rows, V_shard, K)
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP. */
+LILICORR_API size_t lilicorr_topk_shard_workspace_bytes(int rows, int V_shard, int K);
+LILICORR_API int lilicorr_topk_shard(const void* logits, int rows, int V_shard, int K, int dtype,
+                                     int id_offset, void* workspace, size_t workspace_bytes,
+                                     float* part_val, int32_t* part_idx, float* part_ms,
+                                     void* stream);
+
+/* Merge side. The G shard outputs stacked as part_val/part_idx [G, rows, K] and
+ * part_ms [G, rows, 2] (device), the shards in ascending order of their id ranges (all
+ * ids of shard g below those of shard g + 1), G in 1..64 -> topk_idx int32 [rows, K],
+ * topk_logp float [rows, K], lse float [rows] (may be NULL), as lilicorr_topk_lse.
+ * Errors: EINVAL, EHIP. */
+LILICORR_API int lilicorr_topk_merge(const float* part_val, const int32_t* part_idx,
+                                     const float* part_ms, int G, int rows, int K,
+                                     int32_t* topk_idx, float* topk_logp, float* lse, void* stream);
+
 /* Pair scores (LiLiCorr paper, Eq. (1) and Section 3.5: one product per
  * adjacent slot pair, batched over the block).
  *   outv, inv  device bf16 bits [N, B, K, d_e]; cos device float [N, B-1, K, K]. */

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     for must in ("lilicorr_rerank", "lilicorr_validate", "lilicorr_workspace_bytes",
                  "lilicorr_weights_bytes", "lilicorr_weights_init", "lilicorr_strerror",
                  "lilicorr_topk_lse", "lilicorr_greedy_walk", "lilicorr_pair_scores",
-                 "lilicorr_best_path", "lilicorr_sample_path"):
+                 "lilicorr_best_path", "lilicorr_sample_path", "lilicorr_topk_shard",
+                 "lilicorr_topk_merge"):
         assert must in names
 
 

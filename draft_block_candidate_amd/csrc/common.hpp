@@ -151,6 +151,42 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// The value held by lane (lane ^ j), j in {1, 2, 4, 8, 16, 32}, without the
+// LDS crossbar: quad permutes for 1 and 2, a row shift each way for 4 and 8
+// (each lane keeps the one that stays in its 16-lane row), and the gfx950
+// row-swap permutes for 16 and 32. Lane layout of the swaps (measured): with
+// both operands v, permlane16_swap returns {v of lane l - 16 on odd rows,
+// own on even rows} and {v of lane l + 16 on even rows, own on odd rows};
+// permlane32_swap likewise for the halves. j must fold to a constant (call
+// from fully unrolled loops); every lane must take part.
+__device__ __forceinline__ int xor_lane(int v, int j, int lane) {
+  switch (j) {
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    case 4: {
+      const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+      const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0xf, false);  // row_shl:4
+      return (lane & 4) ? dn : up;
+    }
+    case 8: {
+      const int dn = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+      const int up = __builtin_amdgcn_update_dpp(0, v, 0x108, 0xf, 0xf, false);  // row_shl:8
+      return (lane & 8) ? dn : up;
+    }
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+      return (int)((lane & 16) ? r[0] : r[1]);
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+      return (int)((lane & 32) ? r[0] : r[1]);
+    }
+  }
+}
+__device__ __forceinline__ float xor_lane(float v, int j, int lane) {
+  return __int_as_float(xor_lane(__float_as_int(v), j, lane));
+}
+
 // SiLU with the hardware exponential and reciprocal (v_exp_f32, v_rcp_f32;
 // about 1 ulp each): the result is rounded to bfloat16 by every caller.
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }

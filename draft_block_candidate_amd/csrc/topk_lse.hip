@@ -163,7 +163,8 @@ __device__ __forceinline__ void rebase(State& st, const u32x4_t (&w0)[NV], float
 }
 
 // Seed the list from a group: the 64 lanes' best elements, bitonic-sorted
-// (descending key); the first K become the list. Returns this lane's best id
+// (descending key; lane exchanges by DPP and row-swap permutes, no LDS); the
+// first K become the list. Returns this lane's best id
 // (to be skipped by the candidate scan: inside the list it would be a
 // duplicate, outside it fails the strict key test anyway).
 template <int NV, int EPV, int LS>
@@ -186,8 +187,8 @@ __device__ __forceinline__ int seed_list(State& st, const u32x4_t (&w)[NV], int 
   for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const float ov = __shfl_xor(sv, j, 64);
-      const int oi = __shfl_xor(si, j, 64);
+      const float ov = xor_lane(sv, j, lane);
+      const int oi = xor_lane(si, j, lane);
       const bool keep_better = ((lane & j) == 0) == ((lane & k) == 0);
       const bool swap = keep_better != key_gt(sv, si, ov, oi);
       sv = swap ? ov : sv;

@@ -248,13 +248,21 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
         int bi = 0;
         const float lj = s_logp[s * K + j];
         const float* ccol = s_cos + (s - 1) * KK + j;
-        for (int i = 0; i < K; ++i) {
-          const float term = __fmul_rn(alpha, ccol[i * K]);
-          const float z = use_logp ? __fadd_rn(lj, term) : term;
-          const float cand = __fadd_rn(readlane_f(G, i), z);
-          const bool better = cand > best;
-          best = better ? cand : best;
-          bi = better ? i : bi;
+        // eight predecessors at a time, their eight LDS reads issued together
+        for (int i0 = 0; i0 < K; i0 += 8) {
+          float cv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cv[u] = ccol[min(i0 + u, K - 1) * K];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u;   // < 64: i0 <= 56 since K <= 64
+            const float term = __fmul_rn(alpha, cv[u]);
+            const float z = use_logp ? __fadd_rn(lj, term) : term;
+            const float cand = __fadd_rn(readlane_f(G, i), z);
+            const bool better = (i < K) & (cand > best);
+            best = better ? cand : best;
+            bi = better ? i : bi;
+          }
         }
         if (lane < K) s_tc[(s - 2) * K + lane] = bi;
         G = lane < K ? best : -INFINITY;

@@ -21,6 +21,10 @@ Parity status per part (pins live in the test suite, marked ``not gpu``):
     torch build from library routines. The trained head of the paper is not
     published, so no printed value pins the encoder's outputs.
   * synthetic weights: pinned to the published SplitMix64 test vector.
+  * the paper's own head (drafter hidden state, target fusion, anchor out
+    vector): pinned by an independent float64 torch build and closed forms
+    (constant fusion output, zero target projection, hand-worked anchor vector,
+    the anchor slot's candidates leaving the lattice untouched).
   * exact best path (paper, Appendix E): pinned (brute force over every path
     of tiny lattices, hand-worked fixtures, never below the greedy total).
   * vocabulary-sharded top-K / log-partition: pinned (equal to the unsplit
@@ -38,4 +42,5 @@ from .scores import pair_scores  # noqa: F401
 from .walk import greedy_walk, WalkResult  # noqa: F401
 from .sharded import shard_bounds, shard_partial, merge_partials, topk_lse_sharded_row  # noqa: F401
 from .paths import best_path, sample_path, path_total, PathResult, SampleResult  # noqa: F401
+from .paper_head import encode_block_paper  # noqa: F401
 from .rerank import rerank_block, BlockResult  # noqa: F401

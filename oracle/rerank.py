@@ -12,6 +12,7 @@ import numpy as np
 
 from .topk_lse import topk_lse
 from .encoder import encode_block
+from .paper_head import encode_block_paper
 from .scores import pair_scores
 from .walk import greedy_walk, WalkResult
 from .paths import best_path, sample_path, PathResult, SampleResult
@@ -41,13 +42,18 @@ class BlockResult:
 
 def rerank_block(logits_block: np.ndarray, K: int, w: OracleWeights, alpha: float = 1.0,
                  use_logp: bool = True, trace: dict | None = None, rule: str = "greedy",
-                 temperature: float = 0.0, uniforms=None) -> BlockResult:
+                 temperature: float = 0.0, uniforms=None, hidden=None, target=None) -> BlockResult:
     """logits_block: [B, V] float32 values or uint16 bfloat16 bit patterns.
 
     rule: "greedy" (Eq. (8)), "exact" (best path, Appendix E) or "sample"
-    (draws from softmax(z / temperature) with the given per-slot uniforms)."""
+    (draws from softmax(z / temperature) with the given per-slot uniforms).
+    With the paper's head (w.dims.paper_head) hidden [B, H_d] and target [H_t]
+    are the block's drafter hidden states and target state (bf16 values)."""
     idx, logp, lse = topk_lse(logits_block, K)
-    outv, inv = encode_block(idx, logp, w, trace)
+    if w.dims.paper_head:
+        outv, inv = encode_block_paper(idx, logp, hidden, target, w, trace)
+    else:
+        outv, inv = encode_block(idx, logp, w, trace)
     cos = pair_scores(outv, inv)
     walk = greedy_walk(idx, logp, cos, alpha, use_logp)
     res = BlockResult(idx, logp, lse, outv, inv, cos, walk)

@@ -52,6 +52,14 @@ class Dims:
     ffn: int
     d_e: int
     layers: int = 2
+    # widths of the inputs of the paper's own head (0: the lattice head without
+    # a drafter or a target, whose node embeds the token with E)
+    target_hidden: int = 0      # H_t: target embedding and target-state width
+    drafter_hidden: int = 0     # H_d: drafter hidden-state width
+
+    @property
+    def paper_head(self) -> bool:
+        return self.target_hidden > 0
 
 
 # Slot and rank tables are sized for the largest supported block (64 slots,
@@ -67,8 +75,8 @@ def _scale(fan_in: int) -> float:
 def weight_table(d: Dims, vocab: int):
     """List of (tensor id, name, shape, scale, kind) with kind in bf16/f32/gamma."""
     H, F, h, de = d.hidden, d.ffn, d.heads, d.d_e
-    t = [
-        (0, "E", (vocab, H), 1.0, "bf16"),
+    t = [] if d.paper_head else [(0, "E", (vocab, H), 1.0, "bf16")]
+    t += [
         (1, "S", (TABLE_ROWS, H), 1.0, "bf16"),
         (2, "R", (TABLE_ROWS, H), 1.0, "bf16"),
         (3, "conf_w1", (H, 5), _scale(5), "bf16"),
@@ -99,6 +107,26 @@ def weight_table(d: Dims, vocab: int):
         (51, "w_in", (de, H), _scale(H), "bf16"),
         (52, "b_in", (de,), _scale(H), "f32"),
     ]
+    if d.paper_head:
+        # LiLiCorr paper, Appendix A "Architecture": the target's frozen input
+        # embedding projected down, the drafter hidden state projected down,
+        # the target state normalised and projected, the concat fusion layer
+        # and the anchor's out head.
+        Ht, Hd = d.target_hidden, d.drafter_hidden
+        t += [
+            (56, "E_t", (vocab, Ht), 1.0, "bf16"),
+            (57, "w_emb", (H, Ht), _scale(Ht), "bf16"),
+            (58, "b_emb", (H,), _scale(Ht), "f32"),
+            (59, "w_hid", (H, Hd), _scale(Hd), "bf16"),
+            (60, "b_hid", (H,), _scale(Hd), "f32"),
+            (61, "gamma_t", (Ht,), 0.0, "gamma"),
+            (62, "w_tgt", (H, Ht), _scale(Ht), "bf16"),
+            (63, "b_tgt", (H,), _scale(Ht), "f32"),
+            (64, "w_fuse", (H, 3 * H), _scale(3 * H), "bf16"),
+            (65, "b_fuse", (H,), _scale(3 * H), "f32"),
+            (66, "w_anchor", (de, H), _scale(H), "bf16"),
+            (67, "b_anchor", (de,), _scale(H), "f32"),
+        ]
     return t
 
 
@@ -155,18 +183,18 @@ class OracleWeights:
     def __getitem__(self, name: str) -> np.ndarray:
         if name in self._overrides:
             return np.asarray(self._overrides[name], dtype=np.float64)
-        if name == "E":
-            raise KeyError("use embedding_rows() for the token embedding table")
+        if name in ("E", "E_t"):
+            raise KeyError("use embedding_rows() for the token embedding tables")
         if name not in self._cache:
             t, shape, scale, kind = self._spec[name]
             n = int(np.prod(shape))
             self._cache[name] = generate_all(t, scale, kind, self.seed, n).reshape(shape)
         return self._cache[name]
 
-    def embedding_rows(self, tokens: np.ndarray) -> np.ndarray:
-        if "E" in self._overrides:
-            return np.asarray(self._overrides["E"], dtype=np.float64)[np.asarray(tokens)]
-        t, shape, scale, kind = self._spec["E"]
+    def embedding_rows(self, tokens: np.ndarray, table: str = "E") -> np.ndarray:
+        if table in self._overrides:
+            return np.asarray(self._overrides[table], dtype=np.float64)[np.asarray(tokens)]
+        t, shape, scale, kind = self._spec[table]
         H = shape[1]
         tok = np.asarray(tokens, dtype=np.uint64).reshape(-1, 1)
         elems = tok * np.uint64(H) + np.arange(H, dtype=np.uint64).reshape(1, -1)

@@ -37,6 +37,10 @@ class Workload:
     temperatures: tuple = field(default=(1.0,))
     alpha: float = 1.0
     layers: int = 2
+    use_logp: bool = True
+    # the paper's own head (drafter hidden states and a target state as inputs)
+    target_hidden: int = 0
+    drafter_hidden: int = 0
 
     @property
     def tokens_per_block(self) -> int:
@@ -65,8 +69,19 @@ WORKLOADS = {
     # many-token node-build path with a ragged last block), 15 slots, a width
     # above 2048 and d_h = 128.
     "odd_h2560": Workload("odd_h2560", 41, 15, 4096, 7, 2560, 20, 512, 128, "bf16", "spiked"),
+    # The paper's own head (LiLiCorr paper, Table 4: width 1024, 8 heads, FFN
+    # 2048, d_e 1024, sigma = 8 with the sigma * cos rule; drafter and target
+    # widths of a Qwen3-8B target, 4096), with a small CPU-checkable twin.
+    "paper_tiny": Workload("paper_tiny", 1, 16, 1024, 4, 64, 2, 128, 32, "f32", "normal",
+                           alpha=8.0, use_logp=False, target_hidden=128, drafter_hidden=128),
+    "paper_qwen3_8b": Workload("paper_qwen3_8b", 1, 16, 151936, 8, 1024, 8, 2048, 1024, "bf16",
+                               "spiked", alpha=8.0, use_logp=False, target_hidden=4096,
+                               drafter_hidden=4096),
+    "paper_c32": Workload("paper_c32", 32, 16, 151936, 8, 1024, 8, 2048, 1024, "bf16", "spiked",
+                          alpha=8.0, use_logp=False, target_hidden=4096, drafter_hidden=4096),
 }
-WORKLOADS_ORDER = ["tiny", "c1_qwen3_8b", "c32", "c256_k16", "entropy_k32", "odd_h2560"]
+WORKLOADS_ORDER = ["tiny", "c1_qwen3_8b", "c32", "c256_k16", "entropy_k32", "odd_h2560",
+                   "paper_tiny", "paper_qwen3_8b", "paper_c32"]
 
 
 def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:
@@ -162,3 +177,16 @@ def make_temperatures(num_blocks: int, seed: int, greedy_every: int = 4) -> np.n
     if greedy_every > 0:
         t[::greedy_every] = 0.0
     return t
+
+
+def make_head_inputs(w: Workload, tier: int = 0, num_blocks: int | None = None):
+    """Inputs of the paper's own head, as bfloat16 bit patterns:
+    hidden [N, B, H_d] (the drafter's hidden state per slot) and target
+    [N, H_t] (the target state behind the last committed token), both
+    standard normal from default_rng(logits_seed(tier) + 500), hidden first;
+    a prefix of blocks is the same at any N."""
+    n = w.num_blocks if num_blocks is None else num_blocks
+    rng = np.random.default_rng(w.logits_seed(tier) + 500)
+    hidden = rng.standard_normal((w.num_blocks, w.slots, w.drafter_hidden), dtype=np.float32)
+    target = rng.standard_normal((w.num_blocks, w.target_hidden), dtype=np.float32)
+    return f32_to_bf16_bits_rne(hidden[:n]), f32_to_bf16_bits_rne(target[:n])

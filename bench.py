@@ -94,8 +94,14 @@ def main():
     if w.dtype == "bf16":
         first = first.view(torch.bfloat16)
     bufs = [first] + [first.clone() for _ in range(nbuf - 1)]
-    dims = L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e)
+    dims = L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e, target_hidden=w.target_hidden,
+                         drafter_hidden=w.drafter_hidden)
     weights = L.Weights(dims, w.vocab, synth.WEIGHTS_SEED, device=dev)
+    head_kw = {}
+    if w.target_hidden > 0:     # the paper's head: drafter hidden states and target states
+        hid_bits, tgt_bits = synth.make_head_inputs(w)
+        head_kw = {"hidden": torch.from_numpy(hid_bits.view(np.int16)).to(dev),
+                   "target": torch.from_numpy(tgt_bits.view(np.int16)).to(dev)}
     ws = L.Workspace(w.num_blocks, w.slots, w.vocab, w.topk, dims, device=dev)
     out = torch.empty((w.num_blocks, w.slots), dtype=torch.int32, device=dev)
     N, B, V, K = w.num_blocks, w.slots, w.vocab, w.topk
@@ -106,7 +112,7 @@ def main():
         rule_kw = {"temperature": torch.from_numpy(synth.make_temperatures(N, seed=1)).to(dev),
                    "uniforms": torch.from_numpy(synth.make_uniforms(N, B, seed=2)).to(dev),
                    "proposal": torch.empty((N, B, K), dtype=torch.float32, device=dev)}
-    params = [L.make_params(N, ldt, weights, ws, w.alpha, True, rule=args.rule, **rule_kw)
+    params = [L.make_params(N, ldt, weights, ws, w.alpha, w.use_logp, rule=args.rule, **rule_kw, **head_kw)
               for _ in range(1)]
     lib = L.lib()
     state = {"i": 0}
@@ -247,6 +253,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "num_blocks": N, "slots": B, "vocab": V, "topk": K,
                    "hidden": H, "heads": w.heads, "ffn": F, "d_e": de, "alpha": w.alpha,
+                   "use_logp": bool(w.use_logp), "head": "paper" if w.target_hidden else "lattice",
+                   "target_hidden": w.target_hidden, "drafter_hidden": w.drafter_hidden,
                    "logits": f"{w.dtype} {w.recipe}", "weights": "seeded random (SplitMix64)",
                    "graph": bool(args.graph), "rotating_logits_buffers": nbuf, "rule": args.rule},
         "roofline": roof,
@@ -352,26 +360,43 @@ def stage_work(w, sid):
     """Algorithmic bytes and flops of one stage for one call over the workload."""
     N, B, V, K = w.num_blocks, w.slots, w.vocab, w.topk
     H, F, de, h = w.hidden, w.ffn, w.d_e, w.heads
-    rows, T = N * B, B * K
-    M = rows * K
+    Ht, Hd = w.target_hidden, w.drafter_hidden
+    paper = Ht > 0
+    rows = N * B
+    Bl = B - 1 if paper else B           # slots in the lattice
+    T = Bl * K
+    M = N * T                            # lattice rows
     es = 2 if w.dtype == "bf16" else 4
 
-    def lin(kd, n, a_b, out_b, resid=False, norm_out=False):
-        by = M * kd * a_b + n * kd * 2 + n * 4 + M * n * out_b
+    def lin(kd, n, a_b, out_b, resid=False, norm_out=False, m=None):
+        m = M if m is None else m
+        by = m * kd * a_b + n * kd * 2 + n * 4 + m * n * out_b
         if resid:
-            by += M * n * 4          # residual read (the write is out_b)
+            by += m * n * 4          # residual read (the write is out_b)
         if norm_out:
-            by += M * n * 2          # bf16 RMSNorm output
-        return {"bytes": by, "flops": 2 * M * n * kd}
+            by += m * n * 2          # bf16 RMSNorm output
+        return {"bytes": by, "flops": 2 * m * n * kd}
+
+    def add(*parts):
+        return {"bytes": sum(p["bytes"] for p in parts), "flops": sum(p["flops"] for p in parts)}
 
     layer = sid - 3
     if sid == 0:
         return {"bytes": rows * V * es + rows * (8 * K + 4), "flops": 0}
-    if sid == 1:   # E rows, S/R tables, first confidence layer; writes x (f32), hid (bf16)
-        return {"bytes": M * H * 2 + 2 * 64 * H * 2 + H * (5 * 2 + 4) + M * 8 + M * H * (4 + 2),
+    if sid == 1:
+        # slot/rank tables, first confidence layer; writes x (f32), hid (bf16)
+        node = {"bytes": 2 * 64 * H * 2 + H * (5 * 2 + 4) + M * 8 + M * H * (4 + 2),
                 "flops": 2 * M * H * 5 + 4 * M * H}
+        if not paper:
+            node["bytes"] += M * H * 2       # E rows
+            return node
+        # projected drafter states (read per node) and the gathered E_t rows
+        node["bytes"] += M * H * 4 + 2 * M * Ht * 2
+        return add(lin(Hd, H, 2, 4, m=rows), node)
     if sid == 2:
-        return lin(H, H, 2, 4, resid=True, norm_out=True)
+        if not paper:
+            return lin(H, H, 2, 4, resid=True, norm_out=True)
+        return add(lin(H, H, 2, 4, resid=True), lin(Ht, H, 2, 4, resid=True, norm_out=True))
     if 3 <= sid <= 12:
         j = layer % 5
         if j == 0:
@@ -385,8 +410,14 @@ def stage_work(w, sid):
             return lin(H, F, 2, 2)
         return lin(F, H, 2, 4, resid=True, norm_out=True)
     if sid == 13:
-        return lin(H, 2 * de, 2, 2)
-    return {"bytes": 2 * M * de * 2 + rows * K * 8 + rows * 4,
+        if not paper:
+            return lin(H, 2 * de, 2, 2)
+        tnorm = {"bytes": N * Ht * 4 + Ht * 4, "flops": 3 * N * Ht}
+        concat = {"bytes": M * H * 2 + N * H * 2 + M * 3 * H * 2, "flops": M * H}
+        assemble = {"bytes": 2 * M * de * 2 * 2 + N * de * 4, "flops": 3 * N * de}
+        return add(tnorm, lin(Ht, H, 2, 2, m=N), lin(H, de, 2, 4, m=N), concat,
+                   lin(3 * H, H, 2, 2), lin(H, 2 * de, 2, 2), assemble)
+    return {"bytes": 2 * rows * K * de * 2 + rows * K * 8 + rows * 4,
             "flops": 2 * N * (B - 1) * K * K * de}
 
 
@@ -526,13 +557,23 @@ def cpu_baseline(w, host, seconds, rule="greedy"):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    ow = oracle.OracleWeights(oracle.Dims(w.hidden, w.heads, w.ffn, w.d_e), w.vocab, synth.WEIGHTS_SEED)
+    import numpy as np
+    ow = oracle.OracleWeights(oracle.Dims(w.hidden, w.heads, w.ffn, w.d_e, target_hidden=w.target_hidden,
+                                          drafter_hidden=w.drafter_hidden), w.vocab, synth.WEIGHTS_SEED)
     temps = synth.make_temperatures(w.num_blocks, seed=1)
     unif = synth.make_uniforms(w.num_blocks, w.slots, seed=2)
 
+    hidden = target = None
+    if w.target_hidden > 0:
+        hb, tb = synth.make_head_inputs(w)
+        hidden = synth.bf16_bits_to_f32(hb).astype(np.float64)
+        target = synth.bf16_bits_to_f32(tb).astype(np.float64)
+
     def one(b):
-        return oracle.rerank_block(host[b], w.topk, ow, w.alpha, rule=rule, temperature=float(temps[b]),
-                                   uniforms=unif[b])
+        return oracle.rerank_block(host[b], w.topk, ow, w.alpha, w.use_logp, rule=rule,
+                                   temperature=float(temps[b]), uniforms=unif[b],
+                                   hidden=None if hidden is None else hidden[b],
+                                   target=None if target is None else target[b])
 
     one(0)   # generates the weights: excluded
     n = 0

@@ -22,7 +22,7 @@ EPI_F32, EPI_BF16, EPI_SILU_BF16, EPI_RESID_F32 = 0, 1, 2, 3
 STAGE_TOPK, STAGE_NODE, STAGE_CONF_LINEAR = 0, 1, 2
 STAGE_QKV, STAGE_ATTENTION, STAGE_O, STAGE_FFN1, STAGE_FFN2 = 3, 4, 5, 6, 7
 STAGE_HEADS, STAGE_SCORES_WALK, STAGE_COUNT = 13, 14, 15
-ABI_VERSION = 2
+ABI_VERSION = 3
 # commit rules (lilicorr_rule)
 RULE_GREEDY, RULE_EXACT, RULE_SAMPLE = 0, 1, 2
 _RULES = {"greedy": RULE_GREEDY, "exact": RULE_EXACT, "sample": RULE_SAMPLE}
@@ -41,7 +41,8 @@ class LilicorrError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("heads", ctypes.c_int32), ("ffn", ctypes.c_int32),
-                ("d_e", ctypes.c_int32), ("layers", ctypes.c_int32)]
+                ("d_e", ctypes.c_int32), ("layers", ctypes.c_int32),
+                ("target_hidden", ctypes.c_int32), ("drafter_hidden", ctypes.c_int32)]
 
 
 class WeightsDesc(ctypes.Structure):
@@ -62,7 +63,8 @@ class Params(ctypes.Structure):
                 ("timing_stage", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
                 ("timing_end", ctypes.c_void_p),
                 ("rule", ctypes.c_int32), ("temperature", ctypes.c_void_p),
-                ("uniforms", ctypes.c_void_p), ("proposal", ctypes.c_void_p)]
+                ("uniforms", ctypes.c_void_p), ("proposal", ctypes.c_void_p),
+                ("hidden", ctypes.c_void_p), ("target", ctypes.c_void_p)]
 
 
 _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -147,9 +149,12 @@ class EncoderDims:
     ffn: int
     d_e: int
     layers: int = 2
+    target_hidden: int = 0      # > 0: the paper's head (with drafter_hidden)
+    drafter_hidden: int = 0
 
     def c(self) -> Dims:
-        return Dims(self.hidden, self.heads, self.ffn, self.d_e, self.layers)
+        return Dims(self.hidden, self.heads, self.ffn, self.d_e, self.layers, self.target_hidden,
+                    self.drafter_hidden)
 
 
 def weights_bytes(dims: EncoderDims, vocab: int) -> int:
@@ -214,8 +219,10 @@ class Workspace:
 
 def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1.0, use_logp=True,
                 stream=None, dbg=None, rule: str = "greedy", temperature=None, uniforms=None,
-                proposal=None) -> Params:
+                proposal=None, hidden=None, target=None) -> Params:
     p = Params()
+    p.hidden = _ptr(hidden)
+    p.target = _ptr(target)
     p.rule = _RULES[rule]
     p.temperature = _ptr(temperature)
     p.uniforms = _ptr(uniforms)
@@ -236,11 +243,13 @@ def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1
 
 def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool = True,
            workspace: Workspace | None = None, debug: bool = False, out=None, rule: str = "greedy",
-           temperature=None, uniforms=None, proposal=None):
+           temperature=None, uniforms=None, proposal=None, hidden=None, target=None):
     """Rerank [N, B, V] device logits; returns int32 tokens [N, B] (and debug tensors).
 
     rule: "greedy", "exact" or "sample" (then temperature [N] and uniforms [N, B]
-    float32 device tensors are required; proposal [N, B, K] float32 is optional)."""
+    float32 device tensors are required; proposal [N, B, K] float32 is optional).
+    With the paper's head (weights.dims.target_hidden > 0) hidden [N, B, H_d] and
+    target [N, H_t] bfloat16 device tensors are required."""
     torch = _torch()
     _require_cuda(logits, "logits")
     N, B, V = logits.shape
@@ -263,7 +272,8 @@ def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool 
             "gap": torch.empty((N, B), dtype=torch.float32, device=dev),
         }
     p = make_params(N, _logits_dtype(logits), weights, workspace, alpha, use_logp, dbg=dbg, rule=rule,
-                    temperature=temperature, uniforms=uniforms, proposal=proposal)
+                    temperature=temperature, uniforms=uniforms, proposal=proposal, hidden=hidden,
+                    target=target)
     _check(lib().lilicorr_rerank(_ptr(logits), B, V, K, ctypes.byref(p), _ptr(out)), "rerank")
     return (out, dbg) if debug else out
 
@@ -272,7 +282,8 @@ def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
              weights_desc: WeightsDesc | None, workspace_ptr: int, workspace_nbytes: int,
              out_ptr: int, abi_version: int = ABI_VERSION, use_logp: int = 1,
              timing: tuple[int, int, int] | None = None, rule: int = RULE_GREEDY,
-             temperature_ptr: int = 0, uniforms_ptr: int = 0) -> int:
+             temperature_ptr: int = 0, uniforms_ptr: int = 0, hidden_ptr: int = 0,
+             target_ptr: int = 0) -> int:
     """Host-only argument check of rerank (no GPU needed); returns the status code.
 
     timing = (stage, begin_event, end_event) as plain integers (handles are
@@ -289,6 +300,8 @@ def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
     p.rule = rule
     p.temperature = ctypes.c_void_p(temperature_ptr)
     p.uniforms = ctypes.c_void_p(uniforms_ptr)
+    p.hidden = ctypes.c_void_p(hidden_ptr)
+    p.target = ctypes.c_void_p(target_ptr)
     if timing is not None:
         p.timing_stage, p.timing_begin, p.timing_end = timing[0], timing[1] or None, timing[2] or None
     return int(lib().lilicorr_validate(ctypes.c_void_p(logits_ptr), B, V, K, ctypes.byref(p),

@@ -22,7 +22,13 @@ bool dims_supported(const lilicorr_dims* d) {
   const int dh = d->hidden / d->heads;
   if (dh != 32 && dh != 64 && dh != 128) return false;
   if (d->ffn < 64 || d->ffn > 16384 || d->ffn % 64) return false;
-  if (d->d_e < 32 || d->d_e > 512 || d->d_e % 32) return false;
+  if (d->d_e < 32 || d->d_e > 1024 || d->d_e % 32) return false;
+  if (d->target_hidden != 0) {   // the paper's head
+    if (d->target_hidden < 64 || d->target_hidden > 8192 || d->target_hidden % 64) return false;
+    if (d->drafter_hidden < 64 || d->drafter_hidden > 16384 || d->drafter_hidden % 64) return false;
+  } else if (d->drafter_hidden != 0) {
+    return false;
+  }
   return true;
 }
 
@@ -170,6 +176,11 @@ int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_pa
       p->rule != LILICORR_RULE_SAMPLE)
     return LILICORR_EINVAL;
   if (p->rule == LILICORR_RULE_SAMPLE && (!p->temperature || !p->uniforms)) return LILICORR_EINVAL;
+  if (w->dims.target_hidden > 0) {   // the paper's head: its inputs, and a drafted slot
+    if (B < 2) return LILICORR_EINVAL;
+    if (!p->hidden || !p->target || ((uintptr_t)p->hidden & 15) || ((uintptr_t)p->target & 15))
+      return LILICORR_EINVAL;
+  }
   if ((p->timing_begin == nullptr) != (p->timing_end == nullptr)) return LILICORR_EINVAL;
   if (p->timing_begin && (p->timing_stage < 0 || p->timing_stage >= LILICORR_STAGE_COUNT))
     return LILICORR_EINVAL;
@@ -221,10 +232,9 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
   LL_STAGE(LILICORR_STAGE_TOPK, LL_TRY(launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
                          (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms), topk_idx,
                          topk_logp, p->dbg_lse, st)));
-  // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0))
-  LL_STAGE(LILICORR_STAGE_NODE,
-           LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, W.S, W.R, W.conf_w1,
-                                    W.conf_b1, hid, x, V, st)));
+  const bool paper = d.target_hidden > 0;
+  const int Bl = paper ? B - 1 : B;             // slots in the lattice
+  const int Mp = N * Bl * K;                    // lattice rows
   auto resid_norm = [&](const float* gamma) {
     LinearEpilogue e;
     e.kind = EPI_RESID_F32;
@@ -239,32 +249,81 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
     e.kind = kind;
     return e;
   };
-  LL_STAGE(LILICORR_STAGE_CONF_LINEAR,
-           LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, resid_norm(W.layer[0].gamma1),
-                                x, gpart, st)));
+  if (!paper) {
+    // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0))
+    LL_STAGE(LILICORR_STAGE_NODE,
+             LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, nullptr, W.S, W.R,
+                                      W.conf_w1, W.conf_b1, hid, x, V, st)));
+    LL_STAGE(LILICORR_STAGE_CONF_LINEAR,
+             LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, resid_norm(W.layer[0].gamma1),
+                                  x, gpart, st)));
+  } else {
+    // a2 (paper's head): x = (((h W_hid^T + b_hid) + S) + R) + (W2c . hid + b2c), then
+    // x += E_t[tok] W_emb^T + b_emb with u = bf16(RMSNorm(x; gamma1 of layer 0))
+    const int Ht = d.target_hidden, Hd = d.drafter_hidden;
+    float* ph = (float*)(ws + L.ph);
+    uint16_t* ae = (uint16_t*)(ws + L.ae);
+    LL_STAGE(LILICORR_STAGE_NODE, {
+      LL_TRY(launch_linear(p->hidden, N * B, Hd, W.w_hid, H, W.b_hid, plain(EPI_F32), ph, gpart, st));
+      LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, nullptr, ph, W.S, W.R, W.conf_w1,
+                               W.conf_b1, hid, x, V, st));
+      LL_TRY(launch_gather_rows(topk_idx, N, B, K, W.E_t, Ht, V, ae, st));
+    });
+    LinearEpilogue add_only = plain(EPI_RESID_F32);
+    add_only.resid = x;
+    LL_STAGE(LILICORR_STAGE_CONF_LINEAR, {
+      LL_TRY(launch_linear(hid, Mp, H, W.conf_w2, H, W.conf_b2, add_only, x, gpart, st));
+      LL_TRY(launch_linear(ae, Mp, Ht, W.w_emb, H, W.b_emb, resid_norm(W.layer[0].gamma1), x, gpart,
+                           st));
+    });
+  }
   // a3: two pre-norm layers; each residual GEMM also produces the next RMSNorm
   for (int l = 0; l < 2; ++l) {
     const LayerPtrs& Lw = W.layer[l];
     const float* next_gamma = l == 0 ? W.layer[1].gamma1 : W.gamma_f;
     const int s0 = 5 * l;
     LL_STAGE(LILICORR_STAGE_QKV + s0,
-             LL_TRY(launch_linear(u, M, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st)));
+             LL_TRY(launch_linear(u, Mp, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st)));
     LL_STAGE(LILICORR_STAGE_ATTENTION + s0,
-             LL_TRY(launch_attention(qkv, N, B, K, H, heads, Lw.dist, Lw.same, attn, st)));
+             LL_TRY(launch_attention(qkv, N, Bl, K, H, heads, Lw.dist, Lw.same, attn, st)));
     LL_STAGE(LILICORR_STAGE_O + s0,
-             LL_TRY(launch_linear(attn, M, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
+             LL_TRY(launch_linear(attn, Mp, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
     LL_STAGE(LILICORR_STAGE_FFN1 + s0,
-             LL_TRY(launch_linear(u, M, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st)));
+             LL_TRY(launch_linear(u, Mp, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st)));
     LL_STAGE(LILICORR_STAGE_FFN2 + s0,
-             LL_TRY(launch_linear(hid, M, F, Lw.w2, H, Lw.b2, resid_norm(next_gamma), x, gpart, st)));
+             LL_TRY(launch_linear(hid, Mp, F, Lw.w2, H, Lw.b2, resid_norm(next_gamma), x, gpart, st)));
   }
   // a4: out|in heads and their unit normalisation
-  {
+  if (!paper) {
     LinearEpilogue e = plain(EPI_F32);
     e.heads_out = outv;
     e.heads_in = inv;
     LL_STAGE(LILICORR_STAGE_HEADS,
              LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st)));
+  } else {
+    // a4 (paper's head): tb = bf16(bf16(RMSNorm(t; gamma_t)) W_tgt^T + b_tgt);
+    // y = bf16(SiLU([u, tb, bf16(u tb)] W_fuse^T + b_fuse)); out|in heads of y;
+    // anchor o_0 = unit(tb W_anchor^T + b_anchor) in slot 0's rows
+    const int Ht = d.target_hidden;
+    uint16_t* tnorm = (uint16_t*)(ws + L.tnorm);
+    uint16_t* tb = (uint16_t*)(ws + L.tb);
+    float* apre = (float*)(ws + L.apre);
+    uint16_t* lat_out = (uint16_t*)(ws + L.lat_out);
+    uint16_t* lat_in = (uint16_t*)(ws + L.lat_in);
+    uint16_t* cat = qkv;     // [Mp, 3H] bf16: the layers are done with qkv
+    uint16_t* y = attn;      // [Mp, H] bf16
+    LinearEpilogue e = plain(EPI_F32);
+    e.heads_out = lat_out;
+    e.heads_in = lat_in;
+    LL_STAGE(LILICORR_STAGE_HEADS, {
+      LL_TRY(launch_rmsnorm_bf16(p->target, N, Ht, W.gamma_t, kRmsEps, tnorm, st));
+      LL_TRY(launch_linear(tnorm, N, Ht, W.w_tgt, H, W.b_tgt, plain(EPI_BF16), tb, gpart, st));
+      LL_TRY(launch_linear(tb, N, H, W.w_anchor, de, W.b_anchor, plain(EPI_F32), apre, gpart, st));
+      LL_TRY(launch_concat(u, tb, N, Bl * K, H, cat, st));
+      LL_TRY(launch_linear(cat, Mp, 3 * H, W.w_fuse, H, W.b_fuse, plain(EPI_SILU_BF16), y, gpart, st));
+      LL_TRY(launch_linear(y, Mp, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st));
+      LL_TRY(launch_assemble(lat_out, lat_in, apre, N, B, K, de, outv, inv, st));
+    });
   }
   // a5: pair scores, a6: the commit (one fused kernel: B * K <= 512 keeps the
   // block's cosines within the kernel's LDS budget)

@@ -849,8 +849,11 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
     if (N <= 256)
       hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 1>), dim3(row_blocks), dim3(256), 0, stream,
                          part, M, N / 2, bias, ep.heads_out, ep.heads_in);
-    else
+    else if (N <= 1024)
       hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 4>), dim3(row_blocks), dim3(256), 0, stream,
+                         part, M, N / 2, bias, ep.heads_out, ep.heads_in);
+    else
+      hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 8>), dim3(row_blocks), dim3(256), 0, stream,
                          part, M, N / 2, bias, ep.heads_out, ep.heads_in);
     return hipGetLastError();
   }

@@ -31,10 +31,27 @@ hipError_t launch_topk_merge_shards(int G, int rows, int K, const float* val, co
 
 // a2: node features, confidence MLP layer 1 and the embedding/slot/rank sum.
 //   hid  bf16 [M, H] = bf16(silu(W1c f + b1c));  xbase float [M, H] = (E[tok] + S[s]) + R[j]
+// With ph set (the paper's head): only slots 1..B-1 (M = N (B-1) K) and
+// xbase = (ph[n B + s] + S[s]) + R[j], ph the projected drafter states [N B, H].
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
-                             int H, const uint16_t* E, const uint16_t* S, const uint16_t* R,
-                             const uint16_t* conf_w1, const float* conf_b1, uint16_t* hid,
-                             float* xbase, int V, hipStream_t stream);
+                             int H, const uint16_t* E, const float* ph, const uint16_t* S,
+                             const uint16_t* R, const uint16_t* conf_w1, const float* conf_b1,
+                             uint16_t* hid, float* xbase, int V, hipStream_t stream);
+
+// The paper's head (paper_head.hip).
+//   gather_rows: out [N (B-1) K, Ht] = table[token] of the drafted candidates
+//   rmsnorm_bf16: out = bf16(RMSNorm(x)) for bf16 rows x [M, H]
+//   concat: out [N P, 3H] = [u, tb[n], bf16(u * tb[n])], P lattice rows per block
+//   assemble: outv/inv [N, B, K, d_e]: slot 0 = unit(apre[n]) (in rows 0), slots
+//             >= 1 = the lattice's out/in rows
+hipError_t launch_gather_rows(const int32_t* topk_idx, int N, int B, int K, const uint16_t* table,
+                              int Ht, int V, uint16_t* out, hipStream_t stream);
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, int M, int H, const float* gamma, float eps,
+                               uint16_t* out, hipStream_t stream);
+hipError_t launch_concat(const uint16_t* u, const uint16_t* tb, int N, int per_block, int H,
+                         uint16_t* out, hipStream_t stream);
+hipError_t launch_assemble(const uint16_t* lat_out, const uint16_t* lat_in, const float* apre, int N,
+                           int B, int K, int de, uint16_t* outv, uint16_t* inv, hipStream_t stream);
 
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SILU_BF16 = 2, EPI_RESID_F32 = 3 };
 

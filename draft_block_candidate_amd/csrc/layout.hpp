@@ -40,7 +40,8 @@ inline std::vector<TensorSpec> weight_specs(const lilicorr_dims& d, int V) {
   auto add = [&](int id, int64_t r, int64_t c, int kind, float scale) {
     t.push_back(TensorSpec{id, r, c, kind, scale, 0});
   };
-  add(0, V, H, WK_BF16, 1.0f);
+  const bool paper = d.target_hidden > 0;
+  if (!paper) add(0, V, H, WK_BF16, 1.0f);
   add(1, kTableRows, H, WK_BF16, 1.0f);
   add(2, kTableRows, H, WK_BF16, 1.0f);
   add(3, H, 5, WK_BF16, inv_sqrt_scale(5));
@@ -69,6 +70,21 @@ inline std::vector<TensorSpec> weight_specs(const lilicorr_dims& d, int V) {
   add(51, de, H, WK_BF16, inv_sqrt_scale((int)H));
   add(50, 1, de, WK_F32, inv_sqrt_scale((int)H));
   add(52, 1, de, WK_F32, inv_sqrt_scale((int)H));
+  if (paper) {
+    const int64_t Ht = d.target_hidden, Hd = d.drafter_hidden;
+    add(56, V, Ht, WK_BF16, 1.0f);
+    add(57, H, Ht, WK_BF16, inv_sqrt_scale((int)Ht));
+    add(58, 1, H, WK_F32, inv_sqrt_scale((int)Ht));
+    add(59, H, Hd, WK_BF16, inv_sqrt_scale((int)Hd));
+    add(60, 1, H, WK_F32, inv_sqrt_scale((int)Hd));
+    add(61, 1, Ht, WK_GAMMA, 0.f);
+    add(62, H, Ht, WK_BF16, inv_sqrt_scale((int)Ht));
+    add(63, 1, H, WK_F32, inv_sqrt_scale((int)Ht));
+    add(64, H, 3 * H, WK_BF16, inv_sqrt_scale((int)(3 * H)));
+    add(65, 1, H, WK_F32, inv_sqrt_scale((int)(3 * H)));
+    add(66, de, H, WK_BF16, inv_sqrt_scale((int)H));
+    add(67, 1, de, WK_F32, inv_sqrt_scale((int)H));
+  }
   size_t off = 0;
   for (auto& s : t) {
     // w_in directly follows w_out, b_in directly follows b_out
@@ -105,12 +121,18 @@ struct WeightPtrs {
   const uint16_t *E, *S, *R, *conf_w1, *conf_w2, *w_heads;
   const float *conf_b1, *conf_b2, *gamma_f, *b_heads;
   LayerPtrs layer[2];
+  // the paper's head (null for the lattice head)
+  const uint16_t *E_t, *w_emb, *w_hid, *w_tgt, *w_fuse, *w_anchor;
+  const float *b_emb, *b_hid, *gamma_t, *b_tgt, *b_fuse, *b_anchor;
 };
 
 inline WeightPtrs weight_ptrs(const lilicorr_weights& w) {
   auto t = weight_specs(w.dims, w.vocab);
   const char* base = (const char*)w.dev;
-  auto P = [&](int id) -> const void* { return base + find_spec(t, id)->offset; };
+  auto P = [&](int id) -> const void* {
+    const TensorSpec* sp = find_spec(t, id);
+    return sp ? base + sp->offset : nullptr;
+  };
   WeightPtrs p;
   p.E = (const uint16_t*)P(0);
   p.S = (const uint16_t*)P(1);
@@ -138,6 +160,18 @@ inline WeightPtrs weight_ptrs(const lilicorr_weights& w) {
   p.gamma_f = (const float*)P(48);
   p.w_heads = (const uint16_t*)P(49);
   p.b_heads = (const float*)P(50);
+  p.E_t = (const uint16_t*)P(56);
+  p.w_emb = (const uint16_t*)P(57);
+  p.b_emb = (const float*)P(58);
+  p.w_hid = (const uint16_t*)P(59);
+  p.b_hid = (const float*)P(60);
+  p.gamma_t = (const float*)P(61);
+  p.w_tgt = (const uint16_t*)P(62);
+  p.b_tgt = (const float*)P(63);
+  p.w_fuse = (const uint16_t*)P(64);
+  p.b_fuse = (const float*)P(65);
+  p.w_anchor = (const uint16_t*)P(66);
+  p.b_anchor = (const float*)P(67);
   return p;
 }
 
@@ -181,17 +215,31 @@ inline TopkWs topk_ws_layout(int rows, int V, int K) {
 
 // ---- rerank workspace ------------------------------------------------------
 struct RerankWs {
-  size_t topk, topk_idx, topk_logp, x, hid, u, qkv, attn, heads, outv, inv, gemm_part, total;
+  size_t topk, topk_idx, topk_logp, x, hid, u, qkv, attn, heads, outv, inv, gemm_part;
+  // the paper's head: projected hidden states [N B, H] f32, gathered target
+  // embedding rows [M', H_t] bf16, normalised target [N, H_t] bf16, projected
+  // target [N, H] bf16, anchor head before normalisation [N, d_e] f32, lattice
+  // out/in vectors [M', d_e] bf16 (M' = N (B-1) K)
+  size_t ph, ae, tnorm, tb, apre, lat_out, lat_in;
+  size_t total;
 };
 
-// Largest split-K scratch over the linear layers of one rerank call.
-inline size_t rerank_gemm_scratch(int M, const lilicorr_dims& d) {
-  const int H = d.hidden, F = d.ffn, de = d.d_e;
+// Largest split-K scratch over the linear layers of one rerank call (M rows
+// of the lattice; the paper's head adds products over N B and N rows).
+inline size_t rerank_gemm_scratch(int M, const lilicorr_dims& d, int NB = 0, int N = 0) {
+  const int H = d.hidden, F = d.ffn, de = d.d_e, Ht = d.target_hidden, Hd = d.drafter_hidden;
   const int shapes[6][2] = {{H, H}, {H, 3 * H}, {H, H}, {H, F}, {F, H}, {H, 2 * de}};  // (Kd, N)
   size_t pf = 0;
   for (const auto& sh : shapes) {
     const GemmPlan p = plan_linear(M, sh[0], sh[1]);
     if (p.part_floats > pf) pf = p.part_floats;
+  }
+  if (Ht > 0) {
+    const int more[5][3] = {{M, Ht, H}, {M, 3 * H, H}, {NB, Hd, H}, {N, Ht, H}, {N, H, de}};  // (M, Kd, N)
+    for (const auto& sh : more) {
+      const GemmPlan p = plan_linear(sh[0], sh[1], sh[2]);
+      if (p.part_floats > pf) pf = p.part_floats;
+    }
   }
   return pf;
 }
@@ -218,7 +266,20 @@ inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims
   w.heads = take(M * 2 * de * 4);
   w.outv = take(M * de * 2);
   w.inv = take(M * de * 2);
-  w.gemm_part = take(rerank_gemm_scratch((int)M, d) * 4);
+  const bool paper = d.target_hidden > 0;
+  const size_t Mp = paper ? (size_t)N * (B - 1) * K : M;   // lattice rows
+  w.gemm_part = take(rerank_gemm_scratch((int)Mp, d, N * B, N) * 4);
+  w.ph = w.ae = w.tnorm = w.tb = w.apre = w.lat_out = w.lat_in = 0;
+  if (paper) {
+    const size_t Ht = d.target_hidden;
+    w.ph = take(rows * H * 4);
+    w.ae = take(Mp * Ht * 2);
+    w.tnorm = take((size_t)N * Ht * 2);
+    w.tb = take((size_t)N * H * 2);
+    w.apre = take((size_t)N * de * 4);
+    w.lat_out = take(Mp * de * 2);
+    w.lat_in = take(Mp * de * 2);
+  }
   w.total = off;
   return w;
 }

@@ -14,12 +14,16 @@ namespace {
 // (CG of them). The first-layer weights and biases of a thread's columns are
 // loaded once per block and kept in registers; the tokens' embedding, slot
 // and rank rows are all loaded before any is used.
-template <int CG, int TPB>
+// PAPER (the paper's own head): the tokens are the drafted candidates of slots
+// 1..B-1 only, and the first term of the table sum is the slot's projected
+// drafter hidden state ph[(n B + s) H ..] (fp32) instead of an E row; the
+// target-embedding term is added by a later linear.
+template <int CG, int TPB, bool PAPER>
 __global__ __launch_bounds__(256) void node_build_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int64_t M, int B,
-    int K, int H, int V, const uint16_t* __restrict__ E, const uint16_t* __restrict__ S,
-    const uint16_t* __restrict__ R, const uint16_t* __restrict__ w1, const float* __restrict__ b1,
-    uint16_t* __restrict__ hid, float* __restrict__ xbase) {
+    int K, int H, int V, const uint16_t* __restrict__ E, const float* __restrict__ ph,
+    const uint16_t* __restrict__ S, const uint16_t* __restrict__ R, const uint16_t* __restrict__ w1,
+    const float* __restrict__ b1, uint16_t* __restrict__ hid, float* __restrict__ xbase) {
   const int tid = threadIdx.x;
   const int h4 = H / 4;
   // this thread's columns: w1 rows are 5 bf16 (10 bytes), so the 4 columns of
@@ -49,17 +53,23 @@ __global__ __launch_bounds__(256) void node_build_kernel(
   // the block's tokens (clamped; the ones past M are computed, not stored)
   int64_t tk[TPB];
   uint2 ev[TPB][CG], sv[TPB][CG], rv[TPB][CG];
+  float4 pv[TPB][CG];
   float f[TPB][5];
 #pragma unroll
   for (int u = 0; u < TPB; ++u) {
     const int64_t t = min((int64_t)blockIdx.x * TPB + u, M - 1);
     tk[u] = t;
-    const int64_t row = t / K;       // (block, slot)
+    int64_t row = t / K;             // (block, slot)
     const int j = (int)(t - row * K);
+    if (PAPER) {                     // lattice row (n, s - 1) -> top-K row (n, s)
+      const int64_t n = row / (B - 1);
+      row = n * B + 1 + (row - n * (B - 1));
+    }
     const int s = (int)(row % B);
-    int64_t tok = topk_idx[t];
+    const int64_t ti = row * K + j;
+    int64_t tok = PAPER ? 0 : topk_idx[ti];
     if (tok < 0 || tok >= V) tok = 0;  // ids come from the top-K stage; never read outside E
-    const float lp = topk_logp[t];
+    const float lp = topk_logp[ti];
     const float lp0 = topk_logp[row * K];
     f[u][0] = lp;
     f[u][1] = expf(lp);
@@ -69,7 +79,10 @@ __global__ __launch_bounds__(256) void node_build_kernel(
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
       const int c4 = min(tid + 256 * g, h4 - 1);
-      ev[u][g] = ((const uint2*)(E + tok * H))[c4];
+      if (PAPER)
+        pv[u][g] = ((const float4*)(ph + row * H))[c4];
+      else
+        ev[u][g] = ((const uint2*)(E + tok * H))[c4];
       sv[u][g] = ((const uint2*)(S + (int64_t)s * H))[c4];
       rv[u][g] = ((const uint2*)(R + (int64_t)j * H))[c4];
     }
@@ -80,13 +93,15 @@ __global__ __launch_bounds__(256) void node_build_kernel(
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
       const int c4 = tid + 256 * g;
-      const uint32_t ew[2] = {ev[u][g].x, ev[u][g].y}, sw[2] = {sv[u][g].x, sv[u][g].y},
-                     rw[2] = {rv[u][g].x, rv[u][g].y};
+      const uint32_t ew[2] = {PAPER ? 0u : ev[u][g].x, PAPER ? 0u : ev[u][g].y},
+                     sw[2] = {sv[u][g].x, sv[u][g].y}, rw[2] = {rv[u][g].x, rv[u][g].y};
+      const float pw[4] = {PAPER ? pv[u][g].x : 0.f, PAPER ? pv[u][g].y : 0.f,
+                           PAPER ? pv[u][g].z : 0.f, PAPER ? pv[u][g].w : 0.f};
       float xb[4], hz[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t sh = (q & 1) ? 16 : 0;
-        const float a = bf16_to_f32((ew[q >> 1] >> sh) & 0xFFFF);
+        const float a = PAPER ? pw[q] : bf16_to_f32((ew[q >> 1] >> sh) & 0xFFFF);
         const float b = bf16_to_f32((sw[q >> 1] >> sh) & 0xFFFF);
         const float c = bf16_to_f32((rw[q >> 1] >> sh) & 0xFFFF);
         xb[q] = __fadd_rn(__fadd_rn(a, b), c);
@@ -106,35 +121,43 @@ __global__ __launch_bounds__(256) void node_build_kernel(
 }  // namespace
 
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
-                             int H, const uint16_t* E, const uint16_t* S, const uint16_t* R,
-                             const uint16_t* conf_w1, const float* conf_b1, uint16_t* hid,
-                             float* xbase, int V, hipStream_t stream) {
-  const int64_t M = (int64_t)N * B * K;
+                             int H, const uint16_t* E, const float* ph, const uint16_t* S,
+                             const uint16_t* R, const uint16_t* conf_w1, const float* conf_b1,
+                             uint16_t* hid, float* xbase, int V, hipStream_t stream) {
+  const bool paper = ph != nullptr;
+  const int64_t M = (int64_t)N * (paper ? B - 1 : B) * K;
+  if (M <= 0) return hipSuccess;
+#define LL_NB(CG, TPB, grid)                                                                     \
+  do {                                                                                         \
+    if (paper)                                                                                 \
+      hipLaunchKernelGGL((node_build_kernel<CG, TPB, true>), grid, dim3(256), 0, stream,      \
+                         topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1, conf_b1,   \
+                         hid, xbase);                                                          \
+    else                                                                                       \
+      hipLaunchKernelGGL((node_build_kernel<CG, TPB, false>), grid, dim3(256), 0, stream,     \
+                         topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1, conf_b1,   \
+                         hid, xbase);                                                          \
+  } while (0)
   // few tokens: one per block (more blocks in flight); many: eight per block
   // (four for the widest rows, to bound the registers)
   if (M < 4096) {
     const dim3 grid((unsigned)M);
     if (H <= 1024)
-      hipLaunchKernelGGL((node_build_kernel<1, 1>), grid, dim3(256), 0, stream, topk_idx, topk_logp,
-                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+      LL_NB(1, 1, grid);
     else if (H <= 2048)
-      hipLaunchKernelGGL((node_build_kernel<2, 1>), grid, dim3(256), 0, stream, topk_idx, topk_logp,
-                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+      LL_NB(2, 1, grid);
     else
-      hipLaunchKernelGGL((node_build_kernel<4, 1>), grid, dim3(256), 0, stream, topk_idx, topk_logp,
-                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+      LL_NB(4, 1, grid);
   } else {
     const dim3 grid8((unsigned)((M + 7) / 8)), grid4((unsigned)((M + 3) / 4));
     if (H <= 1024)
-      hipLaunchKernelGGL((node_build_kernel<1, 8>), grid8, dim3(256), 0, stream, topk_idx, topk_logp,
-                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+      LL_NB(1, 8, grid8);
     else if (H <= 2048)
-      hipLaunchKernelGGL((node_build_kernel<2, 8>), grid8, dim3(256), 0, stream, topk_idx, topk_logp,
-                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+      LL_NB(2, 8, grid8);
     else
-      hipLaunchKernelGGL((node_build_kernel<4, 4>), grid4, dim3(256), 0, stream, topk_idx, topk_logp,
-                         M, B, K, H, V, E, S, R, conf_w1, conf_b1, hid, xbase);
+      LL_NB(4, 4, grid4);
   }
+#undef LL_NB
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ extern "C" {
 #define LILICORR_API
 #endif
 
-#define LILICORR_ABI_VERSION 2u
+#define LILICORR_ABI_VERSION 3u
 #define LILICORR_MAX_SLOTS 64     /* B: slots per block */
 #define LILICORR_MAX_TOPK 64      /* K: candidates per slot (one per wave lane) */
 #define LILICORR_MAX_LATTICE 512  /* T = B*K tokens per block */
@@ -79,9 +79,22 @@ typedef enum { LILICORR_RULE_GREEDY = 0, LILICORR_RULE_EXACT = 1, LILICORR_RULE_
  * a two-layer bidirectional transformer of width `hidden` with `heads`
  * attention heads and feed-forward width `ffn`; in/out vectors of width d_e.
  * Supported: layers == 2; hidden % 64 == 0; ffn % 64 == 0; d_e % 32 == 0;
- * hidden / heads in {32, 64, 128}; hidden <= 4096; ffn <= 16384; d_e <= 512. */
+ * hidden / heads in {32, 64, 128}; hidden <= 4096; ffn <= 16384; d_e <= 1024.
+ *
+ * target_hidden = 0 selects the lattice head over all B slots whose node embeds
+ * the token with its own table E (no drafter or target inputs). target_hidden
+ * > 0 selects the paper's own head (Section 3.2, Appendix A): the lattice holds
+ * the B-1 drafted slots; a node sums the target's frozen input embedding of the
+ * token projected down (E_t, width target_hidden), the drafter's hidden state
+ * at its slot projected down (width drafter_hidden), the confidence network and
+ * the slot/rank tables; after the transformer each node is fused with the
+ * projected target state (concat [node, t', node * t'] -> linear -> SiLU); a
+ * third head gives the anchor's (slot 0's) out vector from t'. Then 64 <=
+ * target_hidden <= 8192, 64 <= drafter_hidden <= 16384, both multiples of 64. */
 typedef struct {
   int32_t hidden, heads, ffn, d_e, layers;
+  int32_t target_hidden;   /* H_t; 0 = lattice head */
+  int32_t drafter_hidden;  /* H_d (paper head only) */
 } lilicorr_dims;
 
 /* Encoder weights: a device blob of lilicorr_weights_bytes() bytes filled by
@@ -156,6 +169,14 @@ typedef struct {
   const float* temperature;
   const float* uniforms;
   float* proposal;
+  /* Inputs of the paper's head (dims.target_hidden > 0; ignored otherwise), required:
+   *   hidden  device bf16 bits [N, B, drafter_hidden]  drafter hidden state per slot (slot 0 unused)
+   *   target  device bf16 bits [N, target_hidden]      target state behind the block's anchor
+   * With this head slot 0 is the anchor: its out vectors (dbg_outv) all hold the anchor
+   * head's vector, its in vectors are zero, and the walk starts from its candidate 0. The
+   * paper's commit rule is use_logp = 0 with alpha = sigma = 8 (Table 4). */
+  const uint16_t* hidden;
+  const uint16_t* target;
 } lilicorr_params;
 
 /* The whole reranking path (LiLiCorr paper, Section 3.5 "Single-pass
@@ -194,7 +215,11 @@ LILICORR_API int lilicorr_weights_init(lilicorr_weights* w, void* stream);
  * layer l (base 16+16l): +0 gamma1[H], +1 wqkv[3H,H], +2 bqkv[3H], +3 wo[H,H],
  * +4 bo[H], +5 gamma2[H], +6 w1[F,H], +7 b1[F], +8 w2[H,F], +9 b2[H],
  * +10 dist[heads,127], +11 same[heads]; 48 gamma_f[H], 49 w_out[d_e,H],
- * 50 b_out[d_e], 51 w_in[d_e,H], 52 b_in[d_e]. Host only. EINVAL if unknown. */
+ * 50 b_out[d_e], 51 w_in[d_e,H], 52 b_in[d_e]. The paper's head (target_hidden
+ * = H_t > 0, drafter_hidden = H_d) has no tensor 0 and adds 56 E_t[V,H_t],
+ * 57 w_emb[H,H_t], 58 b_emb[H], 59 w_hid[H,H_d], 60 b_hid[H], 61 gamma_t[H_t],
+ * 62 w_tgt[H,H_t], 63 b_tgt[H], 64 w_fuse[H,3H], 65 b_fuse[H], 66 w_anchor[d_e,H],
+ * 67 b_anchor[d_e]. Host only. EINVAL if unknown. */
 LILICORR_API int lilicorr_weights_tensor(const lilicorr_dims* dims, int V, int id, size_t* offset_bytes,
                             size_t* numel, int* dtype);
 

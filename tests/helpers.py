@@ -40,16 +40,18 @@ def assert_within(g, o, tol=TOL, what=""):
                              f"gpu {[float(g[tuple(b)]) for b in bad]} oracle {[float(o[tuple(b)]) for b in bad]}")
 
 
-def assert_scores(g, o, what="", alpha=1.0, fraction=COS_FRACTION):
+def assert_scores(g, o, what="", alpha=1.0, fraction=COS_FRACTION, step=False):
     """Cosines / step scores: a fraction (COS_FRACTION unless a case states its
     own, derived from the float32 drift of its shape) within TOL, all within the
-    bf16 bound."""
+    bf16 bound. A step score fl32(logp + fl32(alpha * cos)) carries |alpha| times
+    its cosine's error, so for step=True the TOL part is scaled by max(1, |alpha|)."""
     g = np.asarray(g, dtype=np.float64).ravel()
     o = np.asarray(o, dtype=np.float64).ravel()
     err = np.abs(g - o)
-    hard = TOL * np.maximum(1.0, np.abs(o)) + abs(alpha) * COS_HARD
+    tol = TOL * (max(1.0, abs(alpha)) if step else 1.0)
+    hard = tol * np.maximum(1.0, np.abs(o)) + abs(alpha) * COS_HARD
     assert np.all(err <= hard), f"{what}: max error {err.max()} beyond the bf16 bound"
-    n_bad = int((~within(g, o)).sum())
+    n_bad = int((~within(g, o, tol)).sum())
     allowed = max(1, int((1.0 - fraction) * err.size))
     assert n_bad <= allowed, f"{what}: {n_bad} of {err.size} outside {TOL} (allowed {allowed})"
     return {"n": int(err.size), "over_tol": n_bad, "max": float(err.max()),
@@ -110,9 +112,10 @@ _WEIGHTS = {}
 
 
 def oracle_weights(w: synth.Workload) -> OracleWeights:
-    key = (w.hidden, w.heads, w.ffn, w.d_e, w.vocab)
+    key = (w.hidden, w.heads, w.ffn, w.d_e, w.vocab, w.target_hidden, w.drafter_hidden)
     if key not in _WEIGHTS:
-        _WEIGHTS[key] = OracleWeights(Dims(w.hidden, w.heads, w.ffn, w.d_e), w.vocab, synth.WEIGHTS_SEED)
+        _WEIGHTS[key] = OracleWeights(Dims(w.hidden, w.heads, w.ffn, w.d_e, target_hidden=w.target_hidden,
+                                           drafter_hidden=w.drafter_hidden), w.vocab, synth.WEIGHTS_SEED)
     return _WEIGHTS[key]
 
 
@@ -121,9 +124,11 @@ _DEV_WEIGHTS = {}
 
 def device_weights(w: synth.Workload):
     import draft_block_candidate_amd as L
-    key = (w.hidden, w.heads, w.ffn, w.d_e, w.vocab)
+    key = (w.hidden, w.heads, w.ffn, w.d_e, w.vocab, w.target_hidden, w.drafter_hidden)
     if key not in _DEV_WEIGHTS:
         _DEV_WEIGHTS.clear()   # keep one blob resident at a time
-        _DEV_WEIGHTS[key] = L.Weights(L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e), w.vocab,
+        _DEV_WEIGHTS[key] = L.Weights(L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e,
+                                                    target_hidden=w.target_hidden,
+                                                    drafter_hidden=w.drafter_hidden), w.vocab,
                                       synth.WEIGHTS_SEED)
     return _DEV_WEIGHTS[key]

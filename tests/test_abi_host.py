@@ -57,11 +57,12 @@ def test_strerror_codes():
 
 
 DIMS = L.EncoderDims(64, 2, 256, 32)
+PAPER_DIMS = L.EncoderDims(64, 2, 128, 32, target_hidden=128, drafter_hidden=192)
 
 
 def _good(**over):
     args = dict(logits_ptr=1 << 20, N=1, B=16, V=1024, K=4, logits_dtype=L.F32, vocab=1024,
-                dims=DIMS, wptr=1 << 24, wbytes=None, ws=1 << 28, wsbytes=None, out=1 << 12,
+                dims=over.get("dims", DIMS), wptr=1 << 24, wbytes=None, ws=1 << 28, wsbytes=None, out=1 << 12,
                 abi=L.ABI_VERSION, use_logp=1, weights=True, timing=None, rule=L.RULE_GREEDY,
                 temp=0, unif=0)
     args.update(over)
@@ -69,10 +70,10 @@ def _good(**over):
     desc = L.WeightsDesc(args["dims"].c(), args["vocab"], 42, ctypes.c_void_p(args["wptr"]), wb) if args["weights"] else None
     wsb = args["wsbytes"]
     if wsb is None:
-        wsb = L.workspace_bytes(args["N"], args["B"], args["V"], args["K"], DIMS)
+        wsb = L.workspace_bytes(args["N"], args["B"], args["V"], args["K"], args["dims"]) or (1 << 30)
     return L.validate(args["logits_ptr"], args["N"], args["B"], args["V"], args["K"], args["logits_dtype"],
                       desc, args["ws"], wsb, args["out"], args["abi"], args["use_logp"], args["timing"],
-                      args["rule"], args["temp"], args["unif"])
+                      args["rule"], args["temp"], args["unif"], args.get("hid", 0), args.get("tgt", 0))
 
 
 @pytest.mark.parametrize("over,code", [
@@ -115,6 +116,14 @@ def _good(**over):
     ({"rule": L.RULE_SAMPLE}, L.EINVAL),                           # temperatures and uniforms required
     ({"rule": L.RULE_SAMPLE, "temp": 0x3000}, L.EINVAL),
     ({"rule": L.RULE_SAMPLE, "unif": 0x4000}, L.EINVAL),
+    ({"dims": PAPER_DIMS, "hid": 0x5000, "tgt": 0x6000}, L.OK),    # the paper's head
+    ({"dims": PAPER_DIMS}, L.EINVAL),                               # its inputs are required
+    ({"dims": PAPER_DIMS, "hid": 0x5000}, L.EINVAL),
+    ({"dims": PAPER_DIMS, "hid": 0x5008, "tgt": 0x6000}, L.EINVAL),  # 16-byte alignment
+    ({"dims": PAPER_DIMS, "hid": 0x5000, "tgt": 0x6000, "B": 1, "wsbytes": 1 << 30}, L.EINVAL),  # no drafted slot
+    ({"dims": L.EncoderDims(64, 2, 128, 32, target_hidden=96, drafter_hidden=128)}, L.EUNSUPPORTED),
+    ({"dims": L.EncoderDims(64, 2, 128, 32, drafter_hidden=128)}, L.EUNSUPPORTED),
+    ({"dims": L.EncoderDims(64, 2, 128, 1056)}, L.EUNSUPPORTED),   # d_e <= 1024
 ])
 def test_validate_status_codes(over, code):
     assert _good(**over) == code
@@ -124,7 +133,8 @@ def test_sizes_for_the_workloads():
     import synth
     for name in synth.WORKLOADS_ORDER:
         w = synth.WORKLOADS[name]
-        d = L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e)
+        d = L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e, target_hidden=w.target_hidden,
+                          drafter_hidden=w.drafter_hidden)
         assert L.weights_bytes(d, w.vocab) > 0
         ws = L.workspace_bytes(w.num_blocks, w.slots, w.vocab, w.topk, d)
         M = w.num_blocks * w.slots * w.topk
@@ -133,24 +143,32 @@ def test_sizes_for_the_workloads():
     assert L.weights_bytes(L.EncoderDims(64, 2, 256, 32, layers=3), 10) == 0
 
 
-def test_weight_layout_matches_the_generator_table():
-    d = Dims(64, 2, 256, 32)
+@pytest.mark.parametrize("paper", [False, True])
+def test_weight_layout_matches_the_generator_table(paper):
+    DIMS_ = PAPER_DIMS if paper else DIMS
+    d = Dims(64, 2, 128, 32, target_hidden=128, drafter_hidden=192) if paper else Dims(64, 2, 256, 32)
     spans = []
     for t, name, shape, scale, kind in weight_table(d, 1024):
-        off, n, dt = L.weights_tensor_info(DIMS, 1024, t)
+        off, n, dt = L.weights_tensor_info(DIMS_, 1024, t)
         assert n == (shape[0] * (shape[1] if len(shape) > 1 else 1))
         assert dt == (L.BF16 if kind == "bf16" else L.F32)
         spans.append((off, off + n * (2 if dt == L.BF16 else 4), name))
     spans.sort()
     for (a0, a1, _), (b0, b1, _) in zip(spans, spans[1:]):
         assert a1 <= b0
-    assert spans[-1][1] <= L.weights_bytes(DIMS, 1024)
-    wo, wi = L.weights_tensor_info(DIMS, 1024, 49), L.weights_tensor_info(DIMS, 1024, 51)
+    assert spans[-1][1] <= L.weights_bytes(DIMS_, 1024)
+    wo, wi = L.weights_tensor_info(DIMS_, 1024, 49), L.weights_tensor_info(DIMS_, 1024, 51)
     assert wi[0] == wo[0] + wo[1] * 2      # one GEMM with N = 2 d_e covers both heads
-    bo, bi = L.weights_tensor_info(DIMS, 1024, 50), L.weights_tensor_info(DIMS, 1024, 52)
+    bo, bi = L.weights_tensor_info(DIMS_, 1024, 50), L.weights_tensor_info(DIMS_, 1024, 52)
     assert bi[0] == bo[0] + bo[1] * 4
     with pytest.raises(L.LilicorrError):
-        L.weights_tensor_info(DIMS, 1024, 7)
+        L.weights_tensor_info(DIMS_, 1024, 7)
+    if paper:       # the paper's head embeds with E_t only
+        with pytest.raises(L.LilicorrError):
+            L.weights_tensor_info(DIMS_, 1024, 0)
+    else:
+        with pytest.raises(L.LilicorrError):
+            L.weights_tensor_info(DIMS_, 1024, 56)
 
 
 def test_missing_library_fails_loudly(monkeypatch):

@@ -3,8 +3,9 @@
 Every workload runs at its full size on the GPU, in the launch configuration
 the benchmark times; the oracle recomputes sampled blocks one by one.
 Top-K ids must match exactly; lse and logp within 1e-3 * max(1, |oracle|);
-pair cosines and committed step scores within 1e-3 * max(1, |oracle|) for at
-least 99.9% of the elements and within the bf16 bound for all (the bound and
+pair cosines within 1e-3 * max(1, |oracle|), and committed step scores within
+max(1, |alpha|) times that (a step score carries alpha times its cosine's
+error), for at least 99.9% of the elements and within the bf16 bound for all (the bound and
 its derivation are in tests/helpers.py); committed tokens exactly, except
 where the oracle's score of the GPU's pick is within the score bound of the
 best (each such excused slot is reported).
@@ -82,7 +83,7 @@ def run_case(L, name, tier, sample, alpha=None, use_logp=True):
         frac = COS_FRACTION_OF.get(name, COS_FRACTION)
         sc = assert_scores(np.concatenate([c.ravel() for c in g_cos]),
                            np.concatenate([c.ravel() for c in o_cos]), f"{name} cos", 1.0, frac)
-        sz = assert_scores(np.concatenate(g_z), np.concatenate(o_z), f"{name} step scores", alpha, frac)
+        sz = assert_scores(np.concatenate(g_z), np.concatenate(o_z), f"{name} step scores", alpha, frac, step=True)
         print(f"[scores] {name} tier {tier}: cos {sc} step {sz}", flush=True)
     if excused:
         print(f"[excused] {name} tier {tier}: {excused}", flush=True)

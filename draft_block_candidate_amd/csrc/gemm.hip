@@ -923,7 +923,10 @@ GemmPlan plan_linear(int M, int Kd, int N) {
   int ks = 256;
   while (ks > 64 && (Kd % ks || (int64_t)p.tiles * (Kd / ks) < 256)) ks >>= 1;
   const int S = Kd / ks;
-  if (Kd % ks || S < 2 || S > 16 || (S & (S - 1)) || N % 4) return p;
+  // slice counts the reduce kernels are built for (3, 6 and 12 serve K = 3 x 2^k,
+  // the fusion layer of the paper's head)
+  const bool s_ok = S == 2 || S == 3 || S == 4 || S == 6 || S == 8 || S == 12 || S == 16;
+  if (Kd % ks || !s_ok || N % 4) return p;
   p.ks = ks;
   p.split = Kd / ks;
   p.part_floats = (size_t)p.split * M * N;
@@ -975,8 +978,11 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
   if (e != hipSuccess) return e;
   switch (p.split) {
     case 2: return launch_reduce<2>(M, N, bias, ep, out, part, stream);
+    case 3: return launch_reduce<3>(M, N, bias, ep, out, part, stream);
     case 4: return launch_reduce<4>(M, N, bias, ep, out, part, stream);
+    case 6: return launch_reduce<6>(M, N, bias, ep, out, part, stream);
     case 8: return launch_reduce<8>(M, N, bias, ep, out, part, stream);
+    case 12: return launch_reduce<12>(M, N, bias, ep, out, part, stream);
     default: return launch_reduce<16>(M, N, bias, ep, out, part, stream);
   }
 }

@@ -271,26 +271,15 @@ __device__ __forceinline__ void consume_group(State& st, const u32x4_t (&w)[NV],
   if (!st.seeded || __any(pmax >= st.p_th)) topk_pass<NV, EPV, LS>(st, w, pm, base, K, lane);
 }
 
-// One wave per (row, chunk). DT: 0 = fp32 logits, 1 = bf16 logits.
+// One wave streams chunk `unit` of P of a row: its sorted top-K list (one
+// entry per lane) and its (reference max, per-lane sum) state.
+// DT: 0 = fp32 logits, 1 = bf16 logits.
 template <int DT, int NV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_partial_kernel(const void* __restrict__ logits,
-                                                           int rows, int V, int K, int P,
-                                                           int id_offset, int final_out,
-                                                           float* __restrict__ part_val,
-                                                           int32_t* __restrict__ part_idx,
-                                                           float* __restrict__ part_ms,
-                                                           int32_t* __restrict__ topk_idx,
-                                                           float* __restrict__ topk_logp,
-                                                           float* __restrict__ lse_out) {
+__device__ __forceinline__ State stream_chunk(const void* __restrict__ logits, int row, int V, int K,
+                                              int P, int unit, int lane) {
   constexpr int EPV = DT == 1 ? 8 : 4;
   // a 32-bit word holding -inf in every element
   constexpr uint32_t kNegInfWord = DT == 1 ? 0xFF80FF80u : 0xFF800000u;
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.x * 4 + wid;
-  const int row = g / P, unit = g - (g / P) * P;
-  if (row >= rows) return;
-
   const int64_t rs = (int64_t)row * V, re = rs + V;
   int64_t a0 = (rs + EPV - 1) / EPV * EPV, a1 = re / EPV * EPV;
   if (a1 <= a0) {  // no whole aligned vector: the row is all head
@@ -367,7 +356,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   };
   if (unit == 0 && head_len > 0) do_edge(rs, head_len);
   if (unit == P - 1 && tail_len > 0) do_edge(a1, tail_len);
+  return st;
+}
 
+// One wave per (row, chunk).
+template <int DT, int NV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_partial_kernel(const void* __restrict__ logits,
+                                                           int rows, int V, int K, int P,
+                                                           int id_offset, int final_out,
+                                                           float* __restrict__ part_val,
+                                                           int32_t* __restrict__ part_idx,
+                                                           float* __restrict__ part_ms,
+                                                           int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_logp,
+                                                           float* __restrict__ lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.x * 4 + wid;
+  const int row = g / P, unit = g - (g / P) * P;
+  if (row >= rows) return;
+  const State st = stream_chunk<DT, NV>(logits, row, V, K, P, unit, lane);
   const float S = wave_sum(st.s);
   if (P == 1 && final_out) {
     // the row is one chunk: its sorted list is the answer
@@ -389,6 +397,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (lane == 0) {
     part_ms[2 * o] = st.ref;
     part_ms[2 * o + 1] = S;
+  }
+}
+
+// K-step tournament over P sorted lists held in LDS (list p at sv/si + p K,
+// ordered by (value desc, id asc), list p's ids all below list p + 1's):
+// lane k < K receives the k-th best (value, id). Lane p < P walks list p; hp
+// is its read position. Every step is straight-line (selects, a clamped LDS
+// read in every lane).
+__device__ __forceinline__ void tournament(const float* sv, const int* si, int P, int K, int lane,
+                                           float& rv, int& ri) {
+  const bool live = lane < P;
+  const int lb = min(lane, P - 1) * K;
+  float hv = live ? sv[lb] : -INFINITY;
+  int hi = live ? si[lb] : kInvalid;
+  int hp = 0;
+  rv = -INFINITY;
+  ri = kInvalid;
+  const int width = P <= 16 ? 16 : (P <= 32 ? 32 : 64);   // lanes >= P hold -inf
+  for (int k = 0; k < K; ++k) {
+    // Winner by (value desc, id asc): among equal values the lowest lane
+    // holds the lowest id, so a max plus the lowest lane of the ballot
+    // decides it.
+    const float bv = lanes_max(hv, width);
+    const int bl = __ffsll((long long)__ballot(hv == bv)) - 1;
+    const int bi = readlane_i(hi, bl);
+    rv = lane == k ? bv : rv;
+    ri = lane == k ? bi : ri;
+    const bool adv = (lane == bl) & live;
+    hp += adv ? 1 : 0;
+    const float nv = sv[lb + min(hp, K - 1)];
+    const int ni = si[lb + min(hp, K - 1)];
+    const bool more = hp < K;
+    hv = adv ? (more ? nv : -INFINITY) : hv;
+    hi = adv ? (more ? ni : kInvalid) : hi;
   }
 }
 
@@ -451,33 +493,9 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P, 
   const float S = wave_sum(s * __builtin_amdgcn_exp2f((m - M) * kL2E));
   const float lse = M + logf(S);
   __syncthreads();
-  // Lane p < P walks chunk p's sorted list; hp is its read position. Every
-  // step is straight-line (selects, a clamped LDS read in every lane).
-  const bool live = lane < P;
-  const int lb = min(lane, P - 1) * K;
-  float hv = live ? sv[lb] : -INFINITY;
-  int hi = live ? si[lb] : kInvalid;
-  int hp = 0;
-  float rv = -INFINITY;
-  int ri = kInvalid;
-  const int width = P <= 16 ? 16 : (P <= 32 ? 32 : 64);   // lanes >= P hold -inf
-  for (int k = 0; k < K; ++k) {
-    // Winner by (value desc, id asc): chunk p covers a contiguous id range
-    // below chunk p + 1's, so among equal values the lowest lane holds the
-    // lowest id, and a max plus the lowest lane of the ballot decides it.
-    const float bv = lanes_max(hv, width);
-    const int bl = __ffsll((long long)__ballot(hv == bv)) - 1;
-    const int bi = readlane_i(hi, bl);
-    rv = lane == k ? bv : rv;
-    ri = lane == k ? bi : ri;
-    const bool adv = (lane == bl) & live;
-    hp += adv ? 1 : 0;
-    const float nv = sv[lb + min(hp, K - 1)];
-    const int ni = si[lb + min(hp, K - 1)];
-    const bool more = hp < K;
-    hv = adv ? (more ? nv : -INFINITY) : hv;
-    hi = adv ? (more ? ni : kInvalid) : hi;
-  }
+  float rv;
+  int ri;
+  tournament(sv, si, P, K, lane, rv, ri);
   if (PARTIAL_OUT) {
     // topk_logp receives the merged values, lse_out the (max, sum) pair
     if (lane < K) {

@@ -81,8 +81,8 @@ def test_topk_row_counts_change_chunking(L, rows):
     _check_topk(L, host, 16)
 
 
-def test_topk_crafted_rows(L):
-    V = 5000
+@pytest.mark.parametrize("V", [5000, 40000])     # one chunk per row, several chunks per row
+def test_topk_crafted_rows(L, V):
     rows = []
     rows.append(np.full(V, 0.75, dtype=np.float32))                       # constant
     z = np.zeros(V, dtype=np.float32)

@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=float, default=0.0,
                     help="after the run, stream this many MiB through a plain copy kernel three "
                          "times (the known-size reference for HBM byte counters)")
+    ap.add_argument("--summarize-kernels", metavar="KT_DIR",
+                    help="no GPU: turn a rocprofv3 --kernel-trace --stats run of this script into a "
+                         "markdown table of kernel durations")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE, both with --copy-probe-mib) into HBM bytes per stage launch")
@@ -68,6 +71,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.summarize_kernels:
+        summarize_kernels(args.summarize_kernels)
+        return
     if args.summarize_counters:
         summarize_counters(args)
         return
@@ -534,6 +540,26 @@ def summarize_counters(args):
         f_b = sum(f) / max(1, len(f)) * 1024 * scale["FETCH_SIZE"]
         w_b = sum(wr) / max(1, len(wr)) * 1024 * scale["WRITE_SIZE"]
         print(f"| {st} | {int(round(f_b + w_b))} | {int(round(f_b))} | {int(round(w_b))} | {len(f)} |")
+
+
+def summarize_kernels(d):
+    """Markdown table of a rocprofv3 run_kernel_stats.csv (durations in microseconds)."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {d}")
+    print("| kernel | calls | avg us | min us | max us | % of kernel time |")
+    print("|---|---|---|---|---|---|")
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            m = re.search(r"(\w+(?:<[^()]*>)?)\(", name)
+            short = m.group(1) if m else name[:60]
+            print(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{float(r['Percentage']):.2f} |")
 
 
 def csrc_sha256():

@@ -109,3 +109,34 @@ def test_paper_head_errors_without_inputs(L):
     with pytest.raises(L.LilicorrError) as e:
         L.rerank(to_device(host), w.topk, device_weights(w), w.alpha, w.use_logp)
     assert e.value.code == L.EINVAL
+
+
+@pytest.mark.parametrize("B,K,N", [(2, 1, 3), (2, 5, 2), (3, 7, 4), (17, 3, 2)])
+def test_paper_head_degenerate_and_ragged(L, B, K, N):
+    # one drafted slot (B = 2), one candidate (K = 1), odd lattices and a ragged slot count
+    import torch
+    w = synth.Workload(f"paper_edge_{B}_{K}_{N}", N, B, 4096, K, 128, 2, 128, 64, "f32", "normal",
+                       alpha=8.0, use_logp=False, target_hidden=192, drafter_hidden=128)
+    rng = np.random.default_rng(B * 100 + K * 10 + N)
+    host = rng.standard_normal((N, B, w.vocab), dtype=np.float32)
+    hid_bits = synth.f32_to_bf16_bits_rne(rng.standard_normal((N, B, 128), dtype=np.float32))
+    tgt_bits = synth.f32_to_bf16_bits_rne(rng.standard_normal((N, 192), dtype=np.float32))
+    print(f"[case] paper head edge B {B} K {K} N {N}", flush=True)
+    tokens, dbg = L.rerank(to_device(host), K, device_weights(w), w.alpha, w.use_logp, debug=True,
+                           hidden=to_device(hid_bits), target=to_device(tgt_bits))
+    torch.cuda.synchronize()
+    ow = oracle_weights(w)
+    hidden = synth.bf16_bits_to_f32(hid_bits).astype(np.float64)
+    target = synth.bf16_bits_to_f32(tgt_bits).astype(np.float64)
+    for b in range(N):
+        r = oracle.rerank_block(host[b], K, ow, w.alpha, w.use_logp, hidden=hidden[b], target=target[b])
+        gidx = dbg["topk_idx"][b].cpu().numpy()
+        assert np.array_equal(gidx, r.idx), f"block {b}: top-K ids"
+        go, gi = bf16_to_f64(dbg["outv"][b]), bf16_to_f64(dbg["inv"][b])
+        assert np.abs(go - r.outv).max() < 2e-2 and np.abs(gi - r.inv).max() < 2e-2, f"block {b} in/out"
+        assert_scores(dbg["cos"][b].cpu().numpy(), r.cos, f"edge block {b} cos", 1.0, COS_FRACTION)
+        gtok = tokens[b].cpu().numpy()
+        choice = np.array([int(np.nonzero(gidx[s] == gtok[s])[0][0]) for s in range(B)])
+        ex = compare_walk(r.logp, r.cos, choice, w.alpha, w.use_logp)
+        if not ex:
+            assert np.array_equal(gtok, r.tokens.astype(np.int32)), f"block {b}: tokens"

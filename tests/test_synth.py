@@ -34,3 +34,20 @@ def test_block_prefix_is_reproducible():
 def test_bf16_input_rounding():
     x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0], dtype=np.float32)
     assert synth.bf16_bits_to_f32(synth.f32_to_bf16_bits_rne(x)).tolist() == [1.0, 1.0 + 2 ** -6, -0.0]
+
+
+def test_head_inputs_are_seeded_and_prefix_stable():
+    w = synth.WORKLOADS["paper_c32"]
+    h, t = synth.make_head_inputs(w)
+    assert h.shape == (32, 16, 4096) and t.shape == (32, 4096) and h.dtype == np.uint16
+    h2, t2 = synth.make_head_inputs(w, num_blocks=3)
+    assert np.array_equal(h[:3], h2) and np.array_equal(t[:3], t2)
+    x = synth.bf16_bits_to_f32(t)
+    assert abs(float(x.mean())) < 0.01 and abs(float(x.std()) - 1.0) < 0.01
+
+
+def test_uniforms_and_temperatures():
+    u = synth.make_uniforms(8, 16, seed=3)
+    assert u.dtype == np.float32 and np.all((u >= 0) & (u < 1))
+    t = synth.make_temperatures(9, seed=4)
+    assert np.all(t[::4] == 0) and np.all((t[1:4] >= 0.5) & (t[1:4] < 1.5))

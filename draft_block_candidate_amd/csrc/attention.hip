@@ -380,16 +380,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // Large lattices (T up to 512, where K and V do not fit in LDS together): one
-// workgroup of eight waves per (head, block) runs rounds of eight 16-query
-// tiles. Each round stages the head's K in LDS (row-major), computes every
-// tile's scores twice (first for the exact row max, then again, bit for bit,
-// to form P~ = bf16(p), which stays packed in registers), then overwrites the same LDS with V (row-major) and forms
-// O^T = V^T P~^T with V^T fragments read by ds_read_b64_tr_b16: within each
-// 16-lane group, source lane s addresses key k0 + s/4, columns 4 (s % 4) ..+3
-// of a 16-column d tile, and output lane i receives keys k0 .. k0 + 3 of
-// column i, which is the MFMA A-operand layout. Both K and V rows keep their
-// 32-byte d tiles XOR-swizzled by the key, so fragment reads spread over the
-// banks. K and V are re-staged once per round (from L2).
+// workgroup of eight waves per (head, block); each wave carries two 16-query
+// tiles, so every K or V fragment it reads from LDS feeds two MFMAs (rounds of
+// sixteen tiles). Pass 1 stages the head's K (row-major) and finds every
+// query's exact row max. Pass 2 stages K and V of one half of the keys at a
+// time (256 each) and, chunk of 32 keys by chunk, recomputes the identical
+// scores, forms P~ = bf16(exp(s - max)) and accumulates O^T = V^T P~^T at once,
+// so P~ lives for one chunk only. V^T fragments are read by ds_read_b64_tr_b16:
+// within each 16-lane group, source lane s addresses key k0 + s/4, columns
+// 4 (s % 4) ..+3 of a 16-column d tile, and output lane i receives keys
+// k0 .. k0 + 3 of column i, which is the MFMA A-operand layout. K and V rows
+// keep their 32-byte d tiles XOR-swizzled by the LDS row, so fragment reads
+// spread over the banks.
 template <int DH>
 __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __restrict__ qkv, int B,
                                                             int K, int H,
@@ -401,12 +403,12 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
   constexpr int KT = TMAX / 16, KS = DH / 32, DT = DH / 16, CPR = DH / 8;
   constexpr int SWM = DT - 1;         // d-tile swizzle mask
   constexpr int TOT = TMAX * CPR;     // 16-byte chunks of K (or V)
-  constexpr int NCH = TOT / (64 * NW);
-  static_assert(TOT % (64 * NW) == 0 && NCH % 2 == 0, "chunking");
-  __shared__ __attribute__((aligned(16))) uint16_t buf[TMAX * DH];
+  constexpr int HCH = TOT / 2 / (64 * NW);   // per thread, one half of the keys
+  static_assert(TOT % (2 * 64 * NW) == 0, "chunking");
+  __shared__ __attribute__((aligned(16))) uint16_t buf[TMAX * DH];   // K, or K half | V half
   __shared__ float bias_tab[128];
-  // element offset of 16-byte chunk c (8 columns) of row key
-  auto cat = [](int key, int c) { return key * DH + (((((c >> 1) ^ key) & SWM) << 1 | (c & 1)) << 3); };
+  // element offset of 16-byte chunk c (8 columns) of LDS row r
+  auto cat = [](int r, int c) { return r * DH + (((((c >> 1) ^ r) & SWM) << 1 | (c & 1)) << 3); };
 
   const int T = B * K;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -419,191 +421,205 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
   if (tid < 127) bias_tab[tid] = dist[h * 127 + tid];
   const float same_h = same[h];
 
-  // stage K (which = 1) or V (which = 2) of this head; rows past the lattice
-  // are read from its last token (masked to -inf / met with probability 0)
-  // (in two halves, to bound the staging registers; buffer loads with 32-bit
-  // offsets from a descriptor of this block's rows)
+  // Stage keys [256 kh, 256 kh + 256) of K (which = 1) or V (which = 2) into
+  // LDS rows [256 lh, 256 lh + 256); keys past the lattice are read from its
+  // last token (masked to -inf / met with probability 0). Buffer loads with
+  // 32-bit offsets from a descriptor of this block's rows, all issued before
+  // any store.
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)blk, 0, (int)(T * H3 * 2), 0x00020000);
-  auto stage = [&](int which) __attribute__((always_inline)) {
+  auto stage_half = [&](int which, int kh, int lh) __attribute__((always_inline)) {
     // an opaque copy of the thread index: the offsets below are recomputed
     // per call instead of being kept live (and spilled) across rounds
     int t0 = tid;
     asm volatile("" : "+v"(t0));
+    u32x4_t rr[HCH];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4_t rr[NCH / 2];
+    for (int i = 0; i < HCH; ++i) {
+      const int ch = t0 + 64 * NW * i;
+      const int key = min(256 * kh + ch / CPR, T - 1), c8 = ch % CPR;
+      const int off = (key * (int)H3 + which * H + h * DH + c8 * 8) * 2;
+      rr[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    }
 #pragma unroll
-      for (int i = 0; i < NCH / 2; ++i) {
-        const int ch = t0 + 64 * NW * (i + half * NCH / 2);
-        const int key = min(ch / CPR, T - 1), c8 = ch % CPR;
-        const int off = (key * (int)H3 + which * H + h * DH + c8 * 8) * 2;
-        rr[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < NCH / 2; ++i) {
-        const int ch = t0 + 64 * NW * (i + half * NCH / 2);
-        *(u32x4_t*)(&buf[cat(ch / CPR, ch % CPR)]) = rr[i];
-      }
+    for (int i = 0; i < HCH; ++i) {
+      const int ch = t0 + 64 * NW * i;
+      *(u32x4_t*)(&buf[cat(256 * lh + ch / CPR, ch % CPR)]) = rr[i];
     }
   };
 
   const float scale = 1.0f / __fsqrt_rn((float)DH);
   // slot of a token: (t * kmul) >> 16 equals t / K for t < 1024 and K <= 64
   const unsigned kmul = (65536u + K - 1) / K;
-  const int nkt = (T + 15) / 16, nch = (T + 31) / 32;
   const int ntile = (T + 15) / 16;
-  for (int r0 = 0; r0 < ntile; r0 += NW) {
-    const int qt = r0 + wave;
-    const bool tile_ok = qt < ntile;
-    const int q = qt * 16 + c;
-    const bool q_ok = q < T;
-    const int qc = min(q, T - 1);
-    const int slot_q = qc / K;
-    u32x4_t qf[KS];
+  for (int r0 = 0; r0 < ntile; r0 += 2 * NW) {
+    const int qta = r0 + wave, qtb = r0 + NW + wave;
+    const bool oka = qta < ntile, okb = qtb < ntile;
+    const int qa = qta * 16 + c, qb = qtb * 16 + c;
+    const int qca = min(qa, T - 1), qcb = min(qb, T - 1);
+    const int slot_qa = qca / K, slot_qb = qcb / K;
+    u32x4_t qfa[KS], qfb[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = *(const u32x4_t*)(blk + (int64_t)qc * H3 + h * DH + ks * 32 + 8 * g);
+    for (int ks = 0; ks < KS; ++ks) {
+      qfa[ks] = *(const u32x4_t*)(blk + (int64_t)qca * H3 + h * DH + ks * 32 + 8 * g);
+      qfb[ks] = *(const u32x4_t*)(blk + (int64_t)qcb * H3 + h * DH + ks * 32 + 8 * g);
+    }
     // LDS fragment addresses derive from an opaque per-round base, so they are
     // recomputed each round rather than hoisted out of the loop (and spilled)
     int zb = 0;
     asm volatile("" : "+v"(zb));
     const uint16_t* lb = buf + zb;
-    __syncthreads();   // previous round done with buf (V)
-    stage(1);
+    __syncthreads();   // previous round done with buf
+    stage_half(1, 0, 0);
+    stage_half(1, 1, 1);
     __syncthreads();
-    u32x4_t pb[KT / 2];
-    float lsum = 0.f;
-    if (tile_ok) {
-      // Scores of four key tiles (independent MFMA chains), masked and biased.
-      auto scores4 = [&](int kt0, float (&v)[4][4]) __attribute__((always_inline)) {
-        f32x4_t acc[4];
+    // Scores of key tiles kt0, kt0 + 1 (LDS rows from lr0) for both query
+    // tiles, masked and biased; each K fragment read feeds two MFMAs.
+    auto scores2 = [&](int kt0, int lr0, float (&va)[2][4], float (&vb)[2][4]) __attribute__((always_inline)) {
+      f32x4_t aa[2], ab[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4_t kf = *(const u32x4_t*)(&lb[cat((kt0 + j) * 16 + c, ks * 4 + g)]);
-            acc[j] = mfma16(kf, qf[ks], acc[j]);
-          }
-        if (K % 16 == 0) {
-          // every 16-key tile lies in one slot: one table read per tile, no
-          // per-element branch (a read under one is waited for inside it)
-          float bt[4];
-          int st[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            st[j] = (int)(((unsigned)min((kt0 + j) * 16 + zb, T - 1) * kmul) >> 16);
-            bt[j] = bias_tab[st[j] - slot_q + 63];
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
-              float x = acc[j][i] * scale + bt[j];
-              x = st[j] == slot_q ? x + same_h : x;
-              v[j][i] = key < T ? x : -INFINITY;
-            }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
-              float x = -INFINITY;
-              if (key < T) {
-                const int slot_k = (int)(((unsigned)key * kmul) >> 16);
-                x = acc[j][i] * scale + bias_tab[slot_k - slot_q + 63];
-                if (slot_k == slot_q) x += same_h;
-              }
-              v[j][i] = x;
-            }
-        }
-      };
-      // pass 1: exact row max; pass 2 recomputes the identical scores (the
-      // full strip would not fit in registers beside P~) and forms P~
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt0 = 0; kt0 < KT; kt0 += 4) {
-        if (kt0 * 16 < T) {
-          float v[4][4];
-          scores4(kt0, v);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, v[j][i]);
-        }
+      for (int j = 0; j < 2; ++j) {
+        aa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ab[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 #pragma unroll
-      for (int kt0 = 0; kt0 < KT; kt0 += 4) {
-        float v[4][4];
-        if (kt0 * 16 < T) {
-          scores4(kt0, v);
-        } else {
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[j][i] = -INFINITY;
+        for (int j = 0; j < 2; ++j) {
+          const u32x4_t kf = *(const u32x4_t*)(&lb[cat(lr0 + j * 16 + c, ks * 4 + g)]);
+          aa[j] = mfma16(kf, qfa[ks], aa[j]);
+          ab[j] = mfma16(kf, qfb[ks], ab[j]);
         }
+      if (K % 16 == 0) {
+        // every 16-key tile lies in one slot: one table read per tile and
+        // query tile, no per-element branch
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j) {
+          const int st = (int)(((unsigned)min((kt0 + j) * 16 + zb, T - 1) * kmul) >> 16);
+          const float ba = bias_tab[st - slot_qa + 63], bb = bias_tab[st - slot_qb + 63];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[j][i] = __expf(v[j][i] - mx);
-            lsum += v[j][i];
+            const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
+            float x = aa[j][i] * scale + ba;
+            x = st == slot_qa ? x + same_h : x;
+            va[j][i] = key < T ? x : -INFINITY;
+            float y = ab[j][i] * scale + bb;
+            y = st == slot_qb ? y + same_h : y;
+            vb[j][i] = key < T ? y : -INFINITY;
           }
-        // k-slot j of lane group g stands for key 32*ch + 4g + j (j < 4) or
-        // 32*ch + 16 + 4g + (j - 4) (j >= 4), matching the score layout
+        }
+      } else {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int ch = kt0 / 2 + h2;
-          pb[ch][0] = pack_bf16x2(v[2 * h2][0], v[2 * h2][1]);
-          pb[ch][1] = pack_bf16x2(v[2 * h2][2], v[2 * h2][3]);
-          pb[ch][2] = pack_bf16x2(v[2 * h2 + 1][0], v[2 * h2 + 1][1]);
-          pb[ch][3] = pack_bf16x2(v[2 * h2 + 1][2], v[2 * h2 + 1][3]);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
+            float x = -INFINITY, y = -INFINITY;
+            if (key < T) {
+              const int slot_k = (int)(((unsigned)key * kmul) >> 16);
+              x = aa[j][i] * scale + bias_tab[slot_k - slot_qa + 63];
+              y = ab[j][i] * scale + bias_tab[slot_k - slot_qb + 63];
+              if (slot_k == slot_qa) x += same_h;
+              if (slot_k == slot_qb) y += same_h;
+            }
+            va[j][i] = x;
+            vb[j][i] = y;
+          }
+      }
+    };
+    // pass 1: the exact row maxima
+    float mxa = -INFINITY, mxb = -INFINITY;
+    if (oka) {
+#pragma unroll 4
+      for (int kt0 = 0; kt0 < KT; kt0 += 2) {
+        if (kt0 * 16 < T) {
+          float va[2][4], vb[2][4];
+          scores2(kt0, kt0 * 16, va, vb);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              mxa = fmaxf(mxa, va[j][i]);
+              mxb = fmaxf(mxb, vb[j][i]);
+            }
         }
       }
-      lsum += __shfl_xor(lsum, 16, 64);
-      lsum += __shfl_xor(lsum, 32, 64);
+      mxa = fmaxf(mxa, __shfl_xor(mxa, 16, 64));
+      mxa = fmaxf(mxa, __shfl_xor(mxa, 32, 64));
+      mxb = fmaxf(mxb, __shfl_xor(mxb, 16, 64));
+      mxb = fmaxf(mxb, __shfl_xor(mxb, 32, 64));
     }
-    __syncthreads();   // every wave is done with K
-    stage(2);
-    __syncthreads();
-    if (tile_ok) {
-      f32x4_t oacc[DT];
+    // pass 2: per half of the keys, K and V side by side in LDS
+    f32x4_t oa[DT], ob[DT];
 #pragma unroll
-      for (int d = 0; d < DT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int s = c;   // source lane within the 16-lane group
+    for (int d = 0; d < DT; ++d) {
+      oa[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      ob[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float la = 0.f, lbs = 0.f;
+    for (int kh = 0; kh < 2; ++kh) {
+      if (256 * kh >= T) break;
+      __syncthreads();   // every wave is done with the previous contents
+      stage_half(1, kh, 0);
+      stage_half(2, kh, 1);
+      __syncthreads();
+      if (!oka) continue;
+      for (int ch = 0; ch < 8; ++ch) {
+        const int gch = 8 * kh + ch;   // global 32-key chunk
+        if (gch * 32 >= T) break;
+        float va[2][4], vb[2][4];
+        scores2(2 * gch, 32 * ch, va, vb);
 #pragma unroll
-      for (int ch = 0; ch < KT / 2; ++ch) {
-        if (ch < nch) {
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            va[j][i] = __expf(va[j][i] - mxa);
+            la += va[j][i];
+            vb[j][i] = __expf(vb[j][i] - mxb);
+            lbs += vb[j][i];
+          }
+        // k-slot j of lane group g stands for key 32 ch + 4g + j (j < 4) or
+        // 32 ch + 16 + 4g + (j - 4) (j >= 4), matching the score layout
+        const u32x4_t pa = {pack_bf16x2(va[0][0], va[0][1]), pack_bf16x2(va[0][2], va[0][3]),
+                            pack_bf16x2(va[1][0], va[1][1]), pack_bf16x2(va[1][2], va[1][3])};
+        const u32x4_t pb = {pack_bf16x2(vb[0][0], vb[0][1]), pack_bf16x2(vb[0][2], vb[0][3]),
+                            pack_bf16x2(vb[1][0], vb[1][1]), pack_bf16x2(vb[1][2], vb[1][3])};
+        const int s = c;   // source lane within the 16-lane group
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
-          const int k_lo = 32 * ch + 4 * g + s / 4, k_hi = k_lo + 16;
+          const int k_lo = 256 + 32 * ch + 4 * g + s / 4, k_hi = k_lo + 16;
           const int c8 = 2 * d + (s & 3) / 2, off = 4 * (s & 1);
           const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4i16_t*)(&lb[cat(k_lo, c8) + off]));
           const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4i16_t*)(&lb[cat(k_hi, c8) + off]));
           const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
-          const u32x4_t va = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          oacc[d] = mfma16(va, pb[ch], oacc[d]);
-        }
+          const u32x4_t vf = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          oa[d] = mfma16(vf, pa, oa[d]);
+          ob[d] = mfma16(vf, pb, ob[d]);
         }
       }
-      if (q_ok) {
-        const float inv = 1.0f / lsum;
-        uint16_t* orow = out + (n * T + q) * (int64_t)H + h * DH;
+    }
+    if (oka) {
+      la += __shfl_xor(la, 16, 64);
+      la += __shfl_xor(la, 32, 64);
+      lbs += __shfl_xor(lbs, 16, 64);
+      lbs += __shfl_xor(lbs, 32, 64);
+      if (qa < T) {
+        const float inv = 1.0f / la;
+        uint16_t* orow = out + (n * T + qa) * (int64_t)H + h * DH;
 #pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          const uint32_t w0 = pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv);
-          const uint32_t w1 = pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv);
-          *(uint2*)(orow + d * 16 + 4 * g) = make_uint2(w0, w1);
-        }
+        for (int d = 0; d < DT; ++d)
+          *(uint2*)(orow + d * 16 + 4 * g) =
+              make_uint2(pack_bf16x2(oa[d][0] * inv, oa[d][1] * inv), pack_bf16x2(oa[d][2] * inv, oa[d][3] * inv));
+      }
+      if (okb && qb < T) {
+        const float inv = 1.0f / lbs;
+        uint16_t* orow = out + (n * T + qb) * (int64_t)H + h * DH;
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+          *(uint2*)(orow + d * 16 + 4 * g) =
+              make_uint2(pack_bf16x2(ob[d][0] * inv, ob[d][1] * inv), pack_bf16x2(ob[d][2] * inv, ob[d][3] * inv));
       }
     }
   }

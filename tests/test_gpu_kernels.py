@@ -167,7 +167,8 @@ def test_rmsnorm(L, M, H):
 @pytest.mark.parametrize("N,B,K,heads,dh", [(1, 16, 4, 2, 32), (2, 16, 8, 8, 128), (1, 16, 16, 8, 128),
                                             (1, 16, 32, 16, 128), (3, 5, 3, 2, 64), (1, 1, 1, 1, 32),
                                             (2, 7, 9, 4, 32), (1, 64, 8, 2, 64), (2, 25, 8, 4, 64),
-                                            (3, 10, 13, 2, 128)])
+                                            (3, 10, 13, 2, 128), (2, 20, 15, 2, 32), (1, 17, 16, 4, 128),
+                                            (2, 33, 9, 2, 64)])
 def test_lattice_attention(L, N, B, K, heads, dh):
     rng = np.random.default_rng(N * 1000 + B * 10 + K)
     H = heads * dh

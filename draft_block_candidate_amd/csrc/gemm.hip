@@ -958,8 +958,10 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
         e = launch_dma<256, 256, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
       else if (tiles(256, 128) >= 256)
         e = launch_dma<256, 128, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
-      else
+      else if (tiles(128, 128) >= 384)
         e = launch_dma<128, 128, 4>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+      else   // a few thousand rows of a narrow output: 128 x 64 tiles, three workgroups per CU
+        e = launch_dma<128, 64, 4>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     } else if (M >= 2048)
       e = launch_tile<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     else if (M > 64)

@@ -420,9 +420,9 @@ def stage_work(w, sid):
             return lin(H, 2 * de, 2, 2)
         tnorm = {"bytes": N * Ht * 4 + Ht * 4, "flops": 3 * N * Ht}
         concat = {"bytes": M * H * 2 + N * H * 2 + M * 3 * H * 2, "flops": M * H}
-        assemble = {"bytes": 2 * M * de * 2 * 2 + N * de * 4, "flops": 3 * N * de}
+        anchor = {"bytes": N * de * 4 + 2 * N * K * de * 2, "flops": 3 * N * de}
         return add(tnorm, lin(Ht, H, 2, 2, m=N), lin(H, de, 2, 4, m=N), concat,
-                   lin(3 * H, H, 2, 2), lin(H, 2 * de, 2, 2), assemble)
+                   lin(3 * H, H, 2, 2), lin(H, 2 * de, 2, 2), anchor)
     return {"bytes": 2 * rows * K * de * 2 + rows * K * 8 + rows * 4,
             "flops": 2 * N * (B - 1) * K * K * de}
 

@@ -308,13 +308,13 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
     uint16_t* tnorm = (uint16_t*)(ws + L.tnorm);
     uint16_t* tb = (uint16_t*)(ws + L.tb);
     float* apre = (float*)(ws + L.apre);
-    uint16_t* lat_out = (uint16_t*)(ws + L.lat_out);
-    uint16_t* lat_in = (uint16_t*)(ws + L.lat_in);
     uint16_t* cat = qkv;     // [Mp, 3H] bf16: the layers are done with qkv
     uint16_t* y = attn;      // [Mp, H] bf16
     LinearEpilogue e = plain(EPI_F32);
-    e.heads_out = lat_out;
-    e.heads_in = lat_in;
+    e.heads_out = outv;           // lattice row (n, s - 1, j) -> row (n, s, j)
+    e.heads_in = inv;
+    e.heads_group = Bl * K;
+    e.heads_skip = K;
     LL_STAGE(LILICORR_STAGE_HEADS, {
       LL_TRY(launch_rmsnorm_bf16(p->target, N, Ht, W.gamma_t, kRmsEps, tnorm, st));
       LL_TRY(launch_linear(tnorm, N, Ht, W.w_tgt, H, W.b_tgt, plain(EPI_BF16), tb, gpart, st));
@@ -322,15 +322,24 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
       LL_TRY(launch_concat(u, tb, N, Bl * K, H, cat, st));
       LL_TRY(launch_linear(cat, Mp, 3 * H, W.w_fuse, H, W.b_fuse, plain(EPI_SILU_BF16), y, gpart, st));
       LL_TRY(launch_linear(y, Mp, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st));
-      LL_TRY(launch_assemble(lat_out, lat_in, apre, N, B, K, de, outv, inv, st));
+      LL_TRY(launch_anchor_rows(apre, N, B, K, de, outv, inv, st));
     });
   }
   // a5: pair scores, a6: the commit (one fused kernel: B * K <= 512 keeps the
-  // block's cosines within the kernel's LDS budget)
+  // block's cosines within the kernel's LDS budget). Wide vectors: the pair
+  // products first, in d_e slices over many waves (into the heads buffer,
+  // which the heads are done with), then the walk adds the slices.
   LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, false));
-  LL_TRY(launch_scores_walk(outv, inv, nullptr, topk_idx, topk_logp, N, B, K, de,
-                            commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score, p->dbg_gap,
-                            st));
+  if (de >= kPairSliceMinDe) {
+    LL_TRY(launch_pair_slices(outv, inv, N, B, K, de, heads_v, st));
+    LL_TRY(launch_scores_walk(nullptr, nullptr, heads_v, pair_slice_count(de), topk_idx, topk_logp,
+                              N, B, K, de, commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score,
+                              p->dbg_gap, st));
+  } else {
+    LL_TRY(launch_scores_walk(outv, inv, nullptr, 1, topk_idx, topk_logp, N, B, K, de,
+                              commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score, p->dbg_gap,
+                              st));
+  }
   LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, true));
 #undef LL_STAGE
   return LILICORR_OK;
@@ -427,7 +436,7 @@ int lilicorr_best_path(const int32_t* topk_idx, const float* topk_logp, const fl
   r.kind = RULE_EXACT;
   r.alpha = alpha;
   r.use_logp = use_logp;
-  return hip_status(launch_scores_walk(nullptr, nullptr, cos, topk_idx, topk_logp, N, B, K, 0, r,
+  return hip_status(launch_scores_walk(nullptr, nullptr, cos, 1, topk_idx, topk_logp, N, B, K, 0, r,
                                        nullptr, out_tokens, score, nullptr, (hipStream_t)stream));
 }
 
@@ -447,7 +456,7 @@ int lilicorr_sample_path(const int32_t* topk_idx, const float* topk_logp, const 
   r.temperature = temperature;
   r.uniforms = uniforms;
   r.proposal = proposal;
-  return hip_status(launch_scores_walk(nullptr, nullptr, cos, topk_idx, topk_logp, N, B, K, 0, r,
+  return hip_status(launch_scores_walk(nullptr, nullptr, cos, 1, topk_idx, topk_logp, N, B, K, 0, r,
                                        nullptr, out_tokens, score, nullptr, (hipStream_t)stream));
 }
 

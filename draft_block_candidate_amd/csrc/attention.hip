@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VT_STRIDE];
 
   const int T = B * K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int h = blockIdx.y;
   const int64_t n = blockIdx.z;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto cat = [](int key, int c) { return key * DH + (((((c >> 1) ^ key) & SWM) << 1 | (c & 1)) << 3); };
 
   const int T = B * K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int h = blockIdx.x;
   const int64_t n = blockIdx.y;

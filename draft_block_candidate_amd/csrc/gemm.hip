@@ -740,11 +740,12 @@ __global__ __launch_bounds__(256) void splitk_resid_rmsnorm_kernel(
 }
 
 // Out/in heads: y = A W^T + b over N = 2 d_e, each half normalised to unit
-// length and rounded to bf16. One wave per row; d_e % 4 == 0.
+// length and rounded to bf16, stored in row heads_row(m, group, skip). One
+// wave per row; d_e % 4 == 0.
 template <int S, int NV>
 __global__ __launch_bounds__(256) void splitk_heads_l2norm_kernel(
     const float* __restrict__ part, int M, int de, const float* __restrict__ bias,
-    uint16_t* __restrict__ outv, uint16_t* __restrict__ inv) {
+    uint16_t* __restrict__ outv, uint16_t* __restrict__ inv, int group, int skip) {
   const int lane = threadIdx.x & 63;
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
@@ -776,7 +777,7 @@ __global__ __launch_bounds__(256) void splitk_heads_l2norm_kernel(
     if (gi < n4) {
       const bool hi = gi >= h4;
       const float nr = hi ? n1 : n0;
-      uint16_t* dst = (hi ? inv : outv) + m * de + (hi ? gi - h4 : gi) * 4;
+      uint16_t* dst = (hi ? inv : outv) + heads_row(m, group, skip) * de + (hi ? gi - h4 : gi) * 4;
       *(uint2*)dst = make_uint2(pack_bf16x2(__fdiv_rn(v[i].x, nr), __fdiv_rn(v[i].y, nr)),
                                 pack_bf16x2(__fdiv_rn(v[i].z, nr), __fdiv_rn(v[i].w, nr)));
     }
@@ -848,13 +849,16 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
   if (ep.kind == EPI_F32 && ep.heads_out) {
     if (N <= 256)
       hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 1>), dim3(row_blocks), dim3(256), 0, stream,
-                         part, M, N / 2, bias, ep.heads_out, ep.heads_in);
+                         part, M, N / 2, bias, ep.heads_out, ep.heads_in, ep.heads_group,
+                         ep.heads_skip);
     else if (N <= 1024)
       hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 4>), dim3(row_blocks), dim3(256), 0, stream,
-                         part, M, N / 2, bias, ep.heads_out, ep.heads_in);
+                         part, M, N / 2, bias, ep.heads_out, ep.heads_in, ep.heads_group,
+                         ep.heads_skip);
     else
       hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 8>), dim3(row_blocks), dim3(256), 0, stream,
-                         part, M, N / 2, bias, ep.heads_out, ep.heads_in);
+                         part, M, N / 2, bias, ep.heads_out, ep.heads_in, ep.heads_group,
+                         ep.heads_skip);
     return hipGetLastError();
   }
   const int64_t MN4 = (int64_t)M * N / 4;
@@ -970,7 +974,8 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
       e = launch_tile<64, 32>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     if (e != hipSuccess) return e;
     if (ep.norm_out) return launch_rmsnorm((const float*)out, M, N, ep.norm_gamma, ep.eps, ep.norm_out, stream);
-    if (ep.heads_out) return launch_heads_l2norm((const float*)out, M, N / 2, ep.heads_out, ep.heads_in, stream);
+    if (ep.heads_out) return launch_heads_l2norm((const float*)out, M, N / 2, ep.heads_out, ep.heads_in,
+                                                ep.heads_group, ep.heads_skip, stream);
     return hipSuccess;
   }
   hipError_t e;

@@ -40,18 +40,18 @@ hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, in
 
 // The paper's head (paper_head.hip).
 //   gather_rows: out [N (B-1) K, Ht] = table[token] of the drafted candidates
-//   rmsnorm_bf16: out = bf16(RMSNorm(x)) for bf16 rows x [M, H]
+//   rmsnorm_bf16: out = bf16(RMSNorm(x)) for bf16 rows x [M, H] (H % 8 == 0, H <= 8192)
 //   concat: out [N P, 3H] = [u, tb[n], bf16(u * tb[n])], P lattice rows per block
-//   assemble: outv/inv [N, B, K, d_e]: slot 0 = unit(apre[n]) (in rows 0), slots
-//             >= 1 = the lattice's out/in rows
+//   anchor_rows: slot 0 of outv/inv [N, B, K, d_e]: out rows = unit(apre[n]),
+//                in rows = 0 (d_e <= 1024)
 hipError_t launch_gather_rows(const int32_t* topk_idx, int N, int B, int K, const uint16_t* table,
                               int Ht, int V, uint16_t* out, hipStream_t stream);
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int M, int H, const float* gamma, float eps,
                                uint16_t* out, hipStream_t stream);
 hipError_t launch_concat(const uint16_t* u, const uint16_t* tb, int N, int per_block, int H,
                          uint16_t* out, hipStream_t stream);
-hipError_t launch_assemble(const uint16_t* lat_out, const uint16_t* lat_in, const float* apre, int N,
-                           int B, int K, int de, uint16_t* outv, uint16_t* inv, hipStream_t stream);
+hipError_t launch_anchor_rows(const float* apre, int N, int B, int K, int de, uint16_t* outv,
+                              uint16_t* inv, hipStream_t stream);
 
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SILU_BF16 = 2, EPI_RESID_F32 = 3 };
 
@@ -70,7 +70,9 @@ bool uses_skinny(int M, int Kd, int N);
 //   kind       EPI_* store of y (EPI_RESID_F32: out = resid + y)
 //   norm_out   if set (with EPI_RESID_F32): also u = bf16(RMSNorm(out; norm_gamma, eps))
 //   heads_out  if set (with EPI_F32, N = 2 d_e): unit-normalised bf16 halves to
-//              heads_out / heads_in (out then receives y only when not split)
+//              heads_out / heads_in (out then receives y only when not split);
+//              with heads_group > 0, row m lands in row
+//              m + (m / heads_group + 1) heads_skip of heads_out / heads_in
 struct LinearEpilogue {
   int kind = EPI_F32;
   const float* resid = nullptr;
@@ -79,7 +81,13 @@ struct LinearEpilogue {
   uint16_t* norm_out = nullptr;
   uint16_t* heads_out = nullptr;
   uint16_t* heads_in = nullptr;
+  int heads_group = 0, heads_skip = 0;
 };
+
+// Destination row of the out/in heads' row m (see LinearEpilogue).
+__host__ __device__ inline int64_t heads_row(int64_t m, int group, int skip) {
+  return group > 0 ? m + (m / group + 1) * skip : m;
+}
 
 // Y = A[M,Kd] W[N,Kd]^T + bias with the epilogue above (bf16 in, fp32
 // accumulate, MFMA). part: fp32 scratch of plan_linear(M, Kd, N).part_floats.
@@ -96,7 +104,7 @@ hipError_t launch_attention(const uint16_t* qkv, int N, int B, int K, int H, int
 
 // Row-wise unit normalisation of v [M, 2 d_e] (out half | in half) to bf16.
 hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, uint16_t* inv,
-                               hipStream_t stream);
+                               int group, int skip, hipStream_t stream);
 
 hipError_t launch_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
                               int d_e, float* cos, hipStream_t stream);
@@ -113,14 +121,23 @@ struct CommitRule {
 };
 
 // Fused a5 + a6 (cosines in LDS; cos_out may be null). With cos_in set, the
-// cosines [N, B-1, K, K] are read instead of computed (outv/inv unused).
+// cosines [N, B-1, K, K] are read instead of computed (outv/inv unused); with
+// cos_slices > 1 they are the sum, in slice order, of cos_slices such arrays
+// stored one after another (the partial products of launch_pair_slices).
 // Needs scores_walk_lds_bytes(B, K) <= kScoresWalkMaxLds.
 constexpr size_t kScoresWalkMaxLds = 128 * 1024;
 size_t scores_walk_lds_bytes(int B, int K);
 hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const float* cos_in,
-                              const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
-                              int d_e, const CommitRule& rule, float* cos_out, int32_t* out_tokens,
-                              float* score, float* gap, hipStream_t stream);
+                              int cos_slices, const int32_t* topk_idx, const float* topk_logp,
+                              int N, int B, int K, int d_e, const CommitRule& rule, float* cos_out,
+                              int32_t* out_tokens, float* score, float* gap, hipStream_t stream);
+
+// Pair cosines of wide vectors in 256-wide slices of d_e: part holds
+// pair_slice_count(d_e) arrays [N, B-1, K, K] of partial sums.
+constexpr int kPairSliceMinDe = 512;
+inline int pair_slice_count(int d_e) { return (d_e + 255) / 256; }
+hipError_t launch_pair_slices(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
+                              int d_e, float* part, hipStream_t stream);
 
 hipError_t launch_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos,
                               int N, int B, int K, float alpha, int use_logp, int32_t* out_tokens,

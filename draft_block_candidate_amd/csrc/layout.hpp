@@ -218,9 +218,9 @@ struct RerankWs {
   size_t topk, topk_idx, topk_logp, x, hid, u, qkv, attn, heads, outv, inv, gemm_part;
   // the paper's head: projected hidden states [N B, H] f32, gathered target
   // embedding rows [M', H_t] bf16, normalised target [N, H_t] bf16, projected
-  // target [N, H] bf16, anchor head before normalisation [N, d_e] f32, lattice
-  // out/in vectors [M', d_e] bf16 (M' = N (B-1) K)
-  size_t ph, ae, tnorm, tb, apre, lat_out, lat_in;
+  // target [N, H] bf16, anchor head before normalisation [N, d_e] f32
+  // (M' = N (B-1) K)
+  size_t ph, ae, tnorm, tb, apre;
   size_t total;
 };
 
@@ -269,7 +269,7 @@ inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims
   const bool paper = d.target_hidden > 0;
   const size_t Mp = paper ? (size_t)N * (B - 1) * K : M;   // lattice rows
   w.gemm_part = take(rerank_gemm_scratch((int)Mp, d, N * B, N) * 4);
-  w.ph = w.ae = w.tnorm = w.tb = w.apre = w.lat_out = w.lat_in = 0;
+  w.ph = w.ae = w.tnorm = w.tb = w.apre = 0;
   if (paper) {
     const size_t Ht = d.target_hidden;
     w.ph = take(rows * H * 4);
@@ -277,8 +277,6 @@ inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims
     w.tnorm = take((size_t)N * Ht * 2);
     w.tb = take((size_t)N * H * 2);
     w.apre = take((size_t)N * de * 4);
-    w.lat_out = take(Mp * de * 2);
-    w.lat_in = take(Mp * de * 2);
   }
   w.total = off;
   return w;

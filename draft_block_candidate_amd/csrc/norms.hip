@@ -70,17 +70,19 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const float* __restric
   }
 }
 
-// One wave per (token, head): v / max(|v|, 1e-12) rounded to bf16.
+// One wave per (token, head): v / max(|v|, 1e-12) rounded to bf16, stored
+// in row heads_row(m, group, skip).
 __global__ __launch_bounds__(256) void heads_l2norm_kernel(const float* __restrict__ v, int M,
                                                            int de, uint16_t* __restrict__ outv,
-                                                           uint16_t* __restrict__ inv) {
+                                                           uint16_t* __restrict__ inv, int group,
+                                                           int skip) {
   const int lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= 2 * (int64_t)M) return;
   const int64_t m = w >> 1;
   const int half = (int)(w & 1);
   const float* src = v + m * 2 * de + half * de;
-  uint16_t* dst = (half ? inv : outv) + m * de;
+  uint16_t* dst = (half ? inv : outv) + heads_row(m, group, skip) * de;
   float ss = 0.f;
   for (int d = lane; d < de; d += 64) ss = fmaf(src[d], src[d], ss);
   ss = wave_sum(ss);
@@ -104,11 +106,11 @@ hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, floa
 }
 
 hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, uint16_t* inv,
-                               hipStream_t stream) {
+                               int group, int skip, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int64_t waves = 2 * (int64_t)M;
   hipLaunchKernelGGL(heads_l2norm_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
-                     v, M, d_e, outv, inv);
+                     v, M, d_e, outv, inv, group, skip);
   return hipGetLastError();
 }
 

@@ -5,9 +5,10 @@
 //     as the A operand of the embedding projection;
 //   * RMSNorm of the bf16 target state before its projection;
 //   * the fusion layer's input: the concatenation [node, t', node * t'];
-//   * the anchor's out vector (unit-normalised) and the [N, B, K, d_e] layout
-//     the pair scores read: slot 0 carries the anchor vector in every candidate
-//     row, slots 1..B-1 the lattice's out/in vectors.
+//   * the anchor's out vector (unit-normalised) in slot 0 of the [N, B, K, d_e]
+//     layout the pair scores read: every candidate row of slot 0 carries it
+//     (slots 1..B-1 hold the lattice's out/in vectors, which the heads linear
+//     stores there itself).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,34 +31,53 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restr
   for (int c = threadIdx.x; c < Ht / 8; c += blockDim.x) dst[c] = src[c];
 }
 
-// One wave per row of bf16 x: out = bf16((x * rstd) * gamma), rstd =
-// 1 / sqrt(mean(x^2) + eps), the arithmetic of the fp32 RMSNorm kernels.
-__global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const uint16_t* __restrict__ x, int M, int H,
+// One workgroup per row of bf16 x (H <= 8192): out = bf16((x * rstd) *
+// gamma), rstd = 1 / sqrt(mean(x^2) + eps), the arithmetic of the fp32
+// RMSNorm kernels. Each thread loads its (at most four) 8-element chunks once,
+// all before the first is used.
+__global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const uint16_t* __restrict__ x, int H,
                                                            const float* __restrict__ gamma, float eps,
                                                            uint16_t* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
-  const uint2* xr = (const uint2*)(x + row * H);
+  constexpr int NC = 4;
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int h8 = H / 8;
+  const uint4* xr = (const uint4*)(x + row * H);
+  uint4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) v[i] = xr[min(tid + 256 * i, h8 - 1)];   // clamped: unconditional
   float ss = 0.f;
-  for (int c4 = lane; c4 < H / 4; c4 += 64) {
-    const uint2 v = xr[c4];
-    const float a = bf16_to_f32(v.x & 0xFFFF), b = bf16_to_f32(v.x >> 16);
-    const float c = bf16_to_f32(v.y & 0xFFFF), d = bf16_to_f32(v.y >> 16);
-    ss = fmaf(a, a, ss);
-    ss = fmaf(b, b, ss);
-    ss = fmaf(c, c, ss);
-    ss = fmaf(d, d, ss);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (tid + 256 * i >= h8) continue;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bf16_to_f32(w[q] & 0xFFFF), b = bf16_to_f32(w[q] >> 16);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
   }
   ss = wave_sum(ss);
-  const float rstd = 1.0f / __fsqrt_rn(ss / (float)H + eps);
-  const float4* g4 = (const float4*)gamma;
-  uint2* o2 = (uint2*)(out + row * H);
-  for (int c4 = lane; c4 < H / 4; c4 += 64) {
-    const uint2 v = xr[c4];
-    const float4 g = g4[c4];
-    o2[c4] = make_uint2(pack_bf16x2(bf16_to_f32(v.x & 0xFFFF) * rstd * g.x, bf16_to_f32(v.x >> 16) * rstd * g.y),
-                        pack_bf16x2(bf16_to_f32(v.y & 0xFFFF) * rstd * g.z, bf16_to_f32(v.y >> 16) * rstd * g.w));
+  if (lane == 0) s_red[wave] = ss;
+  __syncthreads();
+  const float tot = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  const float rstd = 1.0f / __fsqrt_rn(tot / (float)H + eps);
+  uint4* o = (uint4*)(out + row * H);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + 256 * i;
+    if (c >= h8) continue;
+    const float4 g0 = ((const float4*)gamma)[2 * c], g1 = ((const float4*)gamma)[2 * c + 1];
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = pack_bf16x2(bf16_to_f32(w[q] & 0xFFFF) * rstd * g[2 * q],
+                         bf16_to_f32(w[q] >> 16) * rstd * g[2 * q + 1]);
+    o[c] = make_uint4(r[0], r[1], r[2], r[3]);
   }
 }
 
@@ -92,44 +112,43 @@ __global__ __launch_bounds__(256) void concat_kernel(const uint16_t* __restrict_
   }
 }
 
-// One workgroup per (block n, slot s). Slot 0: the anchor vector
-// o_0 = bf16(a / max(|a|, 1e-12)), a = apre[n], written to all K candidate rows
-// of outv (the in rows are zero). Slots s >= 1: the K lattice rows of slot s.
-__global__ __launch_bounds__(256) void assemble_kernel(const uint16_t* __restrict__ lat_out,
-                                                       const uint16_t* __restrict__ lat_in,
-                                                       const float* __restrict__ apre, int B, int K,
-                                                       int de, uint16_t* __restrict__ outv,
-                                                       uint16_t* __restrict__ inv) {
+// One workgroup per block n: the anchor vector o_0 = bf16(a / max(|a|, 1e-12)),
+// a = apre[n] (d_e <= 1024, so each thread keeps at most four elements),
+// written to all K candidate rows of slot 0 in outv; the in rows of slot 0
+// are zero.
+__global__ __launch_bounds__(256) void anchor_rows_kernel(const float* __restrict__ apre, int B, int K,
+                                                          int de, uint16_t* __restrict__ outv,
+                                                          uint16_t* __restrict__ inv) {
+  constexpr int NC = 4;
   __shared__ float s_red[4];
-  const int64_t n = blockIdx.x / B;
-  const int s = (int)(blockIdx.x - n * B);
+  const int64_t n = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t dst0 = ((n * B + s) * K) * (int64_t)de;
-  if (s == 0) {
-    const float* a = apre + n * de;
-    float ss = 0.f;
-    for (int d = tid; d < de; d += 256) ss = fmaf(a[d], a[d], ss);
-    ss = wave_sum(ss);
-    if (lane == 0) s_red[wave] = ss;
-    __syncthreads();
-    const float tot = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    const float nr = fmaxf(__fsqrt_rn(tot), 1e-12f);
-    for (int i = tid; i < K * de; i += 256) {
-      const int d = i % de;
-      outv[dst0 + i] = (uint16_t)f32_to_bf16(__fdiv_rn(a[d], nr));
-      inv[dst0 + i] = 0;
+  const float* a = apre + n * de;
+  float av[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) av[i] = a[min(tid + 256 * i, de - 1)];   // clamped: unconditional
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    if (tid + 256 * i < de) ss = fmaf(av[i], av[i], ss);
+  ss = wave_sum(ss);
+  if (lane == 0) s_red[wave] = ss;
+  __syncthreads();
+  const float tot = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  const float nr = fmaxf(__fsqrt_rn(tot), 1e-12f);
+  uint16_t ov[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) ov[i] = (uint16_t)f32_to_bf16(__fdiv_rn(av[i], nr));
+  const int64_t dst0 = (n * B * K) * (int64_t)de;
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int d = tid + 256 * i;
+      if (d < de) {
+        outv[dst0 + (int64_t)j * de + d] = ov[i];
+        inv[dst0 + (int64_t)j * de + d] = 0;
+      }
     }
-    return;
-  }
-  const int64_t src0 = ((n * (B - 1) + s - 1) * K) * (int64_t)de;
-  const uint4* so = (const uint4*)(lat_out + src0);
-  const uint4* si = (const uint4*)(lat_in + src0);
-  uint4* d_o = (uint4*)(outv + dst0);
-  uint4* d_i = (uint4*)(inv + dst0);
-  for (int i = tid; i < K * de / 8; i += 256) {
-    d_o[i] = so[i];
-    d_i[i] = si[i];
-  }
 }
 
 }  // namespace
@@ -146,8 +165,9 @@ hipError_t launch_gather_rows(const int32_t* topk_idx, int N, int B, int K, cons
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int M, int H, const float* gamma, float eps,
                                uint16_t* out, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, x, M,
-                     H, gamma, eps, out);
+  if (H % 8 || H > 8192) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, H, gamma, eps,
+                     out);
   return hipGetLastError();
 }
 
@@ -160,10 +180,12 @@ hipError_t launch_concat(const uint16_t* u, const uint16_t* tb, int N, int per_b
   return hipGetLastError();
 }
 
-hipError_t launch_assemble(const uint16_t* lat_out, const uint16_t* lat_in, const float* apre, int N,
-                           int B, int K, int de, uint16_t* outv, uint16_t* inv, hipStream_t stream) {
-  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((int64_t)N * B)), dim3(256), 0, stream,
-                     lat_out, lat_in, apre, B, K, de, outv, inv);
+hipError_t launch_anchor_rows(const float* apre, int N, int B, int K, int de, uint16_t* outv,
+                              uint16_t* inv, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  if (de > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(anchor_rows_kernel, dim3((unsigned)N), dim3(256), 0, stream, apre, B, K, de,
+                     outv, inv);
   return hipGetLastError();
 }
 

@@ -23,10 +23,14 @@ namespace {
 // Rows past K are clamped to row K - 1 (their results are never emitted), so
 // every load is unconditional and a 256-wide slice of d is loaded ahead of
 // its MFMAs (conditional loads would be serialised).
+// Only columns d0 .. d1 - 1 of the rows (row stride de) enter the sums.
+// MFMAs run on every lane whatever the exec mask, so a fragment outside
+// d0 .. d1 - 1 is zero rather than unloaded: if the compiler turns a guard
+// into an exec mask, the skipped MFMA still adds exactly nothing.
 template <typename Emit>
 __device__ __forceinline__ void pair_matrix(const uint16_t* __restrict__ o,
                                             const uint16_t* __restrict__ in, int K, int de,
-                                            int lane, Emit emit) {
+                                            int d0, int d1, int lane, Emit emit) {
   const int g = lane >> 4, c = lane & 15;
   const int tiles = (K + 15) / 16;
   for (int at = 0; at < tiles; ++at)
@@ -35,17 +39,22 @@ __device__ __forceinline__ void pair_matrix(const uint16_t* __restrict__ o,
       const uint16_t* ar = o + (int64_t)a * de + 8 * g;
       const uint16_t* br = in + (int64_t)b * de + 8 * g;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < de; k0 += 256) {
+      for (int k0 = d0; k0 < d1; k0 += 256) {
         u32x4_t af[8], bf[8];
 #pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          af[ks] = u32x4_t{0u, 0u, 0u, 0u};
+          bf[ks] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          if (k0 + ks * 32 < de) {
+          if (k0 + ks * 32 < d1) {
             af[ks] = *(const u32x4_t*)(ar + k0 + ks * 32);
             bf[ks] = *(const u32x4_t*)(br + k0 + ks * 32);
           }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          if (k0 + ks * 32 < de) acc = mfma16(af[ks], bf[ks], acc);
+          if (k0 + ks * 32 < d1) acc = mfma16(af[ks], bf[ks], acc);
       }
       const int bc = bt * 16 + c;
 #pragma unroll
@@ -61,14 +70,39 @@ __global__ __launch_bounds__(256) void pair_scores_kernel(const uint16_t* __rest
                                                           int B, int K, int de,
                                                           float* __restrict__ cos) {
   const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t pair = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (pair >= (int64_t)N * (B - 1)) return;
   const int64_t n = pair / (B - 1);
   const int s = (int)(pair - n * (B - 1)) + 1;
   const uint16_t* o = outv + ((n * B + s - 1) * K) * (int64_t)de;
   const uint16_t* in = inv + ((n * B + s) * K) * (int64_t)de;
   float* dst = cos + pair * K * K;
-  pair_matrix(o, in, K, de, lane, [&](int ra, int b, float v) { dst[ra * K + b] = v; });
+  pair_matrix(o, in, K, de, 0, de, lane, [&](int ra, int b, float v) { dst[ra * K + b] = v; });
+}
+
+// Wide vectors (d_e of 512 and more), where one workgroup per block would
+// stream every pair's rows through few waves: one wave per (pair, 256-wide
+// slice of d_e), each writing its partial K x K matrix to
+// part[(slice N (B-1) + pair) K K ..]; the walk kernel adds the slices in
+// slice order.
+__global__ __launch_bounds__(256) void pair_slices_kernel(const uint16_t* __restrict__ outv,
+                                                          const uint16_t* __restrict__ inv, int N,
+                                                          int B, int K, int de, int slices,
+                                                          float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pairs = (int64_t)N * (B - 1);
+  // wave-uniform, so the slice bounds below are scalar and their guards branch
+  const int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= pairs * slices) return;
+  const int sl = (int)(item / pairs);
+  const int64_t pair = item - sl * pairs;
+  const int64_t n = pair / (B - 1);
+  const int s = (int)(pair - n * (B - 1)) + 1;
+  const uint16_t* o = outv + ((n * B + s - 1) * K) * (int64_t)de;
+  const uint16_t* in = inv + ((n * B + s) * K) * (int64_t)de;
+  float* dst = part + item * K * K;
+  pair_matrix(o, in, K, de, 256 * sl, min(de, 256 * sl + 256), lane,
+              [&](int ra, int b, float v) { dst[ra * K + b] = v; });
 }
 
 __global__ __launch_bounds__(256) void greedy_walk_kernel(
@@ -123,7 +157,8 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
 template <int RULE>
 __global__ __launch_bounds__(512) void scores_walk_kernel(
     const uint16_t* __restrict__ outv, const uint16_t* __restrict__ inv,
-    const float* __restrict__ cos_in, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ cos_in, int cos_slices, int64_t slice_stride,
+    const int32_t* __restrict__ topk_idx,
     const float* __restrict__ topk_logp, int B, int K, int de, float alpha, int use_logp,
     const float* __restrict__ temperature, const float* __restrict__ uniforms,
     float* __restrict__ proposal, float* __restrict__ cos_out, int32_t* __restrict__ out_tokens,
@@ -137,7 +172,7 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
   float* s_tz = (float*)(s_tc + (B - 1) * K);       // [(B-1) K] its score (SAMPLE: the row max)
   float* s_tg = s_tz + (B - 1) * K;                 // [(B-1) K] its gap (SAMPLE: the row's exp sum)
   int* s_path = (int*)(s_tg + (B - 1) * K);         // [B] committed candidates
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n = blockIdx.x;
   const int64_t base = n * B * K;
   for (int i = tid; i < B * K; i += blockDim.x) {
@@ -146,13 +181,20 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
   }
   const int nw = blockDim.x >> 6;
   if (cos_in) {
+    // one matrix per pair, or the partial sums of its d_e slices (added in
+    // slice order)
     const float* src = cos_in + n * (int64_t)(B - 1) * KK;
-    for (int i = tid; i < (B - 1) * KK; i += blockDim.x) s_cos[i] = src[i];
+    for (int i = tid; i < (B - 1) * KK; i += blockDim.x) {
+      float v = src[i];
+      for (int sl = 1; sl < cos_slices; ++sl) v += src[sl * slice_stride + i];
+      s_cos[i] = v;
+      if (cos_out) cos_out[n * (int64_t)(B - 1) * KK + i] = v;
+    }
   } else {
     for (int p = wave; p < B - 1; p += nw) {
       const uint16_t* o = outv + (base + (int64_t)p * K) * de;
       const uint16_t* in = inv + (base + (int64_t)(p + 1) * K) * de;
-      pair_matrix(o, in, K, de, lane, [&](int ra, int b, float v) {
+      pair_matrix(o, in, K, de, 0, de, lane, [&](int ra, int b, float v) {
         s_cos[p * KK + ra * K + b] = v;
         if (cos_out) cos_out[(n * (B - 1) + p) * KK + ra * K + b] = v;
       });
@@ -331,9 +373,10 @@ size_t scores_walk_lds_bytes(int B, int K) {
 }
 
 hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const float* cos_in,
-                              const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
-                              int d_e, const CommitRule& rule, float* cos_out, int32_t* out_tokens,
-                              float* score, float* gap, hipStream_t stream) {
+                              int cos_slices, const int32_t* topk_idx, const float* topk_logp,
+                              int N, int B, int K, int d_e, const CommitRule& rule, float* cos_out,
+                              int32_t* out_tokens, float* score, float* gap, hipStream_t stream) {
+  const int64_t slice_stride = (int64_t)N * (B - 1) * K * K;
   const size_t lds = scores_walk_lds_bytes(B, K);
   static bool attr_set = false;
   if (!attr_set) {
@@ -347,7 +390,8 @@ hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const f
   }
 #define LL_SW(R)                                                                                  \
   hipLaunchKernelGGL(scores_walk_kernel<R>, dim3((unsigned)N), dim3(512), lds, stream, outv, inv, \
-                     cos_in, topk_idx, topk_logp, B, K, d_e, rule.alpha, rule.use_logp,           \
+                     cos_in, cos_slices, slice_stride, topk_idx, topk_logp, B, K, d_e,           \
+                     rule.alpha, rule.use_logp,                                                   \
                      rule.temperature, rule.uniforms, rule.proposal, cos_out, out_tokens, score,  \
                      gap)
   if (rule.kind == RULE_EXACT)
@@ -366,6 +410,15 @@ hipError_t launch_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, 
   if (pairs <= 0) return hipSuccess;
   hipLaunchKernelGGL(pair_scores_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream,
                      outv, inv, N, B, K, d_e, cos);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_slices(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
+                              int d_e, float* part, hipStream_t stream) {
+  const int64_t items = (int64_t)N * (B - 1) * pair_slice_count(d_e);
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pair_slices_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream,
+                     outv, inv, N, B, K, d_e, pair_slice_count(d_e), part);
   return hipGetLastError();
 }
 

@@ -111,17 +111,19 @@ def test_paper_head_errors_without_inputs(L):
     assert e.value.code == L.EINVAL
 
 
-@pytest.mark.parametrize("B,K,N", [(2, 1, 3), (2, 5, 2), (3, 7, 4), (17, 3, 2)])
-def test_paper_head_degenerate_and_ragged(L, B, K, N):
-    # one drafted slot (B = 2), one candidate (K = 1), odd lattices and a ragged slot count
+@pytest.mark.parametrize("B,K,N,de", [(2, 1, 3, 64), (2, 5, 2, 64), (3, 7, 4, 64), (17, 3, 2, 64),
+                                      (5, 3, 2, 544)])
+def test_paper_head_degenerate_and_ragged(L, B, K, N, de):
+    # one drafted slot (B = 2), one candidate (K = 1), odd lattices, a ragged
+    # slot count, and wide vectors in ragged 256-wide slices (d_e = 544)
     import torch
-    w = synth.Workload(f"paper_edge_{B}_{K}_{N}", N, B, 4096, K, 128, 2, 128, 64, "f32", "normal",
+    w = synth.Workload(f"paper_edge_{B}_{K}_{N}_{de}", N, B, 4096, K, 128, 2, 128, de, "f32", "normal",
                        alpha=8.0, use_logp=False, target_hidden=192, drafter_hidden=128)
     rng = np.random.default_rng(B * 100 + K * 10 + N)
     host = rng.standard_normal((N, B, w.vocab), dtype=np.float32)
     hid_bits = synth.f32_to_bf16_bits_rne(rng.standard_normal((N, B, 128), dtype=np.float32))
     tgt_bits = synth.f32_to_bf16_bits_rne(rng.standard_normal((N, 192), dtype=np.float32))
-    print(f"[case] paper head edge B {B} K {K} N {N}", flush=True)
+    print(f"[case] paper head edge B {B} K {K} N {N} d_e {de}", flush=True)
     tokens, dbg = L.rerank(to_device(host), K, device_weights(w), w.alpha, w.use_logp, debug=True,
                            hidden=to_device(hid_bits), target=to_device(tgt_bits))
     torch.cuda.synchronize()

@@ -46,11 +46,13 @@ CASES = [
 COS_FRACTION_OF = {"odd_h2560": 0.995}
 
 
-def run_case(L, name, tier, sample, alpha=None, use_logp=True):
+def run_case(L, name, tier, sample, alpha=None, use_logp=True, host=None):
     import torch
-    w = synth.WORKLOADS[name]
+    w = name if isinstance(name, synth.Workload) else synth.WORKLOADS[name]
+    name = w.name
     alpha = w.alpha if alpha is None else alpha
-    host = synth.make_logits(w, tier)
+    if host is None:
+        host = synth.make_logits(w, tier)
     print(f"[case] {name} tier {tier} shape {host.shape}", flush=True)
     dev = to_device(host)
     weights = device_weights(w)
@@ -93,6 +95,15 @@ def run_case(L, name, tier, sample, alpha=None, use_logp=True):
 @pytest.mark.parametrize("name,tier,sample", CASES)
 def test_rerank_matches_oracle(L, name, tier, sample):
     run_case(L, name, tier, sample)
+
+
+@pytest.mark.parametrize("de,K,B,N", [(512, 5, 9, 3), (544, 7, 6, 2), (1024, 3, 16, 1)])
+def test_wide_vectors_sliced_pair_products(L, de, K, B, N):
+    # d_e >= 512 takes the pair products in 256-wide slices of d_e over many
+    # waves, summed by the walk in slice order (544: a ragged last slice)
+    w = synth.Workload(f"wide_de{de}_k{K}", N, B, 4096, K, 128, 2, 256, de, "f32", "normal")
+    host = np.random.default_rng(de + K).standard_normal((N, B, w.vocab), dtype=np.float32)
+    run_case(L, w, 0, None, host=host)
 
 
 def test_paper_rule_sigma_cos(L):

@@ -24,9 +24,10 @@ namespace {
 // every load is unconditional and a 256-wide slice of d is loaded ahead of
 // its MFMAs (conditional loads would be serialised).
 // Only columns d0 .. d1 - 1 of the rows (row stride de) enter the sums.
-// MFMAs run on every lane whatever the exec mask, so a fragment outside
-// d0 .. d1 - 1 is zero rather than unloaded: if the compiler turns a guard
-// into an exec mask, the skipped MFMA still adds exactly nothing.
+// d0 and d1 must be wave-uniform values the compiler knows to be uniform
+// (kernel arguments, readfirstlane results): an MFMA runs on every lane
+// whatever the exec mask, so the guards below have to compile to branches,
+// not to exec masks around unloaded fragments.
 template <typename Emit>
 __device__ __forceinline__ void pair_matrix(const uint16_t* __restrict__ o,
                                             const uint16_t* __restrict__ in, int K, int de,
@@ -41,11 +42,6 @@ __device__ __forceinline__ void pair_matrix(const uint16_t* __restrict__ o,
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       for (int k0 = d0; k0 < d1; k0 += 256) {
         u32x4_t af[8], bf[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          af[ks] = u32x4_t{0u, 0u, 0u, 0u};
-          bf[ks] = u32x4_t{0u, 0u, 0u, 0u};
-        }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
           if (k0 + ks * 32 < d1) {

@@ -12,6 +12,8 @@
 // "Sampling the committed path (opt-in)"): further rules of the fused kernel,
 // with the same per-step score z_s(i, j) = fl32(logp[s][j] + fl32(alpha *
 // cos_s[i][j])).
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -374,15 +376,22 @@ hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const f
                               int32_t* out_tokens, float* score, float* gap, hipStream_t stream) {
   const int64_t slice_stride = (int64_t)N * (B - 1) * K * K;
   const size_t lds = scores_walk_lds_bytes(B, K);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_GREEDY>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
-    (void)hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_EXACT>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
-    (void)hipFuncSetAttribute((const void*)scores_walk_kernel<RULE_SAMPLE>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
-    attr_set = true;
+  // The kernel's LDS may exceed the default 64 KiB limit: raise it once per
+  // device (the attribute is set on the current device).
+  static std::atomic<bool> attr_set[64];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    const void* fns[3] = {(const void*)scores_walk_kernel<RULE_GREEDY>,
+                          (const void*)scores_walk_kernel<RULE_EXACT>,
+                          (const void*)scores_walk_kernel<RULE_SAMPLE>};
+    for (const void* f : fns) {
+      err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kScoresWalkMaxLds);
+      if (err != hipSuccess) return err;
+    }
+    attr_set[dev].store(true, std::memory_order_release);
   }
 #define LL_SW(R)                                                                                  \
   hipLaunchKernelGGL(scores_walk_kernel<R>, dim3((unsigned)N), dim3(512), lds, stream, outv, inv, \

@@ -12,16 +12,27 @@ from oracle.walk import step_scores
 # Relative tolerance on float32 scores: |gpu - oracle| <= TOL * max(1, |oracle|).
 # The log-partition and log-probabilities meet it for every element.
 TOL = 1e-3
-# Pair cosines and committed step scores come out of two bf16 transformer
-# layers. Against a float64 oracle, any float32-accumulating implementation of
-# the same rounding points drifts by a bf16 rounding cascade (reproduced on the
-# CPU by tests/test_tolerance_derivation.py), so for them TOL is required of
-# at least COS_FRACTION of the elements, and every element must stay within
-# COS_HARD: both operands are unit vectors stored in bf16; if every component
-# of each disagrees by one rounding (at most 2^-8 relative), the dot product
-# moves by at most 2 * 2^-8 * sum|o_d||i_d| <= 2^-7.
-COS_FRACTION = 0.999
-COS_HARD = 2.0 ** -7
+# Pair cosines, committed step scores and the stored in/out vectors come out of
+# two bf16 transformer layers. Against the float64 oracle, any implementation
+# that accumulates in float32 at the same rounding points rounds a few bf16
+# values the other way, and the flips cascade through the layers. An
+# independent float32 build of the encoder shows the size of that drift at the
+# workloads' real shapes (tests/test_tolerance_derivation.py): its cosines miss
+# TOL by up to ~1.1e-3 on a few elements in 10^4, and ~8 % of its in/out vector
+# components differ from the oracle's by more than one bf16 ulp (up to 2^-9
+# absolute). The bars below are those measured figures with a margin of about
+# two; the derivation test asserts both that the tighter bar fails for the
+# float32 build and that the float32 build sits inside these ones.
+COS_FRACTION = 0.999          # cosines / step scores within TOL (scaled for steps)
+COS_MAX = 2e-3                # every cosine within COS_MAX * max(1, |o|)
+VEC_MAX = 2.0 ** -8           # every in/out component within this (absolute)
+VEC_MEAN = 2e-4               # mean absolute in/out component difference
+VEC_ULP_FRACTION = 0.85       # components equal to the oracle's or one bf16 ulp away
+# Committed tokens: a slot whose GPU pick is not the oracle's argmax is excused
+# only when the oracle scores the pick within TOL * max(1, |z*|) of its best
+# (scaled by max(1, |alpha|) like the step scores), and at most this fraction
+# of a case's compared slots (at least one) may be excused.
+EXCUSE_FRACTION = 0.01
 
 
 def within(g, o, tol=TOL):
@@ -41,21 +52,68 @@ def assert_within(g, o, tol=TOL, what=""):
 
 
 def assert_scores(g, o, what="", alpha=1.0, fraction=COS_FRACTION, step=False):
-    """Cosines / step scores: a fraction (COS_FRACTION unless a case states its
-    own, derived from the float32 drift of its shape) within TOL, all within the
-    bf16 bound. A step score fl32(logp + fl32(alpha * cos)) carries |alpha| times
-    its cosine's error, so for step=True the TOL part is scaled by max(1, |alpha|)."""
+    """Cosines / step scores: at least `fraction` of the elements within TOL and
+    every element within COS_MAX (relative to max(1, |o|)). A step score
+    fl32(logp + fl32(alpha * cos)) carries |alpha| times its cosine's error, so
+    for step=True both bars are scaled by max(1, |alpha|)."""
     g = np.asarray(g, dtype=np.float64).ravel()
     o = np.asarray(o, dtype=np.float64).ravel()
     err = np.abs(g - o)
-    tol = TOL * (max(1.0, abs(alpha)) if step else 1.0)
-    hard = tol * np.maximum(1.0, np.abs(o)) + abs(alpha) * COS_HARD
-    assert np.all(err <= hard), f"{what}: max error {err.max()} beyond the bf16 bound"
-    n_bad = int((~within(g, o, tol)).sum())
+    scale = max(1.0, abs(alpha)) if step else 1.0
+    rel = err / np.maximum(1.0, np.abs(o))
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= COS_MAX * scale, f"{what}: max relative error {worst} beyond {COS_MAX * scale}"
+    n_bad = int((rel > TOL * scale).sum())
     allowed = max(1, int((1.0 - fraction) * err.size))
-    assert n_bad <= allowed, f"{what}: {n_bad} of {err.size} outside {TOL} (allowed {allowed})"
-    return {"n": int(err.size), "over_tol": n_bad, "max": float(err.max()),
+    assert n_bad <= allowed, f"{what}: {n_bad} of {err.size} outside {TOL * scale} (allowed {allowed})"
+    return {"n": int(err.size), "over_tol": n_bad, "max_rel": worst,
             "p999": float(np.percentile(err, 99.9)) if err.size else 0.0}
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 values at |v| (8 significant bits; the smallest
+    normal spacing below 2^-126)."""
+    a = np.maximum(np.abs(np.asarray(v, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def assert_vectors(g, o, what=""):
+    """Stored in/out vectors (bf16 values): every component within VEC_MAX,
+    the mean difference within VEC_MEAN, and at least VEC_ULP_FRACTION of the
+    components equal or one bf16 ulp apart."""
+    g = np.asarray(g, dtype=np.float64).ravel()
+    o = np.asarray(o, dtype=np.float64).ravel()
+    d = np.abs(g - o)
+    ulp_ok = d <= np.maximum(bf16_ulp(o), bf16_ulp(g)) * (1 + 1e-9)
+    st = {"n": int(d.size), "max": float(d.max()), "mean": float(d.mean()),
+          "equal": float(np.mean(d == 0)), "within_ulp": float(np.mean(ulp_ok))}
+    assert st["max"] <= VEC_MAX, f"{what}: component off by {st['max']} > {VEC_MAX}"
+    assert st["mean"] <= VEC_MEAN, f"{what}: mean difference {st['mean']} > {VEC_MEAN}"
+    assert st["within_ulp"] >= VEC_ULP_FRACTION, f"{what}: {st['within_ulp']:.4f} within one ulp"
+    return st
+
+
+def record(case: str, **fields):
+    """Print a parity record and append it to the JSON-lines log that a GPU
+    run returns (gpurun_out/parity.jsonl at the repository root, or the path
+    in LILICORR_PARITY_LOG)."""
+    import json
+    import os
+    line = json.dumps({"case": case, **fields}, default=float)
+    print(f"[parity] {line}", flush=True)
+    path = os.environ.get("LILICORR_PARITY_LOG") or os.path.join(
+        os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out", "parity.jsonl")
+    try:
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(line + "\n")
+    except OSError:
+        pass
+
+
+def assert_excuse_cap(excused, n_slots, what=""):
+    cap = max(1, int(EXCUSE_FRACTION * n_slots))
+    assert len(excused) <= cap, f"{what}: {len(excused)} excused slots of {n_slots} (cap {cap}): {excused}"
 
 
 def bf16_to_f64(t) -> np.ndarray:
@@ -87,10 +145,9 @@ def compare_walk(logp, cos, gpu_choice, alpha, use_logp=True, tol=TOL):
     """Check a GPU path against the oracle's scores slot by slot.
 
     A GPU pick that differs from the oracle's argmax is excused only when the
-    oracle's score of the GPU pick is within the score tolerance of the best
-    score (tol * max(1, |best|) + |alpha| * COS_HARD, the bound the step scores
-    are held to); the oracle walk then follows the GPU's pick. Returns the list
-    of excused (slot, gap) pairs; raises on a real mismatch.
+    oracle's score of the GPU pick is within tol * max(1, |alpha|) * max(1, |best|)
+    of the best score; the oracle walk then follows the GPU's pick. Returns the
+    list of excused (slot, gap) pairs; raises on a real mismatch.
     """
     B, K = logp.shape
     excused = []
@@ -101,7 +158,7 @@ def compare_walk(logp, cos, gpu_choice, alpha, use_logp=True, tol=TOL):
         pick = int(gpu_choice[s])
         if pick != int(np.argmax(z)):
             gap = best - z[pick]
-            if gap > tol * max(1.0, abs(best)) + abs(alpha) * COS_HARD:
+            if gap > tol * max(1.0, abs(alpha)) * max(1.0, abs(best)):
                 raise AssertionError(f"slot {s}: gpu picked {pick} (z={z[pick]}), oracle best "
                                      f"{int(np.argmax(z))} (z={best}), gap {gap}")
             excused.append((s, float(gap)))

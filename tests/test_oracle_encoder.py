@@ -225,3 +225,83 @@ def test_rounding_points_change_result_only_slightly():
     to, _ = _torch_encoder(idx, lp, w, 2)
     err = np.abs(outv - to).max()
     assert 0 < err < 0.05
+
+
+# --- where the encoder rounds to bfloat16 ----------------------------------
+# The pages fix no rounding; the reading taken (bf16 at every GEMM input and at
+# the attention probabilities, float32 residual stream, norms and softmax sums)
+# names nine points. A second float64 torch build places them with torch's own
+# bfloat16 conversion (float64 -> float32 -> bfloat16, round to nearest even at
+# each step, the way a float32 producer stores bfloat16). The oracle must agree
+# with it to float64 round-off, and dropping any single point from the torch
+# build must break that agreement, so a missing or an extra rounding in the
+# oracle cannot pass.
+ROUND_POINTS = ("conf_hidden", "u1", "qkv", "probs", "attn_out", "u2", "ffn_hidden", "uf", "heads")
+
+
+def _bf16(a, name, skip):
+    return a if name in skip else a.to(torch.bfloat16).to(torch.float64)
+
+
+def _torch_encoder_rounded(idx, lp, w, heads, skip=()):
+    t = lambda a: torch.tensor(np.asarray(a), dtype=torch.float64)
+    B, K = idx.shape
+    T = B * K
+    d = w.dims
+    H, dh = d.hidden, d.hidden // heads
+    slot = torch.arange(B).repeat_interleave(K)
+    rank = torch.arange(K).repeat(B)
+    lpt = t(lp)
+    feats = torch.stack([lpt, lpt.exp(), lpt - lpt[:, :1],
+                         (rank.view(B, K).double() / (K - 1)) if K > 1 else torch.zeros(B, K, dtype=torch.float64),
+                         (rank.view(B, K) == 0).double()], dim=-1).reshape(T, 5)
+    hid = _bf16(F.silu(F.linear(feats, t(w["conf_w1"]), t(w["conf_b1"]))), "conf_hidden", skip)
+    x = t(w.embedding_rows(idx.reshape(-1))) + t(w["S"])[slot] + t(w["R"])[rank] \
+        + F.linear(hid, t(w["conf_w2"]), t(w["conf_b2"]))
+    delta = slot[None, :] - slot[:, None]
+    for l in range(d.layers):
+        u = _bf16(F.rms_norm(x, (H,), t(w[f"l{l}.gamma1"]), eps=1e-6), "u1", skip)
+        qkv = _bf16(F.linear(u, t(w[f"l{l}.wqkv"]), t(w[f"l{l}.bqkv"])), "qkv", skip)
+        q, k, v = (a.reshape(T, heads, dh).transpose(0, 1) for a in qkv.split(H, dim=-1))
+        bias = t(w[f"l{l}.dist"])[:, delta + 63] + t(w[f"l{l}.same"])[:, None, None] * (delta == 0)
+        s = torch.matmul(q, k.transpose(1, 2).contiguous()) / math.sqrt(dh) + bias
+        e = torch.exp(s - s.amax(dim=-1, keepdim=True))
+        o = torch.matmul(_bf16(e, "probs", skip), v) / e.sum(dim=-1, keepdim=True)
+        o = _bf16(o.transpose(0, 1).reshape(T, H), "attn_out", skip)
+        x = x + F.linear(o, t(w[f"l{l}.wo"]), t(w[f"l{l}.bo"]))
+        u2 = _bf16(F.rms_norm(x, (H,), t(w[f"l{l}.gamma2"]), eps=1e-6), "u2", skip)
+        hd = _bf16(F.silu(F.linear(u2, t(w[f"l{l}.w1"]), t(w[f"l{l}.b1"]))), "ffn_hidden", skip)
+        x = x + F.linear(hd, t(w[f"l{l}.w2"]), t(w[f"l{l}.b2"]))
+    uf = _bf16(F.rms_norm(x, (H,), t(w["gamma_f"]), eps=1e-6), "uf", skip)
+    out = _bf16(F.normalize(F.linear(uf, t(w["w_out"]), t(w["b_out"])), dim=-1, eps=1e-12), "heads", skip)
+    inn = _bf16(F.normalize(F.linear(uf, t(w["w_in"]), t(w["b_in"])), dim=-1, eps=1e-12), "heads", skip)
+    return out.numpy().reshape(B, K, -1), inn.numpy().reshape(B, K, -1)
+
+
+def _rounded_case(B=16, K=4, H=64, heads=2, F_=256, de=32, V=1000, seed=5):
+    w = OracleWeights(Dims(H, heads, F_, de), V, seed=seed)
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, V, (B, K))
+    lp = -np.sort(np.abs(rng.standard_normal((B, K))).astype(np.float32) * 3, axis=1)
+    return w, idx, lp
+
+
+@pytest.mark.parametrize("B,K,H,heads,F_,de", [(16, 4, 64, 2, 256, 32), (7, 5, 96, 3, 160, 24)])
+def test_rounding_points_match_torch_bfloat16_build(B, K, H, heads, F_, de):
+    w, idx, lp = _rounded_case(B, K, H, heads, F_, de)
+    outv, inv = enc.encode_block(idx, lp, w)
+    to, ti = _torch_encoder_rounded(idx, lp, w, heads)
+    # every stored output is a bf16 value on both sides; they agree exactly
+    # unless a float64 summation-order difference straddles a rounding
+    # boundary (probability ~1e-9 per value), which these cases do not hit
+    assert np.array_equal(outv, to) and np.array_equal(inv, ti)
+
+
+@pytest.mark.parametrize("point", ROUND_POINTS)
+def test_each_rounding_point_is_load_bearing(point):
+    # the agreement above is not vacuous: the torch build without any one of
+    # the nine roundings moves the outputs far beyond float64 round-off
+    w, idx, lp = _rounded_case()
+    outv, inv = enc.encode_block(idx, lp, w)
+    to, ti = _torch_encoder_rounded(idx, lp, w, 2, skip=(point,))
+    assert max(np.abs(outv - to).max(), np.abs(inv - ti).max()) > 1e-4

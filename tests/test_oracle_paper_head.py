@@ -171,3 +171,86 @@ def test_node_terms():
         expect = (E_t[idx[s, r]] @ w["w_emb"].T + w["b_emb"] + hidden[s] @ w["w_hid"].T + w["b_hid"]
                   + w["S"][s] + w["R"][r])
         assert np.allclose(x0[t_], expect, rtol=0, atol=1e-12)
+
+
+# --- where the paper's head rounds to bfloat16 -------------------------------
+# The lattice head's nine points plus the target branch and the fusion: the
+# normalised target state, t', the elementwise product u*t', the fused state y
+# and the anchor vector. A float64 torch build places them with torch's own
+# bfloat16 conversion; the oracle must agree exactly, and dropping any one
+# point from the torch build must break the agreement.
+PAPER_ROUND_POINTS = ("conf_hidden", "u1", "qkv", "probs", "attn_out", "u2", "ffn_hidden", "uf",
+                      "t_norm", "t_proj", "prod", "fused", "heads", "anchor")
+
+
+def _bf16(a, name, skip):
+    return a if name in skip else a.to(torch.bfloat16).to(torch.float64)
+
+
+def _torch_paper_rounded(idx, lp, hidden, target, w, skip=()):
+    import math
+    t = lambda a: torch.tensor(np.asarray(a), dtype=torch.float64)
+    d = w.dims
+    B, K = idx.shape
+    H, heads = d.hidden, d.heads
+    dh = H // heads
+    Tp = (B - 1) * K
+    slot = torch.arange(1, B).repeat_interleave(K)
+    rank = torch.arange(K).repeat(B - 1)
+    lpt = t(lp)[1:]
+    feats = torch.stack([lpt, lpt.exp(), lpt - t(lp)[1:, :1],
+                         (rank.view(B - 1, K).double() / (K - 1)) if K > 1 else torch.zeros(B - 1, K, dtype=torch.float64),
+                         (rank.view(B - 1, K) == 0).double()], dim=-1).reshape(Tp, 5)
+    hid = _bf16(F.silu(F.linear(feats, t(w["conf_w1"]), t(w["conf_b1"]))), "conf_hidden", skip)
+    mlp = F.linear(hid, t(w["conf_w2"]), t(w["conf_b2"]))
+    emb = F.linear(t(w.embedding_rows(idx[1:].reshape(-1), "E_t")), t(w["w_emb"]), t(w["b_emb"]))
+    hp = F.linear(t(hidden)[1:], t(w["w_hid"]), t(w["b_hid"]))[slot - 1]
+    x = emb + hp + mlp + t(w["S"])[slot] + t(w["R"])[rank]
+    delta = slot[None, :] - slot[:, None]
+    for l in range(d.layers):
+        u = _bf16(F.rms_norm(x, (H,), t(w[f"l{l}.gamma1"]), eps=1e-6), "u1", skip)
+        qkv = _bf16(F.linear(u, t(w[f"l{l}.wqkv"]), t(w[f"l{l}.bqkv"])), "qkv", skip)
+        q, k, v = (a.reshape(Tp, heads, dh).transpose(0, 1) for a in qkv.split(H, dim=-1))
+        bias = t(w[f"l{l}.dist"])[:, delta + 63] + t(w[f"l{l}.same"])[:, None, None] * (delta == 0)
+        s = torch.matmul(q, k.transpose(1, 2).contiguous()) / math.sqrt(dh) + bias
+        e = torch.exp(s - s.amax(dim=-1, keepdim=True))
+        o = torch.matmul(_bf16(e, "probs", skip), v) / e.sum(dim=-1, keepdim=True)
+        o = _bf16(o.transpose(0, 1).reshape(Tp, H), "attn_out", skip)
+        x = x + F.linear(o, t(w[f"l{l}.wo"]), t(w[f"l{l}.bo"]))
+        u2 = _bf16(F.rms_norm(x, (H,), t(w[f"l{l}.gamma2"]), eps=1e-6), "u2", skip)
+        hd = _bf16(F.silu(F.linear(u2, t(w[f"l{l}.w1"]), t(w[f"l{l}.b1"]))), "ffn_hidden", skip)
+        x = x + F.linear(hd, t(w[f"l{l}.w2"]), t(w[f"l{l}.b2"]))
+    u = _bf16(F.rms_norm(x, (H,), t(w["gamma_f"]), eps=1e-6), "uf", skip)
+    tn = _bf16(F.rms_norm(t(target), (d.target_hidden,), t(w["gamma_t"]), eps=1e-6), "t_norm", skip)
+    tp = _bf16(F.linear(tn, t(w["w_tgt"]), t(w["b_tgt"])), "t_proj", skip)
+    tpb = tp.expand(Tp, H)
+    cat = torch.cat([u, tpb, _bf16(u * tpb, "prod", skip)], dim=1)
+    y = _bf16(F.silu(F.linear(cat, t(w["w_fuse"]), t(w["b_fuse"]))), "fused", skip)
+    out = _bf16(F.normalize(F.linear(y, t(w["w_out"]), t(w["b_out"])), dim=-1, eps=1e-12), "heads", skip)
+    inn = _bf16(F.normalize(F.linear(y, t(w["w_in"]), t(w["b_in"])), dim=-1, eps=1e-12), "heads", skip)
+    o0 = _bf16(F.normalize(F.linear(tp, t(w["w_anchor"]), t(w["b_anchor"])), dim=-1, eps=1e-12), "anchor", skip)
+    return out.numpy().reshape(B - 1, K, -1), inn.numpy().reshape(B - 1, K, -1), o0.numpy()
+
+
+def _paper_rounded_case(B=16, K=4, H=64, heads=2, F_=128, de=32, Ht=128, Hd=96, seed=21):
+    w = weights(H, heads, F_, de, 300, Ht, Hd, seed=seed)
+    idx, lp, hidden, target = inputs(np.random.default_rng(seed), B, K, 300, Ht, Hd)
+    return w, idx, lp, hidden, target
+
+
+@pytest.mark.parametrize("B,K,H,heads,F_,de,Ht,Hd", [(16, 4, 64, 2, 128, 32, 128, 96), (6, 5, 48, 3, 40, 16, 32, 24)])
+def test_rounding_points_match_torch_bfloat16_build(B, K, H, heads, F_, de, Ht, Hd):
+    w, idx, lp, hidden, target = _paper_rounded_case(B, K, H, heads, F_, de, Ht, Hd)
+    outv, inv = ph.encode_block_paper(idx, lp, hidden, target, w)
+    to, ti, o0 = _torch_paper_rounded(idx, lp, hidden, target, w)
+    assert np.array_equal(outv[1:], to) and np.array_equal(inv[1:], ti)
+    assert np.array_equal(outv[0], np.broadcast_to(o0, outv[0].shape))
+
+
+@pytest.mark.parametrize("point", PAPER_ROUND_POINTS)
+def test_each_rounding_point_is_load_bearing(point):
+    w, idx, lp, hidden, target = _paper_rounded_case()
+    outv, inv = ph.encode_block_paper(idx, lp, hidden, target, w)
+    to, ti, o0 = _torch_paper_rounded(idx, lp, hidden, target, w, skip=(point,))
+    diff = max(np.abs(outv[1:] - to).max(), np.abs(inv[1:] - ti).max(), np.abs(outv[0, 0] - o0).max())
+    assert diff > 1e-4

@@ -1,14 +1,22 @@
-"""Why the pair-cosine tolerance is statistical plus a bf16 bound (CPU only).
+"""Where the parity bars on cosines and in/out vectors come from (CPU only).
 
 The encoder rounds its activations to bfloat16 at every GEMM input and at the
 attention probabilities. Two implementations of those same rounding points
 that differ only in accumulation precision (float32 here, float64 in the
-oracle) round a few values differently; each such flip perturbs the next
-layer's inputs, which flips more roundings, and the cosines drift by up to
-about 1e-3. This test builds the encoder independently in float32 numpy and
-shows that drift: it reaches the order of the 1e-3 bar on its own, while
-staying inside the bf16 bound 2^-7 that the GPU parity tests use as a hard
-ceiling.
+oracle) round a few values differently; each flip perturbs the next layer's
+inputs, which flips more roundings. This module builds the encoder
+independently in float32 numpy and measures that drift at the workloads' real
+shapes (H = 1024 with K = 8 and K = 16, H = 2048 with K = 32). It asserts
+that
+  * the drift is real: some cosine misses 1e-3 and ~8 % of the stored vector
+    components differ by more than one bf16 ulp, so neither an elementwise
+    1e-3 bar on every cosine nor bit-equal vectors is a bar any float32
+    implementation meets;
+  * the bars the GPU tests use (tests/helpers.py) hold the float32 build with
+    a margin of about two: COS_MAX, COS_FRACTION, VEC_MAX, VEC_MEAN and
+    VEC_ULP_FRACTION;
+  * the float32 build commits the oracle's tokens, or differs only at slots
+    whose oracle score gap is within 1e-3 (the token excuse of the GPU tests).
 """
 import math
 
@@ -18,7 +26,9 @@ import synth
 import oracle
 from oracle.bf16 import round_bf16
 from oracle.scores import pair_scores
-from helpers import COS_HARD
+from helpers import (TOL, COS_MAX, COS_FRACTION, VEC_MAX, VEC_MEAN, VEC_ULP_FRACTION,
+                     bf16_ulp, compare_walk)
+from oracle.walk import greedy_walk
 
 
 def _f32(a):
@@ -75,40 +85,54 @@ def encoder_float32(idx, logp, w, K):
     return heads_out
 
 
-def test_float32_build_drifts_to_the_bar_but_not_past_the_bound():
-    V, K = 2048, 8
-    w = synth.Workload("drift", 2, 16, V, K, 128, 1, 512, 64, "bf16", "spiked")
-    synth.WORKLOADS_ORDER.append("drift")
-    try:
-        host = synth.make_logits(w)
-    finally:
-        synth.WORKLOADS_ORDER.remove("drift")
-    ow = oracle.OracleWeights(oracle.Dims(128, 1, 512, 64), V, synth.WEIGHTS_SEED)
-    worst = 0.0
-    for b in range(2):
-        r = oracle.rerank_block(host[b], K, ow, 1.0)
-        o32, i32 = encoder_float32(r.idx, r.logp, ow, K)
-        d = np.abs(pair_scores(o32, i32).astype(np.float64) - r.cos)
-        worst = max(worst, d.max())
-        assert np.mean(o32 != r.outv) > 0.05      # the cascade reaches the stored vectors
-    assert 5e-4 < worst < COS_HARD
+def _drift(name, tier, blocks):
+    """float32-build statistics against the oracle over the given blocks."""
+    w = synth.WORKLOADS[name]
+    host = synth.make_logits(w, tier, num_blocks=max(blocks) + 1)
+    ow = oracle.OracleWeights(oracle.Dims(w.hidden, w.heads, w.ffn, w.d_e), w.vocab, synth.WEIGHTS_SEED)
+    cos_rel, vec_d, vec_ulp, excused, slots = [], [], [], [], 0
+    for b in blocks:
+        r = oracle.rerank_block(host[b], w.topk, ow, 1.0)
+        o32, i32 = encoder_float32(r.idx, r.logp, ow, w.topk)
+        c32 = pair_scores(o32, i32)
+        cos_rel.append((np.abs(c32.astype(np.float64) - r.cos) / np.maximum(1.0, np.abs(r.cos))).ravel())
+        for g, o in ((o32, r.outv), (i32, r.inv)):
+            d = np.abs(g - o).ravel()
+            vec_d.append(d)
+            vec_ulp.append(d <= np.maximum(bf16_ulp(o), bf16_ulp(g)).ravel() * (1 + 1e-9))
+        walk = greedy_walk(r.idx, r.logp, c32, 1.0, True)
+        excused += compare_walk(r.logp, r.cos, walk.choice, 1.0)     # raises beyond TOL
+        slots += w.slots - 1
+    rel, d, ulp = np.concatenate(cos_rel), np.concatenate(vec_d), np.concatenate(vec_ulp)
+    return {"cos_max": rel.max(), "cos_over": np.mean(rel > TOL), "vec_max": d.max(), "vec_mean": d.mean(),
+            "vec_within_ulp": ulp.mean(), "excused": excused, "slots": slots}
+
+
+# (workload, tier, blocks): one or two blocks of each real encoder shape
+REAL_SHAPES = [("c32", 0, [0, 1]), ("c256_k16", 0, [0, 1]), ("entropy_k32", 0, [0])]
+
+
+def test_float32_drift_at_real_shapes_needs_and_fits_the_bars():
+    stats = {f"{n}/{t}": _drift(n, t, b) for n, t, b in REAL_SHAPES}
+    for k, st in stats.items():
+        # the derived bars hold the float32 build with a margin of about two
+        assert st["cos_max"] <= COS_MAX / 1.5, (k, st)
+        assert st["cos_over"] <= (1 - COS_FRACTION) / 2, (k, st)
+        assert st["vec_max"] <= VEC_MAX / 2, (k, st)
+        assert st["vec_mean"] <= VEC_MEAN / 2, (k, st)
+        assert st["vec_within_ulp"] >= VEC_ULP_FRACTION + 0.05, (k, st)
+        # bit-equal-or-one-ulp vectors are out of reach for any float32 build
+        assert st["vec_within_ulp"] < 0.95, (k, st)
+        assert len(st["excused"]) <= max(1, st["slots"] // 100), (k, st)
+    # and an elementwise 1e-3 bar on every cosine fails at a real shape
+    assert max(st["cos_max"] for st in stats.values()) > TOL, stats
 
 
 def test_float32_drift_rate_of_the_wide_odd_shape():
     """The wide odd shape (H = 2560, 15 slots, K = 7) drifts more: the float32
     build misses 1e-3 on more than 0.1 % of its cosines (the bar of the main
-    workloads), still inside the bf16 bound; its GPU case uses fraction 0.995."""
-    w = synth.WORKLOADS["odd_h2560"]
-    host = synth.make_logits(w)
-    ow = oracle.OracleWeights(oracle.Dims(w.hidden, w.heads, w.ffn, w.d_e), w.vocab, synth.WEIGHTS_SEED)
-    bad = total = 0
-    worst = 0.0
-    for b in (0, 1):
-        r = oracle.rerank_block(host[b], w.topk, ow, 1.0)
-        o32, i32 = encoder_float32(r.idx, r.logp, ow, w.topk)
-        d = np.abs(pair_scores(o32, i32).astype(np.float64) - r.cos)
-        bad += int((d > 1e-3 * np.maximum(1.0, np.abs(r.cos))).sum())
-        total += d.size
-        worst = max(worst, d.max())
-    assert 0.001 < bad / total < 0.005
-    assert worst < COS_HARD
+    workloads), still inside COS_MAX; its GPU case uses fraction 0.995."""
+    st = _drift("odd_h2560", 0, [0, 1])
+    assert 0.001 < st["cos_over"] < 0.005, st
+    assert st["cos_max"] <= COS_MAX / 1.5, st
+    assert st["vec_max"] <= VEC_MAX / 2 and st["vec_mean"] <= VEC_MEAN / 2, st

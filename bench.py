@@ -4,9 +4,11 @@
 One step = one lilicorr_rerank call over a batch of synthetic draft blocks:
 fused log-partition + top-K, node build, two encoder layers, in/out heads,
 pair scores and the greedy walk (every row of the hot path). The default
-workload is the concurrency-1, Qwen3-8B-like block (1 block, B = 16,
-V = 151,936 bf16 logits with three spikes per slot, K = 8, encoder width 1024,
-8 heads, FFN 4096, d_e 128).
+workload is the largest batch of the lattice head that the pages' shapes give:
+256 independent blocks, B = 16, V = 151,936 bf16 logits with three spikes per
+slot, K = 16, encoder width 1024, 8 heads, FFN 4096, d_e 128 (1.245 GB of
+logits per step, the top-K stage's bandwidth case). --workload picks another
+(c1_qwen3_8b is the concurrency-1 block).
 
 Logits are resident in HBM before timing; consecutive steps rotate over
 enough logits buffers (>= 768 MiB in total) that each step reads its logits
@@ -44,11 +46,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c1_qwen3_8b")
+    ap.add_argument("--workload", default="c256_k16")
     ap.add_argument("--tier", type=int, default=0)
     ap.add_argument("--rotate-mib", type=float, default=768.0)
     ap.add_argument("--stage-reps", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU-baseline budget: half for the one-core figure, half for the all-core pool")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="most worker processes of the all-core oracle pool (the host's CPU share)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
     ap.add_argument("--rule", default="greedy", choices=["greedy", "exact", "sample"],
@@ -83,16 +88,23 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
-
-    import draft_block_candidate_amd as L
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    host = synth.make_logits(w, args.tier)
+    # The CPU baseline runs first, before this process touches the GPU: its
+    # all-core figure forks worker processes, and a fork of a process holding
+    # GPU state is best avoided.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, host, args.cpu_seconds, args.rule,
+                                                         args.cpu_workers)
+
+    import torch
+
+    import draft_block_candidate_amd as L
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    host = synth.make_logits(w, args.tier)
     esize = 2 if w.dtype == "bf16" else 4
     logit_bytes = host.nbytes
     nbuf = max(1, math.ceil(args.rotate_mib * 2 ** 20 / logit_bytes))
@@ -275,8 +287,8 @@ def main():
         result["topk_sharded"] = bench_topk_shards(L, w, bufs[0].view(N * B, V), args.topk_shards,
                                                    args.rotate_mib, max(args.steps, 20), stream)
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, args.rule)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
     if args.copy_probe_mib > 0:
         n = int(args.copy_probe_mib * 2 ** 20) // 4
@@ -573,46 +585,96 @@ def csrc_sha256():
     return h.hexdigest()
 
 
-def cpu_baseline(w, host, seconds, rule="greedy"):
-    """The oracle, untuned, on this host: repeated passes over the workload's blocks
-    with the same commit rule (and, for sampling, the same temperatures and draws)."""
+_CPU = {}
+
+
+def _cpu_block(b):
+    """One oracle pass over block b (the state is set up before the pool forks)."""
+    st = _CPU
+    import oracle
+    w = st["w"]
+    return oracle.rerank_block(st["host"][b], w.topk, st["ow"], w.alpha, w.use_logp, rule=st["rule"],
+                               temperature=float(st["temps"][b]), uniforms=st["unif"][b],
+                               hidden=None if st["hidden"] is None else st["hidden"][b],
+                               target=None if st["target"] is None else st["target"][b])
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    global _BLAS_LIMIT
+    _BLAS_LIMIT = threadpool_limits(1)     # held for the worker's life
+
+
+def _cpu_chunk(blocks):
+    for b in blocks:
+        _cpu_block(b)
+    return len(blocks)
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, host, seconds, rule="greedy", max_workers=16):
+    """The oracle, untuned, on this host, with the same commit rule (and, for
+    sampling, the same temperatures and draws) as the GPU run. Two figures:
+      * one core: BLAS limited to one thread, passes over the workload's
+        blocks in order for about seconds / 2;
+      * all cores: a fork-started process pool with one worker per core of this
+        process's affinity mask (at most max_workers), BLAS limited to one
+        thread in each, over about seconds / 2 worth of blocks.
+    The dense weights are generated before timing (each pass generates its
+    block's embedding rows, as the oracle does). `value` is the all-core figure."""
+    import multiprocessing as mp
+    import numpy as np
+    from threadpoolctl import threadpool_limits
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    import numpy as np
     ow = oracle.OracleWeights(oracle.Dims(w.hidden, w.heads, w.ffn, w.d_e, target_hidden=w.target_hidden,
                                           drafter_hidden=w.drafter_hidden), w.vocab, synth.WEIGHTS_SEED)
-    temps = synth.make_temperatures(w.num_blocks, seed=1)
-    unif = synth.make_uniforms(w.num_blocks, w.slots, seed=2)
-
     hidden = target = None
     if w.target_hidden > 0:
         hb, tb = synth.make_head_inputs(w)
         hidden = synth.bf16_bits_to_f32(hb).astype(np.float64)
         target = synth.bf16_bits_to_f32(tb).astype(np.float64)
-
-    def one(b):
-        return oracle.rerank_block(host[b], w.topk, ow, w.alpha, w.use_logp, rule=rule,
-                                   temperature=float(temps[b]), uniforms=unif[b],
-                                   hidden=None if hidden is None else hidden[b],
-                                   target=None if target is None else target[b])
-
-    one(0)   # generates the weights: excluded
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        one(n % host.shape[0])
-        n += 1
+    _CPU.update(w=w, host=host, ow=ow, rule=rule, temps=synth.make_temperatures(w.num_blocks, seed=1),
+                unif=synth.make_uniforms(w.num_blocks, w.slots, seed=2), hidden=hidden, target=target)
+    N = host.shape[0]
+    with threadpool_limits(1):
+        _cpu_block(0)                      # generates the dense weights: excluded
+        n1 = 0
+        t0 = time.perf_counter()
+        while True:
+            _cpu_block(n1 % N)
+            n1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= seconds / 2 or n1 >= 100000:
+                break
+    one_core = n1 / el1
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, max_workers))
+    per_worker = max(1, int(round(one_core * seconds / 2)))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_chunk, [[b % N] for b in range(workers)])          # warm the workers
+        chunks = [[(k * workers + i) % N for k in range(per_worker)] for i in range(workers)]
+        t0 = time.perf_counter()
+        done = sum(pool.map(_cpu_chunk, chunks, chunksize=1))
         el = time.perf_counter() - t0
-        if el >= seconds or n >= 100000:
-            break
-    return {"value": n / el, "unit": "blocks/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} oracle passes over the {w.name} block(s) ({el:.1f} s; float64 numpy; "
-                      f"weight generation excluded)"}
+    all_core = done / el
+    _CPU.clear()
+    return {"value": all_core, "unit": "blocks/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} oracle passes over the {w.name} blocks ({el:.1f} s) in a pool of {workers} "
+                      f"processes, BLAS one thread each; float64 numpy; dense weight generation excluded",
+            "one_core": {"value": one_core, "unit": "blocks/s", "cores": 1,
+                         "sample": f"{n1} passes over the first blocks in order ({el1:.1f} s), BLAS one thread"},
+            "affinity_cores": cores, "cpu_model": _cpu_model()}
 
 
 if __name__ == "__main__":

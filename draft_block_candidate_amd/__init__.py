@@ -71,6 +71,8 @@ _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctype
 _SIGNATURES = {
     "lilicorr_rerank": (_c_int, [_vp, _c_int, _c_int, _c_int, ctypes.POINTER(Params), _vp]),
     "lilicorr_validate": (_c_int, [_vp, _c_int, _c_int, _c_int, ctypes.POINTER(Params), _vp]),
+    "lilicorr_rerank_audit": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Dims), _c_int,
+                                       ctypes.c_char_p, _c_size]),
     "lilicorr_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Dims)]),
     "lilicorr_weights_bytes": (_c_size, [ctypes.POINTER(Dims), _c_int]),
     "lilicorr_weights_init": (_c_int, [ctypes.POINTER(WeightsDesc), _vp]),
@@ -135,11 +137,36 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+class LilicorrArgumentError(LilicorrError):
+    """A tensor handed to the binding has the wrong device, layout, dtype or shape
+    (status EINVAL; raised before anything is passed to the library)."""
+
+    def __init__(self, where: str, why: str):
+        self.code = EINVAL
+        RuntimeError.__init__(self, f"{where}: {why}")
+
+
 def _require_cuda(t, name):
     if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+        raise LilicorrArgumentError(name, "must be a device tensor")
     if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+        raise LilicorrArgumentError(name, "must be contiguous")
+
+
+def _require(t, name, dtype, shape, device=None):
+    """Check a tensor the library will read or write through a raw pointer:
+    on the device (the same one as the call's other tensors), contiguous, of
+    the dtype and the exact shape the C ABI documents for it."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise LilicorrArgumentError(name, "must be a torch tensor")
+    _require_cuda(t, name)
+    if device is not None and t.device != device:
+        raise LilicorrArgumentError(name, f"is on {t.device}, the call's other tensors on {device}")
+    if t.dtype != dtype:
+        raise LilicorrArgumentError(name, f"must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise LilicorrArgumentError(name, f"must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 @dataclass(frozen=True)
@@ -252,12 +279,30 @@ def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool 
     target [N, H_t] bfloat16 device tensors are required."""
     torch = _torch()
     _require_cuda(logits, "logits")
+    if logits.dim() != 3:
+        raise LilicorrArgumentError("logits", f"must be [N, B, V], got shape {tuple(logits.shape)}")
     N, B, V = logits.shape
     dev = logits.device
+    d = weights.dims
+    if weights.blob.device != dev:
+        raise LilicorrArgumentError("weights", f"are on {weights.blob.device}, the logits on {dev}")
     if workspace is None:
         workspace = Workspace(N, B, V, K, weights.dims, device=dev)
+    elif workspace.buf.device != dev:
+        raise LilicorrArgumentError("workspace", f"is on {workspace.buf.device}, the logits on {dev}")
     if out is None:
         out = torch.empty((N, B), dtype=torch.int32, device=dev)
+    _require(out, "out", torch.int32, (N, B), dev)
+    if temperature is not None:
+        _require(temperature, "temperature", torch.float32, (N,), dev)
+    if uniforms is not None:
+        _require(uniforms, "uniforms", torch.float32, (N, B), dev)
+    if proposal is not None:
+        _require(proposal, "proposal", torch.float32, (N, B, K), dev)
+    if hidden is not None:
+        _require(hidden, "hidden", torch.bfloat16, (N, B, d.drafter_hidden), dev)
+    if target is not None:
+        _require(target, "target", torch.bfloat16, (N, d.target_hidden), dev)
     dbg = None
     if debug:
         de = weights.dims.d_e
@@ -308,10 +353,20 @@ def validate(logits_ptr: int, N: int, B: int, V: int, K: int, logits_dtype: int,
                                        ctypes.c_void_p(out_ptr)))
 
 
+def rerank_audit(N: int, B: int, V: int, K: int, dims: EncoderDims, drop_step: int = -1):
+    """Host-only audit of the rerank launch sequence; returns (status, report lines)."""
+    d = dims.c()
+    buf = ctypes.create_string_buffer(1 << 16)
+    st = int(lib().lilicorr_rerank_audit(N, B, V, K, ctypes.byref(d), drop_step, buf, len(buf)))
+    return st, buf.value.decode().splitlines()
+
+
 def topk_lse(logits2d, K: int):
     """Fused log-partition + exact top-K of [rows, V] device logits."""
     torch = _torch()
     _require_cuda(logits2d, "logits")
+    if logits2d.dim() != 2:
+        raise LilicorrArgumentError("logits", "must be [rows, V]")
     rows, V = logits2d.shape
     nbytes = int(lib().lilicorr_topk_workspace_bytes(rows, V, K))
     if nbytes == 0:
@@ -331,6 +386,8 @@ def topk_shard(logits2d, K: int, id_offset: int, out=None, workspace=None):
     out: optional (values, ids, ms) views to write into (e.g. slices of stacked buffers)."""
     torch = _torch()
     _require_cuda(logits2d, "logits")
+    if logits2d.dim() != 2:
+        raise LilicorrArgumentError("logits", "must be [rows, V_shard]")
     rows, V = logits2d.shape
     dev = logits2d.device
     nbytes = int(lib().lilicorr_topk_shard_workspace_bytes(rows, V, K))
@@ -343,6 +400,10 @@ def topk_shard(logits2d, K: int, id_offset: int, out=None, workspace=None):
                torch.empty((rows, K), dtype=torch.int32, device=dev),
                torch.empty((rows, 2), dtype=torch.float32, device=dev))
     val, idx, ms = out
+    _require(val, "values", torch.float32, (rows, K), dev)
+    _require(idx, "ids", torch.int32, (rows, K), dev)
+    _require(ms, "ms", torch.float32, (rows, 2), dev)
+    _require(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
     _check(lib().lilicorr_topk_shard(_ptr(logits2d), rows, V, K, _logits_dtype(logits2d), id_offset,
                                      _ptr(workspace), workspace.numel(), _ptr(val), _ptr(idx), _ptr(ms),
                                      _stream()), "topk_shard")
@@ -352,8 +413,14 @@ def topk_shard(logits2d, K: int, id_offset: int, out=None, workspace=None):
 def topk_merge(val, idx, ms):
     """Merge stacked shard outputs [G, rows, K] / [G, rows, 2] -> (ids, logp, lse)."""
     torch = _torch()
+    _require_cuda(val, "values")
+    if val.dim() != 3:
+        raise LilicorrArgumentError("values", "must be [G, rows, K]")
     G, rows, K = val.shape
     dev = val.device
+    _require(val, "values", torch.float32, (G, rows, K), dev)
+    _require(idx, "ids", torch.int32, (G, rows, K), dev)
+    _require(ms, "ms", torch.float32, (G, rows, 2), dev)
     tidx = torch.empty((rows, K), dtype=torch.int32, device=dev)
     logp = torch.empty((rows, K), dtype=torch.float32, device=dev)
     lse = torch.empty((rows,), dtype=torch.float32, device=dev)
@@ -366,8 +433,11 @@ def pair_scores(outv, inv):
     """outv, inv: [N, B, K, d_e] bf16 device tensors -> cos [N, B-1, K, K] float32."""
     torch = _torch()
     _require_cuda(outv, "outv")
-    _require_cuda(inv, "inv")
+    if outv.dim() != 4:
+        raise LilicorrArgumentError("outv", "must be [N, B, K, d_e]")
     N, B, K, de = outv.shape
+    _require(outv, "outv", torch.bfloat16, (N, B, K, de))
+    _require(inv, "inv", torch.bfloat16, (N, B, K, de), outv.device)
     cos = torch.empty((N, B - 1, K, K), dtype=torch.float32, device=outv.device)
     _check(lib().lilicorr_pair_scores(_ptr(outv), _ptr(inv), N, B, K, de, _ptr(cos), _stream()),
            "pair_scores")
@@ -377,8 +447,15 @@ def pair_scores(outv, inv):
 def greedy_walk(topk_idx, topk_logp, cos, alpha: float = 1.0, use_logp: bool = True):
     """Greedy commit; returns (tokens int32 [N,B], score, gap float32 [N,B])."""
     torch = _torch()
+    _require_cuda(topk_idx, "topk_idx")
+    if topk_idx.dim() != 3:
+        raise LilicorrArgumentError("topk_idx", "must be [N, B, K]")
     N, B, K = topk_idx.shape
     dev = topk_idx.device
+    _require(topk_idx, "topk_idx", torch.int32, (N, B, K), dev)
+    _require(topk_logp, "topk_logp", torch.float32, (N, B, K), dev)
+    if B > 1 or cos is not None:
+        _require(cos, "cos", torch.float32, (N, max(B - 1, 1), K, K), dev)
     out = torch.empty((N, B), dtype=torch.int32, device=dev)
     score = torch.empty((N, B), dtype=torch.float32, device=dev)
     gap = torch.empty((N, B), dtype=torch.float32, device=dev)
@@ -391,8 +468,15 @@ def greedy_walk(topk_idx, topk_logp, cos, alpha: float = 1.0, use_logp: bool = T
 def best_path(topk_idx, topk_logp, cos, alpha: float = 1.0, use_logp: bool = True):
     """Exact best path over given scores; returns (tokens int32 [N,B], score float32 [N,B])."""
     torch = _torch()
+    _require_cuda(topk_idx, "topk_idx")
+    if topk_idx.dim() != 3:
+        raise LilicorrArgumentError("topk_idx", "must be [N, B, K]")
     N, B, K = topk_idx.shape
     dev = topk_idx.device
+    _require(topk_idx, "topk_idx", torch.int32, (N, B, K), dev)
+    _require(topk_logp, "topk_logp", torch.float32, (N, B, K), dev)
+    if B > 1 or cos is not None:
+        _require(cos, "cos", torch.float32, (N, max(B - 1, 1), K, K), dev)
     out = torch.empty((N, B), dtype=torch.int32, device=dev)
     score = torch.empty((N, B), dtype=torch.float32, device=dev)
     _check(lib().lilicorr_best_path(_ptr(topk_idx), _ptr(topk_logp), _ptr(cos), N, B, K, alpha,
@@ -405,8 +489,17 @@ def sample_path(topk_idx, topk_logp, cos, temperature, uniforms, alpha: float = 
     """Sampled commit over given scores; returns (tokens int32 [N,B],
     proposal float32 [N,B,K], score float32 [N,B])."""
     torch = _torch()
+    _require_cuda(topk_idx, "topk_idx")
+    if topk_idx.dim() != 3:
+        raise LilicorrArgumentError("topk_idx", "must be [N, B, K]")
     N, B, K = topk_idx.shape
     dev = topk_idx.device
+    _require(topk_idx, "topk_idx", torch.int32, (N, B, K), dev)
+    _require(topk_logp, "topk_logp", torch.float32, (N, B, K), dev)
+    if B > 1 or cos is not None:
+        _require(cos, "cos", torch.float32, (N, max(B - 1, 1), K, K), dev)
+    _require(temperature, "temperature", torch.float32, (N,), dev)
+    _require(uniforms, "uniforms", torch.float32, (N, B), dev)
     out = torch.empty((N, B), dtype=torch.int32, device=dev)
     prop = torch.empty((N, B, K), dtype=torch.float32, device=dev)
     score = torch.empty((N, B), dtype=torch.float32, device=dev)
@@ -419,8 +512,18 @@ def sample_path(topk_idx, topk_logp, cos, temperature, uniforms, alpha: float = 
 def linear(A, W, bias=None, epilogue: int = EPI_F32, resid=None, workspace=None):
     """Y = A W^T + bias on MFMA with the given epilogue; A [M, Kd], W [N, Kd] bf16."""
     torch = _torch()
+    _require_cuda(A, "A")
+    if A.dim() != 2 or W.dim() != 2:
+        raise LilicorrArgumentError("linear", "A and W must be 2-D")
     M, Kd = A.shape
     N = W.shape[0]
+    dev = A.device
+    _require(A, "A", torch.bfloat16, (M, Kd), dev)
+    _require(W, "W", torch.bfloat16, (N, Kd), dev)
+    if bias is not None:
+        _require(bias, "bias", torch.float32, (N,), dev)
+    if resid is not None:
+        _require(resid, "resid", torch.float32, (M, N), dev)
     if epilogue in (EPI_F32, EPI_RESID_F32):
         out = resid if (epilogue == EPI_RESID_F32 and resid is not None) else torch.empty((M, N), dtype=torch.float32, device=A.device)
     else:
@@ -435,7 +538,12 @@ def linear(A, W, bias=None, epilogue: int = EPI_F32, resid=None, workspace=None)
 
 def rmsnorm(x, gamma, eps: float = 1e-6):
     torch = _torch()
+    _require_cuda(x, "x")
+    if x.dim() != 2:
+        raise LilicorrArgumentError("x", "must be [M, H]")
     M, H = x.shape
+    _require(x, "x", torch.float32, (M, H), x.device)
+    _require(gamma, "gamma", torch.float32, (H,), x.device)
     out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
     _check(lib().lilicorr_rmsnorm(_ptr(x), M, H, _ptr(gamma), eps, _ptr(out), _stream()), "rmsnorm")
     return out
@@ -443,6 +551,9 @@ def rmsnorm(x, gamma, eps: float = 1e-6):
 
 def lattice_attention(qkv, N: int, B: int, K: int, hidden: int, heads: int, dist, same):
     torch = _torch()
+    _require(qkv, "qkv", torch.bfloat16, (N * B * K, 3 * hidden))
+    _require(dist, "dist", torch.float32, (heads, 127), qkv.device)
+    _require(same, "same", torch.float32, (heads,), qkv.device)
     out = torch.empty((N * B * K, hidden), dtype=torch.bfloat16, device=qkv.device)
     _check(lib().lilicorr_lattice_attention(_ptr(qkv), N, B, K, hidden, heads, _ptr(dist), _ptr(same),
                                             _ptr(out), _stream()), "lattice_attention")

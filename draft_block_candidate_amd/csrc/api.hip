@@ -2,6 +2,7 @@
 // sequence of the reranking path. See include/lilicorr.h for the contract.
 #include <atomic>
 #include <cstring>
+#include <string>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -89,6 +90,254 @@ int commit_args_ok(const int32_t* topk_idx, const float* topk_logp, const float*
     hipError_t _e = (expr);                         \
     if (_e != hipSuccess) return LILICORR_EHIP;     \
   } while (0)
+
+// Regions of the rerank workspace (rerank_ws_layout), as bits for the audit.
+// outv / inv are split into slot 0's rows and the other slots' rows, which the
+// paper's head writes in separate launches.
+enum WsRegion {
+  WS_TOPK_PART, WS_TOPK_IDX, WS_TOPK_LOGP, WS_X, WS_HID, WS_U, WS_QKV, WS_ATTN, WS_HEADS, WS_OUTV,
+  WS_INV, WS_GEMM_PART, WS_PH, WS_AE, WS_TNORM, WS_TB, WS_APRE, WS_OUTV_SLOT0, WS_INV_SLOT0,
+  WS_REGION_COUNT
+};
+#define WS_BIT(r) (1u << WS_##r)
+const char* const kWsRegionName[WS_REGION_COUNT] = {
+    "topk_part", "topk_idx", "topk_logp", "x", "hid", "u", "qkv", "attn", "heads", "outv",
+    "inv", "gemm_part", "ph", "ae", "tnorm", "tb", "apre", "outv_slot0", "inv_slot0"};
+
+// Dry run of the launch sequence: each step states the workspace regions it
+// reads and writes; a read of a region that no earlier step wrote fails.
+// drop >= 0 leaves that step out (its writes never happen).
+struct Audit {
+  int drop = -1;
+  int index = 0;
+  uint32_t written = 0;
+  std::string log;
+  static std::string names(uint32_t m) {
+    std::string r;
+    for (int i = 0; i < WS_REGION_COUNT; ++i)
+      if (m & (1u << i)) {
+        if (!r.empty()) r += ",";
+        r += kWsRegionName[i];
+      }
+    return r.empty() ? "-" : r;
+  }
+  int step(const char* name, uint32_t reads, uint32_t writes) {
+    const int i = index++;
+    if (i == drop) {
+      log += std::to_string(i) + " " + name + " (left out)\n";
+      return LILICORR_OK;
+    }
+    log += std::to_string(i) + " " + name + " reads " + names(reads) + " writes " + names(writes);
+    const uint32_t missing = reads & ~written;
+    if (missing) {
+      log += " UNWRITTEN " + names(missing) + "\n";
+      return LILICORR_EINVAL;
+    }
+    log += "\n";
+    written |= writes;
+    return LILICORR_OK;
+  }
+};
+
+// The launch sequence of lilicorr_rerank over workspace `ws` (arguments
+// already validated). With `audit` set nothing is launched: every step only
+// records which workspace regions it reads and writes, and the audit fails at
+// the first step that reads a region no earlier step has written.
+int enqueue_rerank(const void* logits, int B, int V, int K, const lilicorr_params& pr, char* ws,
+                   int32_t* out_tokens, Audit* audit) {
+  const lilicorr_params* p = &pr;
+  hipStream_t st = (hipStream_t)p->stream;
+  const int N = p->num_blocks;
+  const lilicorr_dims& d = p->weights->dims;
+  const int H = d.hidden, F = d.ffn, de = d.d_e, heads = d.heads;
+  const int rows = N * B;
+  const int M = rows * K;
+  const WeightPtrs W = weight_ptrs(*p->weights);
+  const RerankWs L = rerank_ws_layout(N, B, V, K, d);
+  const TopkWs TL = topk_ws_layout(rows, V, K);
+  char* tws = ws + L.topk;
+  int32_t* topk_idx = p->dbg_topk_idx ? p->dbg_topk_idx : (int32_t*)(ws + L.topk_idx);
+  float* topk_logp = p->dbg_topk_logp ? p->dbg_topk_logp : (float*)(ws + L.topk_logp);
+  float* x = (float*)(ws + L.x);
+  uint16_t* hid = (uint16_t*)(ws + L.hid);
+  uint16_t* u = (uint16_t*)(ws + L.u);
+  uint16_t* qkv = (uint16_t*)(ws + L.qkv);
+  uint16_t* attn = (uint16_t*)(ws + L.attn);
+  float* heads_v = (float*)(ws + L.heads);
+  uint16_t* outv = p->dbg_outv ? p->dbg_outv : (uint16_t*)(ws + L.outv);
+  uint16_t* inv = p->dbg_inv ? p->dbg_inv : (uint16_t*)(ws + L.inv);
+  float* gpart = (float*)(ws + L.gemm_part);
+  // optional events around one stage (measurement only)
+  const bool timing = p->timing_begin != nullptr;
+  auto mark = [&](int stage, bool end) -> hipError_t {
+    if (audit || !timing || stage != p->timing_stage) return hipSuccess;
+    return hipEventRecord((hipEvent_t)(end ? p->timing_end : p->timing_begin), st);
+  };
+#define LL_STAGE(stage, ...)          \
+  do {                                \
+    LL_TRY(mark((stage), false));     \
+    __VA_ARGS__;                      \
+    LL_TRY(mark((stage), true));      \
+  } while (0)
+  // one launch: its workspace reads and writes (WS_* bits), then the launch
+#define LL_STEP(name, reads, writes, launch)                               \
+  do {                                                                     \
+    if (audit) {                                                           \
+      const int _a = audit->step((name), (reads), (writes));               \
+      if (_a != LILICORR_OK) return _a;                                    \
+    } else {                                                               \
+      LL_TRY(launch);                                                      \
+    }                                                                      \
+  } while (0)
+
+  const bool paper = d.target_hidden > 0;
+  const int Bl = paper ? B - 1 : B;             // slots in the lattice
+  const int Mp = N * Bl * K;                    // lattice rows
+  auto resid_norm = [&](const float* gamma) {
+    LinearEpilogue e;
+    e.kind = EPI_RESID_F32;
+    e.resid = x;
+    e.norm_gamma = gamma;
+    e.eps = kRmsEps;
+    e.norm_out = u;
+    return e;
+  };
+  auto plain = [](int kind) {
+    LinearEpilogue e;
+    e.kind = kind;
+    return e;
+  };
+  // the split-K scratch of a linear is written and read inside its own launch
+  const uint32_t GP = WS_BIT(GEMM_PART);
+  // every row of the out / in vectors
+  const uint32_t VEC_ALL = WS_BIT(OUTV) | WS_BIT(INV) | WS_BIT(OUTV_SLOT0) | WS_BIT(INV_SLOT0);
+
+  // a1: log-partition + top-K (the chunk partials are scratch of this launch)
+  LL_STAGE(LILICORR_STAGE_TOPK,
+           LL_STEP("topk_lse", 0, WS_BIT(TOPK_PART) | WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP),
+                   launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
+                                   (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms),
+                                   topk_idx, topk_logp, p->dbg_lse, st)));
+  if (!paper) {
+    // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0))
+    LL_STAGE(LILICORR_STAGE_NODE,
+             LL_STEP("node_build", WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP), WS_BIT(HID) | WS_BIT(X),
+                     launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, nullptr, W.S, W.R,
+                                       W.conf_w1, W.conf_b1, hid, x, V, st)));
+    LL_STAGE(LILICORR_STAGE_CONF_LINEAR,
+             LL_STEP("linear_conf_w2", WS_BIT(HID) | WS_BIT(X), WS_BIT(X) | WS_BIT(U) | GP,
+                     launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, resid_norm(W.layer[0].gamma1),
+                                   x, gpart, st)));
+  } else {
+    // a2 (paper's head): x = (((h W_hid^T + b_hid) + S) + R) + (W2c . hid + b2c), then
+    // x += E_t[tok] W_emb^T + b_emb with u = bf16(RMSNorm(x; gamma1 of layer 0))
+    const int Ht = d.target_hidden, Hd = d.drafter_hidden;
+    float* ph = (float*)(ws + L.ph);
+    uint16_t* ae = (uint16_t*)(ws + L.ae);
+    LL_STAGE(LILICORR_STAGE_NODE, {
+      LL_STEP("linear_hidden", 0, WS_BIT(PH) | GP,
+              launch_linear(p->hidden, N * B, Hd, W.w_hid, H, W.b_hid, plain(EPI_F32), ph, gpart, st));
+      LL_STEP("node_build", WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP) | WS_BIT(PH), WS_BIT(HID) | WS_BIT(X),
+              launch_node_build(topk_idx, topk_logp, N, B, K, H, nullptr, ph, W.S, W.R, W.conf_w1,
+                                W.conf_b1, hid, x, V, st));
+      LL_STEP("gather_rows", WS_BIT(TOPK_IDX), WS_BIT(AE),
+              launch_gather_rows(topk_idx, N, B, K, W.E_t, Ht, V, ae, st));
+    });
+    LinearEpilogue add_only = plain(EPI_RESID_F32);
+    add_only.resid = x;
+    LL_STAGE(LILICORR_STAGE_CONF_LINEAR, {
+      LL_STEP("linear_conf_w2", WS_BIT(HID) | WS_BIT(X), WS_BIT(X) | GP,
+              launch_linear(hid, Mp, H, W.conf_w2, H, W.conf_b2, add_only, x, gpart, st));
+      LL_STEP("linear_emb", WS_BIT(AE) | WS_BIT(X), WS_BIT(X) | WS_BIT(U) | GP,
+              launch_linear(ae, Mp, Ht, W.w_emb, H, W.b_emb, resid_norm(W.layer[0].gamma1), x, gpart,
+                            st));
+    });
+  }
+  // a3: two pre-norm layers; each residual GEMM also produces the next RMSNorm
+  for (int l = 0; l < 2; ++l) {
+    const LayerPtrs& Lw = W.layer[l];
+    const float* next_gamma = l == 0 ? W.layer[1].gamma1 : W.gamma_f;
+    const int s0 = 5 * l;
+    LL_STAGE(LILICORR_STAGE_QKV + s0,
+             LL_STEP("linear_qkv", WS_BIT(U), WS_BIT(QKV) | GP,
+                     launch_linear(u, Mp, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st)));
+    LL_STAGE(LILICORR_STAGE_ATTENTION + s0,
+             LL_STEP("lattice_attention", WS_BIT(QKV), WS_BIT(ATTN),
+                     launch_attention(qkv, N, Bl, K, H, heads, Lw.dist, Lw.same, attn, st)));
+    LL_STAGE(LILICORR_STAGE_O + s0,
+             LL_STEP("linear_o", WS_BIT(ATTN) | WS_BIT(X), WS_BIT(X) | WS_BIT(U) | GP,
+                     launch_linear(attn, Mp, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
+    LL_STAGE(LILICORR_STAGE_FFN1 + s0,
+             LL_STEP("linear_ffn1", WS_BIT(U), WS_BIT(HID) | GP,
+                     launch_linear(u, Mp, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st)));
+    LL_STAGE(LILICORR_STAGE_FFN2 + s0,
+             LL_STEP("linear_ffn2", WS_BIT(HID) | WS_BIT(X), WS_BIT(X) | WS_BIT(U) | GP,
+                     launch_linear(hid, Mp, F, Lw.w2, H, Lw.b2, resid_norm(next_gamma), x, gpart, st)));
+  }
+  // a4: out|in heads and their unit normalisation
+  if (!paper) {
+    LinearEpilogue e = plain(EPI_F32);
+    e.heads_out = outv;
+    e.heads_in = inv;
+    LL_STAGE(LILICORR_STAGE_HEADS,
+             LL_STEP("linear_heads", WS_BIT(U), VEC_ALL | GP,
+                     launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st)));
+  } else {
+    // a4 (paper's head): tb = bf16(bf16(RMSNorm(t; gamma_t)) W_tgt^T + b_tgt);
+    // y = bf16(SiLU([u, tb, bf16(u tb)] W_fuse^T + b_fuse)); out|in heads of y;
+    // anchor o_0 = unit(tb W_anchor^T + b_anchor) in slot 0's rows
+    const int Ht = d.target_hidden;
+    uint16_t* tnorm = (uint16_t*)(ws + L.tnorm);
+    uint16_t* tb = (uint16_t*)(ws + L.tb);
+    float* apre = (float*)(ws + L.apre);
+    uint16_t* cat = qkv;     // [Mp, 3H] bf16: the layers are done with qkv
+    uint16_t* y = attn;      // [Mp, H] bf16
+    LinearEpilogue e = plain(EPI_F32);
+    e.heads_out = outv;           // lattice row (n, s - 1, j) -> row (n, s, j)
+    e.heads_in = inv;
+    e.heads_group = Bl * K;
+    e.heads_skip = K;
+    LL_STAGE(LILICORR_STAGE_HEADS, {
+      LL_STEP("rmsnorm_target", 0, WS_BIT(TNORM),
+              launch_rmsnorm_bf16(p->target, N, Ht, W.gamma_t, kRmsEps, tnorm, st));
+      LL_STEP("linear_target", WS_BIT(TNORM), WS_BIT(TB) | GP,
+              launch_linear(tnorm, N, Ht, W.w_tgt, H, W.b_tgt, plain(EPI_BF16), tb, gpart, st));
+      LL_STEP("linear_anchor", WS_BIT(TB), WS_BIT(APRE) | GP,
+              launch_linear(tb, N, H, W.w_anchor, de, W.b_anchor, plain(EPI_F32), apre, gpart, st));
+      LL_STEP("concat", WS_BIT(U) | WS_BIT(TB), WS_BIT(QKV),
+              launch_concat(u, tb, N, Bl * K, H, cat, st));
+      LL_STEP("linear_fuse", WS_BIT(QKV), WS_BIT(ATTN) | GP,
+              launch_linear(cat, Mp, 3 * H, W.w_fuse, H, W.b_fuse, plain(EPI_SILU_BF16), y, gpart, st));
+      LL_STEP("linear_heads", WS_BIT(ATTN), WS_BIT(OUTV) | WS_BIT(INV) | GP,
+              launch_linear(y, Mp, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st));
+      LL_STEP("anchor_rows", WS_BIT(APRE), WS_BIT(OUTV_SLOT0) | WS_BIT(INV_SLOT0),
+              launch_anchor_rows(apre, N, B, K, de, outv, inv, st));
+    });
+  }
+  // a5: pair scores, a6: the commit (one fused kernel: B * K <= 512 keeps the
+  // block's cosines within the kernel's LDS budget). Wide vectors: the pair
+  // products first, in d_e slices over many waves (into the heads buffer,
+  // which the heads are done with), then the walk adds the slices.
+  LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, false));
+  const uint32_t walk_reads = WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP);
+  if (de >= kPairSliceMinDe) {
+    LL_STEP("pair_slices", VEC_ALL, WS_BIT(HEADS),
+            launch_pair_slices(outv, inv, N, B, K, de, heads_v, st));
+    LL_STEP("scores_walk", walk_reads | WS_BIT(HEADS), 0,
+            launch_scores_walk(nullptr, nullptr, heads_v, pair_slice_count(de), topk_idx, topk_logp,
+                               N, B, K, de, commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score,
+                               p->dbg_gap, st));
+  } else {
+    LL_STEP("scores_walk", walk_reads | VEC_ALL, 0,
+            launch_scores_walk(outv, inv, nullptr, 1, topk_idx, topk_logp, N, B, K, de,
+                               commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score, p->dbg_gap,
+                               st));
+  }
+  LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, true));
+#undef LL_STEP
+#undef LL_STAGE
+  return LILICORR_OK;
+}
 
 }  // namespace
 
@@ -193,156 +442,33 @@ int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_para
   if (v != LILICORR_OK) return v;
   const int dc = check_device();
   if (dc != LILICORR_OK) return dc;
-  hipStream_t st = (hipStream_t)p->stream;
-  const int N = p->num_blocks;
-  const lilicorr_dims& d = p->weights->dims;
-  const int H = d.hidden, F = d.ffn, de = d.d_e, heads = d.heads;
-  const int rows = N * B;
-  const int M = rows * K;
-  const WeightPtrs W = weight_ptrs(*p->weights);
-  const RerankWs L = rerank_ws_layout(N, B, V, K, d);
-  char* ws = (char*)p->workspace;
-  const TopkWs TL = topk_ws_layout(rows, V, K);
-  char* tws = ws + L.topk;
-  int32_t* topk_idx = p->dbg_topk_idx ? p->dbg_topk_idx : (int32_t*)(ws + L.topk_idx);
-  float* topk_logp = p->dbg_topk_logp ? p->dbg_topk_logp : (float*)(ws + L.topk_logp);
-  float* x = (float*)(ws + L.x);
-  uint16_t* hid = (uint16_t*)(ws + L.hid);
-  uint16_t* u = (uint16_t*)(ws + L.u);
-  uint16_t* qkv = (uint16_t*)(ws + L.qkv);
-  uint16_t* attn = (uint16_t*)(ws + L.attn);
-  float* heads_v = (float*)(ws + L.heads);
-  uint16_t* outv = p->dbg_outv ? p->dbg_outv : (uint16_t*)(ws + L.outv);
-  uint16_t* inv = p->dbg_inv ? p->dbg_inv : (uint16_t*)(ws + L.inv);
-  float* gpart = (float*)(ws + L.gemm_part);
-  // optional events around one stage (measurement only)
-  const bool timing = p->timing_begin != nullptr;
-  auto mark = [&](int stage, bool end) -> hipError_t {
-    if (!timing || stage != p->timing_stage) return hipSuccess;
-    return hipEventRecord((hipEvent_t)(end ? p->timing_end : p->timing_begin), st);
-  };
-#define LL_STAGE(stage, ...)          \
-  do {                                \
-    LL_TRY(mark((stage), false));     \
-    __VA_ARGS__;                      \
-    LL_TRY(mark((stage), true));      \
-  } while (0)
+  return enqueue_rerank(logits, B, V, K, *p, (char*)p->workspace, out_tokens, nullptr);
+}
 
-  // a1: log-partition + top-K
-  LL_STAGE(LILICORR_STAGE_TOPK, LL_TRY(launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
-                         (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms), topk_idx,
-                         topk_logp, p->dbg_lse, st)));
-  const bool paper = d.target_hidden > 0;
-  const int Bl = paper ? B - 1 : B;             // slots in the lattice
-  const int Mp = N * Bl * K;                    // lattice rows
-  auto resid_norm = [&](const float* gamma) {
-    LinearEpilogue e;
-    e.kind = EPI_RESID_F32;
-    e.resid = x;
-    e.norm_gamma = gamma;
-    e.eps = kRmsEps;
-    e.norm_out = u;
-    return e;
-  };
-  auto plain = [](int kind) {
-    LinearEpilogue e;
-    e.kind = kind;
-    return e;
-  };
-  if (!paper) {
-    // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0))
-    LL_STAGE(LILICORR_STAGE_NODE,
-             LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, nullptr, W.S, W.R,
-                                      W.conf_w1, W.conf_b1, hid, x, V, st)));
-    LL_STAGE(LILICORR_STAGE_CONF_LINEAR,
-             LL_TRY(launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, resid_norm(W.layer[0].gamma1),
-                                  x, gpart, st)));
-  } else {
-    // a2 (paper's head): x = (((h W_hid^T + b_hid) + S) + R) + (W2c . hid + b2c), then
-    // x += E_t[tok] W_emb^T + b_emb with u = bf16(RMSNorm(x; gamma1 of layer 0))
-    const int Ht = d.target_hidden, Hd = d.drafter_hidden;
-    float* ph = (float*)(ws + L.ph);
-    uint16_t* ae = (uint16_t*)(ws + L.ae);
-    LL_STAGE(LILICORR_STAGE_NODE, {
-      LL_TRY(launch_linear(p->hidden, N * B, Hd, W.w_hid, H, W.b_hid, plain(EPI_F32), ph, gpart, st));
-      LL_TRY(launch_node_build(topk_idx, topk_logp, N, B, K, H, nullptr, ph, W.S, W.R, W.conf_w1,
-                               W.conf_b1, hid, x, V, st));
-      LL_TRY(launch_gather_rows(topk_idx, N, B, K, W.E_t, Ht, V, ae, st));
-    });
-    LinearEpilogue add_only = plain(EPI_RESID_F32);
-    add_only.resid = x;
-    LL_STAGE(LILICORR_STAGE_CONF_LINEAR, {
-      LL_TRY(launch_linear(hid, Mp, H, W.conf_w2, H, W.conf_b2, add_only, x, gpart, st));
-      LL_TRY(launch_linear(ae, Mp, Ht, W.w_emb, H, W.b_emb, resid_norm(W.layer[0].gamma1), x, gpart,
-                           st));
-    });
+int lilicorr_rerank_audit(int N, int B, int V, int K, const lilicorr_dims* dims, int drop_step,
+                          char* report, size_t report_bytes) {
+  if (!dims || !sizes_ok(N, B, V, K)) return LILICORR_EINVAL;
+  if (!dims_supported(dims)) return LILICORR_EUNSUPPORTED;
+  if (dims->target_hidden > 0 && B < 2) return LILICORR_EINVAL;
+  lilicorr_weights w{};
+  w.dims = *dims;
+  w.vocab = V;
+  lilicorr_params p{};
+  p.abi_version = LILICORR_ABI_VERSION;
+  p.num_blocks = N;
+  p.logits_dtype = LILICORR_BF16;
+  p.alpha = 1.f;
+  p.use_logp = 1;
+  p.weights = &w;
+  Audit a;
+  a.drop = drop_step;
+  const int st = enqueue_rerank(nullptr, B, V, K, p, nullptr, nullptr, &a);
+  if (report && report_bytes > 0) {
+    const size_t n = a.log.size() < report_bytes - 1 ? a.log.size() : report_bytes - 1;
+    std::memcpy(report, a.log.data(), n);
+    report[n] = 0;
   }
-  // a3: two pre-norm layers; each residual GEMM also produces the next RMSNorm
-  for (int l = 0; l < 2; ++l) {
-    const LayerPtrs& Lw = W.layer[l];
-    const float* next_gamma = l == 0 ? W.layer[1].gamma1 : W.gamma_f;
-    const int s0 = 5 * l;
-    LL_STAGE(LILICORR_STAGE_QKV + s0,
-             LL_TRY(launch_linear(u, Mp, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st)));
-    LL_STAGE(LILICORR_STAGE_ATTENTION + s0,
-             LL_TRY(launch_attention(qkv, N, Bl, K, H, heads, Lw.dist, Lw.same, attn, st)));
-    LL_STAGE(LILICORR_STAGE_O + s0,
-             LL_TRY(launch_linear(attn, Mp, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
-    LL_STAGE(LILICORR_STAGE_FFN1 + s0,
-             LL_TRY(launch_linear(u, Mp, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st)));
-    LL_STAGE(LILICORR_STAGE_FFN2 + s0,
-             LL_TRY(launch_linear(hid, Mp, F, Lw.w2, H, Lw.b2, resid_norm(next_gamma), x, gpart, st)));
-  }
-  // a4: out|in heads and their unit normalisation
-  if (!paper) {
-    LinearEpilogue e = plain(EPI_F32);
-    e.heads_out = outv;
-    e.heads_in = inv;
-    LL_STAGE(LILICORR_STAGE_HEADS,
-             LL_TRY(launch_linear(u, M, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st)));
-  } else {
-    // a4 (paper's head): tb = bf16(bf16(RMSNorm(t; gamma_t)) W_tgt^T + b_tgt);
-    // y = bf16(SiLU([u, tb, bf16(u tb)] W_fuse^T + b_fuse)); out|in heads of y;
-    // anchor o_0 = unit(tb W_anchor^T + b_anchor) in slot 0's rows
-    const int Ht = d.target_hidden;
-    uint16_t* tnorm = (uint16_t*)(ws + L.tnorm);
-    uint16_t* tb = (uint16_t*)(ws + L.tb);
-    float* apre = (float*)(ws + L.apre);
-    uint16_t* cat = qkv;     // [Mp, 3H] bf16: the layers are done with qkv
-    uint16_t* y = attn;      // [Mp, H] bf16
-    LinearEpilogue e = plain(EPI_F32);
-    e.heads_out = outv;           // lattice row (n, s - 1, j) -> row (n, s, j)
-    e.heads_in = inv;
-    e.heads_group = Bl * K;
-    e.heads_skip = K;
-    LL_STAGE(LILICORR_STAGE_HEADS, {
-      LL_TRY(launch_rmsnorm_bf16(p->target, N, Ht, W.gamma_t, kRmsEps, tnorm, st));
-      LL_TRY(launch_linear(tnorm, N, Ht, W.w_tgt, H, W.b_tgt, plain(EPI_BF16), tb, gpart, st));
-      LL_TRY(launch_linear(tb, N, H, W.w_anchor, de, W.b_anchor, plain(EPI_F32), apre, gpart, st));
-      LL_TRY(launch_concat(u, tb, N, Bl * K, H, cat, st));
-      LL_TRY(launch_linear(cat, Mp, 3 * H, W.w_fuse, H, W.b_fuse, plain(EPI_SILU_BF16), y, gpart, st));
-      LL_TRY(launch_linear(y, Mp, H, W.w_heads, 2 * de, W.b_heads, e, heads_v, gpart, st));
-      LL_TRY(launch_anchor_rows(apre, N, B, K, de, outv, inv, st));
-    });
-  }
-  // a5: pair scores, a6: the commit (one fused kernel: B * K <= 512 keeps the
-  // block's cosines within the kernel's LDS budget). Wide vectors: the pair
-  // products first, in d_e slices over many waves (into the heads buffer,
-  // which the heads are done with), then the walk adds the slices.
-  LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, false));
-  if (de >= kPairSliceMinDe) {
-    LL_TRY(launch_pair_slices(outv, inv, N, B, K, de, heads_v, st));
-    LL_TRY(launch_scores_walk(nullptr, nullptr, heads_v, pair_slice_count(de), topk_idx, topk_logp,
-                              N, B, K, de, commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score,
-                              p->dbg_gap, st));
-  } else {
-    LL_TRY(launch_scores_walk(outv, inv, nullptr, 1, topk_idx, topk_logp, N, B, K, de,
-                              commit_rule(*p), p->dbg_cos, out_tokens, p->dbg_score, p->dbg_gap,
-                              st));
-  }
-  LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, true));
-#undef LL_STAGE
-  return LILICORR_OK;
+  return st;
 }
 
 int lilicorr_topk_lse(const void* logits, int rows, int V, int K, int dtype, void* workspace,
@@ -421,6 +547,17 @@ int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const 
   if (use_logp != 0 && use_logp != 1) return LILICORR_EINVAL;
   const int dc = check_device();
   if (dc != LILICORR_OK) return dc;
+  if (B * K <= LILICORR_MAX_LATTICE && scores_walk_lds_bytes(B, K) <= kScoresWalkMaxLds) {
+    // the commit kernel of lilicorr_rerank, fed the given cosines
+    CommitRule r;
+    r.kind = RULE_GREEDY;
+    r.alpha = alpha;
+    r.use_logp = use_logp;
+    return hip_status(launch_scores_walk(nullptr, nullptr, cos, 1, topk_idx, topk_logp, N, B, K, 0,
+                                         r, nullptr, out_tokens, score, gap, (hipStream_t)stream));
+  }
+  // lattices whose cosines exceed that kernel's LDS: one wave per block
+  // scanning the cosines in global memory
   return hip_status(launch_greedy_walk(topk_idx, topk_logp, cos, N, B, K, alpha, use_logp,
                                        out_tokens, score, gap, (hipStream_t)stream));
 }

@@ -188,6 +188,24 @@ typedef struct {
 LILICORR_API int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_params* p,
                     int32_t* out_tokens);
 
+/* Host-only audit of lilicorr_rerank's launch sequence for N blocks of B slots,
+ * vocabulary V, K candidates and the given geometry (the commit rule and the
+ * debug outputs do not change which workspace regions are used). Launches
+ * nothing and needs no GPU. Each launch declares the workspace regions it reads
+ * and writes (the split-K and top-K chunk scratch are written and read inside
+ * their own launch); the audit walks the sequence in launch order and fails at
+ * the first launch that reads a region no earlier launch has written, so a
+ * workspace of any prior contents (lilicorr_rerank never clears it) gives the
+ * same result. drop_step >= 0 leaves that launch out of the walk (a test of the
+ * audit itself: a dropped producer must be caught).
+ *   report  host buffer (may be NULL) for one line per launch:
+ *           "<index> <name> reads <regions> writes <regions>", and
+ *           " UNWRITTEN <regions>" on the failing line; NUL-terminated, truncated
+ *           to report_bytes.
+ * Returns OK, EINVAL (bad sizes, or a read before any write), EUNSUPPORTED (dims). */
+LILICORR_API int lilicorr_rerank_audit(int N, int B, int V, int K, const lilicorr_dims* dims,
+                                       int drop_step, char* report, size_t report_bytes);
+
 /* Host-only check of lilicorr_rerank's arguments; launches nothing and needs no GPU.
  * Returns exactly the status lilicorr_rerank would return before launching. */
 LILICORR_API int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_params* p,
@@ -279,7 +297,10 @@ LILICORR_API int lilicorr_pair_scores(const uint16_t* outv, const uint16_t* inv,
  * cos[s-1][c_{s-1}][j])) (use_logp = 1) or fl32(alpha * cos[..]) (use_logp = 0);
  * c_s = lowest j with maximal z_j; out_tokens[s] = topk_idx[s][c_s].
  *   topk_idx int32 / topk_logp float [N,B,K], cos float [N,B-1,K,K] (device)
- *   out_tokens int32 [N,B]; score, gap float [N,B] (device, may be NULL). */
+ *   out_tokens int32 [N,B]; score, gap float [N,B] (device, may be NULL).
+ * For B * K <= 512 this runs the commit kernel of lilicorr_rerank on the given
+ * cosines; larger lattices (up to 64 x 64) run a one-wave-per-block walk over
+ * the cosines in global memory. Errors: EINVAL, EHIP. */
 LILICORR_API int lilicorr_greedy_walk(const int32_t* topk_idx, const float* topk_logp, const float* cos, int N,
                          int B, int K, float alpha, int use_logp, int32_t* out_tokens,
                          float* score, float* gap, void* stream);

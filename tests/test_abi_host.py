@@ -176,3 +176,67 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/liblilicorr.so")
     with pytest.raises(L.LilicorrUnavailable):
         L.lib()
+
+
+def _parse_audit(lines):
+    steps = []
+    for ln in lines:
+        parts = ln.split()
+        reads = set() if parts[3] == "-" else set(parts[3].split(","))
+        writes = set() if parts[5] == "-" else set(parts[5].split(","))
+        steps.append((parts[1], reads, writes))
+    return steps
+
+
+AUDIT_SHAPES = [("tiny", 1), ("c1_qwen3_8b", 1), ("c32", 32), ("c256_k16", 256), ("entropy_k32", 64),
+                ("odd_h2560", 41), ("paper_tiny", 1), ("paper_qwen3_8b", 1), ("paper_c32", 32)]
+
+
+@pytest.mark.parametrize("name,N", AUDIT_SHAPES)
+def test_rerank_reads_no_workspace_region_before_writing_it(name, N):
+    # lilicorr_rerank never clears its workspace: every region a launch reads
+    # must have been written by an earlier launch of the same call
+    import synth
+    w = synth.WORKLOADS[name]
+    dims = L.EncoderDims(w.hidden, w.heads, w.ffn, w.d_e, target_hidden=w.target_hidden,
+                         drafter_hidden=w.drafter_hidden)
+    st, lines = L.rerank_audit(N, w.slots, w.vocab, w.topk, dims)
+    assert st == L.OK, lines
+    steps = _parse_audit(lines)
+    assert steps[0][0] == "topk_lse" and steps[-1][0] == "scores_walk"
+    assert sum(s[0] == "lattice_attention" for s in steps) == 2
+    # the audit is not vacuous: leaving out a launch whose outputs are new
+    # (not all written by an earlier launch) must be caught
+    for i, (nm, _, writes) in enumerate(steps):
+        before = set().union(*[s[2] for s in steps[:i]]) if i else set()
+        st_drop, drop_lines = L.rerank_audit(N, w.slots, w.vocab, w.topk, dims, i)
+        if writes - before - {"gemm_part", "topk_part"}:
+            assert st_drop == L.EINVAL and any("UNWRITTEN" in ln for ln in drop_lines), (i, nm)
+        else:
+            assert st_drop == L.OK, (i, nm)
+
+
+def test_rerank_audit_wide_vectors_and_bad_sizes():
+    # d_e >= 512 adds the sliced pair products, whose partial sums the walk reads
+    dims = L.EncoderDims(128, 2, 256, 544)
+    st, lines = L.rerank_audit(2, 7, 4096, 7, dims)
+    assert st == L.OK
+    names = [s[0] for s in _parse_audit(lines)]
+    assert names[-2:] == ["pair_slices", "scores_walk"]
+    assert L.rerank_audit(0, 16, 4096, 4, dims)[0] == L.EINVAL
+    assert L.rerank_audit(1, 16, 4096, 65, dims)[0] == L.EINVAL
+    assert L.rerank_audit(1, 16, 4096, 4, L.EncoderDims(100, 2, 256, 32))[0] == L.EUNSUPPORTED
+
+
+def test_binding_rejects_host_tensors_before_the_library():
+    # a host tensor never reaches the library as a device pointer
+    import torch
+    w = L.EncoderDims(64, 2, 256, 32)
+    with pytest.raises(L.LilicorrArgumentError) as e:
+        L.rerank(torch.zeros((1, 16, 1024)), 4, None)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.LilicorrArgumentError):
+        L.greedy_walk(torch.zeros((1, 4, 2), dtype=torch.int32), torch.zeros((1, 4, 2)), torch.zeros((1, 3, 2, 2)))
+    with pytest.raises(L.LilicorrArgumentError):
+        L.topk_lse(torch.zeros((4, 100)), 4)
+    del w

@@ -5,18 +5,20 @@ state per slot and the target state per block besides the logits; the
 paper's configuration (Table 4: width 1024, 8 heads, FFN 2048, d_e 1024, the
 sigma * cos rule with sigma = 8) runs at its full size with Qwen3-8B widths
 (4096) for the drafter and target states, and on a small twin the oracle
-checks block by block. The bars are those of the lattice head
-(tests/test_gpu_rerank.py): top-K ids exactly; lse and logp within 1e-3;
-cosines within 1e-3 for a fraction of the elements and all within the bf16
-bound; committed tokens exactly unless excused by a sub-tolerance score gap.
+checks block by block (every block of the 32-block case). The bars are those
+of the lattice head (tests/helpers.py, tests/test_gpu_rerank.py): top-K ids
+exactly; lse and logp within 1e-3; cosines within 1e-3 on 99.9 % of the
+elements and all within 2e-3 (step scores sigma times that); in/out vectors
+within 2^-8 per component; committed tokens exactly unless the oracle's score
+gap of the GPU's pick is within the step tolerance, on at most 1 % of slots.
 Weights: every tensor of the head, sampled elements bit-exact against the
 oracle's generator.
 """
 import numpy as np
 import pytest
 
-from helpers import (assert_within, assert_scores, bf16_to_f64, to_device, oracle_weights,
-                     device_weights, compare_walk, oracle_step_scores, COS_FRACTION)
+from helpers import (assert_within, assert_scores, assert_vectors, assert_excuse_cap, record, bf16_to_f64,
+                     to_device, oracle_weights, device_weights, compare_walk, oracle_step_scores, COS_FRACTION)
 import synth
 import oracle
 from oracle.weights import Dims, weight_table
@@ -51,7 +53,7 @@ def test_paper_weights_bit_exact(L, name):
 
 
 CASES = [("paper_tiny", None, "greedy"), ("paper_qwen3_8b", None, "greedy"),
-         ("paper_c32", [0, 13, 31], "greedy"), ("paper_tiny", None, "exact")]
+         ("paper_c32", None, "greedy"), ("paper_tiny", None, "exact")]
 
 
 @pytest.mark.parametrize("name,sample,rule", CASES)
@@ -67,8 +69,9 @@ def test_paper_head_matches_oracle(L, name, sample, rule):
     ow = oracle_weights(w)
     hidden = synth.bf16_bits_to_f32(hid_bits).astype(np.float64)
     target = synth.bf16_bits_to_f32(tgt_bits).astype(np.float64)
-    g_cos, o_cos, g_z, o_z, excused = [], [], [], [], []
-    for b in (range(w.num_blocks) if sample is None else sample):
+    g_cos, o_cos, g_z, o_z, excused, g_vec, o_vec = [], [], [], [], [], [], []
+    blocks = list(range(w.num_blocks) if sample is None else sample)
+    for b in blocks:
         r = oracle.rerank_block(host[b], w.topk, ow, w.alpha, w.use_logp, rule=rule, hidden=hidden[b],
                                 target=target[b])
         gidx = dbg["topk_idx"][b].cpu().numpy()
@@ -76,7 +79,8 @@ def test_paper_head_matches_oracle(L, name, sample, rule):
         assert_within(dbg["lse"][b].cpu().numpy(), r.lse, what=f"block {b} lse")
         assert_within(dbg["topk_logp"][b].cpu().numpy(), r.logp, what=f"block {b} logp")
         go, gi = bf16_to_f64(dbg["outv"][b]), bf16_to_f64(dbg["inv"][b])
-        assert np.abs(go - r.outv).max() < 2e-2 and np.abs(gi - r.inv).max() < 2e-2, f"block {b} in/out"
+        g_vec += [go.ravel(), gi.ravel()]
+        o_vec += [r.outv.ravel(), r.inv.ravel()]
         assert np.all(gi[0] == 0) and np.all(go[0] == go[0][0]), "anchor rows"
         gtok = tokens[b].cpu().numpy()
         choice = np.array([int(np.nonzero(gidx[s] == gtok[s])[0][0]) for s in range(w.slots)])
@@ -98,9 +102,10 @@ def test_paper_head_matches_oracle(L, name, sample, rule):
     sc = assert_scores(np.concatenate([c.ravel() for c in g_cos]), np.concatenate([c.ravel() for c in o_cos]),
                        f"{name} cos", 1.0, COS_FRACTION)
     sz = assert_scores(np.concatenate(g_z), np.concatenate(o_z), f"{name} step scores", w.alpha, COS_FRACTION, step=True)
-    print(f"[scores] {name}: cos {sc} step {sz}", flush=True)
-    if excused:
-        print(f"[excused] {name}: {excused}", flush=True)
+    vec = assert_vectors(np.concatenate(g_vec), np.concatenate(o_vec), f"{name} in/out vectors")
+    n_slots = len(blocks) * (w.slots - 1)
+    record(f"paper/{name}/{rule}", blocks=len(blocks), slots=n_slots, excused=excused, cos=sc, step=sz, vectors=vec)
+    assert_excuse_cap(excused, n_slots, name)
 
 
 def test_paper_head_errors_without_inputs(L):
@@ -130,15 +135,20 @@ def test_paper_head_degenerate_and_ragged(L, B, K, N, de):
     ow = oracle_weights(w)
     hidden = synth.bf16_bits_to_f32(hid_bits).astype(np.float64)
     target = synth.bf16_bits_to_f32(tgt_bits).astype(np.float64)
+    excused, g_vec, o_vec = [], [], []
     for b in range(N):
         r = oracle.rerank_block(host[b], K, ow, w.alpha, w.use_logp, hidden=hidden[b], target=target[b])
         gidx = dbg["topk_idx"][b].cpu().numpy()
         assert np.array_equal(gidx, r.idx), f"block {b}: top-K ids"
-        go, gi = bf16_to_f64(dbg["outv"][b]), bf16_to_f64(dbg["inv"][b])
-        assert np.abs(go - r.outv).max() < 2e-2 and np.abs(gi - r.inv).max() < 2e-2, f"block {b} in/out"
+        g_vec += [bf16_to_f64(dbg["outv"][b]).ravel(), bf16_to_f64(dbg["inv"][b]).ravel()]
+        o_vec += [r.outv.ravel(), r.inv.ravel()]
         assert_scores(dbg["cos"][b].cpu().numpy(), r.cos, f"edge block {b} cos", 1.0, COS_FRACTION)
         gtok = tokens[b].cpu().numpy()
         choice = np.array([int(np.nonzero(gidx[s] == gtok[s])[0][0]) for s in range(B)])
         ex = compare_walk(r.logp, r.cos, choice, w.alpha, w.use_logp)
+        excused += [(b,) + e for e in ex]
         if not ex:
             assert np.array_equal(gtok, r.tokens.astype(np.int32)), f"block {b}: tokens"
+    vec = assert_vectors(np.concatenate(g_vec), np.concatenate(o_vec), f"edge {B}x{K} in/out vectors")
+    record(f"paper/edge/B{B}/K{K}/N{N}/de{de}", blocks=N, slots=N * (B - 1), excused=excused, vectors=vec)
+    assert_excuse_cap(excused, N * (B - 1), f"edge {B}x{K}")

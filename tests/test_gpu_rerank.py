@@ -1,20 +1,25 @@
 """End-to-end parity of lilicorr_rerank against the oracle (GPU).
 
 Every workload runs at its full size on the GPU, in the launch configuration
-the benchmark times; the oracle recomputes sampled blocks one by one.
-Top-K ids must match exactly; lse and logp within 1e-3 * max(1, |oracle|);
-pair cosines within 1e-3 * max(1, |oracle|), and committed step scores within
-max(1, |alpha|) times that (a step score carries alpha times its cosine's
-error), for at least 99.9% of the elements and within the bf16 bound for all (the bound and
-its derivation are in tests/helpers.py); committed tokens exactly, except
-where the oracle's score of the GPU's pick is within the score bound of the
-best (each such excused slot is reported).
+the benchmark times. Against the oracle:
+  * top-K ids exactly, lse and logp within 1e-3 * max(1, |oracle|), on every
+    row of every workload;
+  * on the compared blocks (all of them up to 32 blocks, 16 spread over the
+    256-block workload, 6 per entropy tier): pair cosines and committed step
+    scores within the bars of tests/helpers.py (1e-3 on at least 99.9 % of
+    the elements, every element within 2e-3; step scores scaled by
+    max(1, |alpha|)), in/out vectors within 2^-8 per component (mean 2e-4,
+    85 % equal or one bf16 ulp apart), committed tokens exactly except where
+    the oracle scores the GPU's pick within 1e-3 * max(1, |z*|) of its best,
+    on at most 1 % of the compared slots. The bars are the float32 drift that
+    tests/test_tolerance_derivation.py measures at these shapes, with margin.
+Each case's figures go to the parity log (helpers.record).
 """
 import numpy as np
 import pytest
 
-from helpers import (assert_within, assert_scores, bf16_to_f64, to_device, oracle_weights,
-                     device_weights, compare_walk, oracle_step_scores, TOL, COS_FRACTION)
+from helpers import (assert_within, assert_scores, assert_vectors, assert_excuse_cap, record, bf16_to_f64,
+                     to_device, oracle_weights, device_weights, compare_walk, oracle_step_scores, COS_FRACTION)
 import synth
 import oracle
 
@@ -30,20 +35,37 @@ def L():
     return lib
 
 
+def spread(n_blocks, count):
+    """`count` block indices spread evenly over [0, n_blocks), first and last included."""
+    return sorted(set(np.linspace(0, n_blocks - 1, count).round().astype(int).tolist()))
+
+
 CASES = [
     ("tiny", 0, None),
     ("c1_qwen3_8b", 0, None),
-    ("c32", 0, [0, 17, 31]),
-    ("c256_k16", 0, [0, 128, 255]),
-    ("entropy_k32", 0, [0]),
-    ("entropy_k32", 1, [31]),
-    ("entropy_k32", 2, [63]),
+    ("c32", 0, None),
+    ("c256_k16", 0, spread(256, 16)),
+    ("entropy_k32", 0, spread(64, 6)),
+    ("entropy_k32", 1, spread(64, 6)),
+    ("entropy_k32", 2, spread(64, 6)),
     ("odd_h2560", 0, [0, 40]),
 ]
 # The wide odd shape (H = 2560) cascades more bf16 rounding flips: an
-# independent float32 build of the encoder already misses TOL on ~0.15 % of its
-# cosines (tests/test_tolerance_derivation.py), so its fraction is 0.995.
+# independent float32 build of the encoder already misses 1e-3 on ~0.15 % of
+# its cosines (tests/test_tolerance_derivation.py), so its fraction is 0.995.
 COS_FRACTION_OF = {"odd_h2560": 0.995}
+
+
+def check_topk_all_rows(host, K, dbg, what):
+    """Top-K ids exactly and lse / logp within TOL on every row of the workload."""
+    V = host.shape[-1]
+    idx, logp, lse = oracle.topk_lse(host.reshape(-1, V), K)
+    g_idx = dbg["topk_idx"].cpu().numpy().reshape(-1, K)
+    bad = np.nonzero((g_idx != idx).any(axis=1))[0]
+    assert bad.size == 0, f"{what}: top-K ids differ on {bad.size} rows, first {bad[:5].tolist()}"
+    assert_within(dbg["lse"].cpu().numpy().ravel(), lse, what=f"{what} lse")
+    assert_within(dbg["topk_logp"].cpu().numpy().reshape(-1, K), logp, what=f"{what} logp")
+    return idx.shape[0]
 
 
 def run_case(L, name, tier, sample, alpha=None, use_logp=True, host=None):
@@ -58,17 +80,15 @@ def run_case(L, name, tier, sample, alpha=None, use_logp=True, host=None):
     weights = device_weights(w)
     tokens, dbg = L.rerank(dev, w.topk, weights, alpha, use_logp, debug=True)
     torch.cuda.synchronize()
+    rows = check_topk_all_rows(host, w.topk, dbg, f"{name} tier {tier}")
     ow = oracle_weights(w)
-    blocks = range(w.num_blocks) if sample is None else sample
+    blocks = list(range(w.num_blocks)) if sample is None else sample
     excused = []
-    g_cos, o_cos, g_z, o_z = [], [], [], []
+    g_cos, o_cos, g_z, o_z, g_vec, o_vec = [], [], [], [], [], []
     for b in blocks:
         r = oracle.rerank_block(host[b], w.topk, ow, alpha, use_logp)
-        assert np.array_equal(dbg["topk_idx"][b].cpu().numpy(), r.idx), f"block {b}: top-K ids"
-        assert_within(dbg["lse"][b].cpu().numpy(), r.lse, what=f"block {b} lse")
-        assert_within(dbg["topk_logp"][b].cpu().numpy(), r.logp, what=f"block {b} logp")
-        go, gi = bf16_to_f64(dbg["outv"][b]), bf16_to_f64(dbg["inv"][b])
-        assert np.abs(go - r.outv).max() < 2e-2 and np.abs(gi - r.inv).max() < 2e-2, f"block {b} in/out"
+        g_vec += [bf16_to_f64(dbg["outv"][b]).ravel(), bf16_to_f64(dbg["inv"][b]).ravel()]
+        o_vec += [r.outv.ravel(), r.inv.ravel()]
         gtok = tokens[b].cpu().numpy()
         gidx = dbg["topk_idx"][b].cpu().numpy()
         choice = np.array([int(np.nonzero(gidx[s] == gtok[s])[0][0]) for s in range(w.slots)])
@@ -81,14 +101,17 @@ def run_case(L, name, tier, sample, alpha=None, use_logp=True, host=None):
         excused += [(b,) + e for e in ex]
         if not ex:
             assert np.array_equal(gtok, r.tokens.astype(np.int32)), f"block {b}: tokens"
+    n_slots = len(blocks) * (w.slots - 1)
+    vec = assert_vectors(np.concatenate(g_vec), np.concatenate(o_vec), f"{name} in/out vectors")
+    sc = sz = None
     if g_cos:
         frac = COS_FRACTION_OF.get(name, COS_FRACTION)
         sc = assert_scores(np.concatenate([c.ravel() for c in g_cos]),
                            np.concatenate([c.ravel() for c in o_cos]), f"{name} cos", 1.0, frac)
         sz = assert_scores(np.concatenate(g_z), np.concatenate(o_z), f"{name} step scores", alpha, frac, step=True)
-        print(f"[scores] {name} tier {tier}: cos {sc} step {sz}", flush=True)
-    if excused:
-        print(f"[excused] {name} tier {tier}: {excused}", flush=True)
+    record(f"rerank/{name}/tier{tier}/alpha{alpha}/logp{int(use_logp)}", topk_rows=rows, blocks=len(blocks),
+           slots=n_slots, excused=excused, cos=sc, step=sz, vectors=vec)
+    assert_excuse_cap(excused, n_slots, f"{name} tier {tier}")
     return tokens, dbg, excused
 
 
@@ -162,3 +185,39 @@ def test_error_paths_raise_without_launch(L):
     with pytest.raises(L.LilicorrError) as e:
         L.rerank(wrong_vocab, 4, weights)
     assert e.value.code == L.EWEIGHTS
+
+
+def test_binding_rejects_mismatched_tensors(L):
+    # the binding checks every tensor it hands to the library by pointer:
+    # device, contiguity, dtype and the exact shape of the C ABI's contract
+    import torch
+    w = synth.WORKLOADS["tiny"]
+    dev = to_device(synth.make_logits(w))
+    weights = device_weights(w)
+    N, B, K = w.num_blocks, w.slots, w.topk
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda")
+    bad = [
+        dict(rule="sample", temperature=f32(N), uniforms=f32(N)),                    # uniforms [N], not [N, B]
+        dict(rule="sample", temperature=f32(N, 1), uniforms=f32(N, B)),              # temperature shape
+        dict(rule="sample", temperature=f32(N), uniforms=f32(N, B).double()),        # dtype
+        dict(rule="sample", temperature=f32(N), uniforms=f32(N, 2 * B)[:, ::2]),     # not contiguous
+        dict(rule="sample", temperature=f32(N), uniforms=f32(N, B), proposal=f32(N, B)),
+        dict(out=torch.zeros((N, B), dtype=torch.int64, device="cuda")),
+    ]
+    for kw in bad:
+        with pytest.raises(L.LilicorrArgumentError) as e:
+            L.rerank(dev, K, weights, **kw)
+        assert e.value.code == L.EINVAL
+    idx = torch.zeros((N, B, K), dtype=torch.int32, device="cuda")
+    with pytest.raises(L.LilicorrArgumentError):
+        L.greedy_walk(idx, f32(N, B, K), f32(N, B, K, K))                          # cos [N, B, K, K]
+    with pytest.raises(L.LilicorrArgumentError):
+        L.best_path(idx, f32(N, B, K).half(), f32(N, B - 1, K, K))
+    with pytest.raises(L.LilicorrArgumentError):
+        L.pair_scores(torch.zeros((N, B, K, 32), dtype=torch.bfloat16, device="cuda"),
+                      torch.zeros((N, B, K, 32), dtype=torch.float32, device="cuda"))
+    pw = synth.WORKLOADS["paper_tiny"]
+    with pytest.raises(L.LilicorrArgumentError):    # a float32 hidden state would be read as bf16
+        L.rerank(to_device(synth.make_logits(pw)), pw.topk, device_weights(pw), pw.alpha, pw.use_logp,
+                 hidden=f32(1, pw.slots, pw.drafter_hidden),
+                 target=torch.zeros((1, pw.target_hidden), dtype=torch.bfloat16, device="cuda"))

@@ -15,7 +15,8 @@ from dataclasses import dataclass
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblilicorr.so")
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EWEIGHTS, EHIP = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EWEIGHTS, EHIP, ETOOLARGE = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 48 << 20
 F32, BF16 = 0, 1
 EPI_F32, EPI_BF16, EPI_SILU_BF16, EPI_RESID_F32 = 0, 1, 2, 3
 # lilicorr_stage values (per-layer stages of layer l: base + 5*l)
@@ -71,6 +72,7 @@ _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctype
 _SIGNATURES = {
     "lilicorr_rerank": (_c_int, [_vp, _c_int, _c_int, _c_int, ctypes.POINTER(Params), _vp]),
     "lilicorr_validate": (_c_int, [_vp, _c_int, _c_int, _c_int, ctypes.POINTER(Params), _vp]),
+    "lilicorr_rerank_noalloc": (_c_int, [_vp, _c_int, _c_int, _c_int, ctypes.POINTER(Params), _vp]),
     "lilicorr_rerank_audit": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Dims), _c_int,
                                        ctypes.c_char_p, _c_size]),
     "lilicorr_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Dims)]),
@@ -244,7 +246,7 @@ class Workspace:
         self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
 
 
-def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1.0, use_logp=True,
+def make_params(N, logits_dtype, weights: Weights, workspace: Workspace | None, alpha=1.0, use_logp=True,
                 stream=None, dbg=None, rule: str = "greedy", temperature=None, uniforms=None,
                 proposal=None, hidden=None, target=None) -> Params:
     p = Params()
@@ -260,8 +262,8 @@ def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1
     p.alpha = alpha
     p.use_logp = 1 if use_logp else 0
     p.weights = ctypes.pointer(weights.desc)
-    p.workspace = ctypes.c_void_p(workspace.buf.data_ptr())
-    p.workspace_bytes = workspace.nbytes
+    p.workspace = ctypes.c_void_p(workspace.buf.data_ptr() if workspace is not None else 0)
+    p.workspace_bytes = workspace.nbytes if workspace is not None else 0
     p.stream = stream if stream is not None else _stream()
     for k, v in (dbg or {}).items():
         setattr(p, "dbg_" + k, ctypes.c_void_p(v.data_ptr()))
@@ -270,8 +272,12 @@ def make_params(N, logits_dtype, weights: Weights, workspace: Workspace, alpha=1
 
 def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool = True,
            workspace: Workspace | None = None, debug: bool = False, out=None, rule: str = "greedy",
-           temperature=None, uniforms=None, proposal=None, hidden=None, target=None):
+           temperature=None, uniforms=None, proposal=None, hidden=None, target=None,
+           noalloc: bool = False):
     """Rerank [N, B, V] device logits; returns int32 tokens [N, B] (and debug tensors).
+
+    noalloc=True calls lilicorr_rerank_noalloc, whose workspace is the library's
+    fixed device scratch (no workspace is allocated or passed).
 
     rule: "greedy", "exact" or "sample" (then temperature [N] and uniforms [N, B]
     float32 device tensors are required; proposal [N, B, K] float32 is optional).
@@ -286,7 +292,9 @@ def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool 
     d = weights.dims
     if weights.blob.device != dev:
         raise LilicorrArgumentError("weights", f"are on {weights.blob.device}, the logits on {dev}")
-    if workspace is None:
+    if noalloc:
+        workspace = None
+    elif workspace is None:
         workspace = Workspace(N, B, V, K, weights.dims, device=dev)
     elif workspace.buf.device != dev:
         raise LilicorrArgumentError("workspace", f"is on {workspace.buf.device}, the logits on {dev}")
@@ -319,7 +327,10 @@ def rerank(logits, K: int, weights: Weights, alpha: float = 1.0, use_logp: bool 
     p = make_params(N, _logits_dtype(logits), weights, workspace, alpha, use_logp, dbg=dbg, rule=rule,
                     temperature=temperature, uniforms=uniforms, proposal=proposal, hidden=hidden,
                     target=target)
-    _check(lib().lilicorr_rerank(_ptr(logits), B, V, K, ctypes.byref(p), _ptr(out)), "rerank")
+    if noalloc:
+        _check(lib().lilicorr_rerank_noalloc(_ptr(logits), B, V, K, ctypes.byref(p), _ptr(out)), "rerank_noalloc")
+    else:
+        _check(lib().lilicorr_rerank(_ptr(logits), B, V, K, ctypes.byref(p), _ptr(out)), "rerank")
     return (out, dbg) if debug else out
 
 

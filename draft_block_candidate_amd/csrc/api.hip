@@ -61,6 +61,39 @@ int check_device() {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LILICORR_OK : LILICORR_EHIP; }
 
+int validate_args(const void* logits, int B, int V, int K, const lilicorr_params* p,
+                  const int32_t* out_tokens, bool with_workspace);
+
+// Fixed device scratch of lilicorr_rerank_noalloc: the rerank workspace of
+// callers that cannot allocate. Each device that runs the library holds its
+// own copy for the life of the process. In host code `scratch` is only the
+// symbol's host-side stand-in; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[LILICORR_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_dev[64];
+std::atomic<int> g_scratch_lock{0};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LILICORR_EHIP;
+  if (dev < 0 || dev >= 64) return LILICORR_EUNSUPPORTED;
+  void* ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    int expected = 0;
+    while (!g_scratch_lock.compare_exchange_weak(expected, 1, std::memory_order_acquire)) expected = 0;
+    ptr = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    hipError_t e = hipSuccess;
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e == hipSuccess && ptr) g_scratch_dev[dev].store(ptr, std::memory_order_release);
+    }
+    g_scratch_lock.store(0, std::memory_order_release);
+    if (e != hipSuccess || !ptr) return LILICORR_EHIP;
+  }
+  *out = ptr;
+  return LILICORR_OK;
+}
+
 CommitRule commit_rule(const lilicorr_params& p) {
   CommitRule r;
   r.kind = p.rule;
@@ -351,6 +384,8 @@ const char* lilicorr_strerror(int code) {
     case LILICORR_EWORKSPACE: return "workspace missing or too small";
     case LILICORR_EWEIGHTS: return "weights do not match the requested dims/vocabulary";
     case LILICORR_EHIP: return "HIP runtime or launch error";
+    case LILICORR_ETOOLARGE:
+      return "problem needs more than the fixed scratch of lilicorr_rerank_noalloc";
     default: return "unknown status";
   }
 }
@@ -405,6 +440,30 @@ int lilicorr_weights_init(lilicorr_weights* w, void* stream) {
 
 int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_params* p,
                       const int32_t* out_tokens) {
+  return validate_args(logits, B, V, K, p, out_tokens, true);
+}
+
+int lilicorr_rerank_noalloc(const void* logits, int B, int V, int K, const lilicorr_params* p,
+                            int32_t* out_tokens) {
+  const int v = validate_args(logits, B, V, K, p, out_tokens, false);
+  if (v != LILICORR_OK) return v;
+  if (rerank_ws_layout(p->num_blocks, B, V, K, p->weights->dims).total >
+      (size_t)LILICORR_NOALLOC_SCRATCH_BYTES)
+    return LILICORR_ETOOLARGE;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  void* ws = nullptr;
+  const int sc = scratch_address(&ws);
+  if (sc != LILICORR_OK) return sc;
+  return enqueue_rerank(logits, B, V, K, *p, (char*)ws, out_tokens, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+int validate_args(const void* logits, int B, int V, int K, const lilicorr_params* p,
+                  const int32_t* out_tokens, bool with_workspace) {
   if (!p || !logits || !out_tokens) return LILICORR_EINVAL;
   if (p->abi_version != LILICORR_ABI_VERSION) return LILICORR_EINVAL;
   if (!sizes_ok(p->num_blocks, B, V, K)) return LILICORR_EINVAL;
@@ -419,7 +478,8 @@ int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_pa
       w->bytes < weights_total_bytes(w->dims, w->vocab))
     return LILICORR_EWEIGHTS;
   const size_t need = rerank_ws_layout(p->num_blocks, B, V, K, w->dims).total;
-  if (!p->workspace || p->workspace_bytes < need || ((uintptr_t)p->workspace & 255))
+  if (with_workspace &&
+      (!p->workspace || p->workspace_bytes < need || ((uintptr_t)p->workspace & 255)))
     return LILICORR_EWORKSPACE;
   if (p->rule != LILICORR_RULE_GREEDY && p->rule != LILICORR_RULE_EXACT &&
       p->rule != LILICORR_RULE_SAMPLE)
@@ -435,6 +495,10 @@ int lilicorr_validate(const void* logits, int B, int V, int K, const lilicorr_pa
     return LILICORR_EINVAL;
   return LILICORR_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_params* p,
                     int32_t* out_tokens) {

@@ -55,7 +55,8 @@ typedef enum {
   LILICORR_EUNSUPPORTED = -2, /* dtype or geometry outside what the kernels build for, or device is not gfx950 */
   LILICORR_EWORKSPACE = -3,   /* workspace missing or smaller than lilicorr_workspace_bytes() */
   LILICORR_EWEIGHTS = -4,     /* weight descriptor does not match dims/vocabulary, or blob too small */
-  LILICORR_EHIP = -5          /* a HIP runtime call or kernel launch failed */
+  LILICORR_EHIP = -5,         /* a HIP runtime call or kernel launch failed */
+  LILICORR_ETOOLARGE = -6     /* lilicorr_rerank_noalloc: workspace need above its fixed scratch */
 } lilicorr_status;
 
 typedef enum { LILICORR_F32 = 0, LILICORR_BF16 = 1 } lilicorr_dtype;
@@ -187,6 +188,26 @@ typedef struct {
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EWEIGHTS (host checks), EHIP. */
 LILICORR_API int lilicorr_rerank(const void* logits, int B, int V, int K, const lilicorr_params* p,
                     int32_t* out_tokens);
+
+/* Allocation-free variant of lilicorr_rerank, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, outputs and launch sequence
+ * as lilicorr_rerank, except that p->workspace / p->workspace_bytes are ignored:
+ * the workspace is a fixed array of LILICORR_NOALLOC_SCRATCH_BYTES in the
+ * library's device code, one per device, held until the process ends. The call
+ * allocates nothing (its first call on a device only looks the array's address
+ * up, so make that first call outside graph capture). Nothing in it needs to
+ * start at zero (lilicorr_rerank_audit: every region is written before it is
+ * read). Every call on a device shares that device's array: calls that overlap
+ * on one device (concurrent streams, or other host threads) race and must be
+ * serialised by the caller; a call's results are its outputs, not the array.
+ * Errors: those of lilicorr_rerank except EWORKSPACE, plus ETOOLARGE when
+ * lilicorr_workspace_bytes(N, B, V, K, dims) exceeds the array (host check, nothing
+ * launched): 1-4 blocks of the 1024-wide encoder at K = 8, one block at K = 16,
+ * one block of the paper's head at its Table 4 size. */
+#define LILICORR_NOALLOC_SCRATCH_BYTES (48u << 20)
+LILICORR_API int lilicorr_rerank_noalloc(const void* logits, int B, int V, int K,
+                                         const lilicorr_params* p, int32_t* out_tokens);
 
 /* Host-only audit of lilicorr_rerank's launch sequence for N blocks of B slots,
  * vocabulary V, K candidates and the given geometry (the commit rule and the

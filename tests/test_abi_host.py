@@ -240,3 +240,10 @@ def test_binding_rejects_host_tensors_before_the_library():
     with pytest.raises(L.LilicorrArgumentError):
         L.topk_lse(torch.zeros((4, 100)), 4)
     del w
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define LILICORR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES
+    assert L.strerror(L.ETOOLARGE).startswith("problem needs more")

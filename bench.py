@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--summarize-kernels", metavar="KT_DIR",
                     help="no GPU: turn a rocprofv3 --kernel-trace --stats run of this script into a "
                          "markdown table of kernel durations")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="no GPU: turn a rocprofv3 --kernel-trace --pmc MfmaUtil MfmaFlopsBF16 run of this "
+                         "script into MFMA utilisation and counted bf16 MFMA flops per stage launch")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE, both with --copy-probe-mib) into HBM bytes per stage launch")
@@ -81,6 +84,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path here "
@@ -278,7 +284,8 @@ def main():
         "roofline": roof,
         "topk_hbm": {"achieved_GB_s": topk_gbs, "frac": topk_gbs / PEAK_HBM_GBS},
         "encoder_mfma": {"achieved_TFLOP_s": enc_flops / (enc_ms * 1e-3) / 1e12,
-                         "frac": enc_flops / (enc_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+                         "frac": enc_flops / (enc_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "counters": counter_mfma(w.name)},
         "stages": stages,
         "wall_s_timed": wall,
     }
@@ -552,6 +559,105 @@ def summarize_counters(args):
         f_b = sum(f) / max(1, len(f)) * 1024 * scale["FETCH_SIZE"]
         w_b = sum(wr) / max(1, len(wr)) * 1024 * scale["WRITE_SIZE"]
         print(f"| {st} | {int(round(f_b + w_b))} | {int(round(f_b))} | {int(round(w_b))} | {len(f)} |")
+
+
+def read_kernel_durations(d):
+    """dispatch id -> duration (ns) from a rocprofv3 kernel-trace CSV, if present."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return {}
+    out = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            try:
+                out[int(r["Dispatch_Id"])] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            except (KeyError, ValueError):
+                continue
+    return out
+
+
+def summarize_mfma(args):
+    """Per-stage MFMA counters of one workload: bf16 MFMA flops counted by the
+    hardware (MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512) against the
+    stage's algorithmic flops, and MFMA utilisation (MfmaUtil = MFMA-busy cycles
+    over GRBM_GUI_ACTIVE cycles of all SIMDs), weighted by kernel duration over
+    the stage's kernels."""
+    d = args.summarize_mfma
+    util = {k: (n, v) for k, n, v in read_counter_csv(d, "MfmaUtil")}
+    flops = {k: (n, v) for k, n, v in read_counter_csv(d, "MfmaFlopsBF16")}
+    dur = read_kernel_durations(d)
+    ids = sorted(util)
+    names = [util[k][0] for k in ids]
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    stage_ids = {v: k for k, v in stage_table(w).items()}
+    per = {}
+    i = 0
+    while i < len(ids):
+        if "topk_partial" not in names[i]:
+            i += 1
+            continue
+        j = i
+        while j < len(ids) and not ("scores_walk" in names[j] or "greedy_walk" in names[j]):
+            j += 1
+        if j >= len(ids):
+            break
+        seq = ids[i:j + 1]
+        acc = {}
+        for k, st in zip(seq, split_step_stages([util[k][0] for k in seq])):
+            if st is None:
+                continue
+            a = acc.setdefault(st, [0.0, 0.0, 0.0])
+            t = dur.get(k, 1.0)
+            a[0] += flops.get(k, (None, 0.0))[1]
+            a[1] += util[k][1] * t
+            a[2] += t
+        for st, a in acc.items():
+            per.setdefault(st, []).append(a)
+        i = j + 1
+    print(f"# MFMA counters per stage launch: {w.name}\n")
+    print("rocprofv3 --kernel-trace --pmc MfmaUtil MfmaFlopsBF16 (derived counters of")
+    print("SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16), one run.")
+    print("`util` = MFMA-busy cycles / (GRBM_GUI_ACTIVE x SIMDs), weighted by kernel duration over the")
+    print("stage's kernels; `counted` = bf16 MFMA flops the hardware issued per launch;")
+    print("`algorithmic` = the stage's flops from the method (bench.py stage_work).\n")
+    print(f"csrc_sha256: {csrc_sha256()}\n")
+    print("| stage | MFMA util % | counted bf16 MFMA flops | algorithmic flops | counted / algorithmic | us (trace) | steps |")
+    print("|---|---|---|---|---|---|---|")
+    tot_busy = tot_t = 0.0
+    for st, lst in per.items():
+        fl = sum(a[0] for a in lst) / len(lst)
+        t = sum(a[2] for a in lst) / len(lst)
+        u = sum(a[1] for a in lst) / max(sum(a[2] for a in lst), 1e-30)
+        alg = stage_work(w, stage_ids[st])["flops"] if st in stage_ids else 0
+        ratio = f"{fl / alg:.3f}" if alg else "-"
+        if st not in ("topk_lse", "scores_walk"):
+            tot_busy += u * t
+            tot_t += t
+        print(f"| {st} | {u:.1f} | {fl:.4g} | {alg:.4g} | {ratio} | {t / 1e3:.1f} | {len(lst)} |")
+    if tot_t:
+        print(f"\nencoder MFMA util (duration-weighted over node build .. heads): {tot_busy / tot_t:.1f} %")
+
+
+def counter_mfma(workload):
+    """Encoder MFMA utilisation from the committed MfmaUtil summary of this
+    workload, while the kernel sources hash the same; else None."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"^csrc_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m_h or m_h.group(1) != csrc_sha256():
+        return None
+    m = re.search(r"encoder MFMA util \(duration-weighted[^)]*\): ([0-9.]+) %", text)
+    stages = {mm.group(1): float(mm.group(2)) for mm in
+              re.finditer(r"^\|\s*([\w.]+)\s*\|\s*([0-9.]+)\s*\|", text, re.M)}
+    return {"util_frac": float(m.group(1)) / 100 if m else None,
+            "stage_util_frac": {k: v / 100 for k, v in stages.items()},
+            "source": f"profiles/mfma_{workload}.md (rocprofv3 MfmaUtil)"}
 
 
 def summarize_kernels(d):

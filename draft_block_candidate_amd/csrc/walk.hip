@@ -277,7 +277,70 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
     const int64_t r0 = n * B;
     int choice = 0;
     float my_score = s_logp[0], my_gap = 0.f;
-    if (RULE == RULE_EXACT) {
+    if (RULE == RULE_EXACT && K <= 8) {
+      // K <= 8: every (predecessor i, candidate j) pair of a slot in its own
+      // lane of an 8 x 8 grid. The lane layout alternates between slots so
+      // that each slot's totals are already where the next slot reads them:
+      //   layout A (odd s):  j = lane >> 3, i = lane & 7; the maximum over i
+      //                      within each 8-lane group leaves G_s(lane >> 3);
+      //   layout B (even s): i = lane >> 3, j = lane & 7; the maximum over i
+      //                      across the eight groups leaves G_s(lane & 7),
+      // and G_1(j) = z_1(0, j) starts as if made by layout A. Candidates are
+      // fl32(G_{s-1}(i) + z_s(i, j)) (left-to-right sums); the lowest i among
+      // equal maxima is the predecessor s_tc[(s-2) K + j], as in the scan.
+      const int hi = lane >> 3, lo = lane & 7;
+      float G = (B > 1 && hi < K) ? zval(1, 0, hi) : -INFINITY;
+      // this slot's and the next slot's z operands, loaded one slot ahead
+      auto zload = [&](int s, float& c, float& lp) {
+        const int i = (s & 1) ? lo : hi, j = (s & 1) ? hi : lo;
+        c = s_cos[(s - 1) * KK + min(i, K - 1) * K + min(j, K - 1)];
+        lp = s_logp[s * K + min(j, K - 1)];
+      };
+      float cn = 0.f, ln = 0.f;
+      if (B > 2) zload(2, cn, ln);
+      for (int s = 2; s < B; ++s) {
+        const float cc = cn, lc = ln;
+        if (s + 1 < B) zload(s + 1, cn, ln);
+        const bool odd = s & 1;
+        const int i = odd ? lo : hi, j = odd ? hi : lo;
+        const float term = __fmul_rn(alpha, cc);
+        const float z = use_logp ? __fadd_rn(lc, term) : term;
+        const float cand = (i < K && j < K) ? __fadd_rn(G, z) : -INFINITY;
+        int key = fkey(cand);
+        if (odd) {
+          key = max(key, xor_lane(key, 1, lane));
+          key = max(key, xor_lane(key, 2, lane));
+          key = max(key, xor_lane(key, 4, lane));
+        } else {
+          key = max(key, xor_lane(key, 8, lane));
+          key = max(key, xor_lane(key, 16, lane));
+          key = max(key, xor_lane(key, 32, lane));
+        }
+        G = fkey_inv(key);
+        const uint64_t hit = __ballot(cand == G && i < K);
+        int pred;
+        if (odd) {
+          pred = __ffsll((long long)((hit >> (lane & 56)) & 0xffull)) - 1;
+        } else {
+          pred = (__ffsll((long long)((hit >> lo) & 0x0101010101010101ull)) - 1) >> 3;
+        }
+        const bool writer = odd ? (lo == 0 && hi < K) : (hi == 0 && lo < K);
+        if (writer) s_tc[(s - 2) * K + j] = pred < 0 ? 0 : pred;
+      }
+      if (B > 1) {
+        // best final candidate (lowest index on a tie), then the trace-back
+        float gv = G;
+        int c = ((B - 1) & 1) || B == 2 ? hi : lo;    // the candidate this lane's total belongs to
+        gv = c < K ? gv : -INFINITY;
+        wave_argmax(gv, c);
+        c = c < K ? c : 0;
+        choice = lane == B - 1 ? c : choice;
+        for (int s = B - 1; s >= 2; --s) {
+          c = s_tc[(s - 2) * K + c];
+          choice = lane == s - 1 ? c : choice;
+        }
+      }
+    } else if (RULE == RULE_EXACT) {
       // G in lane j: the best float32 total of a path ending at candidate j of
       // slot s (left-to-right sums); s_tc[(s-2) K + j] its predecessor. The
       // predecessor scan runs i upward and keeps the first maximum.

@@ -151,6 +151,24 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Float32 product, sum and difference, each rounded once, that the compiler
+// may not fuse into an FMA with a neighbouring operation (HIP compiles with
+// floating-point contraction on, and __fmul_rn / __fadd_rn are plain operators
+// there). The commit rules' score fl32(logp + fl32(alpha * cos)) is two
+// roundings; an FMA would round once.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ float add_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+__device__ __forceinline__ float sub_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a - b;
+}
+
 // The value held by lane (lane ^ j), j in {1, 2, 4, 8, 16, 32}, without the
 // LDS crossbar: quad permutes for 1 and 2, a row shift each way for 4 and 8
 // (each lane keeps the one that stays in its 16-lane row), and the gfx950

@@ -13,6 +13,7 @@
 // with the same per-step score z_s(i, j) = fl32(logp[s][j] + fl32(alpha *
 // cos_s[i][j])).
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -121,8 +122,8 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
     float z = -INFINITY;
     if (lane < K) {
       const float cs = cos[((n * (B - 1) + s - 1) * K + cprev) * K + lane];
-      const float term = __fmul_rn(alpha, cs);
-      z = use_logp ? __fadd_rn(topk_logp[(r0 + s) * K + lane], term) : term;
+      const float term = mul_rn(alpha, cs);
+      z = use_logp ? add_rn(topk_logp[(r0 + s) * K + lane], term) : term;
     }
     const float bz = lanes_max(z, width);
     int bl = __ffsll((long long)__ballot(z == bz)) - 1;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(
     const float second = gap ? wave_max(lane == bl ? -INFINITY : z) : 0.f;
     choice = lane == s ? bl : choice;
     my_score = lane == s ? bz : my_score;
-    my_gap = lane == s ? (K > 1 ? __fsub_rn(bz, second) : 0.f) : my_gap;
+    my_gap = lane == s ? (K > 1 ? sub_rn(bz, second) : 0.f) : my_gap;
     cprev = bl;
   }
   if (lane < B) {
@@ -199,10 +200,10 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
     }
   }
   __syncthreads();
-  // z_s(i, j): the walk's own arithmetic (fl32, no contraction)
+  // z_s(i, j): the walk's own arithmetic (fl32, each step rounded, never fused)
   auto zval = [&](int s, int i, int j) {
-    const float term = __fmul_rn(alpha, s_cos[(s - 1) * KK + i * K + j]);
-    return use_logp ? __fadd_rn(s_logp[s * K + j], term) : term;
+    const float term = mul_rn(alpha, s_cos[(s - 1) * KK + i * K + j]);
+    return use_logp ? add_rn(s_logp[s * K + j], term) : term;
   };
   const float T = RULE == RULE_SAMPLE ? temperature[n] : 0.f;
   const bool draw = RULE == RULE_SAMPLE && T > 0.f;   // uniform over the workgroup
@@ -236,8 +237,8 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float term = __fmul_rn(alpha, cv[u]);
-          const float z = use_logp ? __fadd_rn(lv[u], term) : term;
+          const float term = mul_rn(alpha, cv[u]);
+          const float z = use_logp ? add_rn(lv[u], term) : term;
           const int j = jv[u];
           const bool better = (jj0 + u < K) & ((z > best) | ((z == best) & (j < bj)));
           second = (jj0 + u < K) ? (better ? best : fmaxf(second, z)) : second;
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
       }
       s_tc[e] = bj < K ? bj : 0;   // bj == K only if every score is NaN; keeps the walk in range
       s_tz[e] = best;
-      s_tg[e] = K > 1 ? __fsub_rn(best, second) : 0.f;
+      s_tg[e] = K > 1 ? sub_rn(best, second) : 0.f;
     }
   } else if (draw) {
     // Sample table: the row maximum m, the float32 sum S of e_j =
@@ -259,12 +260,12 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
       float m = -INFINITY;
       for (int j = 0; j < K; ++j) m = fmaxf(m, zval(s, cp, j));
       float S = 0.f;
-      for (int j = 0; j < K; ++j) S = __fadd_rn(S, __expf(__fmul_rn(__fsub_rn(zval(s, cp, j), m), inv_t)));
-      const float target = __fmul_rn(uniforms[n * B + s], S);
+      for (int j = 0; j < K; ++j) S = add_rn(S, __expf(mul_rn(sub_rn(zval(s, cp, j), m), inv_t)));
+      const float target = mul_rn(uniforms[n * B + s], S);
       float C = 0.f;
       int cnt = 0;
       for (int j = 0; j < K; ++j) {
-        C = __fadd_rn(C, __expf(__fmul_rn(__fsub_rn(zval(s, cp, j), m), inv_t)));
+        C = add_rn(C, __expf(mul_rn(sub_rn(zval(s, cp, j), m), inv_t)));
         cnt += C <= target ? 1 : 0;
       }
       s_tc[e] = min(cnt, K - 1);
@@ -287,57 +288,85 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
       //                      across the eight groups leaves G_s(lane & 7),
       // and G_1(j) = z_1(0, j) starts as if made by layout A. Candidates are
       // fl32(G_{s-1}(i) + z_s(i, j)) (left-to-right sums); the lowest i among
-      // equal maxima is the predecessor s_tc[(s-2) K + j], as in the scan.
+      // equal maxima is the predecessor of j, as in the scan below.
       const int hi = lane >> 3, lo = lane & 7;
       float G = (B > 1 && hi < K) ? zval(1, 0, hi) : -INFINITY;
-      // this slot's and the next slot's z operands, loaded one slot ahead
-      auto zload = [&](int s, float& c, float& lp) {
-        const int i = (s & 1) ? lo : hi, j = (s & 1) ? hi : lo;
+      // [(B-2) 8] predecessor bytes, 8-byte aligned, in the table area the
+      // exact rule does not otherwise use (s_tc, s_tz, s_tg: 12 (B-1) K bytes)
+      uint8_t* s_pred8 = (uint8_t*)(((uintptr_t)s_tc + 7) & ~(uintptr_t)7);
+      // z operands of slot s in layout ODD (loaded one slot ahead)
+      auto zload = [&](auto odd_tag, int s, float& c, float& lp) {
+        constexpr bool ODD = decltype(odd_tag)::value;
+        const int i = ODD ? lo : hi, j = ODD ? hi : lo;
         c = s_cos[(s - 1) * KK + min(i, K - 1) * K + min(j, K - 1)];
         lp = s_logp[s * K + min(j, K - 1)];
       };
-      float cn = 0.f, ln = 0.f;
-      if (B > 2) zload(2, cn, ln);
-      for (int s = 2; s < B; ++s) {
-        const float cc = cn, lc = ln;
-        if (s + 1 < B) zload(s + 1, cn, ln);
-        const bool odd = s & 1;
-        const int i = odd ? lo : hi, j = odd ? hi : lo;
-        const float term = __fmul_rn(alpha, cc);
-        const float z = use_logp ? __fadd_rn(lc, term) : term;
-        const float cand = (i < K && j < K) ? __fadd_rn(G, z) : -INFINITY;
+      // one slot of the program in layout ODD, from its loaded operands
+      auto step = [&](auto odd_tag, int s, float cc, float lc) {
+        constexpr bool ODD = decltype(odd_tag)::value;
+        const int i = ODD ? lo : hi, j = ODD ? hi : lo;
+        const float term = mul_rn(alpha, cc);
+        const float z = use_logp ? add_rn(lc, term) : term;
+        const float cand = (i < K && j < K) ? add_rn(G, z) : -INFINITY;
         int key = fkey(cand);
-        if (odd) {
+        if (ODD) {
+          // within each 8-lane group: the two quad permutes, then lane k
+          // against lane 7 - k (row_half_mirror) joins the two quads
           key = max(key, xor_lane(key, 1, lane));
           key = max(key, xor_lane(key, 2, lane));
-          key = max(key, xor_lane(key, 4, lane));
+          key = max(key, __builtin_amdgcn_update_dpp(INT_MIN, key, 0x141, 0xf, 0xf, false));
         } else {
-          key = max(key, xor_lane(key, 8, lane));
+          // across the eight groups: lane k against k + 8 within its row
+          // (row_ror:8), then the two row swaps
+          key = max(key, __builtin_amdgcn_update_dpp(INT_MIN, key, 0x128, 0xf, 0xf, false));
           key = max(key, xor_lane(key, 16, lane));
           key = max(key, xor_lane(key, 32, lane));
         }
         G = fkey_inv(key);
+        // lowest i reaching the maximum: from the ballot, in every lane of
+        // the group; one lane per candidate stores it as slot s's byte j
         const uint64_t hit = __ballot(cand == G && i < K);
-        int pred;
-        if (odd) {
-          pred = __ffsll((long long)((hit >> (lane & 56)) & 0xffull)) - 1;
-        } else {
-          pred = (__ffsll((long long)((hit >> lo) & 0x0101010101010101ull)) - 1) >> 3;
+        const int pred = ODD ? __ffsll((long long)((hit >> (lane & 56)) & 0xffull)) - 1
+                             : (__ffsll((long long)((hit >> lo) & 0x0101010101010101ull)) - 1) >> 3;
+        const bool writer = ODD ? (lo == 0 && hi < K) : (hi == 0 && lo < K);
+        if (writer) s_pred8[(s - 2) * 8 + j] = (uint8_t)(pred < 0 ? 0 : pred);
+      };
+      using Even = std::integral_constant<bool, false>;
+      using Odd = std::integral_constant<bool, true>;
+      // slots in pairs (even s in layout B, odd s + 1 in layout A)
+      float ce = 0.f, le = 0.f, co = 0.f, lo_ = 0.f;
+      if (B > 2) zload(Even{}, 2, ce, le);
+      for (int s = 2; s < B; s += 2) {
+        if (s + 1 < B) zload(Odd{}, s + 1, co, lo_);
+        step(Even{}, s, ce, le);
+        if (s + 1 < B) {
+          if (s + 2 < B) zload(Even{}, s + 2, ce, le);
+          step(Odd{}, s + 1, co, lo_);
         }
-        const bool writer = odd ? (lo == 0 && hi < K) : (hi == 0 && lo < K);
-        if (writer) s_tc[(s - 2) * K + j] = pred < 0 ? 0 : pred;
       }
       if (B > 1) {
-        // best final candidate (lowest index on a tie), then the trace-back
+        // best final candidate (lowest index on a tie), then the trace-back:
+        // each slot's eight predecessor bytes are one 8-byte LDS word, read
+        // eight slots ahead of the chain that picks a byte per slot
         float gv = G;
         int c = ((B - 1) & 1) || B == 2 ? hi : lo;    // the candidate this lane's total belongs to
         gv = c < K ? gv : -INFINITY;
         wave_argmax(gv, c);
         c = c < K ? c : 0;
         choice = lane == B - 1 ? c : choice;
-        for (int s = B - 1; s >= 2; --s) {
-          c = s_tc[(s - 2) * K + c];
-          choice = lane == s - 1 ? c : choice;
+        const uint64_t* rows8 = (const uint64_t*)s_pred8;
+        for (int s0 = B - 1; s0 >= 2; s0 -= 8) {
+          uint64_t row[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) row[u] = rows8[max(s0 - u - 2, 0)];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int s = s0 - u;
+            if (s >= 2) {
+              c = (int)((row[u] >> (8 * c)) & 0xffull);
+              choice = lane == s - 1 ? c : choice;
+            }
+          }
         }
       }
     } else if (RULE == RULE_EXACT) {
@@ -359,9 +388,9 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int i = i0 + u;   // < 64: i0 <= 56 since K <= 64
-            const float term = __fmul_rn(alpha, cv[u]);
-            const float z = use_logp ? __fadd_rn(lj, term) : term;
-            const float cand = __fadd_rn(readlane_f(G, i), z);
+            const float term = mul_rn(alpha, cv[u]);
+            const float z = use_logp ? add_rn(lj, term) : term;
+            const float cand = add_rn(readlane_f(G, i), z);
             const bool better = (i < K) & (cand > best);
             best = better ? cand : best;
             bi = better ? i : bi;
@@ -420,7 +449,7 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
         q = j == s_path[s] ? 1.f : 0.f;
       } else {
         const int cp = s_path[s - 1], e = (s - 1) * K + cp;
-        q = __expf(__fmul_rn(__fsub_rn(zval(s, cp, j), s_tz[e]), inv_t)) / s_tg[e];
+        q = __expf(mul_rn(sub_rn(zval(s, cp, j), s_tz[e]), inv_t)) / s_tg[e];
       }
       proposal[base + t] = q;
     }

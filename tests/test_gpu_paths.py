@@ -61,7 +61,7 @@ SHAPES = [(1, 4), (2, 1), (2, 5), (16, 3), (16, 8), (16, 32), (8, 64), (64, 8), 
 
 
 @pytest.mark.parametrize("B,K", SHAPES)
-@pytest.mark.parametrize("alpha,use_logp", [(1.0, True), (0.5, True), (8.0, False)])
+@pytest.mark.parametrize("alpha,use_logp", [(1.0, True), (0.5, True), (0.7, True), (8.0, False)])
 @pytest.mark.parametrize("coarse", [False, True])
 def test_best_path_bit_exact(L, B, K, alpha, use_logp, coarse):
     rng = np.random.default_rng(B * 977 + K * 13 + int(alpha * 10) + coarse)
@@ -104,7 +104,7 @@ def _check_sample_block(gidx_choice, gprop, r_logp, r_cos, idx, T, u, alpha, use
 
 
 @pytest.mark.parametrize("B,K", SHAPES)
-@pytest.mark.parametrize("alpha,use_logp", [(1.0, True), (8.0, False)])
+@pytest.mark.parametrize("alpha,use_logp", [(1.0, True), (1.3, True), (8.0, False)])
 @pytest.mark.parametrize("coarse", [False, True])
 def test_sample_path(L, B, K, alpha, use_logp, coarse):
     rng = np.random.default_rng(B * 1009 + K * 17 + int(alpha) + coarse)

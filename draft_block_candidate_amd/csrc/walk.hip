@@ -291,9 +291,7 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
       // equal maxima is the predecessor of j, as in the scan below.
       const int hi = lane >> 3, lo = lane & 7;
       float G = (B > 1 && hi < K) ? zval(1, 0, hi) : -INFINITY;
-      // [(B-2) 8] predecessor bytes, 8-byte aligned, in the table area the
-      // exact rule does not otherwise use (s_tc, s_tz, s_tg: 12 (B-1) K bytes)
-      uint8_t* s_pred8 = (uint8_t*)(((uintptr_t)s_tc + 7) & ~(uintptr_t)7);
+      int hlo = 0, hhi = 0;   // lane s: the ballot of slot s (B <= 64)
       // z operands of slot s in layout ODD (loaded one slot ahead)
       auto zload = [&](auto odd_tag, int s, float& c, float& lp) {
         constexpr bool ODD = decltype(odd_tag)::value;
@@ -325,11 +323,12 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
         G = fkey_inv(key);
         // lowest i reaching the maximum: from the ballot, in every lane of
         // the group; one lane per candidate stores it as slot s's byte j
+        // the lanes that reach their candidate's maximum: slot s's ballot,
+        // kept in lane s of (hlo, hhi); the trace-back reads the lowest
+        // predecessor of its candidate from it
         const uint64_t hit = __ballot(cand == G && i < K);
-        const int pred = ODD ? __ffsll((long long)((hit >> (lane & 56)) & 0xffull)) - 1
-                             : (__ffsll((long long)((hit >> lo) & 0x0101010101010101ull)) - 1) >> 3;
-        const bool writer = ODD ? (lo == 0 && hi < K) : (hi == 0 && lo < K);
-        if (writer) s_pred8[(s - 2) * 8 + j] = (uint8_t)(pred < 0 ? 0 : pred);
+        hlo = lane == s ? (int)(uint32_t)hit : hlo;
+        hhi = lane == s ? (int)(uint32_t)(hit >> 32) : hhi;
       };
       using Even = std::integral_constant<bool, false>;
       using Odd = std::integral_constant<bool, true>;
@@ -345,28 +344,25 @@ __global__ __launch_bounds__(512) void scores_walk_kernel(
         }
       }
       if (B > 1) {
-        // best final candidate (lowest index on a tie), then the trace-back:
-        // each slot's eight predecessor bytes are one 8-byte LDS word, read
-        // eight slots ahead of the chain that picks a byte per slot
+        // best final candidate (lowest index on a tie), then the trace-back,
+        // scalar: slot s's ballot from lane s; in layout A (odd s) candidate
+        // c's lanes are 8c .. 8c + 7 with i = lane - 8c, in layout B (even s)
+        // lanes c, c + 8, .. with i = lane / 8; the lowest set lane is the
+        // lowest predecessor
         float gv = G;
         int c = ((B - 1) & 1) || B == 2 ? hi : lo;    // the candidate this lane's total belongs to
         gv = c < K ? gv : -INFINITY;
         wave_argmax(gv, c);
         c = c < K ? c : 0;
         choice = lane == B - 1 ? c : choice;
-        const uint64_t* rows8 = (const uint64_t*)s_pred8;
-        for (int s0 = B - 1; s0 >= 2; s0 -= 8) {
-          uint64_t row[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) row[u] = rows8[max(s0 - u - 2, 0)];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int s = s0 - u;
-            if (s >= 2) {
-              c = (int)((row[u] >> (8 * c)) & 0xffull);
-              choice = lane == s - 1 ? c : choice;
-            }
-          }
+        for (int s = B - 1; s >= 2; --s) {
+          const uint64_t hit = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hhi, s) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane(hlo, s);
+          const uint64_t bits = (s & 1) ? (hit >> (8 * c)) & 0xffull : (hit >> c) & 0x0101010101010101ull;
+          int p = __ffsll((long long)bits) - 1;
+          p = (s & 1) ? p : (p >> 3);
+          c = p < 0 ? 0 : p;   // p < 0 only if no lane reached the maximum (non-finite scores)
+          choice = lane == s - 1 ? c : choice;
         }
       }
     } else if (RULE == RULE_EXACT) {

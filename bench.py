@@ -409,18 +409,21 @@ def stage_work(w, sid):
     if sid == 0:
         return {"bytes": rows * V * es + rows * (8 * K + 4), "flops": 0}
     if sid == 1:
-        # slot/rank tables, first confidence layer; writes x (f32), hid (bf16)
-        node = {"bytes": 2 * 64 * H * 2 + H * (5 * 2 + 4) + M * 8 + M * H * (4 + 2),
-                "flops": 2 * M * H * 5 + 4 * M * H}
+        # first confidence layer: reads the ids and log-probabilities, writes hid (bf16)
+        node = {"bytes": H * (5 * 2 + 4) + M * 8 + M * H * 2, "flops": 2 * M * H * 5}
         if not paper:
-            node["bytes"] += M * H * 2       # E rows
+            # the lattice head's table sum is formed in the next stage
             return node
-        # projected drafter states (read per node) and the gathered E_t rows
-        node["bytes"] += M * H * 4 + 2 * M * Ht * 2
+        # slot/rank tables, projected drafter states (read per node), the
+        # gathered E_t rows; writes x (f32)
+        node["bytes"] += 2 * 64 * H * 2 + M * H * 4 + 2 * M * Ht * 2 + M * H * 4
+        node["flops"] += 4 * M * H
         return add(lin(Hd, H, 2, 4, m=rows), node)
     if sid == 2:
         if not paper:
-            return lin(H, H, 2, 4, resid=True, norm_out=True)
+            # the residual is rebuilt from the tables: E rows by id, slot and rank rows
+            tables = {"bytes": M * 4 + M * H * 2 + 2 * 64 * H * 2, "flops": 2 * M * H}
+            return add(lin(H, H, 2, 4, norm_out=True), tables)
         return add(lin(H, H, 2, 4, resid=True), lin(Ht, H, 2, 4, resid=True, norm_out=True))
     if 3 <= sid <= 12:
         j = layer % 5

@@ -251,8 +251,33 @@ int enqueue_rerank(const void* logits, int B, int V, int K, const lilicorr_param
                    launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
                                    (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms),
                                    topk_idx, topk_logp, p->dbg_lse, st)));
-  if (!paper) {
-    // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0))
+  if (!paper && linear_takes_node_source(M, H, H)) {
+    // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0)).
+    // The table sum ((E + S) + R) is formed by the W2c linear's epilogue from
+    // the tables (same float32 order), so x is written once.
+    NodeSource nd;
+    nd.tok = topk_idx;
+    nd.E = W.E;
+    nd.S = W.S;
+    nd.R = W.R;
+    nd.K = K;
+    nd.B = B;
+    nd.V = V;
+    nd.magic_k = div_magic(K);
+    nd.magic_b = div_magic(B);
+    LinearEpilogue e = resid_norm(W.layer[0].gamma1);
+    e.resid = nullptr;
+    e.node = &nd;
+    LL_STAGE(LILICORR_STAGE_NODE,
+             LL_STEP("node_build", WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP), WS_BIT(HID),
+                     launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, nullptr, W.S, W.R,
+                                       W.conf_w1, W.conf_b1, hid, nullptr, V, st)));
+    LL_STAGE(LILICORR_STAGE_CONF_LINEAR,
+             LL_STEP("linear_conf_w2", WS_BIT(HID) | WS_BIT(TOPK_IDX), WS_BIT(X) | WS_BIT(U) | GP,
+                     launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, e, x, gpart, st)));
+  } else if (!paper) {
+    // a2 with the table sum written by the node build (few-row shapes whose
+    // W2c linear has no node-source epilogue)
     LL_STAGE(LILICORR_STAGE_NODE,
              LL_STEP("node_build", WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP), WS_BIT(HID) | WS_BIT(X),
                      launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, nullptr, W.S, W.R,

@@ -173,10 +173,32 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited).
 constexpr int waitcnt_vm(int v) { return (v & 15) | ((v >> 4) << 14) | 0x70 | 0xF00; }
 
+// Residual epilogue whose residual is the node build's table sum (NodeSource)
+constexpr int EPI_NODE = 4;
+
+// ((E[tok] + S[s]) + R[j]) of row m, columns n .. n + 3 (float32, the order
+// the node is written in); N is the row length of the tables.
+__device__ __forceinline__ float4 node_resid4(const NodeSource& nd, uint32_t m, int64_t n, int N) {
+  const uint32_t q = div_by(m, nd.magic_k);
+  const int j = (int)(m - q * (uint32_t)nd.K);
+  const int s = (int)(q - div_by(q, nd.magic_b) * (uint32_t)nd.B);
+  int64_t tok = nd.tok[m];
+  if (tok < 0 || tok >= nd.V) tok = 0;   // ids come from the top-K stage; never read outside E
+  const uint2 e = *(const uint2*)(nd.E + tok * N + n);
+  const uint2 sv = *(const uint2*)(nd.S + (int64_t)s * N + n);
+  const uint2 rv = *(const uint2*)(nd.R + (int64_t)j * N + n);
+  auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+  auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+  return make_float4((lo(e.x) + lo(sv.x)) + lo(rv.x), (hi(e.x) + hi(sv.x)) + hi(rv.x),
+                     (lo(e.y) + lo(sv.y)) + lo(rv.y), (hi(e.y) + hi(sv.y)) + hi(rv.y));
+}
+
 template <int BM, int BN, int EPI, int NW = 4>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN * 4 / NW >= 32768 ? 1 : 2, BM * BN * 4 / NW >= 32768 ? 1 : 2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int M, int N, int Kd,
-    const float* __restrict__ bias, const float* resid, void* out, int tiles_n, int ntiles) {
+    const float* __restrict__ bias, const float* resid, void* out, int tiles_n, int ntiles,
+    NodeSource node) {
+  constexpr bool RES = EPI == EPI_RESID_F32 || EPI == EPI_NODE;   // a residual is added
   // K advances 64 per stage, so a stage row is one whole 128-byte line of A or
   // W (10-17 % faster than 32 per stage, whose load instructions each touched
   // half of 16 lines). Stages in LDS: three for 256 x 128 tiles (144 KiB), two
@@ -327,13 +349,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
   // Residual epilogue: the residual rows of slice i + 1 are loaded while
   // slice i is staged and stored (double-buffered), so the reads overlap.
   constexpr int U = 32 * CPRW / 64;
-  float4 rbuf[2][EPI == EPI_RESID_F32 ? U : 1];
-  auto load_resid = [&](int i, float4 (&r)[EPI == EPI_RESID_F32 ? U : 1]) __attribute__((always_inline)) {
+  float4 rbuf[2][RES ? U : 1];
+  auto load_resid = [&](int i, float4 (&r)[RES ? U : 1]) __attribute__((always_inline)) {
     if constexpr (EPI == EPI_RESID_F32) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t m = m0 + wm * WM + i * 32 + (lane + 64 * u) / CPRW;
         r[u] = *(const float4*)(resid + min(m, (int64_t)M - 1) * N + nc);
+      }
+    } else if constexpr (EPI == EPI_NODE) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t m = m0 + wm * WM + i * 32 + (lane + 64 * u) / CPRW;
+        r[u] = node_resid4(node, (uint32_t)min(m, (int64_t)M - 1), nc, N);
       }
     }
   };
@@ -356,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
       __builtin_amdgcn_wave_barrier();
       // the slice's staged values are read together, except in the residual
       // epilogue, whose double-buffered residual rows leave no registers
-      constexpr int UY = EPI == EPI_RESID_F32 ? 1 : U;
+      constexpr int UY = RES ? 1 : U;
       float4 ys[UY];
       if constexpr (UY > 1) {
 #pragma unroll
@@ -392,26 +420,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
 
 template <int BM, int BN, int NW = 4>
 hipError_t launch_dma(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, const float* bias,
-                      int epi, const float* resid, void* out, hipStream_t stream) {
+                      int epi, const float* resid, void* out, hipStream_t stream,
+                      const NodeSource* node = nullptr) {
+  const NodeSource nd = node ? *node : NodeSource{};
   const int tiles_n = (N + BN - 1) / BN;
   const int ntiles = ((M + BM - 1) / BM) * tiles_n;
   const dim3 grid((unsigned)ntiles), block(64 * NW);
   switch (epi) {
     case EPI_F32:
       hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_F32, NW>), grid, block, 0, stream, A, W, M, N,
-                         Kd, bias, resid, out, tiles_n, ntiles);
+                         Kd, bias, resid, out, tiles_n, ntiles, nd);
       break;
     case EPI_BF16:
       hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_BF16, NW>), grid, block, 0, stream, A, W, M, N,
-                         Kd, bias, resid, out, tiles_n, ntiles);
+                         Kd, bias, resid, out, tiles_n, ntiles, nd);
       break;
     case EPI_SILU_BF16:
       hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_SILU_BF16, NW>), grid, block, 0, stream, A, W,
-                         M, N, Kd, bias, resid, out, tiles_n, ntiles);
+                         M, N, Kd, bias, resid, out, tiles_n, ntiles, nd);
       break;
     default:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_RESID_F32, NW>), grid, block, 0, stream, A, W,
-                         M, N, Kd, bias, resid, out, tiles_n, ntiles);
+      if (node)
+        hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_NODE, NW>), grid, block, 0, stream, A, W,
+                           M, N, Kd, bias, resid, out, tiles_n, ntiles, nd);
+      else
+        hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, EPI_RESID_F32, NW>), grid, block, 0, stream, A, W,
+                           M, N, Kd, bias, resid, out, tiles_n, ntiles, nd);
       break;
   }
   return hipGetLastError();
@@ -687,11 +721,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // x = resid + (y + bias) written back, then u = bf16(x * rstd * gamma).
 // Thread t holds the 4-column groups t, t + 256, ...; the sum of squares is
 // reduced per wave, then over the four waves in a fixed order.
-template <int S, int NV>
+template <int S, int NV, bool NODE = false>
 __global__ __launch_bounds__(256) void splitk_resid_rmsnorm_kernel(
     const float* __restrict__ part, int M, int N, const float* __restrict__ bias,
     const float* resid, float* x_out, const float* __restrict__ gamma, float eps,
-    uint16_t* __restrict__ u_out) {
+    uint16_t* __restrict__ u_out, NodeSource node) {
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m = blockIdx.x;
@@ -709,7 +743,7 @@ __global__ __launch_bounds__(256) void splitk_resid_rmsnorm_kernel(
     const int64_t q = m * n4 + gc;
     const float4 y = splitk_sum4<S>(part4, MN4, q);
     const float4 b = bias ? ((const float4*)bias)[gc] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 r = ((const float4*)resid)[q];
+    const float4 r = NODE ? node_resid4(node, (uint32_t)m, (int64_t)gc * 4, N) : ((const float4*)resid)[q];
     gv[i] = ((const float4*)gamma)[gc];
     v[i] = make_float4(r.x + (y.x + b.x), r.y + (y.y + b.y), r.z + (y.z + b.z), r.w + (y.w + b.w));
     if (gi >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -832,18 +866,22 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
                          const float* part, hipStream_t stream) {
   const unsigned row_blocks = (unsigned)((M + 3) / 4);
   if (ep.kind == EPI_RESID_F32 && ep.norm_out) {
-    if (N <= 1024)
-      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 1>), dim3((unsigned)M), dim3(256), 0,
-                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
-                         ep.norm_out);
-    else if (N <= 2048)
-      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 2>), dim3((unsigned)M), dim3(256), 0,
-                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
-                         ep.norm_out);
-    else
-      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, 4>), dim3((unsigned)M), dim3(256), 0,
-                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,
-                         ep.norm_out);
+    const NodeSource nd = ep.node ? *ep.node : NodeSource{};
+#define LL_RRN(NV)                                                                                 \
+  do {                                                                                             \
+    if (ep.node)                                                                                   \
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, NV, true>), dim3((unsigned)M), dim3(256), 0, \
+                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,    \
+                         ep.norm_out, nd);                                                         \
+    else                                                                                           \
+      hipLaunchKernelGGL((splitk_resid_rmsnorm_kernel<S, NV, false>), dim3((unsigned)M), dim3(256), 0, \
+                         stream, part, M, N, bias, ep.resid, (float*)out, ep.norm_gamma, ep.eps,    \
+                         ep.norm_out, nd);                                                         \
+  } while (0)
+    if (N <= 1024) LL_RRN(1);
+    else if (N <= 2048) LL_RRN(2);
+    else LL_RRN(4);
+#undef LL_RRN
     return hipGetLastError();
   }
   if (ep.kind == EPI_F32 && ep.heads_out) {
@@ -937,10 +975,19 @@ GemmPlan plan_linear(int M, int Kd, int N) {
   return p;
 }
 
+bool linear_takes_node_source(int M, int Kd, int N) {
+  // the many-row DMA kernel (M >= 2048, K a multiple of 64, N of 4, aligned
+  // operands) or the split-K row reduce (plan_linear splits K)
+  if (M >= 2048) return Kd % 64 == 0 && N % 4 == 0;
+  return plan_linear(M, Kd, N).split > 1;
+}
+
 hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
                          const float* bias, const LinearEpilogue& ep, void* out, float* part,
                          hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (ep.node && (ep.kind != EPI_RESID_F32 || !ep.norm_out || !linear_takes_node_source(M, Kd, N)))
+    return hipErrorInvalidValue;
   // Few rows and enough 16-column tiles to occupy the GPU: one pass over K
   // with the epilogue fused (row-wide epilogues need whole rows: not here).
   if (uses_skinny(M, Kd, N) && ep.norm_out == nullptr && ep.heads_out == nullptr)
@@ -952,6 +999,7 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
     const auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (M >= 2048 && Kd % 64 == 0 && N % 4 == 0 && al16(out) && (bias == nullptr || al16(bias)) &&
         (ep.resid == nullptr || al16(ep.resid))) {
+      const NodeSource* nd = ep.node;
       // the largest tile that still gives (nearly) every CU work
       // (eight waves, two per SIMD, for the large tiles: each wave then owns a
       // 128 x 64 or 128 x 32 block, and one wave's barrier wait overlaps the
@@ -959,13 +1007,15 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
       // beat all of them with 256 x 128 ones (QKV at 4,096 rows: 36 against
       // 43 us).
       if (tiles(256, 256) >= 192)
-        e = launch_dma<256, 256, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+        e = launch_dma<256, 256, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream, nd);
       else if (tiles(256, 128) >= 256)
-        e = launch_dma<256, 128, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+        e = launch_dma<256, 128, 8>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream, nd);
       else if (tiles(128, 128) >= 384)
-        e = launch_dma<128, 128, 4>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+        e = launch_dma<128, 128, 4>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream, nd);
       else   // a few thousand rows of a narrow output: 128 x 64 tiles, three workgroups per CU
-        e = launch_dma<128, 64, 4>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
+        e = launch_dma<128, 64, 4>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream, nd);
+    } else if (ep.node) {
+      return hipErrorInvalidValue;   // misaligned operands: no node-source kernel here
     } else if (M >= 2048)
       e = launch_tile<128, 128>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     else if (M > 64)

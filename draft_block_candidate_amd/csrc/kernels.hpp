@@ -33,6 +33,8 @@ hipError_t launch_topk_merge_shards(int G, int rows, int K, const float* val, co
 //   hid  bf16 [M, H] = bf16(silu(W1c f + b1c));  xbase float [M, H] = (E[tok] + S[s]) + R[j]
 // With ph set (the paper's head): only slots 1..B-1 (M = N (B-1) K) and
 // xbase = (ph[n B + s] + S[s]) + R[j], ph the projected drafter states [N B, H].
+// xbase may be null (lattice head only): then only hid is written and the
+// table sum is left to the next linear's epilogue (NodeSource).
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
                              int H, const uint16_t* E, const float* ph, const uint16_t* S,
                              const uint16_t* R, const uint16_t* conf_w1, const float* conf_b1,
@@ -66,6 +68,25 @@ GemmPlan plan_linear(int M, int Kd, int N);
 // (no split-K scratch) for epilogues that need no whole rows.
 bool uses_skinny(int M, int Kd, int N);
 
+// Residual of the node build: the residual of row m is not read from memory
+// but formed from the tables, ((E[tok[m]] + S[s]) + R[j]) in float32 with
+// m = (n B + s) K + j (the lattice head's table sum, added in the order the
+// node is written); the confidence network's output is then added to it.
+struct NodeSource {
+  const int32_t* tok = nullptr;   // [M] token ids (the top-K ids)
+  const uint16_t *E = nullptr, *S = nullptr, *R = nullptr;   // bf16 tables, rows of N
+  int K = 1, B = 1, V = 1;        // candidates per slot, slots per block, rows of E
+  uint64_t magic_k = 0, magic_b = 0;   // div_magic(K), div_magic(B)
+};
+// floor(m / d) for any 32-bit m and 1 <= d <= 64 as (m * ceil(2^38 / d)) >> 38
+// (the round-up multiplier with 6 extra bits is exact for 32-bit numerators),
+// evaluated in 64-bit pieces.
+__host__ __device__ inline uint64_t div_magic(int d) { return ((1ull << 38) + (uint64_t)d - 1) / (uint64_t)d; }
+__host__ __device__ inline uint32_t div_by(uint32_t m, uint64_t magic) {
+  const uint64_t lo = magic & 0xffffffffull, hi = magic >> 32;
+  return (uint32_t)(((uint64_t)m * hi + (((uint64_t)m * lo) >> 32)) >> 6);
+}
+
 // What follows the product y = A W^T + bias:
 //   kind       EPI_* store of y (EPI_RESID_F32: out = resid + y)
 //   norm_out   if set (with EPI_RESID_F32): also u = bf16(RMSNorm(out; norm_gamma, eps))
@@ -82,7 +103,14 @@ struct LinearEpilogue {
   uint16_t* heads_out = nullptr;
   uint16_t* heads_in = nullptr;
   int heads_group = 0, heads_skip = 0;
+  // EPI_RESID_F32 only: the residual comes from the node tables instead of
+  // `resid` (see NodeSource); allowed where linear_takes_node_source() holds
+  const NodeSource* node = nullptr;
 };
+// True when launch_linear forms a residual-plus-RMSNorm epilogue (EPI_RESID_F32
+// with norm_out) of an M x Kd -> N product in a kernel that can take the node
+// tables as its residual (the many-row DMA kernel, the split-K row reduce).
+bool linear_takes_node_source(int M, int Kd, int N);
 
 // Destination row of the out/in heads' row m (see LinearEpilogue).
 __host__ __device__ inline int64_t heads_row(int64_t m, int group, int skip) {

@@ -18,7 +18,9 @@ namespace {
 // 1..B-1 only, and the first term of the table sum is the slot's projected
 // drafter hidden state ph[(n B + s) H ..] (fp32) instead of an E row; the
 // target-embedding term is added by a later linear.
-template <int CG, int TPB, bool PAPER>
+// WX = false (lattice head): only hid is written; the table sum is formed by
+// the next linear's epilogue instead (NodeSource), so E, S and R are not read.
+template <int CG, int TPB, bool PAPER, bool WX = true>
 __global__ __launch_bounds__(256) void node_build_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int64_t M, int B,
     int K, int H, int V, const uint16_t* __restrict__ E, const float* __restrict__ ph,
@@ -78,6 +80,7 @@ __global__ __launch_bounds__(256) void node_build_kernel(
     f[u][4] = j == 0 ? 1.f : 0.f;
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
+      if (!WX) break;
       const int c4 = min(tid + 256 * g, h4 - 1);
       if (PAPER)
         pv[u][g] = ((const float4*)(ph + row * H))[c4];
@@ -93,10 +96,11 @@ __global__ __launch_bounds__(256) void node_build_kernel(
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
       const int c4 = tid + 256 * g;
-      const uint32_t ew[2] = {PAPER ? 0u : ev[u][g].x, PAPER ? 0u : ev[u][g].y},
-                     sw[2] = {sv[u][g].x, sv[u][g].y}, rw[2] = {rv[u][g].x, rv[u][g].y};
-      const float pw[4] = {PAPER ? pv[u][g].x : 0.f, PAPER ? pv[u][g].y : 0.f,
-                           PAPER ? pv[u][g].z : 0.f, PAPER ? pv[u][g].w : 0.f};
+      const uint32_t ew[2] = {PAPER || !WX ? 0u : ev[u][g].x, PAPER || !WX ? 0u : ev[u][g].y},
+                     sw[2] = {WX ? sv[u][g].x : 0u, WX ? sv[u][g].y : 0u},
+                     rw[2] = {WX ? rv[u][g].x : 0u, WX ? rv[u][g].y : 0u};
+      const float pw[4] = {PAPER && WX ? pv[u][g].x : 0.f, PAPER && WX ? pv[u][g].y : 0.f,
+                           PAPER && WX ? pv[u][g].z : 0.f, PAPER && WX ? pv[u][g].w : 0.f};
       float xb[4], hz[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(256) void node_build_kernel(
         hz[q] = silu(z + bv[g][q]);
       }
       if (tok_ok && c4 < h4) {
-        ((float4*)(xbase + tk[u] * H))[c4] = make_float4(xb[0], xb[1], xb[2], xb[3]);
+        if (WX) ((float4*)(xbase + tk[u] * H))[c4] = make_float4(xb[0], xb[1], xb[2], xb[3]);
         ((uint2*)(hid + tk[u] * H))[c4] = make_uint2(pack_bf16x2(hz[0], hz[1]), pack_bf16x2(hz[2], hz[3]));
       }
     }
@@ -127,16 +131,21 @@ hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, in
   const bool paper = ph != nullptr;
   const int64_t M = (int64_t)N * (paper ? B - 1 : B) * K;
   if (M <= 0) return hipSuccess;
+  if (paper && !xbase) return hipErrorInvalidValue;
 #define LL_NB(CG, TPB, grid)                                                                     \
   do {                                                                                         \
     if (paper)                                                                                 \
       hipLaunchKernelGGL((node_build_kernel<CG, TPB, true>), grid, dim3(256), 0, stream,      \
                          topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1, conf_b1,   \
                          hid, xbase);                                                          \
-    else                                                                                       \
+    else if (xbase)                                                                            \
       hipLaunchKernelGGL((node_build_kernel<CG, TPB, false>), grid, dim3(256), 0, stream,     \
                          topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1, conf_b1,   \
                          hid, xbase);                                                          \
+    else                                                                                       \
+      hipLaunchKernelGGL((node_build_kernel<CG, TPB, false, false>), grid, dim3(256), 0,      \
+                         stream, topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1,    \
+                         conf_b1, hid, xbase);                                                 \
   } while (0)
   // few tokens: one per block (more blocks in flight); many: eight per block
   // (four for the widest rows, to bound the registers)

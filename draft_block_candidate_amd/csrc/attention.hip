@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 // independent MFMA chains, exact row max, P~ = bf16(exp(s - max)),
 // O^T = V^T P~^T with V^T fragments read by ds_read_b64_tr_b16, O / l. K and V
 // are read from HBM once per (block, head).
-template <int TMAX, int DH, int NW>
+template <int TMAX, int DH, int NW, bool K4>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
                                                             int K, int H,
                                                             const float* __restrict__ dist,
@@ -290,31 +290,56 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);
       __builtin_amdgcn_sched_barrier(0);   // keep each k-step's reads with it
     }
-    // Masking by select: the bias-table reads use a clamped slot, are
-    // unconditional (a read under a per-element branch is waited for inside
-    // it) and are issued together in a region of their own.
+    // Bias, same-slot term and mask. With K a multiple of 4 (K4) a lane's
+    // four keys of a tile share one slot: one slot computation, one
+    // bias-table read and one same-slot test per tile and lane. Otherwise per
+    // element, with the bias-table reads unconditional on a clamped slot (a
+    // read under a per-element branch is waited for inside it) and issued
+    // together in a region of their own. Both compute fl32(fma(acc, scale,
+    // bias)), then + Same in its own rounding on same-slot pairs.
     float s[KT][4];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot_k = (int)(((unsigned)min(kt * 16 + 4 * g + i, T - 1) * kmul) >> 16);
-        s[kt][i] = bias_tab[slot_k - slot_q + 63];
-      }
-    __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
+    if constexpr (K4) {
+      // an opaque per-tile copy of the lane's key offset: the per-key masks
+      // are recomputed per query tile instead of hoisted out of the tile
+      // loop (a mask register pair per strip element, spilled)
+      int g4 = 4 * g;
+      asm volatile("" : "+v"(g4));
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int kt = 0; kt < KT; ++kt) {
+        const int key0 = kt * 16 + g4;
+        const int slot_k = (int)(((unsigned)min(key0, T - 1) * kmul) >> 16);
+        const float b = bias_tab[slot_k - slot_q + 63];
+        const float sm = slot_k == slot_q ? same_h : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt * 16 + 4 * g + i;
-        const int slot_k = (int)(((unsigned)min(key, T - 1) * kmul) >> 16);
-        float v = acc[kt][i] * scale + s[kt][i];
-        v = slot_k == slot_q ? v + same_h : v;
-        v = key < T ? v : -INFINITY;
-        s[kt][i] = v;
-        mx = fmaxf(mx, v);
+        for (int i = 0; i < 4; ++i) {
+          const float v = key0 + i < T ? (acc[kt][i] * scale + b) + sm : -INFINITY;
+          s[kt][i] = v;
+          mx = fmaxf(mx, v);
+        }
       }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot_k = (int)(((unsigned)min(kt * 16 + 4 * g + i, T - 1) * kmul) >> 16);
+          s[kt][i] = bias_tab[slot_k - slot_q + 63];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt * 16 + 4 * g + i;
+          const int slot_k = (int)(((unsigned)min(key, T - 1) * kmul) >> 16);
+          float v = acc[kt][i] * scale + s[kt][i];
+          v = slot_k == slot_q ? v + same_h : v;
+          v = key < T ? v : -INFINITY;
+          s[kt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     float lsum = 0.f;
@@ -635,15 +660,19 @@ hipError_t launch_res(int dh, const uint16_t* qkv, int N, int B, int K, int H, i
   constexpr int NW = TMAX <= 128 ? 4 : 8;
   const int ntile = (B * K + 15) / 16;
   const dim3 grid((unsigned)heads, (unsigned)N, TMAX <= 128 && ntile > NW ? 2u : 1u);
-  if (dh == 32)
-    hipLaunchKernelGGL((attention_res_kernel<TMAX, 32, NW>), grid, dim3(64 * NW), 0, stream, qkv, B,
-                       K, H, dist, same, out);
-  else if (dh == 64)
-    hipLaunchKernelGGL((attention_res_kernel<TMAX, 64, NW>), grid, dim3(64 * NW), 0, stream, qkv, B,
-                       K, H, dist, same, out);
-  else
-    hipLaunchKernelGGL((attention_res_kernel<TMAX, 128, NW>), grid, dim3(64 * NW), 0, stream, qkv, B,
-                       K, H, dist, same, out);
+#define LL_RES(DH)                                                                              \
+  do {                                                                                        \
+    if ((K & 3) == 0)                                                                         \
+      hipLaunchKernelGGL((attention_res_kernel<TMAX, DH, NW, true>), grid, dim3(64 * NW), 0,   \
+                         stream, qkv, B, K, H, dist, same, out);                              \
+    else                                                                                      \
+      hipLaunchKernelGGL((attention_res_kernel<TMAX, DH, NW, false>), grid, dim3(64 * NW), 0,  \
+                         stream, qkv, B, K, H, dist, same, out);                              \
+  } while (0)
+  if (dh == 32) LL_RES(32);
+  else if (dh == 64) LL_RES(64);
+  else LL_RES(128);
+#undef LL_RES
   return hipGetLastError();
 }
 

@@ -348,8 +348,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
   if (bias) bv = *(const float4*)(bias + nc);
   // Residual epilogue: the residual rows of slice i + 1 are loaded while
   // slice i is staged and stored (double-buffered), so the reads overlap.
+  // The node-table residual (three row gathers and the index arithmetic per
+  // row) does not fit twice in the register budget: it is loaded per slice,
+  // before the slice is staged, so the staging overlaps its reads.
   constexpr int U = 32 * CPRW / 64;
-  float4 rbuf[2][RES ? U : 1];
+  constexpr int RB = EPI == EPI_NODE ? 1 : 2;
+  float4 rbuf[RB][RES ? U : 1];
   auto load_resid = [&](int i, float4 (&r)[RES ? U : 1]) __attribute__((always_inline)) {
     if constexpr (EPI == EPI_RESID_F32) {
 #pragma unroll
@@ -372,10 +376,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
   const bool full = m0 + BM <= M && n0 + BN <= N;
   auto slices = [&](auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
-    load_resid(0, rbuf[0]);
+    if constexpr (RB == 2) load_resid(0, rbuf[0]);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      if (i + 1 < MT) load_resid(i + 1, rbuf[(i + 1) & 1]);
+      if constexpr (RB == 2) {
+        if (i + 1 < MT) load_resid(i + 1, rbuf[(i + 1) & 1]);
+      } else {
+        load_resid(i, rbuf[0]);
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
             *(uint2*)((uint16_t*)out + o) =
                 make_uint2(pack_bf16x2(silu(y.x), silu(y.y)), pack_bf16x2(silu(y.z), silu(y.w)));
         } else {
-          const float4 rv = rbuf[i & 1][u];
+          const float4 rv = rbuf[RB == 2 ? (i & 1) : 0][u];
           if (ok) *(float4*)((float*)out + o) = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
         }
       }

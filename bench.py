@@ -467,7 +467,7 @@ def counter_traffic(workload, stage):
 
 # Kernel roles, by name, for splitting a step's dispatch sequence into stages.
 _GEMM_MAIN = ("gemm_kernel", "gemm_part_kernel", "gemm_dma_kernel", "gemm_fullk_kernel", "gemm_skinny_kernel")
-_GEMM_TAIL = ("splitk_", "rmsnorm", "heads_l2norm")
+_GEMM_TAIL = ("splitk_", "rmsnorm")
 _LINEAR_ORDER = ["linear_conf_w2"] + [f"{n}.l{l}" for l in range(2)
                                       for n in ("linear_qkv", "linear_o", "linear_ffn1", "linear_ffn2")] \
     + ["linear_heads"]

@@ -783,7 +783,8 @@ __global__ __launch_bounds__(256) void splitk_resid_rmsnorm_kernel(
 
 // Out/in heads: y = A W^T + b over N = 2 d_e, each half normalised to unit
 // length and rounded to bf16, stored in row heads_row(m, group, skip). One
-// wave per row; d_e % 4 == 0.
+// wave per row; d_e % 4 == 0. With S = 1 and no bias it normalises rows the
+// many-row GEMM has already finished (16-byte loads, a whole row per wave).
 template <int S, int NV>
 __global__ __launch_bounds__(256) void splitk_heads_l2norm_kernel(
     const float* __restrict__ part, int M, int de, const float* __restrict__ bias,
@@ -801,7 +802,7 @@ __global__ __launch_bounds__(256) void splitk_heads_l2norm_kernel(
     const int gi = lane + 64 * i;
     const int gc = min(gi, n4 - 1);   // clamped: loads stay unconditional
     const float4 y = splitk_sum4<S>(part4, MN4, m * n4 + gc);
-    const float4 b = ((const float4*)bias)[gc];
+    const float4 b = bias ? ((const float4*)bias)[gc] : make_float4(0.f, 0.f, 0.f, 0.f);
     v[i] = make_float4(y.x + b.x, y.y + b.y, y.z + b.z, y.w + b.w);
     if (gi >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -1032,8 +1033,20 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
       e = launch_tile<64, 32>(A, M, Kd, W, N, bias, ep.kind, ep.resid, out, stream);
     if (e != hipSuccess) return e;
     if (ep.norm_out) return launch_rmsnorm((const float*)out, M, N, ep.norm_gamma, ep.eps, ep.norm_out, stream);
-    if (ep.heads_out) return launch_heads_l2norm((const float*)out, M, N / 2, ep.heads_out, ep.heads_in,
-                                                ep.heads_group, ep.heads_skip, stream);
+    if (ep.heads_out) {
+      const dim3 grid((unsigned)((M + 3) / 4));
+      const float* y = (const float*)out;
+      if (N <= 256)
+        hipLaunchKernelGGL((splitk_heads_l2norm_kernel<1, 1>), grid, dim3(256), 0, stream, y, M, N / 2,
+                           nullptr, ep.heads_out, ep.heads_in, ep.heads_group, ep.heads_skip);
+      else if (N <= 1024)
+        hipLaunchKernelGGL((splitk_heads_l2norm_kernel<1, 4>), grid, dim3(256), 0, stream, y, M, N / 2,
+                           nullptr, ep.heads_out, ep.heads_in, ep.heads_group, ep.heads_skip);
+      else
+        hipLaunchKernelGGL((splitk_heads_l2norm_kernel<1, 8>), grid, dim3(256), 0, stream, y, M, N / 2,
+                           nullptr, ep.heads_out, ep.heads_in, ep.heads_group, ep.heads_skip);
+      return hipGetLastError();
+    }
     return hipSuccess;
   }
   hipError_t e;

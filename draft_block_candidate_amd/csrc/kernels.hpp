@@ -130,9 +130,6 @@ hipError_t launch_attention(const uint16_t* qkv, int N, int B, int K, int H, int
                             const float* dist, const float* same, uint16_t* out,
                             hipStream_t stream);
 
-// Row-wise unit normalisation of v [M, 2 d_e] (out half | in half) to bf16.
-hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, uint16_t* inv,
-                               int group, int skip, hipStream_t stream);
 
 hipError_t launch_pair_scores(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
                               int d_e, float* cos, hipStream_t stream);

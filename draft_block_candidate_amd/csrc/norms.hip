@@ -1,6 +1,7 @@
-// Row normalisations: RMSNorm before each sub-layer and the final unit-norm
-// of the in/out vectors (LiLiCorr paper, Appendix A: RMSNorm; Section 3.2:
-// in and out vectors normalised to unit norm).
+// RMSNorm of the fp32 residual stream before each sub-layer (LiLiCorr paper,
+// Appendix A: pre-norm blocks with RMSNorm) for rows whose producing linear
+// ran as whole tiles; the unit normalisation of the in/out vectors is in the
+// heads linear's row kernel (gemm.hip).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -70,26 +71,6 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const float* __restric
   }
 }
 
-// One wave per (token, head): v / max(|v|, 1e-12) rounded to bf16, stored
-// in row heads_row(m, group, skip).
-__global__ __launch_bounds__(256) void heads_l2norm_kernel(const float* __restrict__ v, int M,
-                                                           int de, uint16_t* __restrict__ outv,
-                                                           uint16_t* __restrict__ inv, int group,
-                                                           int skip) {
-  const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= 2 * (int64_t)M) return;
-  const int64_t m = w >> 1;
-  const int half = (int)(w & 1);
-  const float* src = v + m * 2 * de + half * de;
-  uint16_t* dst = (half ? inv : outv) + heads_row(m, group, skip) * de;
-  float ss = 0.f;
-  for (int d = lane; d < de; d += 64) ss = fmaf(src[d], src[d], ss);
-  ss = wave_sum(ss);
-  const float n = fmaxf(__fsqrt_rn(ss), 1e-12f);
-  for (int d = lane; d < de; d += 64) dst[d] = (uint16_t)f32_to_bf16(__fdiv_rn(src[d], n));
-}
-
 }  // namespace
 
 hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, float eps,
@@ -102,15 +83,6 @@ hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, floa
     hipLaunchKernelGGL(rmsnorm_reg_kernel<8>, grid, dim3(256), 0, stream, x, M, H, gamma, eps, out);
   else
     hipLaunchKernelGGL(rmsnorm_kernel, grid, dim3(256), 0, stream, x, M, H, gamma, eps, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_heads_l2norm(const float* v, int M, int d_e, uint16_t* outv, uint16_t* inv,
-                               int group, int skip, hipStream_t stream) {
-  if (M <= 0) return hipSuccess;
-  const int64_t waves = 2 * (int64_t)M;
-  hipLaunchKernelGGL(heads_l2norm_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
-                     v, M, d_e, outv, inv, group, skip);
   return hipGetLastError();
 }
 

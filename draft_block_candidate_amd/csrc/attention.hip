@@ -307,13 +307,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       asm volatile("" : "+v"(g4));
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
+        // T = B K is a multiple of 4 too, so the four keys are all inside the
+        // lattice or all past it: the mask is a bias of -inf (fma(a, s, -inf)
+        // is -inf for finite a)
         const int key0 = kt * 16 + g4;
         const int slot_k = (int)(((unsigned)min(key0, T - 1) * kmul) >> 16);
-        const float b = bias_tab[slot_k - slot_q + 63];
+        const float b = key0 < T ? bias_tab[slot_k - slot_q + 63] : -INFINITY;
         const float sm = slot_k == slot_q ? same_h : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = key0 + i < T ? (acc[kt][i] * scale + b) + sm : -INFINITY;
+          const float v = (acc[kt][i] * scale + b) + sm;
           s[kt][i] = v;
           mx = fmaxf(mx, v);
         }
@@ -516,21 +519,22 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
           ab[j] = mfma16(kf, qfb[ks], ab[j]);
         }
       if (K % 16 == 0) {
-        // every 16-key tile lies in one slot: one table read per tile and
-        // query tile, no per-element branch
+        // every 16-key tile lies in one slot, and T = B K is a multiple of 16,
+        // so a tile is all inside the lattice or all past it: one table read
+        // per tile and query tile, the mask a bias of -inf (fma(a, s, -inf) is
+        // -inf for finite a) and the same-slot term one add
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int st = (int)(((unsigned)min((kt0 + j) * 16 + zb, T - 1) * kmul) >> 16);
-          const float ba = bias_tab[st - slot_qa + 63], bb = bias_tab[st - slot_qb + 63];
+          const int key0 = (kt0 + j) * 16 + zb;   // zb == 0, opaque
+          const int st = (int)(((unsigned)min(key0, T - 1) * kmul) >> 16);
+          const bool in = key0 < T;
+          const float ba = in ? bias_tab[st - slot_qa + 63] : -INFINITY;
+          const float bb = in ? bias_tab[st - slot_qb + 63] : -INFINITY;
+          const float sa = st == slot_qa ? same_h : 0.f, sb = st == slot_qb ? same_h : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = (kt0 + j) * 16 + 4 * g + i + zb;   // zb == 0, opaque
-            float x = aa[j][i] * scale + ba;
-            x = st == slot_qa ? x + same_h : x;
-            va[j][i] = key < T ? x : -INFINITY;
-            float y = ab[j][i] * scale + bb;
-            y = st == slot_qb ? y + same_h : y;
-            vb[j][i] = key < T ? y : -INFINITY;
+            va[j][i] = (aa[j][i] * scale + ba) + sa;
+            vb[j][i] = (ab[j][i] * scale + bb) + sb;
           }
         }
       } else {

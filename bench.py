@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="no GPU: turn a rocprofv3 --kernel-trace --pmc MfmaUtil MfmaFlopsBF16 run of this "
                          "script into MFMA utilisation and counted bf16 MFMA flops per stage launch")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="PMC_DIR",
+                    help="no GPU: turn rocprofv3 --pmc runs of this script (any counters, one or "
+                         "more runs) into per-stage means of every counter, summed over a stage's "
+                         "kernels, with the wave-time fractions of the SQ wait/active counters")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE, both with --copy-probe-mib) into HBM bytes per stage launch")
@@ -87,6 +91,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path here "
@@ -642,6 +649,75 @@ def summarize_mfma(args):
         print(f"| {st} | {u:.1f} | {fl:.4g} | {alg:.4g} | {ratio} | {t / 1e3:.1f} | {len(lst)} |")
     if tot_t:
         print(f"\nencoder MFMA util (duration-weighted over node build .. heads): {tot_busy / tot_t:.1f} %")
+
+
+def summarize_pmc(args):
+    """Per-stage means of every counter in one or more rocprofv3 --pmc runs,
+    each summed over the stage's kernels in a step. SQ_WAVE_CYCLES, the
+    SQ_WAIT_* and the SQ_ACTIVE_INST_* counters share a unit (wave-cycles), so
+    their ratios are the fractions of the waves' resident time spent waiting
+    or issuing each instruction class."""
+    import csv
+    import glob
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    per = {}
+    names_all = []
+    for d in args.summarize_pmc:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no *counter_collection.csv under {d}")
+        rows = {}
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                key = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+                ent = rows.setdefault(key, [r["Kernel_Name"], {}])
+                c = r["Counter_Name"]
+                ent[1][c] = ent[1].get(c, 0.0) + float(r["Counter_Value"])
+        ids = sorted(rows)
+        names = [rows[k][0] for k in ids]
+        for c in (rows[ids[0]][1] if ids else {}):
+            if c not in names_all:
+                names_all.append(c)
+        i = 0
+        while i < len(ids):
+            if "topk_partial" not in names[i]:
+                i += 1
+                continue
+            j = i
+            while j < len(ids) and not ("scores_walk" in names[j] or "greedy_walk" in names[j]):
+                j += 1
+            if j >= len(ids):
+                break
+            seq = ids[i:j + 1]
+            acc = {}
+            for k, st in zip(seq, split_step_stages([rows[k][0] for k in seq])):
+                if st is None:
+                    continue
+                a = acc.setdefault(st, {})
+                for c, v in rows[k][1].items():
+                    a[c] = a.get(c, 0.0) + v
+            for st, a in acc.items():
+                for c, v in a.items():
+                    per.setdefault(st, {}).setdefault(c, []).append(v)
+            i = j + 1
+    print(f"# SQ counters per stage launch: {w.name}\n")
+    print("Means over the run's steps of each counter summed over a stage's kernels "
+          "(rocprofv3 --pmc, one run per counter group).\n")
+    print(f"csrc_sha256: {csrc_sha256()}\n")
+    print("| stage | " + " | ".join(names_all) + " |")
+    print("|---" * (len(names_all) + 1) + "|")
+    for st, d in per.items():
+        print(f"| {st} | " + " | ".join(f"{sum(d[c]) / len(d[c]):.4g}" if c in d else "-" for c in names_all) + " |")
+    frac = [c for c in names_all if c.startswith(("SQ_WAIT_", "SQ_ACTIVE_INST_"))]
+    if "SQ_WAVE_CYCLES" in names_all and frac:
+        print("\nFractions of wave-resident time (counter / SQ_WAVE_CYCLES):\n")
+        print("| stage | " + " | ".join(frac) + " |")
+        print("|---" * (len(frac) + 1) + "|")
+        for st, d in per.items():
+            wc = sum(d["SQ_WAVE_CYCLES"]) / len(d["SQ_WAVE_CYCLES"]) if "SQ_WAVE_CYCLES" in d else 0.0
+            print(f"| {st} | " + " | ".join(
+                f"{sum(d[c]) / len(d[c]) / wc:.3f}" if c in d and wc else "-" for c in frac) + " |")
 
 
 def counter_mfma(workload):

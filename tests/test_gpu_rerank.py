@@ -120,6 +120,18 @@ def test_rerank_matches_oracle(L, name, tier, sample):
     run_case(L, name, tier, sample)
 
 
+def test_rerank_mid_size_tiles(L):
+    # The first 24 blocks of the 256-block workload: 6,144 lattice rows, where
+    # the confidence linear (its residual formed from the node tables) and the
+    # other H-wide outputs run on 128 x 128 tiles, a size no workload above
+    # reaches.
+    import dataclasses
+    base = synth.WORKLOADS["c256_k16"]
+    w = dataclasses.replace(base, name="c256_k16_first24", num_blocks=24)
+    host = synth.make_logits(base, 0, num_blocks=24)
+    run_case(L, w, 0, spread(24, 6), host=host)
+
+
 @pytest.mark.parametrize("de,K,B,N", [(512, 5, 9, 3), (544, 7, 6, 2), (1024, 3, 16, 1)])
 def test_wide_vectors_sliced_pair_products(L, de, K, B, N):
     # d_e >= 512 takes the pair products in 256-wide slices of d_e over many

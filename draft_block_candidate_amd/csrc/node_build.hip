@@ -25,8 +25,9 @@ __global__ __launch_bounds__(256) void node_build_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int64_t M, int B,
     int K, int H, int V, const uint16_t* __restrict__ E, const float* __restrict__ ph,
     const uint16_t* __restrict__ S, const uint16_t* __restrict__ R, const uint16_t* __restrict__ w1,
-    const float* __restrict__ b1, uint16_t* __restrict__ hid, float* __restrict__ xbase) {
-  const int tid = threadIdx.x;
+    const float* __restrict__ b1, uint16_t* __restrict__ hid, float* __restrict__ xbase,
+    uint64_t mk, uint64_t mb, uint64_t mb1) {
+  const int tid = threadIdx.x, lane = tid & 63;
   const int h4 = H / 4;
   // this thread's columns: w1 rows are 5 bf16 (10 bytes), so the 4 columns of
   // a group are 40 contiguous bytes
@@ -52,32 +53,48 @@ __global__ __launch_bounds__(256) void node_build_kernel(
     const float4 b = ((const float4*)b1)[c4];
     bv[g][0] = b.x; bv[g][1] = b.y; bv[g][2] = b.z; bv[g][3] = b.w;
   }
-  // the block's tokens (clamped; the ones past M are computed, not stored)
+  // The block's tokens (clamped; the ones past M are computed, not stored).
+  // Lane u works out token u's indices and features (slot and rank by the
+  // exact multiply-shift division, M < 2^31), then every lane takes them by
+  // readlane: the per-token work is done once per wave, not once per lane.
   int64_t tk[TPB];
   uint2 ev[TPB][CG], sv[TPB][CG], rv[TPB][CG];
   float4 pv[TPB][CG];
   float f[TPB][5];
-#pragma unroll
-  for (int u = 0; u < TPB; ++u) {
-    const int64_t t = min((int64_t)blockIdx.x * TPB + u, M - 1);
-    tk[u] = t;
-    int64_t row = t / K;             // (block, slot)
-    const int j = (int)(t - row * K);
+  int tok_l, s_l, j_l, row_l;
+  float fl[5];
+  {
+    const uint32_t t = (uint32_t)min((int64_t)blockIdx.x * TPB + min(lane, TPB - 1), M - 1);
+    uint32_t row = div_by(t, mk);   // (block, slot)
+    const int j = (int)(t - row * (uint32_t)K);
     if (PAPER) {                     // lattice row (n, s - 1) -> top-K row (n, s)
-      const int64_t n = row / (B - 1);
-      row = n * B + 1 + (row - n * (B - 1));
+      const uint32_t n = div_by(row, mb1);
+      row = n * (uint32_t)B + 1 + (row - n * (uint32_t)(B - 1));
     }
-    const int s = (int)(row % B);
-    const int64_t ti = row * K + j;
-    int64_t tok = PAPER ? 0 : topk_idx[ti];
+    const int s = (int)(row - div_by(row, mb) * (uint32_t)B);
+    const int64_t ti = (int64_t)row * K + j;
+    int tok = PAPER ? 0 : topk_idx[ti];
     if (tok < 0 || tok >= V) tok = 0;  // ids come from the top-K stage; never read outside E
     const float lp = topk_logp[ti];
-    const float lp0 = topk_logp[row * K];
-    f[u][0] = lp;
-    f[u][1] = expf(lp);
-    f[u][2] = __fsub_rn(lp, lp0);
-    f[u][3] = K > 1 ? __fdiv_rn((float)j, (float)(K - 1)) : 0.f;
-    f[u][4] = j == 0 ? 1.f : 0.f;
+    const float lp0 = topk_logp[(int64_t)row * K];
+    fl[0] = lp;
+    fl[1] = expf(lp);
+    fl[2] = __fsub_rn(lp, lp0);
+    fl[3] = K > 1 ? __fdiv_rn((float)j, (float)(K - 1)) : 0.f;
+    fl[4] = j == 0 ? 1.f : 0.f;
+    tok_l = tok;
+    s_l = s;
+    j_l = j;
+    row_l = (int)row;
+  }
+#pragma unroll
+  for (int u = 0; u < TPB; ++u) {
+    tk[u] = min((int64_t)blockIdx.x * TPB + u, M - 1);
+    const int64_t tok = readlane_i(tok_l, u);
+    const int s = readlane_i(s_l, u), j = readlane_i(j_l, u);
+    const int64_t row = readlane_i(row_l, u);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) f[u][i] = readlane_f(fl[i], u);
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
       if (!WX) break;
@@ -132,20 +149,22 @@ hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, in
   const int64_t M = (int64_t)N * (paper ? B - 1 : B) * K;
   if (M <= 0) return hipSuccess;
   if (paper && !xbase) return hipErrorInvalidValue;
+  if (M >= ((int64_t)1 << 31) || K > 64 || B > 64) return hipErrorInvalidValue;
+  const uint64_t mk = div_magic(K), mb = div_magic(B), mb1 = div_magic(B > 1 ? B - 1 : 1);
 #define LL_NB(CG, TPB, grid)                                                                     \
   do {                                                                                         \
     if (paper)                                                                                 \
       hipLaunchKernelGGL((node_build_kernel<CG, TPB, true>), grid, dim3(256), 0, stream,      \
                          topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1, conf_b1,   \
-                         hid, xbase);                                                          \
+                         hid, xbase, mk, mb, mb1);                                             \
     else if (xbase)                                                                            \
       hipLaunchKernelGGL((node_build_kernel<CG, TPB, false>), grid, dim3(256), 0, stream,     \
                          topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1, conf_b1,   \
-                         hid, xbase);                                                          \
+                         hid, xbase, mk, mb, mb1);                                             \
     else                                                                                       \
       hipLaunchKernelGGL((node_build_kernel<CG, TPB, false, false>), grid, dim3(256), 0,      \
                          stream, topk_idx, topk_logp, M, B, K, H, V, E, ph, S, R, conf_w1,    \
-                         conf_b1, hid, xbase);                                                 \
+                         conf_b1, hid, xbase, mk, mb, mb1);                                    \
   } while (0)
   // few tokens: one per block (more blocks in flight); many: eight per block
   // (four for the widest rows, to bound the registers)

@@ -373,9 +373,10 @@ int enqueue_rerank(const void* logits, int B, int V, int K, const lilicorr_param
     });
   }
   // a5: pair scores, a6: the commit (one fused kernel: B * K <= 512 keeps the
-  // block's cosines within the kernel's LDS budget). Wide vectors: the pair
-  // products first, in d_e slices over many waves (into the heads buffer,
-  // which the heads are done with), then the walk adds the slices.
+  // block's cosines within the kernel's LDS budget). Vectors of 256 or more:
+  // the pair products first, in 256-wide d_e slices over many waves (into
+  // the heads buffer, which the heads are done with), then the walk adds the
+  // slices.
   LL_TRY(mark(LILICORR_STAGE_SCORES_WALK, false));
   const uint32_t walk_reads = WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP);
   if (de >= kPairSliceMinDe) {

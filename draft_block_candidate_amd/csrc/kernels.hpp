@@ -159,7 +159,9 @@ hipError_t launch_scores_walk(const uint16_t* outv, const uint16_t* inv, const f
 
 // Pair cosines of wide vectors in 256-wide slices of d_e: part holds
 // pair_slice_count(d_e) arrays [N, B-1, K, K] of partial sums.
-constexpr int kPairSliceMinDe = 512;
+// From d_e = 256 the rerank path forms the cosines this way (one wave per
+// pair and slice instead of one workgroup per block).
+constexpr int kPairSliceMinDe = 256;
 inline int pair_slice_count(int d_e) { return (d_e + 255) / 256; }
 hipError_t launch_pair_slices(const uint16_t* outv, const uint16_t* inv, int N, int B, int K,
                               int d_e, float* part, hipStream_t stream);

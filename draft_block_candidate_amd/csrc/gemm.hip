@@ -176,21 +176,30 @@ constexpr int waitcnt_vm(int v) { return (v & 15) | ((v >> 4) << 14) | 0x70 | 0x
 // Residual epilogue whose residual is the node build's table sum (NodeSource)
 constexpr int EPI_NODE = 4;
 
+// Token id of row m, clamped into E (the ids come from the top-K stage; a
+// row never reads outside the table).
+__device__ __forceinline__ int node_token(const NodeSource& nd, uint32_t m) {
+  const int64_t tok = nd.tok[m];
+  return tok < 0 || tok >= nd.V ? 0 : (int)tok;
+}
+
 // ((E[tok] + S[s]) + R[j]) of row m, columns n .. n + 3 (float32, the order
 // the node is written in); N is the row length of the tables.
-__device__ __forceinline__ float4 node_resid4(const NodeSource& nd, uint32_t m, int64_t n, int N) {
+__device__ __forceinline__ float4 node_sum4(const NodeSource& nd, uint32_t m, int tok, int64_t n, int N) {
   const uint32_t q = div_by(m, nd.magic_k);
   const int j = (int)(m - q * (uint32_t)nd.K);
   const int s = (int)(q - div_by(q, nd.magic_b) * (uint32_t)nd.B);
-  int64_t tok = nd.tok[m];
-  if (tok < 0 || tok >= nd.V) tok = 0;   // ids come from the top-K stage; never read outside E
-  const uint2 e = *(const uint2*)(nd.E + tok * N + n);
+  const uint2 e = *(const uint2*)(nd.E + (int64_t)tok * N + n);
   const uint2 sv = *(const uint2*)(nd.S + (int64_t)s * N + n);
   const uint2 rv = *(const uint2*)(nd.R + (int64_t)j * N + n);
   auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
   auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
   return make_float4((lo(e.x) + lo(sv.x)) + lo(rv.x), (hi(e.x) + hi(sv.x)) + hi(rv.x),
                      (lo(e.y) + lo(sv.y)) + lo(rv.y), (hi(e.y) + hi(sv.y)) + hi(rv.y));
+}
+
+__device__ __forceinline__ float4 node_resid4(const NodeSource& nd, uint32_t m, int64_t n, int N) {
+  return node_sum4(nd, m, node_token(nd, m), n, N);
 }
 
 template <int BM, int BN, int EPI, int NW = 4>
@@ -350,7 +359,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
   // slice i is staged and stored (double-buffered), so the reads overlap.
   // The node-table residual (three row gathers and the index arithmetic per
   // row) does not fit twice in the register budget: it is loaded per slice,
-  // before the slice is staged, so the staging overlaps its reads.
+  // before the slice is staged, so the staging overlaps its reads, and only
+  // its token ids are read ahead.
   constexpr int U = 32 * CPRW / 64;
   constexpr int RB = EPI == EPI_NODE ? 1 : 2;
   float4 rbuf[RB][RES ? U : 1];
@@ -361,12 +371,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
         const int64_t m = m0 + wm * WM + i * 32 + (lane + 64 * u) / CPRW;
         r[u] = *(const float4*)(resid + min(m, (int64_t)M - 1) * N + nc);
       }
-    } else if constexpr (EPI == EPI_NODE) {
+    }
+  };
+  // The node-table residual's token ids (the first of its two dependent
+  // gathers) are read one slice ahead; the E, S and R rows at use.
+  int tbuf[EPI == EPI_NODE ? U : 1];
+  auto load_tok = [&](int i) __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_NODE) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t m = m0 + wm * WM + i * 32 + (lane + 64 * u) / CPRW;
-        r[u] = node_resid4(node, (uint32_t)min(m, (int64_t)M - 1), nc, N);
-      }
+      for (int u = 0; u < U; ++u)
+        tbuf[u] = node_token(node, (uint32_t)min(m0 + wm * WM + i * 32 + (lane + 64 * u) / CPRW, (int64_t)M - 1));
+    }
+  };
+  auto load_node = [&](int i, float4 (&r)[RES ? U : 1]) __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_NODE) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        r[u] = node_sum4(node, (uint32_t)min(m0 + wm * WM + i * 32 + (lane + 64 * u) / CPRW, (int64_t)M - 1),
+                         tbuf[u], nc, N);
     }
   };
   // Whole tiles (the wave-uniform common case) store with no predicate at
@@ -377,12 +399,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(BM * BN
   auto slices = [&](auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     if constexpr (RB == 2) load_resid(0, rbuf[0]);
+    if constexpr (EPI == EPI_NODE) load_tok(0);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       if constexpr (RB == 2) {
         if (i + 1 < MT) load_resid(i + 1, rbuf[(i + 1) & 1]);
       } else {
-        load_resid(i, rbuf[0]);
+        load_node(i, rbuf[0]);
+        if (i + 1 < MT) load_tok(i + 1);
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j)

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 // independent MFMA chains, exact row max, P~ = bf16(exp(s - max)),
 // O^T = V^T P~^T with V^T fragments read by ds_read_b64_tr_b16, O / l. K and V
 // are read from HBM once per (block, head).
-template <int TMAX, int DH, int NW, bool K4>
+template <int TMAX, int DH, int NW, int KM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
                                                             int K, int H,
                                                             const float* __restrict__ dist,
@@ -290,16 +290,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);
       __builtin_amdgcn_sched_barrier(0);   // keep each k-step's reads with it
     }
-    // Bias, same-slot term and mask. With K a multiple of 4 (K4) a lane's
-    // four keys of a tile share one slot: one slot computation, one
-    // bias-table read and one same-slot test per tile and lane. Otherwise per
-    // element, with the bias-table reads unconditional on a clamped slot (a
-    // read under a per-element branch is waited for inside it) and issued
-    // together in a region of their own. Both compute fl32(fma(acc, scale,
-    // bias)), then + Same in its own rounding on same-slot pairs.
+    // Bias, same-slot term and mask (KM is 16 or 4 when K is a multiple of
+    // it, else 0). With K a multiple of 4 a lane's four keys of a tile share one slot:
+    // one slot computation, one bias-table read and one same-slot test per
+    // tile and lane. Otherwise per element, with the bias-table reads
+    // unconditional on a clamped slot (a read under a per-element branch is
+    // waited for inside it) and issued together in a region of their own.
+    // All compute fl32(fma(acc, scale, bias)), then + Same in its own
+    // rounding on same-slot pairs (adding 0 elsewhere changes nothing).
     float s[KT][4];
     float mx = -INFINITY;
-    if constexpr (K4) {
+    if constexpr (KM == 16) {
+      // K a multiple of 16: a 16-key tile and the 16-query tile each lie in
+      // one slot and T is a multiple of 16, so the slots, the bias, the mask
+      // and the same-slot test are wave-uniform per tile (scalar registers
+      // and branches), leaving fma(acc, scale, bias) and the running max per
+      // score, plus the Same add on the K / 16 same-slot tiles
+      const int sq = __builtin_amdgcn_readfirstlane(slot_q);
+      const float* __restrict__ dist_h = dist + h * 127;
+      // the tiles' bias entries, read together (slot distances are within
+      // +-63, so the clamped key's entry is always inside the table)
+      float bt[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+        bt[kt] = dist_h[(int)(((unsigned)min(kt * 16, T - 1) * kmul) >> 16) - sq + 63];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int key0 = kt * 16;
+        const int sk = (int)(((unsigned)min(key0, T - 1) * kmul) >> 16);
+        const float b = key0 < T ? bt[kt] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kt][i] = acc[kt][i] * scale + b;
+        if (sk == sq) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[kt][i] += same_h;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
+      }
+    } else if constexpr (KM == 4) {
       // an opaque per-tile copy of the lane's key offset: the per-key masks
       // are recomputed per query tile instead of hoisted out of the tile
       // loop (a mask register pair per strip element, spilled)
@@ -479,6 +508,7 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
   const float scale = 1.0f / __fsqrt_rn((float)DH);
   // slot of a token: (t * kmul) >> 16 equals t / K for t < 1024 and K <= 64
   const unsigned kmul = (65536u + K - 1) / K;
+  const float* __restrict__ dist_h = dist + h * 127;
   const int ntile = (T + 15) / 16;
   for (int r0 = 0; r0 < ntile; r0 += 2 * NW) {
     const int qta = r0 + wave, qtb = r0 + NW + wave;
@@ -523,18 +553,28 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
         // so a tile is all inside the lattice or all past it: one table read
         // per tile and query tile, the mask a bias of -inf (fma(a, s, -inf) is
         // -inf for finite a) and the same-slot term one add
+        // (slots, bias and the same-slot tests are wave-uniform: scalar)
+        const int sqa = __builtin_amdgcn_readfirstlane(slot_qa), sqb = __builtin_amdgcn_readfirstlane(slot_qb);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int key0 = (kt0 + j) * 16 + zb;   // zb == 0, opaque
+          const int key0 = (kt0 + j) * 16;
           const int st = (int)(((unsigned)min(key0, T - 1) * kmul) >> 16);
           const bool in = key0 < T;
-          const float ba = in ? bias_tab[st - slot_qa + 63] : -INFINITY;
-          const float bb = in ? bias_tab[st - slot_qb + 63] : -INFINITY;
-          const float sa = st == slot_qa ? same_h : 0.f, sb = st == slot_qb ? same_h : 0.f;
+          const float ta = dist_h[st - sqa + 63], tb = dist_h[st - sqb + 63];   // clamped key: in the table
+          const float ba = in ? ta : -INFINITY;
+          const float bb = in ? tb : -INFINITY;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            va[j][i] = (aa[j][i] * scale + ba) + sa;
-            vb[j][i] = (ab[j][i] * scale + bb) + sb;
+            va[j][i] = aa[j][i] * scale + ba;
+            vb[j][i] = ab[j][i] * scale + bb;
+          }
+          if (st == sqa) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) va[j][i] += same_h;
+          }
+          if (st == sqb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vb[j][i] += same_h;
           }
         }
       } else {
@@ -561,7 +601,41 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
     if (oka) {
 #pragma unroll 4
       for (int kt0 = 0; kt0 < KT; kt0 += 2) {
-        if (kt0 * 16 < T) {
+        if (kt0 * 16 >= T) continue;
+        if (K % 16 == 0) {
+          // fl(fl(a s + bias) + Same) does not decrease with a, and bias and
+          // Same are one per 16-key tile here: the tile's largest score is
+          // that of its largest product
+          f32x4_t aa[2], ab[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            aa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ab[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const u32x4_t kf = *(const u32x4_t*)(&lb[cat(kt0 * 16 + j * 16 + c, ks * 4 + g)]);
+              aa[j] = mfma16(kf, qfa[ks], aa[j]);
+              ab[j] = mfma16(kf, qfb[ks], ab[j]);
+            }
+          const int sqa = __builtin_amdgcn_readfirstlane(slot_qa), sqb = __builtin_amdgcn_readfirstlane(slot_qb);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int key0 = (kt0 + j) * 16;
+            const int st = (int)(((unsigned)min(key0, T - 1) * kmul) >> 16);
+            const bool in = key0 < T;
+            const float da = dist_h[st - sqa + 63], db = dist_h[st - sqb + 63];   // clamped key: in the table
+            const float ba = in ? da : -INFINITY;
+            const float bb = in ? db : -INFINITY;
+            const float sa = st == sqa ? same_h : 0.f, sb = st == sqb ? same_h : 0.f;
+            const float ta = fmaxf(fmaxf(aa[j][0], aa[j][1]), fmaxf(aa[j][2], aa[j][3]));
+            const float tb = fmaxf(fmaxf(ab[j][0], ab[j][1]), fmaxf(ab[j][2], ab[j][3]));
+            mxa = fmaxf(mxa, (ta * scale + ba) + sa);
+            mxb = fmaxf(mxb, (tb * scale + bb) + sb);
+          }
+        } else {
           float va[2][4], vb[2][4];
           scores2(kt0, kt0 * 16, va, vb);
 #pragma unroll
@@ -666,11 +740,14 @@ hipError_t launch_res(int dh, const uint16_t* qkv, int N, int B, int K, int H, i
   const dim3 grid((unsigned)heads, (unsigned)N, TMAX <= 128 && ntile > NW ? 2u : 1u);
 #define LL_RES(DH)                                                                              \
   do {                                                                                        \
-    if ((K & 3) == 0)                                                                         \
-      hipLaunchKernelGGL((attention_res_kernel<TMAX, DH, NW, true>), grid, dim3(64 * NW), 0,   \
+    if ((K & 15) == 0)                                                                        \
+      hipLaunchKernelGGL((attention_res_kernel<TMAX, DH, NW, 16>), grid, dim3(64 * NW), 0,     \
+                         stream, qkv, B, K, H, dist, same, out);                              \
+    else if ((K & 3) == 0)                                                                    \
+      hipLaunchKernelGGL((attention_res_kernel<TMAX, DH, NW, 4>), grid, dim3(64 * NW), 0,      \
                          stream, qkv, B, K, H, dist, same, out);                              \
     else                                                                                      \
-      hipLaunchKernelGGL((attention_res_kernel<TMAX, DH, NW, false>), grid, dim3(64 * NW), 0,  \
+      hipLaunchKernelGGL((attention_res_kernel<TMAX, DH, NW, 0>), grid, dim3(64 * NW), 0,      \
                          stream, qkv, B, K, H, dist, same, out);                              \
   } while (0)
   if (dh == 32) LL_RES(32);

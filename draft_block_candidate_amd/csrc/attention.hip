@@ -443,7 +443,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // query's exact row max. Pass 2 stages K and V of one half of the keys at a
 // time (256 each) and, chunk of 32 keys by chunk, recomputes the identical
 // scores, forms P~ = bf16(exp(s - max)) and accumulates O^T = V^T P~^T at once,
-// so P~ lives for one chunk only. V^T fragments are read by ds_read_b64_tr_b16:
+// so P~ lives for one chunk only. With K a multiple of 16 the first round's
+// pass 1 also takes the second round's tiles, so K is staged whole once per
+// block, and the first half of each pass 2 that follows a pass 1 reuses the K
+// half still in LDS (staged bytes per block 768 -> 576 KiB at T = 512).
+// V^T fragments are read by ds_read_b64_tr_b16:
 // within each 16-lane group, source lane s addresses key k0 + s/4, columns
 // 4 (s % 4) ..+3 of a 16-column d tile, and output lane i receives keys
 // k0 .. k0 + 3 of column i, which is the MFMA A-operand layout. K and V rows
@@ -510,7 +514,13 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
   const unsigned kmul = (65536u + K - 1) / K;
   const float* __restrict__ dist_h = dist + h * 127;
   const int ntile = (T + 15) / 16;
+  // With K a multiple of 16 and a second round, round 0's pass 1 also takes
+  // round 1's query tiles (K is then staged whole once per block), and their
+  // maxima wait here.
+  const bool ahead = K % 16 == 0 && ntile > 2 * NW;
+  float mxc_s = -INFINITY, mxd_s = -INFINITY;
   for (int r0 = 0; r0 < ntile; r0 += 2 * NW) {
+    const bool p1 = !(ahead && r0 > 0);   // this round runs pass 1
     const int qta = r0 + wave, qtb = r0 + NW + wave;
     const bool oka = qta < ntile, okb = qtb < ntile;
     const int qa = qta * 16 + c, qb = qtb * 16 + c;
@@ -527,10 +537,12 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
     int zb = 0;
     asm volatile("" : "+v"(zb));
     const uint16_t* lb = buf + zb;
-    __syncthreads();   // previous round done with buf
-    stage_half(1, 0, 0);
-    stage_half(1, 1, 1);
-    __syncthreads();
+    if (p1) {
+      __syncthreads();   // previous round done with buf
+      stage_half(1, 0, 0);
+      stage_half(1, 1, 1);
+      __syncthreads();
+    }
     // Scores of key tiles kt0, kt0 + 1 (LDS rows from lr0) for both query
     // tiles, masked and biased; each K fragment read feeds two MFMAs.
     auto scores2 = [&](int kt0, int lr0, float (&va)[2][4], float (&vb)[2][4]) __attribute__((always_inline)) {
@@ -598,7 +610,68 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
     };
     // pass 1: the exact row maxima
     float mxa = -INFINITY, mxb = -INFINITY;
-    if (oka) {
+    if (!p1) {
+      mxa = mxc_s;
+      mxb = mxd_s;
+    } else if (ahead) {
+      // round 0 with round 1's tiles qta + 2 NW, qtb + 2 NW alongside: every
+      // K fragment read feeds four MFMAs; raw-product maxima per tile as below
+      const int qcc = min(qa + 32 * NW, T - 1), qcd = min(qb + 32 * NW, T - 1);
+      const int sqa = __builtin_amdgcn_readfirstlane(slot_qa), sqb = __builtin_amdgcn_readfirstlane(slot_qb);
+      const int sqc = __builtin_amdgcn_readfirstlane(qcc / K), sqd = __builtin_amdgcn_readfirstlane(qcd / K);
+      u32x4_t qfc[KS], qfd[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qfc[ks] = *(const u32x4_t*)(blk + (int64_t)qcc * H3 + h * DH + ks * 32 + 8 * g);
+        qfd[ks] = *(const u32x4_t*)(blk + (int64_t)qcd * H3 + h * DH + ks * 32 + 8 * g);
+      }
+      float mxc = -INFINITY, mxd = -INFINITY;
+#pragma unroll 2
+      for (int kt0 = 0; kt0 < KT; kt0 += 2) {
+        if (kt0 * 16 >= T) continue;
+        f32x4_t a4[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) a4[t][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const u32x4_t kf = *(const u32x4_t*)(&lb[cat(kt0 * 16 + j * 16 + c, ks * 4 + g)]);
+            a4[0][j] = mfma16(kf, qfa[ks], a4[0][j]);
+            a4[1][j] = mfma16(kf, qfb[ks], a4[1][j]);
+            a4[2][j] = mfma16(kf, qfc[ks], a4[2][j]);
+            a4[3][j] = mfma16(kf, qfd[ks], a4[3][j]);
+          }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int key0 = (kt0 + j) * 16;
+          const int st = (int)(((unsigned)min(key0, T - 1) * kmul) >> 16);
+          const bool in = key0 < T;
+          const int sq[4] = {sqa, sqb, sqc, sqd};
+          float* const mx[4] = {&mxa, &mxb, &mxc, &mxd};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float dv = dist_h[st - sq[t] + 63];   // clamped key: in the table
+            const float b = in ? dv : -INFINITY;
+            const float sm = st == sq[t] ? same_h : 0.f;
+            const float tm = fmaxf(fmaxf(a4[t][j][0], a4[t][j][1]), fmaxf(a4[t][j][2], a4[t][j][3]));
+            *mx[t] = fmaxf(*mx[t], (tm * scale + b) + sm);
+          }
+        }
+      }
+      mxa = fmaxf(mxa, __shfl_xor(mxa, 16, 64));
+      mxa = fmaxf(mxa, __shfl_xor(mxa, 32, 64));
+      mxb = fmaxf(mxb, __shfl_xor(mxb, 16, 64));
+      mxb = fmaxf(mxb, __shfl_xor(mxb, 32, 64));
+      mxc = fmaxf(mxc, __shfl_xor(mxc, 16, 64));
+      mxc = fmaxf(mxc, __shfl_xor(mxc, 32, 64));
+      mxd = fmaxf(mxd, __shfl_xor(mxd, 16, 64));
+      mxd = fmaxf(mxd, __shfl_xor(mxd, 32, 64));
+      mxc_s = mxc;
+      mxd_s = mxd;
+    } else if (oka) {
 #pragma unroll 4
       for (int kt0 = 0; kt0 < KT; kt0 += 2) {
         if (kt0 * 16 >= T) continue;
@@ -663,7 +736,8 @@ __global__ __launch_bounds__(512) void attention_big_kernel(const uint16_t* __re
     for (int kh = 0; kh < 2; ++kh) {
       if (256 * kh >= T) break;
       __syncthreads();   // every wave is done with the previous contents
-      stage_half(1, kh, 0);
+      // after this round's pass 1 the first K half is still in rows 0..255
+      if (kh > 0 || !p1) stage_half(1, kh, 0);
       stage_half(2, kh, 1);
       __syncthreads();
       if (!oka) continue;

@@ -85,6 +85,7 @@ def main():
     args = parse()
     if args.summarize_kernels:
         summarize_kernels(args.summarize_kernels)
+        summarize_stage_kernels(args.summarize_kernels)
         return
     if args.summarize_counters:
         summarize_counters(args)
@@ -497,7 +498,7 @@ def split_step_stages(names):
             lin += 1
         elif any(k in n for k in _GEMM_TAIL):
             out.append(_LINEAR_ORDER[lin - 1])
-        elif "scores_walk" in n or "pair_scores" in n or "greedy_walk" in n:
+        elif "scores_walk" in n or "pair_scores" in n or "pair_slices" in n or "greedy_walk" in n:
             out.append("scores_walk")
         else:
             out.append(None)
@@ -757,6 +758,63 @@ def summarize_kernels(d):
             print(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                   f"{float(r['Percentage']):.2f} |")
+
+
+def summarize_stage_kernels(d):
+    """Per-stage kernel time per step from a rocprofv3 kernel trace (lattice head).
+
+    Each step's dispatches (top-K through the walk) are split into stages by
+    kernel role; a stage's duration is the sum of its kernels' durations in
+    that step, averaged over every step of the run. Steps whose linear launches
+    do not match the lattice head's sequence are left out."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return
+    with open(files[0]) as f:
+        rows = sorted(((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                       for r in csv.DictReader(f)), key=lambda t: t[0])
+    names = [n for _, n, _ in rows]
+    per, kern, steps = {}, {}, 0
+    i = 0
+    while i < len(rows):
+        if "topk_partial" not in names[i]:
+            i += 1
+            continue
+        j = i
+        while j < len(rows) and not ("scores_walk" in names[j] or "greedy_walk" in names[j]):
+            j += 1
+        if j >= len(rows):
+            break
+        seq = rows[i:j + 1]
+        if sum(any(k in n for k in _GEMM_MAIN) for _, n, _ in seq) != len(_LINEAR_ORDER):
+            i = j + 1
+            continue
+        step = {}
+        for (_, n, ns), st in zip(seq, split_step_stages([n for _, n, _ in seq])):
+            if st is None:
+                continue
+            step[st] = step.get(st, 0) + ns
+            m = re.search(r"(\w+)(?:<|\()", n)
+            kern.setdefault(st, [])
+            short = m.group(1) if m else n[:40]
+            if short not in kern[st]:
+                kern[st].append(short)
+        for st, ns in step.items():
+            per.setdefault(st, []).append(ns)
+        steps += 1
+        i = j + 1
+    if not steps:
+        return
+    print(f"\nPer stage, from the kernel trace ({steps} steps of the run): the sum of the stage's kernel")
+    print("durations in a step, averaged over the steps.\n")
+    print("| stage | kernels | mean us per step | min us |")
+    print("|---|---|---|---|")
+    for st in sorted(per, key=lambda k: -sum(per[k]) / len(per[k])):
+        v = per[st]
+        print(f"| {st} | {' + '.join(kern[st])} | {sum(v) / len(v) / 1e3:.2f} | {min(v) / 1e3:.2f} |")
 
 
 def csrc_sha256():

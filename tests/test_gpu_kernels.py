@@ -168,7 +168,11 @@ def test_rmsnorm(L, M, H):
                                             (1, 16, 32, 16, 128), (3, 5, 3, 2, 64), (1, 1, 1, 1, 32),
                                             (2, 7, 9, 4, 32), (1, 64, 8, 2, 64), (2, 25, 8, 4, 64),
                                             (3, 10, 13, 2, 128), (2, 20, 15, 2, 32), (1, 17, 16, 4, 128),
-                                            (2, 33, 9, 2, 64)])
+                                            (2, 33, 9, 2, 64),
+                                            # K a multiple of 16 (wave-uniform slots) at each d_h, both
+                                            # kernels; two-pass with a part-full second round
+                                            (1, 8, 16, 2, 64), (1, 12, 16, 4, 32), (1, 12, 8, 2, 64),
+                                            (1, 9, 32, 4, 64), (2, 24, 16, 2, 32)])
 def test_lattice_attention(L, N, B, K, heads, dh):
     rng = np.random.default_rng(N * 1000 + B * 10 + K)
     H = heads * dh

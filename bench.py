@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=float, default=0.0,
                     help="after the run, stream this many MiB through a plain copy kernel three "
                          "times (the known-size reference for HBM byte counters)")
+    ap.add_argument("--no-clock-probe", dest="clock_probe", action="store_false",
+                    help="skip the shader-clock readings taken after the run (untimed): the "
+                         "library's diagnostic probe on a second stream, with the GPU idle, beside "
+                         "full steps, and beside the dominant linear's kernel run on its own")
     ap.add_argument("--summarize-kernels", metavar="KT_DIR",
                     help="no GPU: turn a rocprofv3 --kernel-trace --stats run of this script into a "
                          "markdown table of kernel durations")
@@ -302,6 +306,12 @@ def main():
         result["topk_sharded"] = bench_topk_shards(L, w, bufs[0].view(N * B, V), args.topk_shards,
                                                    args.rotate_mib, max(args.steps, 20), stream)
 
+    if args.clock_probe:
+        try:
+            result["clock"] = clock_probe(L, w, run, ms, roof, stream)
+        except Exception as e:   # a diagnostic: its failure must not cost the bench line
+            result["clock"] = {"error": f"{type(e).__name__}: {e}"}
+
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
@@ -312,6 +322,94 @@ def main():
         for _ in range(3):
             torch.neg(src, out=dst)    # reads and writes n * 4 bytes once each
         torch.cuda.synchronize()
+
+
+# gfx950's dense bf16 MFMA peak is quoted at its 2.4 GHz peak shader clock
+PEAK_CLOCK_GHZ = 2.4
+
+
+def clock_probe(L, w, run, ms_step, roof, stream):
+    """Shader clock (GHz) read by the library's probe (one wave on a second
+    stream comparing the shader-clock counter with the 100 MHz constant
+    counter over a window) with the GPU idle, beside full steps on the main
+    stream, and beside repeated calls of the dominant linear (random operands
+    of its shape). `concurrent` says whether the probe's window ended before
+    the work beside it did, i.e. whether the reading is of that work."""
+    import torch
+    side = torch.cuda.Stream()
+    out = torch.zeros(2, dtype=torch.int64, device=stream.device)
+
+    def read():
+        v = out.cpu().tolist()
+        return 0.1 * v[1] / max(v[0], 1)
+
+    def beside(work, total_ms):
+        # the probe covers the middle of the work's span
+        window_us = max(1, int(total_ms * 1e3 * 0.6))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e_probe = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(int(total_ms * 1e3 * 0.2 * 1000))   # start inside the work
+            L.clock_probe(out, window_us, side)
+            e_probe.record(side)
+        work()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return read(), e0.elapsed_time(e_probe) < e0.elapsed_time(e1)
+
+    torch.cuda.synchronize()
+    L.clock_probe(out, 2000, stream)
+    torch.cuda.synchronize()
+    res = {"idle_GHz": round(read(), 3)}
+    n_steps = max(4, int(math.ceil(20.0 / max(ms_step, 1e-3))))
+    def steps():
+        for _ in range(n_steps):
+            run()
+
+    ghz, ok = beside(steps, n_steps * ms_step)
+    res["steps_GHz"] = round(ghz, 3)
+    res["steps_concurrent"] = ok
+    dom = roof["kernel"]
+    shapes = {"linear_ffn1": (w.hidden, w.ffn, L.EPI_SILU_BF16), "linear_ffn2": (w.ffn, w.hidden, L.EPI_RESID_F32),
+              "linear_qkv": (w.hidden, 3 * w.hidden, L.EPI_BF16), "linear_o": (w.hidden, w.hidden, L.EPI_RESID_F32)}
+    key = dom.split(".")[0]
+    if key in shapes and roof["unit"] == "TFLOP/s":
+        kd, n, epi = shapes[key]
+        m = w.num_blocks * w.slots * w.topk
+        g = torch.Generator(device=stream.device).manual_seed(5)
+        A = (torch.randn((m, kd), device=stream.device, generator=g) * 0.5).to(torch.bfloat16)
+        Wt = (torch.randn((n, kd), device=stream.device, generator=g) * 0.03).to(torch.bfloat16)
+        b = torch.zeros(n, dtype=torch.float32, device=stream.device)
+        r = torch.zeros((m, n), dtype=torch.float32, device=stream.device) if epi == L.EPI_RESID_F32 else None
+        wsz = L.lib().lilicorr_linear_workspace_bytes(m, kd, n)
+        wsp = torch.empty(max(wsz, 256), dtype=torch.uint8, device=stream.device)
+        L.linear(A, Wt, b, epi, r, wsp)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        L.linear(A, Wt, b, epi, r, wsp)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        call_ms = t0.elapsed_time(t1)
+        calls = max(4, int(math.ceil(20.0 / max(call_ms, 1e-3))))
+        def linears():
+            for _ in range(calls):
+                L.linear(A, Wt, b, epi, r, wsp)
+
+        ghz, ok = beside(linears, calls * call_ms)
+        peak = PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ
+        res.update({"dominant_kernel": dom, "dominant_kernel_GHz": round(ghz, 3),
+                    "dominant_concurrent": ok,
+                    "mfma_peak_at_that_clock_TFLOP_s": round(peak, 1),
+                    "roofline_frac_at_that_clock": round(roof["achieved"] / peak, 4)})
+    res["method"] = ("lilicorr_clock_probe: shader-clock cycles (s_memtime) per 100 MHz constant-counter "
+                     "tick (s_memrealtime) over a window inside the work; peaks scale with clock from "
+                     f"{PEAK_BF16_TFLOPS:.0f} TFLOP/s at {PEAK_CLOCK_GHZ} GHz")
+    return res
 
 
 def bench_topk_shards(L, w, logits2d, G, rotate_mib, reps, stream):

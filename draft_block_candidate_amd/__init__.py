@@ -96,6 +96,7 @@ _SIGNATURES = {
     "lilicorr_linear": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "lilicorr_rmsnorm": (_c_int, [_vp, _c_int, _c_int, _vp, _f, _vp, _vp]),
     "lilicorr_lattice_attention": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "lilicorr_clock_probe": (_c_int, [_vp, ctypes.c_int64, _vp]),
 }
 
 _lib = None
@@ -558,6 +559,17 @@ def rmsnorm(x, gamma, eps: float = 1e-6):
     out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
     _check(lib().lilicorr_rmsnorm(_ptr(x), M, H, _ptr(gamma), eps, _ptr(out), _stream()), "rmsnorm")
     return out
+
+
+def clock_probe(out, window_us: int, stream=None):
+    """Diagnostic (not part of the path): launch the shader-clock probe on
+    `stream` (default: the current one). `out` is a device int64 tensor [2];
+    once the probe has run, 0.1 * out[1] / out[0] is the shader clock in GHz
+    over its window (see lilicorr_clock_probe)."""
+    torch = _torch()
+    _require(out, "out", torch.int64, (2,))
+    s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    _check(lib().lilicorr_clock_probe(_ptr(out), int(window_us), ctypes.c_void_p(s)), "clock_probe")
 
 
 def lattice_attention(qkv, N: int, B: int, K: int, hidden: int, heads: int, dist, same):

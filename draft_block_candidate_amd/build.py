@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "liblilicorr.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "weights_init.hip", "topk_lse.hip", "node_build.hip", "gemm.hip", "norms.hip",
-           "attention.hip", "walk.hip", "paper_head.hip"]
+           "attention.hip", "walk.hip", "paper_head.hip", "diag.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gfx950",

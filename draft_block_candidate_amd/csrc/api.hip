@@ -740,4 +740,12 @@ int lilicorr_lattice_attention(const uint16_t* qkv, int N, int B, int K, int hid
       launch_attention(qkv, N, B, K, hidden, heads, dist, same, out, (hipStream_t)stream));
 }
 
+int lilicorr_clock_probe(uint64_t* out, int64_t window_us, void* stream) {
+  if (!out || ((uintptr_t)out & 7)) return LILICORR_EINVAL;
+  if (window_us < 1 || window_us > 1000000) return LILICORR_EINVAL;
+  const int dc = check_device();
+  if (dc != LILICORR_OK) return dc;
+  return hip_status(launch_clock_probe(out, (uint64_t)window_us * 100u, (hipStream_t)stream));
+}
+
 }  // extern "C"

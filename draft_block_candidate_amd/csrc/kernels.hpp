@@ -170,4 +170,9 @@ hipError_t launch_greedy_walk(const int32_t* topk_idx, const float* topk_logp, c
                               int N, int B, int K, float alpha, int use_logp, int32_t* out_tokens,
                               float* score, float* gap, hipStream_t stream);
 
+// Diagnostic: shader-clock probe. out[0] = ticks of the 100 MHz constant
+// counter over a window of window_ticks of them, out[1] = shader-clock cycles
+// (s_memtime) over the same window; out is device uint64 [2].
+hipError_t launch_clock_probe(uint64_t* out, uint64_t window_ticks, hipStream_t stream);
+
 }  // namespace ll

@@ -373,6 +373,18 @@ LILICORR_API int lilicorr_rmsnorm(const float* x, int M, int H, const float* gam
 LILICORR_API int lilicorr_lattice_attention(const uint16_t* qkv, int N, int B, int K, int hidden, int heads,
                                const float* dist, const float* same, uint16_t* out, void* stream);
 
+/* Diagnostic, not part of the reranking path: the shader clock of the GPU
+ * over a window. One wave reads the 100 MHz constant counter and the shader
+ * clock counter at the start and the end of a window of window_us
+ * microseconds (1 .. 1,000,000) of the constant counter, sleeping in between,
+ * and writes out[0] = constant-counter ticks elapsed, out[1] = shader-clock
+ * cycles elapsed (clock in GHz = 0.1 * out[1] / out[0]). Launched on its own
+ * stream beside a running launch, it reads the clock that launch runs at.
+ * out: device uint64 [2], 8-byte aligned, written by the probe. Errors: EINVAL
+ * (null or misaligned out, window out of range), EUNSUPPORTED (not gfx950),
+ * EHIP. */
+LILICORR_API int lilicorr_clock_probe(uint64_t* out, int64_t window_us, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

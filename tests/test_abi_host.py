@@ -50,6 +50,16 @@ def test_bindings_cover_the_header():
     assert set(declared_functions()) == set(L._SIGNATURES)
 
 
+def test_clock_probe_rejects_bad_arguments():
+    """The diagnostic clock probe checks its arguments before touching a device."""
+    lib = L.lib()
+    fake = ctypes.c_void_p(4096)
+    assert lib.lilicorr_clock_probe(None, 100, None) == L.EINVAL
+    assert lib.lilicorr_clock_probe(ctypes.c_void_p(4097), 100, None) == L.EINVAL   # misaligned
+    assert lib.lilicorr_clock_probe(fake, 0, None) == L.EINVAL
+    assert lib.lilicorr_clock_probe(fake, 1000001, None) == L.EINVAL
+
+
 def test_strerror_codes():
     assert L.strerror(0) == "ok"
     assert "workspace" in L.strerror(L.EWORKSPACE)

@@ -695,6 +695,101 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
     }
 }
 
+// The same pass for 65..128 rows on 64 x 32 tiles: workgroup (x, y) takes
+// columns 32 x .. 32 x + 31 of rows 64 y .. 64 y + 63. Each workgroup then
+// streams 64 rows of A and 32 of W (192 KiB at K = 1,024) instead of all 128
+// rows of A and 16 of W (288 KiB), with as many workgroups; the per-CU rate
+// of these streams, not the L2 total, bounds the pass. Wave w multiplies rows
+// 16 w .. 16 w + 15 against both 16-column halves. The two row halves of a
+// column tile are tiles_n apart in launch order, which is a multiple of 8 for
+// the encoder's widths, so they run on one XCD and W is read from HBM once.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_skinny2_kernel(const uint16_t* __restrict__ A,
+                                                           const uint16_t* __restrict__ W, int M,
+                                                           int N, int Kd,
+                                                           const float* __restrict__ bias,
+                                                           const float* resid, void* out) {
+  constexpr int BM = 64, BN = 32, BK = 128, NS = 4;
+  constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
+  constexpr int NI = STAGE / 512;              // 1 KiB DMA instructions per stage (24)
+  constexpr int PER = NI / 4;                  // per wave (6)
+  static_assert(NI % 4 == 0, "stage split");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
+
+  // Instruction j of a stage fills elements [512 j, 512 j + 512): rows
+  // 4 j .. 4 j + 3 of the stage (A rows first, then the W rows); lane i
+  // fills row 4 j + i / 16, slot i % 16, which holds chunk (i % 16) ^ (row & 15).
+  const uint16_t* src[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int j = wave * PER + u, row = 4 * j + lane / 16;
+    const int chunk = (lane % 16) ^ (row & 15);
+    src[u] = row < BM ? A + min(m0 + row, (int64_t)M - 1) * Kd + chunk * 8
+                      : W + min(n0 + (row - BM), (int64_t)N - 1) * Kd + chunk * 8;
+  }
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    uint16_t* st = smem + (kt % NS) * STAGE;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      __builtin_amdgcn_global_load_lds((const void*)(src[u] + kt * BK),
+                                       (__attribute__((address_space(3))) void*)(st + (wave * PER + u) * 512),
+                                       16, 0, 0);
+  };
+  auto at = [](int row, int chunk) { return row * BK + ((chunk ^ (row & 15)) << 3); };
+
+  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const int nk = Kd / BK;
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER));
+    else if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    if (kt + 3 < nk) issue(kt + 3);
+    const uint16_t* st = smem + (kt % NS) * STAGE;
+    u32x4_t fa[BK / 32], fw[BK / 32][2];
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      fa[ks] = *(const u32x4_t*)(&st[at(wave * 16 + c, ks * 4 + g)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fw[ks][j] = *(const u32x4_t*)(&st[at(BM + j * 16 + c, ks * 4 + g)]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] = mfma16(fa[ks], fw[ks][j], acc[j]);
+  }
+  // acc[j][q]: row m0 + 16 w + 4 g + q, column n0 + 16 j + c
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + 16 * j + c, nc = min(n, (int64_t)N - 1);
+    const float bv = bias ? bias[nc] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t m = m0 + wave * 16 + 4 * g + q;
+      const bool ok = m < M && n < N;
+      const float y = acc[j][q] + bv;
+      const int64_t o = m * N + n;
+      if constexpr (EPI == EPI_F32) {
+        if (ok) ((float*)out)[o] = y;
+      } else if constexpr (EPI == EPI_BF16) {
+        if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(y);
+      } else if constexpr (EPI == EPI_SILU_BF16) {
+        if (ok) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16(silu(y));
+      } else {
+        const float r = resid[min(m, (int64_t)M - 1) * N + nc];
+        if (ok) ((float*)out)[o] = r + y;
+      }
+    }
+  }
+}
+
 // Partial sums are added in the fixed order s = 0..S-1; S is a compile-time
 // constant so the S loads of a group are issued together.
 template <int S>
@@ -960,6 +1055,28 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
 hipError_t launch_skinny(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
                          const float* bias, int epi, const float* resid, void* out,
                          hipStream_t stream) {
+  if (M > 64) {
+    const dim3 grid2((unsigned)((N + 31) / 32), (unsigned)((M + 63) / 64));
+    switch (epi) {
+      case EPI_F32:
+        hipLaunchKernelGGL((gemm_skinny2_kernel<EPI_F32>), grid2, dim3(256), 0, stream, A, W, M, N, Kd,
+                           bias, resid, out);
+        break;
+      case EPI_BF16:
+        hipLaunchKernelGGL((gemm_skinny2_kernel<EPI_BF16>), grid2, dim3(256), 0, stream, A, W, M, N, Kd,
+                           bias, resid, out);
+        break;
+      case EPI_SILU_BF16:
+        hipLaunchKernelGGL((gemm_skinny2_kernel<EPI_SILU_BF16>), grid2, dim3(256), 0, stream, A, W, M,
+                           N, Kd, bias, resid, out);
+        break;
+      default:
+        hipLaunchKernelGGL((gemm_skinny2_kernel<EPI_RESID_F32>), grid2, dim3(256), 0, stream, A, W, M,
+                           N, Kd, bias, resid, out);
+        break;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((N + 15) / 16));
   switch (epi) {
     case EPI_F32:

@@ -121,7 +121,8 @@ def _rand_bf16(rng, shape, scale=1.0):
                                     (2100, 512, 200), (4096, 1024, 4096), (128, 4096, 1024),
                                     (8192, 1024, 4096), (33000, 256, 1000), (6000, 192, 640),
                                     (64, 1024, 256), (50, 512, 1000), (128, 768, 4096), (7, 256, 48), (1, 4096, 1024), (1, 1024, 1024), (16, 4096, 1024),
-                                    (4096, 512, 3072), (5000, 256, 2500), (4096, 4096, 1024), (3840, 3072, 1024)])
+                                    (4096, 512, 3072), (5000, 256, 2500), (4096, 4096, 1024), (3840, 3072, 1024),
+                                    (100, 1024, 3000), (65, 2048, 2080), (120, 1024, 4096)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
 def test_linear(L, M, Kd, N, epi):
     import torch

@@ -233,3 +233,13 @@ def test_binding_rejects_mismatched_tensors(L):
         L.rerank(to_device(synth.make_logits(pw)), pw.topk, device_weights(pw), pw.alpha, pw.use_logp,
                  hidden=f32(1, pw.slots, pw.drafter_hidden),
                  target=torch.zeros((1, pw.target_hidden), dtype=torch.bfloat16, device="cuda"))
+
+
+@pytest.mark.parametrize("de,K,N", [(128, 11, 280), (256, 7, 220)])
+def test_fused_heads_ragged_rows(L, de, K, N):
+    # Enough lattice rows for 256 x 256 tiles, with every out or in vector
+    # inside one tile: the unit normalisation runs in the heads linear's
+    # epilogue. The row counts (49,280 and 24,640) leave a part-full last tile.
+    w = synth.Workload(f"heads_de{de}_k{K}", N, 16, 2048, K, 1024, 8, 4096, de, "f32", "normal")
+    host = np.random.default_rng(de + K).standard_normal((N, 16, w.vocab), dtype=np.float32)
+    run_case(L, w, 0, spread(N, 4), host=host)

@@ -173,7 +173,14 @@ def test_rmsnorm(L, M, H):
                                             # K a multiple of 16 (wave-uniform slots) at each d_h, both
                                             # kernels; two-pass with a part-full second round
                                             (1, 8, 16, 2, 64), (1, 12, 16, 4, 32), (1, 12, 8, 2, 64),
-                                            (1, 9, 32, 4, 64), (2, 24, 16, 2, 32)])
+                                            (1, 9, 32, 4, 64), (2, 24, 16, 2, 32),
+                                            # 129-256 tokens at d_h = 128: two workgroups per
+                                            # (head, block) with K and V in turn; part-full tile
+                                            # rounds, K a multiple of 4 but not 16, and a
+                                            # (head, block) count that leaves the last group of
+                                            # eight pairs part-full
+                                            (3, 12, 16, 3, 128), (2, 20, 12, 2, 128), (2, 9, 16, 2, 128),
+                                            (1, 11, 20, 5, 128)])
 def test_lattice_attention(L, N, B, K, heads, dh):
     rng = np.random.default_rng(N * 1000 + B * 10 + K)
     H = heads * dh

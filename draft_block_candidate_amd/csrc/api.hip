@@ -126,16 +126,18 @@ int commit_args_ok(const int32_t* topk_idx, const float* topk_logp, const float*
 
 // Regions of the rerank workspace (rerank_ws_layout), as bits for the audit.
 // outv / inv are split into slot 0's rows and the other slots' rows, which the
-// paper's head writes in separate launches.
+// paper's head writes in separate launches. o_part is the gemm_part memory
+// while it carries the fused attention's per-head output-projection slices to
+// the next launch (gemm_part itself is scratch within one linear's launches).
 enum WsRegion {
   WS_TOPK_PART, WS_TOPK_IDX, WS_TOPK_LOGP, WS_X, WS_HID, WS_U, WS_QKV, WS_ATTN, WS_HEADS, WS_OUTV,
   WS_INV, WS_GEMM_PART, WS_PH, WS_AE, WS_TNORM, WS_TB, WS_APRE, WS_OUTV_SLOT0, WS_INV_SLOT0,
-  WS_REGION_COUNT
+  WS_O_PART, WS_REGION_COUNT
 };
 #define WS_BIT(r) (1u << WS_##r)
 const char* const kWsRegionName[WS_REGION_COUNT] = {
     "topk_part", "topk_idx", "topk_logp", "x", "hid", "u", "qkv", "attn", "heads", "outv",
-    "inv", "gemm_part", "ph", "ae", "tnorm", "tb", "apre", "outv_slot0", "inv_slot0"};
+    "inv", "gemm_part", "ph", "ae", "tnorm", "tb", "apre", "outv_slot0", "inv_slot0", "o_part"};
 
 // Dry run of the launch sequence: each step states the workspace regions it
 // reads and writes; a read of a region that no earlier step wrote fails.
@@ -319,12 +321,23 @@ int enqueue_rerank(const void* logits, int B, int V, int K, const lilicorr_param
     LL_STAGE(LILICORR_STAGE_QKV + s0,
              LL_STEP("linear_qkv", WS_BIT(U), WS_BIT(QKV) | GP,
                      launch_linear(u, Mp, H, Lw.wqkv, 3 * H, Lw.bqkv, plain(EPI_BF16), qkv, gpart, st)));
-    LL_STAGE(LILICORR_STAGE_ATTENTION + s0,
-             LL_STEP("lattice_attention", WS_BIT(QKV), WS_BIT(ATTN),
-                     launch_attention(qkv, N, Bl, K, H, heads, Lw.dist, Lw.same, attn, st)));
-    LL_STAGE(LILICORR_STAGE_O + s0,
-             LL_STEP("linear_o", WS_BIT(ATTN) | WS_BIT(X), WS_BIT(X) | WS_BIT(U) | GP,
-                     launch_linear(attn, Mp, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
+    if (attention_o_fusable(N, Bl, K, H, heads)) {
+      // few rows: the attention launch also forms the output projection's
+      // per-head split-K slices, and the linear is only its ordered reduce
+      LL_STAGE(LILICORR_STAGE_ATTENTION + s0,
+               LL_STEP("lattice_attention_o", WS_BIT(QKV), WS_BIT(O_PART),
+                       launch_attention_o(qkv, N, Bl, K, H, heads, Lw.dist, Lw.same, Lw.wo, gpart, st)));
+      LL_STAGE(LILICORR_STAGE_O + s0,
+               LL_STEP("linear_o_reduce", WS_BIT(O_PART) | WS_BIT(X), WS_BIT(X) | WS_BIT(U),
+                       launch_splitk_reduce(heads, Mp, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
+    } else {
+      LL_STAGE(LILICORR_STAGE_ATTENTION + s0,
+               LL_STEP("lattice_attention", WS_BIT(QKV), WS_BIT(ATTN),
+                       launch_attention(qkv, N, Bl, K, H, heads, Lw.dist, Lw.same, attn, st)));
+      LL_STAGE(LILICORR_STAGE_O + s0,
+               LL_STEP("linear_o", WS_BIT(ATTN) | WS_BIT(X), WS_BIT(X) | WS_BIT(U) | GP,
+                       launch_linear(attn, Mp, H, Lw.wo, H, Lw.bo, resid_norm(Lw.gamma2), x, gpart, st)));
+    }
     LL_STAGE(LILICORR_STAGE_FFN1 + s0,
              LL_STEP("linear_ffn1", WS_BIT(U), WS_BIT(HID) | GP,
                      launch_linear(u, Mp, H, Lw.w1, F, Lw.b1, plain(EPI_SILU_BF16), hid, gpart, st)));

@@ -27,12 +27,25 @@ namespace {
 // independent MFMA chains, exact row max, P~ = bf16(exp(s - max)),
 // O^T = V^T P~^T with V^T fragments read by ds_read_b64_tr_b16, O / l. K and V
 // are read from HBM once per (block, head).
-template <int TMAX, int DH, int NW, int KM>
+//
+// With OPROJ (few rows: T of 65..128, d_h = 128) the kernel also applies the
+// output projection's split-K slice of its head: workgroup z = half + 2 cq
+// takes half `half` of the query tiles and columns 128 cq .. 128 cq + 127 of
+// W_o, staged in LDS with K and V. Each wave multiplies its bf16 output tile
+// (the attention output's rounding point) by that W_o slice over the head's
+// d_h = 128 input columns and writes the fp32 partial
+// part[head][row][column]; the linear's ordered split-K reduce (K slice =
+// head) then adds bias, residual and RMSNorm. The attention output itself is
+// not written.
+template <int TMAX, int DH, int NW, int KM, bool OPROJ = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_res_kernel(const uint16_t* __restrict__ qkv, int B,
                                                             int K, int H,
                                                             const float* __restrict__ dist,
                                                             const float* __restrict__ same,
-                                                            uint16_t* __restrict__ out) {
+                                                            uint16_t* __restrict__ out,
+                                                            const uint16_t* __restrict__ wo = nullptr,
+                                                            float* __restrict__ part = nullptr,
+                                                            int M = 0) {
   constexpr int KT = TMAX / 16;   // 16-key tiles
   constexpr int KS = DH / 32;     // MFMA k-steps over d_h
   constexpr int DT = DH / 16;     // 16-wide d tiles of the output
@@ -41,6 +54,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) uint16_t Ks[TMAX * DH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[TMAX * DH];
   __shared__ float bias_tab[128];
+  static_assert(!OPROJ || (DH == 128 && TMAX == 128), "fused output projection tiling");
+  constexpr int WCOLS = 128;   // W_o columns per workgroup (OPROJ)
+  __shared__ __attribute__((aligned(16))) uint16_t Wos[OPROJ ? WCOLS * DH : 8];
   // K chunk (key, c) lives at chunk c ^ swz(key) of its row. A 16-byte LDS
   // read is served 16 lanes (256 bytes, all 64 banks) at a time, and a K
   // fragment read has those lanes on 16 consecutive keys at one chunk, so the
@@ -65,7 +81,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // The block's query tiles are dealt to the gridDim.z workgroups of this
   // (head, block) and, within one, to its waves: tile qt0 + j * qstep.
-  const int qt0 = blockIdx.z * NW + wave, qstep = NW * gridDim.z;
+  // OPROJ: z = half + 2 cq, the halves deal the tiles.
+  const int zh = OPROJ ? (int)(blockIdx.z & 1) : (int)blockIdx.z;
+  const int qt0 = zh * NW + wave, qstep = NW * (OPROJ ? 2 : (int)gridDim.z);
+  const int64_t wn0 = OPROJ ? (int64_t)(blockIdx.z >> 1) * WCOLS : 0;   // first W_o column
   // Query fragments of this wave's first tile, issued before the staging
   // loads so that their latency overlaps them.
   u32x4_t qf0[KS];
@@ -92,12 +111,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     kr[i] = *(const u32x4_t*)(blk + (int64_t)kk * H3 + H + h * DH + kc * 8);
     vr[i] = *(const u32x4_t*)(blk + (int64_t)kk * H3 + 2 * H + h * DH + kc * 8);
   }
+  // OPROJ: the W_o slice, rows wn0 .. wn0 + 127 (output columns), input
+  // columns h DH .. h DH + DH - 1; 16-byte chunk c of row r at c ^ (r & 15)
+  constexpr int WCH = OPROJ ? WCOLS * CPR / (64 * NW) : 1;   // chunks per thread
+  u32x4_t wr[WCH];
+  if constexpr (OPROJ) {
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int ch = tid + 64 * NW * i;
+      wr[i] = *(const u32x4_t*)(wo + (wn0 + ch / CPR) * (int64_t)H + h * DH + (ch % CPR) * 8);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int ch = tid + 64 * NW * i;
     if (!EXACT && ch >= TOT) break;
     *(u32x4_t*)(&Ks[kat(ch / CPR, ch % CPR)]) = kr[i];
     *(u32x4_t*)(&Vs[cat(ch / CPR, ch % CPR)]) = vr[i];
+  }
+  if constexpr (OPROJ) {
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int ch = tid + 64 * NW * i, r = ch / CPR, cc = ch % CPR;
+      *(u32x4_t*)(&Wos[r * DH + ((cc ^ (r & 15)) << 3)]) = wr[i];
+    }
   }
   __syncthreads();
 
@@ -270,7 +307,39 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);
       __builtin_amdgcn_sched_barrier(0);   // bound the V reads in flight
     }
-    if (q_ok) {
+    if constexpr (OPROJ) {
+      // The tile's output, rounded to bf16 as stored otherwise, is the B
+      // operand of P^T = W_o O^T: for k-step kk (d of 32 kk .. 32 kk + 31)
+      // lane (g, c) holds query c at d = 32 kk + 4 g + 0..3 and
+      // 32 kk + 16 + 4 g + 0..3 (its own accumulator elements), so the W_o
+      // fragment takes the same d at the same k-slots. Output element
+      // (row 4 g + i, column c) is column wn0 + 16 j + 4 g + i of query c.
+      const float inv = 1.0f / lsum;
+      u32x4_t ob[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        ob[kk] = u32x4_t{pack_bf16x2(oacc[2 * kk][0] * inv, oacc[2 * kk][1] * inv),
+                         pack_bf16x2(oacc[2 * kk][2] * inv, oacc[2 * kk][3] * inv),
+                         pack_bf16x2(oacc[2 * kk + 1][0] * inv, oacc[2 * kk + 1][1] * inv),
+                         pack_bf16x2(oacc[2 * kk + 1][2] * inv, oacc[2 * kk + 1][3] * inv)};
+      float* prow = part + ((int64_t)h * M + n * T + q) * (int64_t)H + wn0 + 4 * g;
+#pragma unroll
+      for (int j = 0; j < WCOLS / 16; ++j) {
+        const int r = j * 16 + c;   // W_o row of this lane's A fragment
+        u32x4_t wf[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int c_lo = 4 * kk + (g >> 1), c_hi = c_lo + 2, hw = (g & 1) * 4;
+          const u32x2_t lo = *(const u32x2_t*)(&Wos[r * DH + ((c_lo ^ (r & 15)) << 3) + hw]);
+          const u32x2_t hi2 = *(const u32x2_t*)(&Wos[r * DH + ((c_hi ^ (r & 15)) << 3) + hw]);
+          wf[kk] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
+        }
+        f32x4_t pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) pacc = mfma16(wf[kk], ob[kk], pacc);
+        if (q_ok) *(float4*)(prow + j * 16) = make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
+      }
+    } else if (q_ok) {
       const float inv = 1.0f / lsum;
       uint16_t* orow = out + (n * T + q) * (int64_t)H + h * DH;
 #pragma unroll
@@ -679,6 +748,30 @@ hipError_t launch_res(int dh, const uint16_t* qkv, int N, int B, int K, int H, i
 }
 
 }  // namespace
+
+bool attention_o_fusable(int N, int B, int K, int H, int heads) {
+  const int T = B * K;
+  return heads >= 1 && H == heads * 128 && T > 64 && T <= 128 && (int64_t)N * T < 2048 &&
+         (heads == 2 || heads == 3 || heads == 4 || heads == 6 || heads == 8 || heads == 12 || heads == 16);
+}
+
+hipError_t launch_attention_o(const uint16_t* qkv, int N, int B, int K, int H, int heads,
+                              const float* dist, const float* same, const uint16_t* wo, float* part,
+                              hipStream_t stream) {
+  if (!attention_o_fusable(N, B, K, H, heads)) return hipErrorInvalidValue;
+  const int M = N * B * K;
+  const dim3 grid((unsigned)heads, (unsigned)N, (unsigned)(2 * (H / 128)));
+  if ((K & 15) == 0)
+    hipLaunchKernelGGL((attention_res_kernel<128, 128, 4, 16, true>), grid, dim3(256), 0, stream, qkv, B, K, H,
+                       dist, same, nullptr, wo, part, M);
+  else if ((K & 3) == 0)
+    hipLaunchKernelGGL((attention_res_kernel<128, 128, 4, 4, true>), grid, dim3(256), 0, stream, qkv, B, K, H,
+                       dist, same, nullptr, wo, part, M);
+  else
+    hipLaunchKernelGGL((attention_res_kernel<128, 128, 4, 0, true>), grid, dim3(256), 0, stream, qkv, B, K, H,
+                       dist, same, nullptr, wo, part, M);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const uint16_t* qkv, int N, int B, int K, int H, int heads,
                             const float* dist, const float* same, uint16_t* out,

@@ -1099,6 +1099,20 @@ hipError_t launch_skinny(const uint16_t* A, int M, int Kd, const uint16_t* W, in
   return hipGetLastError();
 }
 
+hipError_t launch_splitk_reduce(int S, int M, int N, const float* bias, const LinearEpilogue& ep,
+                                void* out, const float* part, hipStream_t stream) {
+  switch (S) {
+    case 2: return launch_reduce<2>(M, N, bias, ep, out, part, stream);
+    case 3: return launch_reduce<3>(M, N, bias, ep, out, part, stream);
+    case 4: return launch_reduce<4>(M, N, bias, ep, out, part, stream);
+    case 6: return launch_reduce<6>(M, N, bias, ep, out, part, stream);
+    case 8: return launch_reduce<8>(M, N, bias, ep, out, part, stream);
+    case 12: return launch_reduce<12>(M, N, bias, ep, out, part, stream);
+    case 16: return launch_reduce<16>(M, N, bias, ep, out, part, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 bool uses_skinny(int M, int Kd, int N) {
   return M <= 128 && Kd % 128 == 0 && (N + 15) / 16 >= 128;
 }

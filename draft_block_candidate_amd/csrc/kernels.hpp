@@ -126,6 +126,19 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
 hipError_t launch_rmsnorm(const float* x, int M, int H, const float* gamma, float eps,
                           uint16_t* out, hipStream_t stream);
 
+// Few-row lattices (65..128 tokens, d_h = 128, fewer than 2,048 rows, a head
+// count the split-K reduce is built for): attention and the output
+// projection's per-head split-K slices in one launch. part: [heads][M][H]
+// fp32, M = N B K; the attention output is not written. Reduce with
+// launch_splitk_reduce(heads, ...).
+bool attention_o_fusable(int N, int B, int K, int H, int heads);
+hipError_t launch_attention_o(const uint16_t* qkv, int N, int B, int K, int H, int heads,
+                              const float* dist, const float* same, const uint16_t* wo, float* part,
+                              hipStream_t stream);
+// The split-K reduce of launch_linear for S given slices part[S][M][N] with
+// the epilogue ep (S in {2, 3, 4, 6, 8, 12, 16}).
+hipError_t launch_splitk_reduce(int S, int M, int N, const float* bias, const LinearEpilogue& ep,
+                                void* out, const float* part, hipStream_t stream);
 hipError_t launch_attention(const uint16_t* qkv, int N, int B, int K, int H, int heads,
                             const float* dist, const float* same, uint16_t* out,
                             hipStream_t stream);

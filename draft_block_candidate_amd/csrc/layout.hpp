@@ -268,7 +268,11 @@ inline RerankWs rerank_ws_layout(int N, int B, int V, int K, const lilicorr_dims
   w.inv = take(M * de * 2);
   const bool paper = d.target_hidden > 0;
   const size_t Mp = paper ? (size_t)N * (B - 1) * K : M;   // lattice rows
-  w.gemm_part = take(rerank_gemm_scratch((int)Mp, d, N * B, N) * 4);
+  size_t pf = rerank_gemm_scratch((int)Mp, d, N * B, N);
+  // attention fused with the output projection's per-head K slices
+  if (attention_o_fusable(N, paper ? B - 1 : B, K, (int)H, d.heads) && (size_t)d.heads * Mp * H > pf)
+    pf = (size_t)d.heads * Mp * H;
+  w.gemm_part = take(pf * 4);
   w.ph = w.ae = w.tnorm = w.tb = w.apre = 0;
   if (paper) {
     const size_t Ht = d.target_hidden;

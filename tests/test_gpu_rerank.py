@@ -243,3 +243,16 @@ def test_fused_heads_ragged_rows(L, de, K, N):
     w = synth.Workload(f"heads_de{de}_k{K}", N, 16, 2048, K, 1024, 8, 4096, de, "f32", "normal")
     host = np.random.default_rng(de + K).standard_normal((N, 16, w.vocab), dtype=np.float32)
     run_case(L, w, 0, spread(N, 4), host=host)
+
+
+@pytest.mark.parametrize("N,B,K", [(2, 16, 5), (1, 8, 16), (1, 10, 12)])
+def test_attention_fused_output_projection(L, N, B, K):
+    # Few-row lattices of 65..128 tokens at d_h = 128: the attention launch
+    # also forms the output projection's per-head K slices, which the split-K
+    # reduce sums (K not a multiple of 4, a multiple of 16, of 4). The
+    # one-block workload's encoder and logits recipe, other lattice shapes.
+    import dataclasses
+    base = synth.WORKLOADS["c1_qwen3_8b"]
+    w = dataclasses.replace(base, num_blocks=N, slots=B, topk=K)
+    host = synth.make_logits(w)   # the one-block workload's seed, this lattice's shape
+    run_case(L, dataclasses.replace(w, name=f"c1_b{B}_k{K}"), 0, None, host=host)

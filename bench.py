@@ -302,6 +302,27 @@ def main():
         "wall_s_timed": wall,
     }
 
+    # step-time spread: a separate untimed pass, each step between its own
+    # event pair (the timed region above carries no per-step events, so its
+    # mean is not inflated by them)
+    n_spread = min(args.steps, 100)
+    spread_ev = [(new_event(), new_event()) for _ in range(n_spread)]
+    torch.cuda.synchronize()
+    for i in range(n_spread):
+        spread_ev[i][0].record(stream)
+        run()
+        spread_ev[i][1].record(stream)
+    spread_ev[-1][1].synchronize()
+    st_ms = np.sort(np.array([a.elapsed_time(b) for a, b in spread_ev]))
+    result["step_ms"] = {"median": float(np.median(st_ms)), "p10": float(np.percentile(st_ms, 10)),
+                         "p90": float(np.percentile(st_ms, 90)), "steps": n_spread,
+                         "blocks_per_s_at_median": N / (float(np.median(st_ms)) * 1e-3),
+                         "source": "per-step event pairs in a separate untimed pass after the timed steps"}
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                        "compute_units": props.multi_processor_count,
+                        "memory_GiB": round(props.total_memory / 2**30, 1)}
+
     if args.topk_shards > 0:
         result["topk_sharded"] = bench_topk_shards(L, w, bufs[0].view(N * B, V), args.topk_shards,
                                                    args.rotate_mib, max(args.steps, 20), stream)

@@ -552,14 +552,25 @@ def stage_work(w, sid):
             tables = {"bytes": M * 4 + M * H * 2 + 2 * 64 * H * 2, "flops": 2 * M * H}
             return add(lin(H, H, 2, 4, norm_out=True), tables)
         return add(lin(H, H, 2, 4, resid=True), lin(Ht, H, 2, 4, resid=True, norm_out=True))
+    # few rows with d_h = 128 and 65..128 tokens: the attention launch also
+    # multiplies by W_o (the library's attention_o_fusable), and the O stage is
+    # the residual + RMSNorm reduce
+    fused_o = (H == h * 128 and 64 < T <= 128 and M < 2048 and h in (2, 3, 4, 6, 8, 12, 16))
     if 3 <= sid <= 12:
         j = layer % 5
         if j == 0:
             return lin(H, 3 * H, 2, 2)
         if j == 1:
-            return {"bytes": M * 3 * H * 2 + M * H * 2 + h * 128 * 4,
-                    "flops": 4 * N * h * T * T * (H // h)}
+            att = {"bytes": M * 3 * H * 2 + M * H * 2 + h * 128 * 4,
+                   "flops": 4 * N * h * T * T * (H // h)}
+            if fused_o:
+                # W_o read and the product instead of the bf16 output write
+                att = {"bytes": M * 3 * H * 2 + H * H * 2 + h * 128 * 4,
+                       "flops": att["flops"] + 2 * M * H * H}
+            return att
         if j == 2:
+            if fused_o:
+                return {"bytes": H * 4 + M * H * 4 + M * H * 4 + M * H * 2, "flops": 0}
             return lin(H, H, 2, 4, resid=True, norm_out=True)
         if j == 3:
             return lin(H, F, 2, 2)
@@ -593,7 +604,15 @@ def counter_traffic(workload, stage):
 
 
 # Kernel roles, by name, for splitting a step's dispatch sequence into stages.
-_GEMM_MAIN = ("gemm_kernel", "gemm_part_kernel", "gemm_dma_kernel", "gemm_fullk_kernel", "gemm_skinny_kernel")
+_GEMM_MAIN = ("gemm_kernel", "gemm_part_kernel", "gemm_dma_kernel", "gemm_fullk_kernel", "gemm_skinny_kernel",
+              "gemm_skinny2_kernel")
+
+
+def _fused_attention_o(name):
+    """The attention launch that also forms the output projection's per-head
+    K slices (few rows): its O linear is then only the split-K reduce."""
+    import re
+    return re.search(r"attention_res_kernel<[^>]*true>", name) is not None
 _GEMM_TAIL = ("splitk_", "rmsnorm")
 _LINEAR_ORDER = ["linear_conf_w2"] + [f"{n}.l{l}" for l in range(2)
                                       for n in ("linear_qkv", "linear_o", "linear_ffn1", "linear_ffn2")] \
@@ -612,6 +631,8 @@ def split_step_stages(names):
         elif re.search(r"attention_\w*kernel", n):
             out.append(f"lattice_attention.l{att}")
             att += 1
+            if _fused_attention_o(n):
+                lin += 1   # the launch is also the O linear's product; its reduce follows
         elif any(k in n for k in _GEMM_MAIN):
             out.append(_LINEAR_ORDER[lin])
             lin += 1
@@ -908,7 +929,7 @@ def summarize_stage_kernels(d):
         if j >= len(rows):
             break
         seq = rows[i:j + 1]
-        if sum(any(k in n for k in _GEMM_MAIN) for _, n, _ in seq) != len(_LINEAR_ORDER):
+        if sum(any(k in n for k in _GEMM_MAIN) or _fused_attention_o(n) for _, n, _ in seq) != len(_LINEAR_ORDER):
             i = j + 1
             continue
         step = {}

@@ -512,7 +512,10 @@ __global__ __launch_bounds__(256) void gemm_part_kernel(const uint16_t* __restri
   constexpr int CH_A = BM * CPR, CH_W = BN * CPR;
   constexpr int NCH = (CH_A + CH_W) / 256;
   static_assert((CH_A + CH_W) % 256 == 0, "chunking");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[(BM + BN) * KS];
+  // the A and W slices, later the fp32 tile (row-major, 4-float pad) staged for the stores
+  constexpr int ES = BN + 4;
+  constexpr int SMEM = (BM + BN) * KS > BM * ES * 2 ? (BM + BN) * KS : BM * ES * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
   uint16_t* As = smem;
   uint16_t* Ws = smem + BM * KS;
   auto at = [](int row, int chunk) { return row * KS + ((chunk ^ (row & SWM)) << 3); };
@@ -574,8 +577,6 @@ __global__ __launch_bounds__(256) void gemm_part_kernel(const uint16_t* __restri
 
   // The tile goes out through LDS (row-major, 4-float pad) as 16-byte row
   // stores; N % 4 == 0, so a 4-column chunk is entirely inside or outside.
-  constexpr int ES = BN + 4;
-  static_assert(BM * ES * 4 <= (BM + BN) * KS * 2, "epilogue staging fits");
   __syncthreads();   // every wave is done with the A and W slices
   float* stg = (float*)smem;
 #pragma unroll
@@ -974,11 +975,16 @@ hipError_t launch_tile(const uint16_t* A, int M, int Kd, const uint16_t* W, int 
 
 template <int KS>
 hipError_t launch_part(const uint16_t* A, int M, int Kd, const uint16_t* W, int N, float* part,
-                       int S, int bm, hipStream_t stream) {
+                       int S, int bm, int bn, hipStream_t stream) {
   if (bm == 128) {
     const int tiles_n = (N + 31) / 32;
     const dim3 grid((unsigned)(((M + 127) / 128) * tiles_n), (unsigned)S);
     hipLaunchKernelGGL((gemm_part_kernel<128, 32, KS>), grid, dim3(256), 0, stream, A, W, M, N, Kd,
+                       part, tiles_n);
+  } else if (bn == 64) {
+    const int tiles_n = (N + 63) / 64;
+    const dim3 grid((unsigned)(((M + 63) / 64) * tiles_n), (unsigned)S);
+    hipLaunchKernelGGL((gemm_part_kernel<64, 64, KS>), grid, dim3(256), 0, stream, A, W, M, N, Kd,
                        part, tiles_n);
   } else {
     const int tiles_n = (N + 31) / 32;
@@ -1121,8 +1127,10 @@ GemmPlan plan_linear(int M, int Kd, int N) {
   GemmPlan p{};
   p.split = 1;
   if (M >= 2048 || Kd < 128 || Kd % 64) return p;
-  p.bm = M > 64 ? 128 : 64;
-  p.bn = 32;
+  // 64 x 64 tiles above 64 rows: as many workgroups as 128 x 32 ones, each
+  // staging 128 rows of A and W per K slice instead of 160
+  p.bm = 64;
+  p.bn = M > 64 ? 64 : 32;
   p.tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   // Widest K slice (<= 256, so the slice sits in LDS) that still gives about
   // 256 workgroups; at least two slices.
@@ -1205,9 +1213,9 @@ hipError_t launch_linear(const uint16_t* A, int M, int Kd, const uint16_t* W, in
     return hipSuccess;
   }
   hipError_t e;
-  if (p.ks == 64) e = launch_part<64>(A, M, Kd, W, N, part, p.split, p.bm, stream);
-  else if (p.ks == 128) e = launch_part<128>(A, M, Kd, W, N, part, p.split, p.bm, stream);
-  else e = launch_part<256>(A, M, Kd, W, N, part, p.split, p.bm, stream);
+  if (p.ks == 64) e = launch_part<64>(A, M, Kd, W, N, part, p.split, p.bm, p.bn, stream);
+  else if (p.ks == 128) e = launch_part<128>(A, M, Kd, W, N, part, p.split, p.bm, p.bn, stream);
+  else e = launch_part<256>(A, M, Kd, W, N, part, p.split, p.bm, p.bn, stream);
   if (e != hipSuccess) return e;
   switch (p.split) {
     case 2: return launch_reduce<2>(M, N, bias, ep, out, part, stream);

@@ -247,12 +247,24 @@ int enqueue_rerank(const void* logits, int B, int V, int K, const lilicorr_param
   // every row of the out / in vectors
   const uint32_t VEC_ALL = WS_BIT(OUTV) | WS_BIT(INV) | WS_BIT(OUTV_SLOT0) | WS_BIT(INV_SLOT0);
 
+  // Few-row lattice head with rows split into chunks: the node build merges
+  // the chunk outputs itself (one launch fewer).
+  const int topk_P = topk_chunks_per_row(rows, V);
+  const bool merge_in_node = !paper && linear_takes_node_source(M, H, H) && node_build_merges(N, B, K, topk_P);
   // a1: log-partition + top-K (the chunk partials are scratch of this launch)
-  LL_STAGE(LILICORR_STAGE_TOPK,
-           LL_STEP("topk_lse", 0, WS_BIT(TOPK_PART) | WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP),
-                   launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
-                                   (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms),
-                                   topk_idx, topk_logp, p->dbg_lse, st)));
+  if (merge_in_node) {
+    LL_STAGE(LILICORR_STAGE_TOPK,
+             LL_STEP("topk_chunks", 0, WS_BIT(TOPK_PART),
+                     launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
+                                     (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms),
+                                     topk_idx, topk_logp, p->dbg_lse, st, false)));
+  } else {
+    LL_STAGE(LILICORR_STAGE_TOPK,
+             LL_STEP("topk_lse", 0, WS_BIT(TOPK_PART) | WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP),
+                     launch_topk_lse(logits, rows, V, K, p->logits_dtype, (float*)(tws + TL.part_val),
+                                     (int32_t*)(tws + TL.part_idx), (float*)(tws + TL.part_ms),
+                                     topk_idx, topk_logp, p->dbg_lse, st)));
+  }
   if (!paper && linear_takes_node_source(M, H, H)) {
     // a2: nodes. x = ((E + S) + R) + (W2c . hid + b2c); u = bf16(RMSNorm(x; gamma1 of layer 0)).
     // The table sum ((E + S) + R) is formed by the W2c linear's epilogue from
@@ -270,10 +282,17 @@ int enqueue_rerank(const void* logits, int B, int V, int K, const lilicorr_param
     LinearEpilogue e = resid_norm(W.layer[0].gamma1);
     e.resid = nullptr;
     e.node = &nd;
-    LL_STAGE(LILICORR_STAGE_NODE,
-             LL_STEP("node_build", WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP), WS_BIT(HID),
-                     launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, nullptr, W.S, W.R,
-                                       W.conf_w1, W.conf_b1, hid, nullptr, V, st)));
+    if (merge_in_node)
+      LL_STAGE(LILICORR_STAGE_NODE,
+               LL_STEP("node_build_merge", WS_BIT(TOPK_PART), WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP) | WS_BIT(HID),
+                       launch_node_build_merge((float*)(tws + TL.part_val), (int32_t*)(tws + TL.part_idx),
+                                               (float*)(tws + TL.part_ms), topk_P, topk_idx, topk_logp,
+                                               p->dbg_lse, N, B, K, H, W.conf_w1, W.conf_b1, hid, V, st)));
+    else
+      LL_STAGE(LILICORR_STAGE_NODE,
+               LL_STEP("node_build", WS_BIT(TOPK_IDX) | WS_BIT(TOPK_LOGP), WS_BIT(HID),
+                       launch_node_build(topk_idx, topk_logp, N, B, K, H, W.E, nullptr, W.S, W.R,
+                                         W.conf_w1, W.conf_b1, hid, nullptr, V, st)));
     LL_STAGE(LILICORR_STAGE_CONF_LINEAR,
              LL_STEP("linear_conf_w2", WS_BIT(HID) | WS_BIT(TOPK_IDX), WS_BIT(X) | WS_BIT(U) | GP,
                      launch_linear(hid, M, H, W.conf_w2, H, W.conf_b2, e, x, gpart, st)));

@@ -11,9 +11,11 @@ hipError_t launch_weights_init(void* dst, uint64_t numel, uint64_t key, int kind
 
 // a1: fused log-partition + exact top-K. part_* are scratch of the sizes in
 // topk_ws_layout(); outputs topk_idx/topk_logp [rows, K], lse [rows] (may be null).
+// merge = false with rows split into P > 1 chunks leaves the chunk outputs
+// in part_* for launch_node_build_merge (topk_idx / topk_logp / lse unwritten).
 hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype, float* part_val,
                            int32_t* part_idx, float* part_ms, int32_t* topk_idx, float* topk_logp,
-                           float* lse, hipStream_t stream);
+                           float* lse, hipStream_t stream, bool merge = true);
 
 // a1 over one shard of a split vocabulary: the shard's [rows, V] slice holds
 // ids id_offset .. id_offset + V - 1. Outputs per row the shard's K best
@@ -35,6 +37,16 @@ hipError_t launch_topk_merge_shards(int G, int rows, int K, const float* val, co
 // xbase = (ph[n B + s] + S[s]) + R[j], ph the projected drafter states [N B, H].
 // xbase may be null (lattice head only): then only hid is written and the
 // table sum is left to the next linear's epilogue (NodeSource).
+// Few-row lattice head (N B K < 4096 tokens, rows split into 1 < P <= 64
+// chunks): the node build of the lattice head (hidden activations only) that
+// also merges each token's row from the top-K chunk outputs (part_* as
+// launch_topk_lse(..., merge = false) leaves them) and writes topk_idx,
+// topk_logp and, if given, lse, as the merge kernel would.
+bool node_build_merges(int N, int B, int K, int P);
+hipError_t launch_node_build_merge(const float* part_val, const int32_t* part_idx, const float* part_ms,
+                                   int P, int32_t* topk_idx, float* topk_logp, float* lse, int N, int B,
+                                   int K, int H, const uint16_t* conf_w1, const float* conf_b1,
+                                   uint16_t* hid, int V, hipStream_t stream);
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
                              int H, const uint16_t* E, const float* ph, const uint16_t* S,
                              const uint16_t* R, const uint16_t* conf_w1, const float* conf_b1,

@@ -6,6 +6,7 @@
 // sum; the second layer is an MFMA GEMM whose epilogue adds the table sum.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk_merge.hpp"
 
 namespace ll {
 namespace {
@@ -20,14 +21,59 @@ namespace {
 // target-embedding term is added by a later linear.
 // WX = false (lattice head): only hid is written; the table sum is formed by
 // the next linear's epilogue instead (NodeSource), so E, S and R are not read.
-template <int CG, int TPB, bool PAPER, bool WX = true>
+// MERGE (lattice head, one token per block, vocabulary rows split into P > 1
+// chunks): the block's first wave merges its token's row from the chunk lists
+// and (max, sum) pairs (part_*) itself, as the top-K merge kernel would, and
+// the block writes its token's id and log-prob (and the row's lse from rank
+// 0) to topk_idx / topk_logp, which are outputs here. This takes one launch
+// out of the few-row step; every block of a row repeats the row's merge.
+struct MergeSource {
+  const float* part_val = nullptr;
+  const int32_t* part_idx = nullptr;
+  const float* part_ms = nullptr;
+  int P = 1;
+  float* lse = nullptr;   // optional
+};
+
+template <int CG, int TPB, bool PAPER, bool WX = true, bool MERGE = false>
 __global__ __launch_bounds__(256) void node_build_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_logp, int64_t M, int B,
     int K, int H, int V, const uint16_t* __restrict__ E, const float* __restrict__ ph,
     const uint16_t* __restrict__ S, const uint16_t* __restrict__ R, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, uint16_t* __restrict__ hid, float* __restrict__ xbase,
-    uint64_t mk, uint64_t mb, uint64_t mb1) {
+    uint64_t mk, uint64_t mb, uint64_t mb1, MergeSource ms = MergeSource{}) {
+  static_assert(!MERGE || (TPB == 1 && !PAPER && !WX), "in-block merge: one lattice token per block");
   const int tid = threadIdx.x, lane = tid & 63;
+  // MERGE: the row's chunk entries (at most 64 lists of 64) and the merged
+  // token (its log-prob, the row's top log-prob, its id)
+  __shared__ float msv[MERGE ? 64 * 64 : 1];
+  __shared__ int msi[MERGE ? 64 * 64 : 1];
+  __shared__ float mres[3];
+  if constexpr (MERGE) {
+    const uint32_t t = (uint32_t)min((int64_t)blockIdx.x, M - 1);
+    const uint32_t row = div_by(t, mk);
+    const int j = (int)(t - row * (uint32_t)K);
+    if (tid < 64) {
+      float rv, Mx, Sx;
+      int ri;
+      const float lse = merge_row_lists((int)row, K, ms.P, K, (int64_t)ms.P * K, 1, ms.P, ms.part_val,
+                                        ms.part_idx, ms.part_ms, msv, msi, lane, rv, ri, Mx, Sx);
+      const float lpj = __fsub_rn(readlane_f(rv, j), lse);
+      const float lp0 = __fsub_rn(readlane_f(rv, 0), lse);
+      const int idj = readlane_i(ri, j);
+      if (lane == 0) {
+        if ((int64_t)blockIdx.x < M) {
+          ((int32_t*)topk_idx)[t] = idj;
+          ((float*)topk_logp)[t] = lpj;
+          if (j == 0 && ms.lse) ms.lse[row] = lse;
+        }
+        mres[0] = lpj;
+        mres[1] = lp0;
+        mres[2] = __int_as_float(idj);
+      }
+    }
+    __syncthreads();
+  }
   const int h4 = H / 4;
   // this thread's columns: w1 rows are 5 bf16 (10 bytes), so the 4 columns of
   // a group are 40 contiguous bytes
@@ -73,10 +119,10 @@ __global__ __launch_bounds__(256) void node_build_kernel(
     }
     const int s = (int)(row - div_by(row, mb) * (uint32_t)B);
     const int64_t ti = (int64_t)row * K + j;
-    int tok = PAPER ? 0 : topk_idx[ti];
+    int tok = PAPER ? 0 : (MERGE ? __float_as_int(mres[2]) : topk_idx[ti]);
     if (tok < 0 || tok >= V) tok = 0;  // ids come from the top-K stage; never read outside E
-    const float lp = topk_logp[ti];
-    const float lp0 = topk_logp[(int64_t)row * K];
+    const float lp = MERGE ? mres[0] : topk_logp[ti];
+    const float lp0 = MERGE ? mres[1] : topk_logp[(int64_t)row * K];
     fl[0] = lp;
     fl[1] = expf(lp);
     fl[2] = __fsub_rn(lp, lp0);
@@ -140,6 +186,39 @@ __global__ __launch_bounds__(256) void node_build_kernel(
 }
 
 }  // namespace
+
+bool node_build_merges(int N, int B, int K, int P) {
+  const int64_t M = (int64_t)N * B * K;
+  return P > 1 && P <= 64 && K <= 64 && B <= 64 && M < 4096;
+}
+
+hipError_t launch_node_build_merge(const float* part_val, const int32_t* part_idx, const float* part_ms,
+                                   int P, int32_t* topk_idx, float* topk_logp, float* lse, int N, int B,
+                                   int K, int H, const uint16_t* conf_w1, const float* conf_b1,
+                                   uint16_t* hid, int V, hipStream_t stream) {
+  if (!node_build_merges(N, B, K, P)) return hipErrorInvalidValue;
+  const int64_t M = (int64_t)N * B * K;
+  const uint64_t mk = div_magic(K), mb = div_magic(B), mb1 = div_magic(1);
+  MergeSource ms;
+  ms.part_val = part_val;
+  ms.part_idx = part_idx;
+  ms.part_ms = part_ms;
+  ms.P = P;
+  ms.lse = lse;
+  const dim3 grid((unsigned)M);
+#define LL_NBM(CG)                                                                                  \
+  hipLaunchKernelGGL((node_build_kernel<CG, 1, false, false, true>), grid, dim3(256), 0, stream,    \
+                     topk_idx, topk_logp, M, B, K, H, V, nullptr, nullptr, nullptr, nullptr, conf_w1,  \
+                     conf_b1, hid, nullptr, mk, mb, mb1, ms)
+  if (H <= 1024)
+    LL_NBM(1);
+  else if (H <= 2048)
+    LL_NBM(2);
+  else
+    LL_NBM(4);
+#undef LL_NBM
+  return hipGetLastError();
+}
 
 hipError_t launch_node_build(const int32_t* topk_idx, const float* topk_logp, int N, int B, int K,
                              int H, const uint16_t* E, const float* ph, const uint16_t* S,

@@ -36,20 +36,18 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
+#include "topk_merge.hpp"
 
 namespace ll {
 namespace {
 
-constexpr float kL2E = 1.4426950408889634f;
 // A term exp(x - ref) above 2^23 (x more than ~15.9 above the reference)
 // triggers a rebase of the reference to the group maximum.
 constexpr float kRebase = 8388608.0f;
-constexpr float kMInit = -1e30f;
 // The top-K gate compares exp(x - ref) with exp(threshold - ref) scaled down
 // by this factor, so that rounding of the exponential (a few ulp) can only
 // let extra elements through, never drop one.
 constexpr float kGateSlack = 0.99998474f;   // 1 - 2^-16
-constexpr int kInvalid = 0x7fffffff;
 // Buffer descriptor word 3 for raw (untyped) loads on gfx9-family targets.
 constexpr int kBufferWord3 = 0x00020000;
 // Cache-policy operand of a buffer load: non-temporal (streamed once).
@@ -400,40 +398,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   }
 }
 
-// K-step tournament over P sorted lists held in LDS (list p at sv/si + p K,
-// ordered by (value desc, id asc), list p's ids all below list p + 1's):
-// lane k < K receives the k-th best (value, id). Lane p < P walks list p; hp
-// is its read position. Every step is straight-line (selects, a clamped LDS
-// read in every lane).
-__device__ __forceinline__ void tournament(const float* sv, const int* si, int P, int K, int lane,
-                                           float& rv, int& ri) {
-  const bool live = lane < P;
-  const int lb = min(lane, P - 1) * K;
-  float hv = live ? sv[lb] : -INFINITY;
-  int hi = live ? si[lb] : kInvalid;
-  int hp = 0;
-  rv = -INFINITY;
-  ri = kInvalid;
-  const int width = P <= 16 ? 16 : (P <= 32 ? 32 : 64);   // lanes >= P hold -inf
-  for (int k = 0; k < K; ++k) {
-    // Winner by (value desc, id asc): among equal values the lowest lane
-    // holds the lowest id, so a max plus the lowest lane of the ballot
-    // decides it.
-    const float bv = lanes_max(hv, width);
-    const int bl = __ffsll((long long)__ballot(hv == bv)) - 1;
-    const int bi = readlane_i(hi, bl);
-    rv = lane == k ? bv : rv;
-    ri = lane == k ? bi : ri;
-    const bool adv = (lane == bl) & live;
-    hp += adv ? 1 : 0;
-    const float nv = sv[lb + min(hp, K - 1)];
-    const int ni = si[lb + min(hp, K - 1)];
-    const bool more = hp < K;
-    hv = adv ? (more ? nv : -INFINITY) : hv;
-    hi = adv ? (more ? ni : kInvalid) : hi;
-  }
-}
-
 // One wave per row: combine the P chunk lists (tournament) and (max, sum)
 // pairs. The row's P * K partial entries are staged in LDS first, so each of
 // the K tournament steps reads the winner's next entry from LDS. Entry k of
@@ -456,46 +420,10 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(int rows, int K, int P, 
   int* si = (int*)(sm + P * K);         // [P K]
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
-  const int64_t rbase = (int64_t)row * sr;
-  const int n = P * K;
-  // Eight entries per lane per batch, every load issued before the first
-  // is used (indices clamped to the row, duplicates written twice with the
-  // same value), so staging costs one memory round trip per 512 entries.
-  for (int i0 = 0; i0 < n; i0 += 512) {
-    float bv[8];
-    int bi[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = min(i0 + j * 64 + lane, n - 1);
-      int64_t a = rbase + i;         // lists of a row contiguous (sp == K)
-      if (sp != K) {
-        const int p = i / K;
-        a = rbase + p * sp + (i - p * K);
-      }
-      bv[j] = part_val[a];
-      bi[j] = part_idx[a];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = min(i0 + j * 64 + lane, n - 1);
-      sv[i] = bv[j];
-      si[i] = bi[j];
-    }
-  }
-  const int pl = min(lane, P - 1);
-  float m = part_ms[2 * (pl * mp + row * mr)];
-  float s = part_ms[2 * (pl * mp + row * mr) + 1];
-  if (lane >= P) {
-    m = kMInit;
-    s = 0.f;
-  }
-  const float M = wave_max(m);
-  const float S = wave_sum(s * __builtin_amdgcn_exp2f((m - M) * kL2E));
-  const float lse = M + logf(S);
-  __syncthreads();
-  float rv;
+  float rv, M, S;
   int ri;
-  tournament(sv, si, P, K, lane, rv, ri);
+  const float lse = merge_row_lists(row, K, P, sp, sr, mp, mr, part_val, part_idx, part_ms, sv, si, lane,
+                                    rv, ri, M, S);
   if (PARTIAL_OUT) {
     // topk_logp receives the merged values, lse_out the (max, sum) pair
     if (lane < K) {
@@ -539,11 +467,11 @@ hipError_t launch_partial(const void* logits, int rows, int V, int K, int dtype,
 
 hipError_t launch_topk_lse(const void* logits, int rows, int V, int K, int dtype, float* part_val,
                            int32_t* part_idx, float* part_ms, int32_t* topk_idx, float* topk_logp,
-                           float* lse, hipStream_t stream) {
+                           float* lse, hipStream_t stream, bool merge) {
   const int P = topk_chunks_per_row(rows, V);
   hipError_t e = launch_partial(logits, rows, V, K, dtype, P, 0, 1, part_val, part_idx, part_ms,
                                 topk_idx, topk_logp, lse, stream);
-  if (e != hipSuccess || P == 1) return e;
+  if (e != hipSuccess || P == 1 || !merge) return e;
   hipLaunchKernelGGL(topk_merge_kernel<false>, dim3((unsigned)rows), dim3(64), (size_t)P * K * 8,
                      stream, rows, K, P, (int64_t)K, (int64_t)P * K, (int64_t)1, (int64_t)P,
                      part_val, part_idx, part_ms, topk_idx, topk_logp, lse);

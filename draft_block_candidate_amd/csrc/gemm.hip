@@ -830,7 +830,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             const float* resid, void* out) {
   const int64_t MN4 = (int64_t)M * N / 4;
   const float4* part4 = (const float4*)part;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < MN4; q += (int64_t)gridDim.x * 256) {
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < MN4; q += (int64_t)gridDim.x * blockDim.x) {
     float4 v = splitk_sum4<S>(part4, MN4, q);
     const int n = (int)((q * 4) % N);
     if (bias) {
@@ -947,6 +947,61 @@ __global__ __launch_bounds__(256) void splitk_heads_l2norm_kernel(
   }
 }
 
+// The same for wide heads over few rows (N = 2 d_e > 256): one 256-thread
+// workgroup per row, thread t holding the 4-column groups t, t + 256, ...;
+// each half's sum of squares is reduced per wave, then over the four waves in
+// a fixed order (a wave per row left most CUs idle at one block).
+template <int S, int NV>
+__global__ __launch_bounds__(256) void splitk_heads_l2norm_row_kernel(
+    const float* __restrict__ part, int M, int de, const float* __restrict__ bias,
+    uint16_t* __restrict__ outv, uint16_t* __restrict__ inv, int group, int skip) {
+  __shared__ float red[4][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m = blockIdx.x;
+  const int N = 2 * de, n4 = N / 4, h4 = de / 4;
+  const int64_t MN4 = (int64_t)M * n4;
+  const float4* part4 = (const float4*)part;
+  float4 v[NV];
+  float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = tid + 256 * i;
+    const int gc = min(gi, n4 - 1);   // clamped: loads stay unconditional
+    const float4 y = splitk_sum4<S>(part4, MN4, m * n4 + gc);
+    const float4 b = bias ? ((const float4*)bias)[gc] : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = make_float4(y.x + b.x, y.y + b.y, y.z + b.z, y.w + b.w);
+    if (gi >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = tid + 256 * i;
+    const float sq = v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    if (gi < h4) ss0 += sq; else ss1 += sq;
+  }
+  ss0 = wave_sum(ss0);
+  ss1 = wave_sum(ss1);
+  if (lane == 0) {
+    red[wave][0] = ss0;
+    red[wave][1] = ss1;
+  }
+  __syncthreads();
+  const float t0 = ((red[0][0] + red[1][0]) + red[2][0]) + red[3][0];
+  const float t1 = ((red[0][1] + red[1][1]) + red[2][1]) + red[3][1];
+  const float n0 = fmaxf(__fsqrt_rn(t0), 1e-12f);
+  const float n1 = fmaxf(__fsqrt_rn(t1), 1e-12f);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int gi = tid + 256 * i;
+    if (gi < n4) {
+      const bool hi = gi >= h4;
+      const float nr = hi ? n1 : n0;
+      uint16_t* dst = (hi ? inv : outv) + heads_row(m, group, skip) * de + (hi ? gi - h4 : gi) * 4;
+      *(uint2*)dst = make_uint2(pack_bf16x2(__fdiv_rn(v[i].x, nr), __fdiv_rn(v[i].y, nr)),
+                                pack_bf16x2(__fdiv_rn(v[i].z, nr), __fdiv_rn(v[i].w, nr)));
+    }
+  }
+}
+
 template <int BM, int BN>
 hipError_t launch_tile(const uint16_t* A, int M, int Kd, const uint16_t* W, int N,
                        const float* bias, int epi, const float* resid, void* out,
@@ -1019,6 +1074,16 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
     return hipGetLastError();
   }
   if (ep.kind == EPI_F32 && ep.heads_out) {
+    if (N > 256 && N <= 2048 && M < 1024) {
+      // wide vectors, few rows: a workgroup per row
+      if (N <= 1024)
+        hipLaunchKernelGGL((splitk_heads_l2norm_row_kernel<S, 1>), dim3((unsigned)M), dim3(256), 0, stream,
+                           part, M, N / 2, bias, ep.heads_out, ep.heads_in, ep.heads_group, ep.heads_skip);
+      else
+        hipLaunchKernelGGL((splitk_heads_l2norm_row_kernel<S, 2>), dim3((unsigned)M), dim3(256), 0, stream,
+                           part, M, N / 2, bias, ep.heads_out, ep.heads_in, ep.heads_group, ep.heads_skip);
+      return hipGetLastError();
+    }
     if (N <= 256)
       hipLaunchKernelGGL((splitk_heads_l2norm_kernel<S, 1>), dim3(row_blocks), dim3(256), 0, stream,
                          part, M, N / 2, bias, ep.heads_out, ep.heads_in, ep.heads_group,
@@ -1034,22 +1099,26 @@ hipError_t launch_reduce(int M, int N, const float* bias, const LinearEpilogue& 
     return hipGetLastError();
   }
   const int64_t MN4 = (int64_t)M * N / 4;
-  const unsigned blocks = (unsigned)std::min<int64_t>((MN4 + 255) / 256, 4096);
+  // 64-thread workgroups when 256-thread ones would leave most CUs idle (one
+  // output group per thread either way; few rows: the S loads of a group are
+  // the whole per-thread work)
+  const int tpb = (MN4 + 255) / 256 < 256 ? 64 : 256;
+  const unsigned blocks = (unsigned)std::min<int64_t>((MN4 + tpb - 1) / tpb, 4096);
   switch (ep.kind) {
     case EPI_F32:
-      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_F32, S>), dim3(blocks), dim3(256), 0, stream,
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_F32, S>), dim3(blocks), dim3(tpb), 0, stream,
                          part, M, N, bias, ep.resid, out);
       break;
     case EPI_BF16:
-      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_BF16, S>), dim3(blocks), dim3(256), 0, stream,
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_BF16, S>), dim3(blocks), dim3(tpb), 0, stream,
                          part, M, N, bias, ep.resid, out);
       break;
     case EPI_SILU_BF16:
-      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_SILU_BF16, S>), dim3(blocks), dim3(256), 0,
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_SILU_BF16, S>), dim3(blocks), dim3(tpb), 0,
                          stream, part, M, N, bias, ep.resid, out);
       break;
     default:
-      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_RESID_F32, S>), dim3(blocks), dim3(256), 0,
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI_RESID_F32, S>), dim3(blocks), dim3(tpb), 0,
                          stream, part, M, N, bias, ep.resid, out);
       break;
   }

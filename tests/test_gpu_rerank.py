@@ -256,3 +256,18 @@ def test_attention_fused_output_projection(L, N, B, K):
     w = dataclasses.replace(base, num_blocks=N, slots=B, topk=K)
     host = synth.make_logits(w)   # the one-block workload's seed, this lattice's shape
     run_case(L, dataclasses.replace(w, name=f"c1_b{B}_k{K}"), 0, None, host=host)
+
+
+def test_fused_paths_at_their_limits(L):
+    # One block of 4 slots with K = 64 over the full vocabulary: 64 chunk lists
+    # of 64 entries per row, the most the node build's in-block merge stages.
+    import dataclasses
+    base = synth.WORKLOADS["c1_qwen3_8b"]
+    w = dataclasses.replace(base, num_blocks=1, slots=4, topk=64)
+    run_case(L, dataclasses.replace(w, name="c1_b4_k64"), 0, None, host=synth.make_logits(w))
+    # Three heads of d_h = 128 (H = 384) with 96 tokens, the one-block
+    # workload's logits recipe: the attention launch fused with the output
+    # projection, reduced over three per-head slices.
+    w3 = dataclasses.replace(base, num_blocks=2, slots=12, topk=8, hidden=384, heads=3, ffn=1536)
+    host3 = synth.make_logits(w3)
+    run_case(L, dataclasses.replace(w3, name="c1_h384_heads3"), 0, None, host=host3)

@@ -11,8 +11,9 @@
 // query's column: that layout is directly the B operand of O^T = V^T P~^T,
 // the second MFMA product. The row maximum is exact before any exponential
 // (no online rescaling). Kernels: the resident one (K and V of a (head,
-// block) in LDS, up to 256 tokens) and the two-pass one (up to 512 tokens,
-// where K and V do not fit in LDS together).
+// block) in LDS, up to 256 tokens; at few rows it can also apply the output
+// projection's per-head split-K slice) and the two-pass one (up to 512
+// tokens, where K and V do not fit in LDS together).
 #include "common.hpp"
 #include "kernels.hpp"
 

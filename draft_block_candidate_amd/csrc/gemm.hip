@@ -14,9 +14,11 @@
 //    misaligned operands): 128 x 128 tiles over the whole K, double-buffered
 //    in LDS, four waves in a 2 x 2 arrangement of 16 x 16 MFMA tiles;
 //  * few rows (M <= 128) and at least 128 tiles of 16 columns: one DMA-
-//    pipelined pass over K per 16-column tile with the epilogue fused;
+//    pipelined pass over K per 16-column tile (64 x 32 tiles from 65 rows)
+//    with the epilogue fused;
 //  * other few-row shapes (one or a few draft blocks, M = B*K*N of 64..2047):
-//    the GEMM is weight-streaming and latency bound, so K is split S ways.
+//    the GEMM is weight-streaming and latency bound, so K is split S ways
+//    (64 x 64 tiles from 65 rows, 64 x 32 below).
 //    Each workgroup stages its whole A and W K-slice (64..256 wide) in LDS
 //    with every load in flight at once, multiplies, and writes an fp32
 //    partial tile. A second kernel sums the S partials in the fixed order

@@ -25,8 +25,9 @@
 //    lanes' best elements, so it starts at a tight threshold;
 //  * a row split over several chunks is merged by a second kernel (one wave
 //    per row: a K-step tournament over the chunks' sorted lists plus the
-//    log-sum-exp combination of the chunks' (max, sum) pairs); a row that is
-//    one chunk is written directly.
+//    log-sum-exp combination of the chunks' (max, sum) pairs; few-row lattice
+//    heads do this merge inside the node build instead); a row that is one
+//    chunk is written directly.
 // Exactness: the gate can only let extra elements through (its slack covers
 // the rounding of the exponential); every element that reaches the scan is
 // decided on the full (value, id) key, and the top-K of a set under a total

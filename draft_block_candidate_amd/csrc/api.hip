@@ -247,10 +247,10 @@ int enqueue_rerank(const void* logits, int B, int V, int K, const lilicorr_param
   // every row of the out / in vectors
   const uint32_t VEC_ALL = WS_BIT(OUTV) | WS_BIT(INV) | WS_BIT(OUTV_SLOT0) | WS_BIT(INV_SLOT0);
 
-  // Few-row lattice head with rows split into chunks: the node build merges
-  // the chunk outputs itself (one launch fewer).
+  // Lattice head with rows split into chunks (few tokens, or K = 8): the node
+  // build merges the chunk outputs itself (one launch fewer).
   const int topk_P = topk_chunks_per_row(rows, V);
-  const bool merge_in_node = !paper && linear_takes_node_source(M, H, H) && node_build_merges(N, B, K, topk_P);
+  const bool merge_in_node = !paper && linear_takes_node_source(M, H, H) && node_build_merges(N, B, K, H, topk_P);
   // a1: log-partition + top-K (the chunk partials are scratch of this launch)
   if (merge_in_node) {
     LL_STAGE(LILICORR_STAGE_TOPK,

@@ -37,12 +37,12 @@ hipError_t launch_topk_merge_shards(int G, int rows, int K, const float* val, co
 // xbase = (ph[n B + s] + S[s]) + R[j], ph the projected drafter states [N B, H].
 // xbase may be null (lattice head only): then only hid is written and the
 // table sum is left to the next linear's epilogue (NodeSource).
-// Few-row lattice head (N B K < 4096 tokens, rows split into 1 < P <= 64
-// chunks): the node build of the lattice head (hidden activations only) that
+// Lattice head with rows split into 1 < P <= 64 chunks and either fewer than
+// 4,096 tokens or K = 8 (H <= 2048): the node build of the lattice head (hidden activations only) that
 // also merges each token's row from the top-K chunk outputs (part_* as
 // launch_topk_lse(..., merge = false) leaves them) and writes topk_idx,
 // topk_logp and, if given, lse, as the merge kernel would.
-bool node_build_merges(int N, int B, int K, int P);
+bool node_build_merges(int N, int B, int K, int H, int P);
 hipError_t launch_node_build_merge(const float* part_val, const int32_t* part_idx, const float* part_ms,
                                    int P, int32_t* topk_idx, float* topk_logp, float* lse, int N, int B,
                                    int K, int H, const uint16_t* conf_w1, const float* conf_b1,

@@ -42,35 +42,41 @@ __global__ __launch_bounds__(256) void node_build_kernel(
     const uint16_t* __restrict__ S, const uint16_t* __restrict__ R, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, uint16_t* __restrict__ hid, float* __restrict__ xbase,
     uint64_t mk, uint64_t mb, uint64_t mb1, MergeSource ms = MergeSource{}) {
-  static_assert(!MERGE || (TPB == 1 && !PAPER && !WX), "in-block merge: one lattice token per block");
+  static_assert(!MERGE || ((TPB == 1 || TPB == 8) && !PAPER && !WX), "in-block merge: lattice tokens of one row");
   const int tid = threadIdx.x, lane = tid & 63;
   // MERGE: the row's chunk entries (at most 64 lists of 64) and the merged
-  // token (its log-prob, the row's top log-prob, its id)
+  // tokens (log-prob, the row's top log-prob, id). With TPB = 8 the launch
+  // guarantees K % 8 == 0, so a block's eight tokens lie in one row.
   __shared__ float msv[MERGE ? 64 * 64 : 1];
   __shared__ int msi[MERGE ? 64 * 64 : 1];
-  __shared__ float mres[3];
+  __shared__ float mres[TPB][3];
   if constexpr (MERGE) {
-    const uint32_t t = (uint32_t)min((int64_t)blockIdx.x, M - 1);
-    const uint32_t row = div_by(t, mk);
-    const int j = (int)(t - row * (uint32_t)K);
+    const uint32_t t0 = (uint32_t)min((int64_t)blockIdx.x * TPB, M - 1);
+    const uint32_t row = div_by(t0, mk);
+    const int j0 = (int)(t0 - row * (uint32_t)K);
     if (tid < 64) {
       float rv, Mx, Sx;
       int ri;
       const float lse = merge_row_lists((int)row, K, ms.P, K, (int64_t)ms.P * K, 1, ms.P, ms.part_val,
                                         ms.part_idx, ms.part_ms, msv, msi, lane, rv, ri, Mx, Sx);
-      const float lpj = __fsub_rn(readlane_f(rv, j), lse);
       const float lp0 = __fsub_rn(readlane_f(rv, 0), lse);
-      const int idj = readlane_i(ri, j);
-      if (lane == 0) {
-        if ((int64_t)blockIdx.x < M) {
-          ((int32_t*)topk_idx)[t] = idj;
-          ((float*)topk_logp)[t] = lpj;
-          if (j == 0 && ms.lse) ms.lse[row] = lse;
+#pragma unroll
+      for (int u = 0; u < TPB; ++u) {
+        const int j = min(j0 + u, K - 1);
+        const float lpj = __fsub_rn(readlane_f(rv, j), lse);
+        const int idj = readlane_i(ri, j);
+        if (lane == u) {
+          const int64_t t = (int64_t)blockIdx.x * TPB + u;
+          if (t < M) {
+            ((int32_t*)topk_idx)[t] = idj;
+            ((float*)topk_logp)[t] = lpj;
+          }
+          mres[u][0] = lpj;
+          mres[u][1] = lp0;
+          mres[u][2] = __int_as_float(idj);
         }
-        mres[0] = lpj;
-        mres[1] = lp0;
-        mres[2] = __int_as_float(idj);
       }
+      if (lane == 0 && j0 == 0 && ms.lse) ms.lse[row] = lse;
     }
     __syncthreads();
   }
@@ -119,10 +125,11 @@ __global__ __launch_bounds__(256) void node_build_kernel(
     }
     const int s = (int)(row - div_by(row, mb) * (uint32_t)B);
     const int64_t ti = (int64_t)row * K + j;
-    int tok = PAPER ? 0 : (MERGE ? __float_as_int(mres[2]) : topk_idx[ti]);
+    const int mu = min(lane, TPB - 1);   // MERGE: this lane's token of the block
+    int tok = PAPER ? 0 : (MERGE ? __float_as_int(mres[mu][2]) : topk_idx[ti]);
     if (tok < 0 || tok >= V) tok = 0;  // ids come from the top-K stage; never read outside E
-    const float lp = MERGE ? mres[0] : topk_logp[ti];
-    const float lp0 = MERGE ? mres[1] : topk_logp[(int64_t)row * K];
+    const float lp = MERGE ? mres[mu][0] : topk_logp[ti];
+    const float lp0 = MERGE ? mres[mu][1] : topk_logp[(int64_t)row * K];
     fl[0] = lp;
     fl[1] = expf(lp);
     fl[2] = __fsub_rn(lp, lp0);
@@ -187,16 +194,21 @@ __global__ __launch_bounds__(256) void node_build_kernel(
 
 }  // namespace
 
-bool node_build_merges(int N, int B, int K, int P) {
+bool node_build_merges(int N, int B, int K, int H, int P) {
   const int64_t M = (int64_t)N * B * K;
-  return P > 1 && P <= 64 && K <= 64 && B <= 64 && M < 4096;
+  // One token per block below 4,096 tokens; above, eight tokens per block,
+  // which is exactly one row at K = 8. Wider rows would make every block of a
+  // row repeat a longer tournament (K = 32 at the entropy shape: node build
+  // 38 -> 68 us against 8 us saved in the top-K stage).
+  return P > 1 && P <= 64 && K <= 64 && B <= 64 && M < ((int64_t)1 << 31) &&
+         (M < 4096 || (K == 8 && H <= 2048));
 }
 
 hipError_t launch_node_build_merge(const float* part_val, const int32_t* part_idx, const float* part_ms,
                                    int P, int32_t* topk_idx, float* topk_logp, float* lse, int N, int B,
                                    int K, int H, const uint16_t* conf_w1, const float* conf_b1,
                                    uint16_t* hid, int V, hipStream_t stream) {
-  if (!node_build_merges(N, B, K, P)) return hipErrorInvalidValue;
+  if (!node_build_merges(N, B, K, H, P)) return hipErrorInvalidValue;
   const int64_t M = (int64_t)N * B * K;
   const uint64_t mk = div_magic(K), mb = div_magic(B), mb1 = div_magic(1);
   MergeSource ms;
@@ -205,17 +217,27 @@ hipError_t launch_node_build_merge(const float* part_val, const int32_t* part_id
   ms.part_ms = part_ms;
   ms.P = P;
   ms.lse = lse;
-  const dim3 grid((unsigned)M);
-#define LL_NBM(CG)                                                                                  \
-  hipLaunchKernelGGL((node_build_kernel<CG, 1, false, false, true>), grid, dim3(256), 0, stream,    \
+#define LL_NBM(CG, TPB, grid)                                                                       \
+  hipLaunchKernelGGL((node_build_kernel<CG, TPB, false, false, true>), grid, dim3(256), 0, stream,  \
                      topk_idx, topk_logp, M, B, K, H, V, nullptr, nullptr, nullptr, nullptr, conf_w1,  \
                      conf_b1, hid, nullptr, mk, mb, mb1, ms)
-  if (H <= 1024)
-    LL_NBM(1);
-  else if (H <= 2048)
-    LL_NBM(2);
-  else
-    LL_NBM(4);
+  if (M < 4096) {
+    const dim3 grid((unsigned)M);
+    if (H <= 1024)
+      LL_NBM(1, 1, grid);
+    else if (H <= 2048)
+      LL_NBM(2, 1, grid);
+    else
+      LL_NBM(4, 1, grid);
+  } else {   // K % 8 == 0: eight tokens of one row per block
+    const dim3 grid8((unsigned)(M / 8));
+    if (H <= 1024)
+      LL_NBM(1, 8, grid8);
+    else if (H <= 2048)
+      LL_NBM(2, 8, grid8);
+    else
+      return hipErrorInvalidValue;   // the widest rows take four tokens per block
+  }
 #undef LL_NBM
   return hipGetLastError();
 }
